@@ -1,0 +1,13 @@
+"""float64 CPU oracle for the CSA / HCA hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library or its binding.
+"""
+from . import codecs
+from .dsv4 import (softmax_pool, csa_compress, csa_pool_weights, hca_compress,
+                   visible_count, indexer_score, topk_select, core_attention,
+                   window_rows, sparse_mqa, hca_dense)
+
+__all__ = ["codecs", "softmax_pool", "csa_compress", "csa_pool_weights", "hca_compress",
+           "visible_count", "indexer_score", "topk_select", "core_attention",
+           "window_rows", "sparse_mqa", "hca_dense"]

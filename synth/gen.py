@@ -1,0 +1,197 @@
+"""Seeded synthetic inputs for the CSA / HCA hot path.
+
+This module only draws random numbers and casts them to storage formats; it
+holds none of the method's arithmetic.  The HIP library and the float64
+oracle both read the exact bytes produced here.
+
+Draws: N(mean, variance) throughout ("N(0,1/d)" means standard deviation
+d**-0.5; "N(0,0.02)" means standard deviation 0.02**0.5).  Every named stream
+has its own numpy PCG64 generator keyed by (seed, stream id, chunk id), so a
+draw does not depend on the order of other draws or on the thread count.
+Casts: bf16 and OCP E4M3 use torch's CPU conversions; MXFP4 keys (an E8M0
+scale per 32 values, then E2M1 elements) use a nearest-grid quantiser that
+exists here only to prepare inputs.
+
+Query-side tensors (q, q^I, w^I) are drawn directly with the variance that
+the query projections of the pages would give for these weight
+distributions; the projections themselves are outside the six calls.
+"""
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from .configs import (BF16, F32, ROW_BF16, ROW_F32, ROW_FP8_ROPE_BF16, ROW_MXFP4, config)
+
+CHUNK = 1 << 22
+_POOL = ThreadPoolExecutor(max_workers=8)
+
+STREAMS = ["H", "W_kv", "W_ki", "W_hca", "B_kv", "B_ki", "B_hca", "q", "qI", "wI", "q_hca",
+           "sink", "sink_hca", "cache_kv", "cache_ki", "cache_hca", "win_kv", "win_hca", "extra"]
+
+
+def normal(seed, stream, shape, std=1.0):
+    """float32 N(0, std**2) draws of a named stream."""
+    sid = STREAMS.index(stream) if isinstance(stream, str) else int(stream)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+
+    def fill(ch):
+        lo, hi = ch * CHUNK, min(n, (ch + 1) * CHUNK)
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(sid, ch))
+        np.random.Generator(np.random.PCG64(ss)).standard_normal(hi - lo, dtype=np.float32,
+                                                                  out=out[lo:hi])
+    list(_POOL.map(fill, range(max(1, math.ceil(n / CHUNK)))))
+    if std != 1.0:
+        out *= np.float32(std)
+    return out.reshape(shape)
+
+
+# ----------------------------------------------------------------- casts
+
+def to_bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def to_fp8_rope_rows(x):
+    """[..., c] float32 -> [..., (c-64) + 128] bytes: E4M3 dims then bf16 RoPE dims."""
+    c = x.shape[-1]
+    lo = to_e4m3(x[..., :c - 64])
+    hi = to_bf16(x[..., c - 64:]).view(np.uint8).reshape(x.shape[:-1] + (128,))
+    return np.concatenate([lo, hi], axis=-1)
+
+
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+
+def to_mxfp4(x):
+    """[..., c] float32 -> (codes [..., c/2], scales [..., c/32]) by nearest-grid
+    rounding after dividing by 2**(floor(log2 amax) - 2)."""
+    c = x.shape[-1]
+    blk = x.reshape(x.shape[:-1] + (c // 32, 32)).astype(np.float32)
+    amax = np.abs(blk).max(axis=-1)
+    _, e = np.frexp(amax)
+    E = np.where(amax > 0, np.clip(e - 3 + 127, 0, 254), 0)
+    X = np.where(amax > 0, np.ldexp(np.float32(1.0), (E - 127).astype(np.int32)), 1.0).astype(np.float32)
+    y = np.abs(blk) / X[..., None]
+    mag = np.searchsorted(_E2M1_MIDS, y.ravel(), side="left").reshape(y.shape).astype(np.uint8)
+    el = mag | (np.signbit(blk).astype(np.uint8) << 3)
+    el[mag == 0] = 0
+    el = el.reshape(x.shape[:-1] + (c,))
+    codes = (el[..., 0::2] & 0xF) | (el[..., 1::2] << 4)
+    return codes.astype(np.uint8), E.astype(np.uint8)
+
+
+def store(x, layout):
+    """float32 -> stored array of a row layout (bytes for packed layouts)."""
+    if layout == ROW_F32:
+        return np.ascontiguousarray(x, dtype=np.float32), None
+    if layout == ROW_BF16:
+        return to_bf16(x), None
+    if layout == ROW_FP8_ROPE_BF16:
+        return to_fp8_rope_rows(x), None
+    if layout == ROW_MXFP4:
+        return to_mxfp4(x)
+    raise ValueError(layout)
+
+
+def act(x, dtype):
+    return np.ascontiguousarray(x, dtype=np.float32) if dtype == F32 else to_bf16(x)
+
+
+def row_bytes(layout, c):
+    return {ROW_F32: 4 * c, ROW_BF16: 2 * c, ROW_FP8_ROPE_BF16: c + 64, ROW_MXFP4: c // 2}[layout]
+
+
+# ----------------------------------------------------------------- configurations
+
+BIAS_STD = math.sqrt(0.02)
+
+
+def _compressor(seed, stream_w, stream_b, nmat, c, d, bias_rows, dtype):
+    W = act(normal(seed, stream_w, (nmat * c, d), d ** -0.5), dtype)
+    B = normal(seed, stream_b, bias_rows + (c,), BIAS_STD)
+    return W, B
+
+
+def make(cfg_id, **over):
+    """Inputs of configuration cfg_id (1..5) as numpy arrays in stored form.
+    Keyword overrides (e.g. n=...) shrink a configuration for quick tests."""
+    cfg = config(cfg_id)
+    cfg.update(over)
+    s, kind = cfg["seed"], cfg["kind"]
+    dt = cfg["act"]
+    out = dict(cfg=cfg)
+    if kind == "csa_prefill":
+        n, d, c, m, cI = cfg["n"], cfg["d"], cfg["c"], cfg["m"], cfg["cI"]
+        out["H"] = act(normal(s, "H", (n, d)), dt)
+        out["W_kv"], out["B_kv"] = _compressor(s, "W_kv", "B_kv", 4, c, d, (2, m), dt)
+        out["W_ki"], out["B_ki"] = _compressor(s, "W_ki", "B_ki", 4, cI, d, (2, m), dt)
+        out["q"] = act(normal(s, "q", (n, cfg["nh"], c), cfg["q_std"]), dt)
+        out["qI"] = act(normal(s, "qI", (n, cfg["hI"], cI), cfg["q_std"]), dt)
+        out["wI"] = normal(s, "wI", (n, cfg["hI"]))
+        out["sink"] = normal(s, "sink", (cfg["nh"],), BIAS_STD)
+    elif kind == "hca_prefill":
+        n, d, c = cfg["n"], cfg["d"], cfg["c"]
+        out["H"] = act(normal(s, "H", (n, d)), dt)
+        out["W_hca"], out["B_hca"] = _compressor(s, "W_hca", "B_hca", 2, c, d, (cfg["mp"],), dt)
+        out["q"] = act(normal(s, "q", (n, cfg["nh"], c), cfg["q_std"]), dt)
+        out["sink"] = normal(s, "sink", (cfg["nh"],), BIAS_STD)
+    elif kind == "csa_decode":
+        B, c, S = cfg["B"], cfg["c"], cfg["ctx"] // cfg["m"]
+        Sh = cfg["ctx"] // cfg["mp"]
+        nw, p = cfg["n_win"], cfg["ctx"]
+        out["q"] = act(normal(s, "q", (B, 1, cfg["nh"], c), cfg["q_std"]), dt)
+        out["qI"] = act(normal(s, "qI", (B, 1, cfg["hI"], cfg["cI"]), cfg["q_std"]), dt)
+        out["wI"] = normal(s, "wI", (B, 1, cfg["hI"]))
+        out["q_hca"] = act(normal(s, "q_hca", (B, 1, cfg["nh"], c), cfg["q_std"]), dt)
+        out["sink"] = normal(s, "sink", (cfg["nh"],), BIAS_STD)
+        out["sink_hca"] = normal(s, "sink_hca", (cfg["nh"],), BIAS_STD)
+        out["kv_cache"], _ = store(normal(s, "cache_kv", (B, S, c)), cfg["kv_layout"])
+        out["ki_codes"], out["ki_scales"] = store(normal(s, "cache_ki", (B, S, cfg["cI"])),
+                                                  cfg["key_layout"])
+        out["hca_cache"], _ = store(normal(s, "cache_hca", (B, Sh, c)), cfg["kv_layout"])
+        out["kv_win"], _ = store(normal(s, "win_kv", (B, nw, c)), cfg["kv_layout"])
+        out["hca_win"], _ = store(normal(s, "win_hca", (B, nw, c)), cfg["kv_layout"])
+        out["q_pos0"] = np.full(B, p, dtype=np.int64)
+        out["win_pos0"] = np.full(B, p - nw + 1, dtype=np.int64)
+    elif kind == "pair":
+        n, nl, d, c, cI = cfg["n"], cfg["n_left"], cfg["d"], cfg["c"], cfg["cI"]
+        m, mp, nw, P = cfg["m"], cfg["mp"], cfg["n_win"], cfg["ctx"]
+        S0, Sh0 = P // m, P // mp
+        out["H"] = act(normal(s, "H", (nl + n, d)), dt)
+        out["W_kv"], out["B_kv"] = _compressor(s, "W_kv", "B_kv", 4, c, d, (2, m), dt)
+        out["W_ki"], out["B_ki"] = _compressor(s, "W_ki", "B_ki", 4, cI, d, (2, m), dt)
+        out["W_hca"], out["B_hca"] = _compressor(s, "W_hca", "B_hca", 2, c, d, (mp,), dt)
+        out["q"] = act(normal(s, "q", (n, cfg["nh"], c), cfg["q_std"]), dt)
+        out["qI"] = act(normal(s, "qI", (n, cfg["hI"], cI), cfg["q_std"]), dt)
+        out["wI"] = normal(s, "wI", (n, cfg["hI"]))
+        out["q_hca"] = act(normal(s, "q_hca", (n, cfg["nh"], c), cfg["q_std"]), dt)
+        out["sink"] = normal(s, "sink", (cfg["nh"],), BIAS_STD)
+        out["sink_hca"] = normal(s, "sink_hca", (cfg["nh"],), BIAS_STD)
+        rb = row_bytes(cfg["kv_layout"], c)
+        kv = np.zeros((S0 + n // m, rb), np.uint8)
+        kv[:S0], _ = store(normal(s, "cache_kv", (S0, c)), cfg["kv_layout"])
+        kc = np.zeros((S0 + n // m, cI // 2), np.uint8)
+        ks = np.zeros((S0 + n // m, cI // 32), np.uint8)
+        kc[:S0], ks[:S0] = store(normal(s, "cache_ki", (S0, cI)), cfg["key_layout"])
+        hc = np.zeros((Sh0 + n // mp, rb), np.uint8)
+        hc[:Sh0], _ = store(normal(s, "cache_hca", (Sh0, c)), cfg["kv_layout"])
+        wk = np.zeros((nw + n, rb), np.uint8)
+        wk[:nw], _ = store(normal(s, "win_kv", (nw, c)), cfg["kv_layout"])
+        wh = np.zeros((nw + n, rb), np.uint8)
+        wh[:nw], _ = store(normal(s, "win_hca", (nw, c)), cfg["kv_layout"])
+        out.update(kv_cache=kv, ki_codes=kc, ki_scales=ks, hca_cache=hc, kv_win=wk, hca_win=wh)
+        out["S0"], out["Sh0"] = S0, Sh0
+        out["q_pos0"] = np.array([P], dtype=np.int64)
+        out["win_pos0"] = np.array([P - nw], dtype=np.int64)
+    else:
+        raise ValueError(kind)
+    return out

@@ -1,0 +1,417 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix:
+invariants, closed forms, special cases that reduce to a textbook routine
+(torch's scaled_dot_product_attention on the CPU in float64) and pairwise
+brute force on tiny inputs.  CPU only.
+
+Each test names the passage it pins: "digest" is the ai-papers-daily page
+"DeepSeek-V4: Towards Highly Efficient Million-Token Context Intelligence",
+"blog" the jsqmd page "DeepSeek V4大模型算法解析"."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+
+def rnd(seed, *shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def csa_weights(c, d, seed, zscale=1.0):
+    W = rnd(seed, 4 * c, d) / np.sqrt(d)
+    W[2 * c:] *= zscale
+    return W
+
+
+# ======================================================================
+# CSA compressor (digest 模块 B eq 9-12; blog 第一阶段)
+# ======================================================================
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_csa_pool_weights_sum_to_one(m):
+    """blog 第一阶段: the softmax normalises the 2m weights to sum 1."""
+    d, c, n = 16, 8, 8 * m
+    H, W, B = rnd(0, n, d), csa_weights(c, d, 1, zscale=4.0), rnd(2, 2, m, c)
+    for i in range(n // m):
+        Wt = O.csa_pool_weights(H, W, B, m, i)
+        assert Wt.shape == ((2 * m if i else m), c)
+        assert np.allclose(Wt.sum(axis=0), 1.0, atol=1e-14)
+        assert (Wt > 0).all()
+
+
+@pytest.mark.parametrize("m,block0", [(1, 0), (2, 0), (4, 0), (4, 3)])
+def test_csa_constant_kv_pools_to_constant(m, block0):
+    """Constant C^a = C^b = v pools to v for every entry, entry 0 included."""
+    d, c, n = 12, 8, 6 * m
+    n_left = m if block0 else 0
+    H = rnd(3, n_left + n, d)
+    H[:, 0] = 1.0
+    v = rnd(4, c)
+    W = csa_weights(c, d, 5, zscale=3.0)
+    W[:2 * c] = 0.0
+    W[0:c, 0] = v          # C^a = H W_aKV^T = v for every row
+    W[c:2 * c, 0] = v      # C^b = v
+    comp, raw = O.csa_compress(H, W, rnd(6, 2, m, c), m, block0, n_left)
+    assert np.allclose(comp, v[None, :], atol=1e-13)
+    assert np.allclose(raw, v[None, :], atol=1e-13)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_csa_zero_logits_is_mean_of_window_rows(m):
+    """Z = 0, B = 0: every softmax weight is 1/(2m) (1/m for entry 0), so entry
+    i is the mean of C^a rows [m i, m i + m) and C^b rows [m (i-1), m i)
+    (blog 第一阶段 window description)."""
+    d, c, n = 10, 6, 7 * m
+    H = rnd(7, n, d)
+    W = csa_weights(c, d, 8)
+    W[2 * c:] = 0.0
+    comp, raw = O.csa_compress(H, W, np.zeros((2, m, c)), m)
+    Ca, Cb = H @ W[:c].T, H @ W[c:2 * c].T
+    assert np.allclose(raw, Ca)
+    assert np.allclose(comp[0], Ca[0:m].mean(axis=0))
+    for i in range(1, n // m):
+        want = (Ca[m * i:m * i + m].sum(axis=0) + Cb[m * (i - 1):m * i].sum(axis=0)) / (2 * m)
+        assert np.allclose(comp[i], want)
+
+
+def test_csa_contraction_orientation():
+    """H = I, m = 1, Z = B = 0: entry i = (W_aKV[:, i] + W_bKV[:, i-1]) / 2, which
+    fixes C = H W^T with W stored [out, in]."""
+    d = c = 6
+    W = csa_weights(c, d, 9)
+    W[2 * c:] = 0.0
+    comp, _ = O.csa_compress(np.eye(d), W, np.zeros((2, 1, c)), 1)
+    assert np.allclose(comp[0], W[:c, 0])
+    for i in range(1, d):
+        assert np.allclose(comp[i], (W[:c, i] + W[c:2 * c, i - 1]) / 2)
+
+
+@pytest.mark.parametrize("r0", [0, 1, 3])
+def test_csa_bias_selects_row(r0):
+    """A +60 position bias on row r0 of B^a (Z = 0) picks C^a[m i + r0]; on B^b it
+    picks C^b[m (i-1) + r0] for i >= 1 and leaves entry 0 the a-mean."""
+    m, d, c, n = 4, 9, 5, 24
+    H = rnd(10, n, d)
+    W = csa_weights(c, d, 11)
+    W[2 * c:] = 0.0
+    Ca, Cb = H @ W[:c].T, H @ W[c:2 * c].T
+    B = np.zeros((2, m, c))
+    B[0, r0] = 60.0
+    comp, _ = O.csa_compress(H, W, B, m)
+    for i in range(n // m):
+        assert np.allclose(comp[i], Ca[m * i + r0], atol=1e-20 + 1e-12)
+    B = np.zeros((2, m, c))
+    B[1, r0] = 60.0
+    comp, _ = O.csa_compress(H, W, B, m)
+    assert np.allclose(comp[0], Ca[:m].mean(axis=0))
+    for i in range(1, n // m):
+        assert np.allclose(comp[i], Cb[m * (i - 1) + r0], atol=1e-12)
+
+
+def test_csa_logit_shift_invariance():
+    """Adding the same constant to every Z logit of a channel changes nothing."""
+    m, d, c, n = 4, 8, 6, 32
+    H = rnd(12, n, d)
+    H[:, 0] = 1.0
+    W = csa_weights(c, d, 13, zscale=2.0)
+    B = rnd(14, 2, m, c)
+    base, _ = O.csa_compress(H, W, B, m)
+    W2 = W.copy()
+    shift = rnd(15, c) * 5
+    W2[2 * c:3 * c, 0] += shift
+    W2[3 * c:4 * c, 0] += shift
+    comp, _ = O.csa_compress(H, W2, B, m)
+    assert np.allclose(comp, base, atol=1e-12)
+
+
+def test_csa_chunked_equals_whole():
+    """Compressing in two chunks (the second with block0 and m rows of left
+    context) equals one call over the whole sequence (digest 模块 F: cached
+    entries are reused and only incomplete blocks are recomputed)."""
+    m, d, c, n = 4, 8, 5, 40
+    H, W, B = rnd(16, n, d), csa_weights(c, d, 17, 2.0), rnd(18, 2, m, c)
+    whole, raw = O.csa_compress(H, W, B, m)
+    n1 = 16
+    a, ra = O.csa_compress(H[:n1], W, B, m)
+    b, rb = O.csa_compress(H[n1 - m:], W, B, m, block0=n1 // m, n_left=m)
+    assert np.allclose(np.concatenate([a, b]), whole, atol=1e-13)
+    assert np.allclose(np.concatenate([ra, rb]), raw)
+
+
+def test_csa_incomplete_tail_emits_nothing_and_stays_in_hull():
+    m, d, c = 4, 8, 5
+    H, W, B = rnd(19, 22, d), csa_weights(c, d, 20, 3.0), rnd(21, 2, m, c)
+    comp, raw = O.csa_compress(H, W, B, m)
+    assert comp.shape == (5, c) and raw.shape == (22, c)
+    Ca, Cb = H @ W[:c].T, H @ W[c:2 * c].T
+    for i in range(1, 5):
+        rows = np.concatenate([Ca[m * i:m * i + m], Cb[m * (i - 1):m * i]])
+        assert (comp[i] <= rows.max(axis=0) + 1e-12).all()
+        assert (comp[i] >= rows.min(axis=0) - 1e-12).all()
+
+
+def test_csa_b_window_vanishing_reduces_to_non_overlapping_pool():
+    """B^b -> -inf removes the b-window: CSA then equals the non-overlapping HCA
+    pooling with ratio m on (W_aKV, W_aZ, B^a) (digest 模块 C: HCA is CSA without
+    overlap)."""
+    m, d, c, n = 4, 8, 5, 32
+    H, W, B = rnd(22, n, d), csa_weights(c, d, 23, 2.0), rnd(24, 2, m, c)
+    B[1] = -1e4
+    comp, _ = O.csa_compress(H, W, B, m)
+    Wh = np.concatenate([W[:c], W[2 * c:3 * c]])
+    hca, _ = O.hca_compress(H, Wh, B[0], m)
+    assert np.allclose(comp, hca, atol=1e-12)
+
+
+def test_csa_missing_left_context_raises():
+    with pytest.raises(ValueError):
+        O.csa_compress(rnd(0, 8, 4), rnd(1, 8, 4), np.zeros((2, 4, 2)), 4, block0=2, n_left=0)
+
+
+# ======================================================================
+# HCA compressor (digest 模块 C eq 20-23)
+# ======================================================================
+
+def test_hca_closed_forms():
+    mp, d, c, n = 8, 10, 6, 40
+    H = rnd(25, n, d)
+    W = rnd(26, 2 * c, d)
+    W[c:] = 0.0
+    comp, raw = O.hca_compress(H, W, np.zeros((mp, c)), mp)
+    C = H @ W[:c].T
+    assert comp.shape == (5, c)
+    for i in range(5):
+        assert np.allclose(comp[i], C[mp * i:mp * (i + 1)].mean(axis=0))   # mean pooling
+    B = np.zeros((mp, c))
+    B[5] = 60.0
+    comp, _ = O.hca_compress(H, W, B, mp)
+    for i in range(5):
+        assert np.allclose(comp[i], C[mp * i + 5], atol=1e-12)
+    # constant KV pools to the constant
+    H[:, 0] = 1.0
+    W2 = rnd(27, 2 * c, d)
+    W2[:c] = 0
+    W2[:c, 0] = np.arange(c)
+    comp, _ = O.hca_compress(H, W2, rnd(28, mp, c), mp)
+    assert np.allclose(comp, np.arange(c)[None, :])
+
+
+# ======================================================================
+# Lightning indexer (digest 模块 B eq 13-16; blog 第二阶段)
+# ======================================================================
+
+def test_indexer_single_head_is_relu_dot():
+    qI, KI = rnd(30, 6, 1, 8), rnd(31, 20, 8)
+    I = O.indexer_score(qI, np.ones((6, 1)), KI, 1, np.full(6, 100))
+    assert np.allclose(I, np.maximum(qI[:, 0] @ KI.T, 0))
+
+
+def test_indexer_basis_query_picks_key_coordinate():
+    """q^I_{t,h} = e_{j_h}: I[t,s] = sum_h w_h ReLU(K[s, j_h]) -- fixes which axis
+    is contracted."""
+    KI = rnd(32, 12, 5)
+    qI = np.zeros((1, 3, 5))
+    js = [4, 0, 2]
+    for h, j in enumerate(js):
+        qI[0, h, j] = 1.0
+    w = np.array([[0.5, -2.0, 3.0]])
+    I = O.indexer_score(qI, w, KI, 1, [11])
+    want = sum(w[0, h] * np.maximum(KI[:, j], 0) for h, j in enumerate(js))
+    assert np.allclose(I[0], want)
+
+
+def test_indexer_integer_closed_form():
+    """q_h = (h+1) e_0, K_s = (s-2) e_0, w = 1: I[s] = (s-2) H (H+1) / 2 for s > 2
+    and 0 otherwise (ReLU clips every negative dot product)."""
+    nh, S = 4, 9
+    qI = np.zeros((1, nh, 3))
+    qI[0, :, 0] = np.arange(1, nh + 1)
+    KI = np.zeros((S, 3))
+    KI[:, 0] = np.arange(S) - 2
+    I = O.indexer_score(qI, np.ones((1, nh)), KI, 1, [S - 1])
+    want = np.where(np.arange(S) > 2, (np.arange(S) - 2) * nh * (nh + 1) / 2, 0)
+    assert np.array_equal(I[0], want)
+
+
+def test_indexer_negative_dots_are_zero_and_weights_linear():
+    KI = np.abs(rnd(33, 10, 4))
+    qI = -np.abs(rnd(34, 2, 3, 4))
+    I = O.indexer_score(qI, rnd(35, 2, 3), KI, 1, [20, 20])
+    assert np.array_equal(I, np.zeros_like(I))
+    qI, KI = rnd(36, 3, 4, 6), rnd(37, 15, 6)
+    w1, w2 = rnd(38, 3, 4), rnd(39, 3, 4)
+    pos = [40, 40, 40]
+    I1 = O.indexer_score(qI, w1, KI, 1, pos)
+    I2 = O.indexer_score(qI, w2, KI, 1, pos)
+    I12 = O.indexer_score(qI, w1 + w2, KI, 1, pos)
+    assert np.allclose(I12, I1 + I2)
+    assert np.allclose(O.indexer_score(qI, -w1, KI, 1, pos), -I1)
+    perm = [2, 0, 3, 1]
+    assert np.allclose(O.indexer_score(qI[:, perm], w1[:, perm], KI, 1, pos), I1)
+
+
+@pytest.mark.parametrize("p,nvis", [(0, 0), (2, 0), (3, 1), (6, 1), (7, 2), (8, 2), (11, 3), (1000, 6)])
+def test_indexer_visibility_boundary(p, nvis):
+    """Entry s (pooling tokens up to m(s+1)-1) is visible at p iff m(s+1) <= p+1
+    (digest 模块 D: a query attends only to earlier compressed blocks)."""
+    I = O.indexer_score(rnd(40, 1, 2, 3), rnd(41, 1, 2), rnd(42, 6, 3), 4, [p])
+    assert np.isfinite(I[0, :nvis]).all()
+    assert np.isneginf(I[0, nvis:]).all()
+
+
+# ======================================================================
+# Top-k selector (digest 模块 B eq 17)
+# ======================================================================
+
+def _beats(a, b, scores):
+    return scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_pairwise_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    S = 12
+    scores = rng.integers(-3, 4, (5, S)).astype(np.float64)   # many ties
+    scores[0, 3] = -0.0
+    scores[0, 5] = 0.0
+    pos = rng.integers(0, 4 * S + 4, 5)
+    for k in (1, 3, 5, 12, 20):
+        idx = O.topk_select(scores, 4, pos, k)
+        for t in range(5):
+            nv = min(S, (pos[t] + 1) // 4)
+            sel = [s for s in idx[t] if s >= 0]
+            assert len(sel) == min(k, nv)
+            assert all(s == -1 for s in idx[t][len(sel):])
+            assert all(0 <= s < nv for s in sel)
+            rest = [s for s in range(nv) if s not in sel]
+            for a, b in itertools.product(sel, rest):
+                assert _beats(a, b, scores[t])
+            for a, b in zip(sel, sel[1:]):
+                assert _beats(a, b, scores[t])
+            want = sorted(range(nv), key=lambda s: (-scores[t, s], s))[:k]
+            assert sel == want
+
+
+def test_topk_all_equal_and_signed_zero():
+    I = np.zeros((1, 10))
+    I[0, ::2] = -0.0
+    assert list(O.topk_select(I, 1, [100], 4)[0]) == [0, 1, 2, 3]
+    assert list(O.topk_select(I, 1, [3], 6)[0]) == [0, 1, 2, 3, -1, -1]
+
+
+# ======================================================================
+# Core attention (digest 模块 B eq 18-19, 模块 C eq 24-26, 模块 D)
+# ======================================================================
+
+def sdpa(q, k, v, mask, scale):
+    """torch's textbook attention in float64 on the CPU; q [nh, T, c]."""
+    return F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                          torch.from_numpy(v), attn_mask=torch.from_numpy(mask),
+                                          scale=scale).numpy()
+
+
+def test_sparse_m1_full_topk_no_window_is_causal_mqa():
+    """m = 1, k >= n, n_win = 0, no sink: dense causal MQA with K = V = C^Comp."""
+    n, nh, c = 14, 3, 8
+    q, C = rnd(50, n, nh, c), rnd(51, n, c)
+    pos = np.arange(n)
+    idx = O.topk_select(rnd(52, n, n), 1, pos, n + 3)
+    scale = 1 / np.sqrt(c)
+    out = O.sparse_mqa(q, C, idx, C[:0], 0, 0, pos, None, scale)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    ref = sdpa(q.transpose(1, 0, 2), np.broadcast_to(C, (nh, n, c)).copy(),
+               np.broadcast_to(C, (nh, n, c)).copy(), causal, scale)
+    assert np.allclose(out, ref.transpose(1, 0, 2), atol=1e-12)
+
+
+def test_sparse_no_selection_is_banded_causal_over_window():
+    n, nh, c, nw = 20, 2, 6, 5
+    q, R = rnd(53, n, nh, c), rnd(54, n, c)
+    pos = np.arange(n)
+    idx = -np.ones((n, 4), dtype=np.int32)
+    out = O.sparse_mqa(q, R[:3], idx, R, 0, nw, pos, None, 0.7)
+    u = np.arange(n)
+    band = (u[None, :] <= pos[:, None]) & (u[None, :] > pos[:, None] - nw)
+    ref = sdpa(q.transpose(1, 0, 2), np.broadcast_to(R, (nh, n, c)).copy(),
+               np.broadcast_to(R, (nh, n, c)).copy(), band, 0.7)
+    assert np.allclose(out, ref.transpose(1, 0, 2), atol=1e-12)
+
+
+def test_hca_window_covering_sequence_is_masked_dense():
+    """n_win >= n: HCA equals dense attention over [C^Comp ; raw] with the
+    visibility mask of the compressed entries and the causal mask of raw rows."""
+    n, mp, nh, c = 24, 4, 3, 8
+    q, raw = rnd(55, n, nh, c), rnd(56, n, c)
+    comp = rnd(57, n // mp, c)
+    pos = np.arange(n)
+    scale = 0.3
+    out = O.hca_dense(q, comp, mp, raw, 0, n, pos, None, scale)
+    keys = np.concatenate([comp, raw])
+    s = np.arange(n // mp)
+    vis = mp * (s[None, :] + 1) <= pos[:, None] + 1
+    causal = np.arange(n)[None, :] <= pos[:, None]
+    mask = np.concatenate([vis, causal], axis=1)
+    K = np.broadcast_to(keys, (nh,) + keys.shape).copy()
+    ref = sdpa(q.transpose(1, 0, 2), K, K, mask, scale)
+    assert np.allclose(out, ref.transpose(1, 0, 2), atol=1e-12)
+
+
+def test_hca_short_sequence_sees_no_block():
+    n, mp, nh, c = 6, 8, 2, 4
+    q, raw = rnd(58, n, nh, c), rnd(59, n, c)
+    out = O.hca_dense(q, rnd(60, 3, c), mp, raw, 0, 16, np.arange(n), None, 0.5)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    K = np.broadcast_to(raw, (nh, n, c)).copy()
+    assert np.allclose(out, sdpa(q.transpose(1, 0, 2), K, K, causal, 0.5).transpose(1, 0, 2))
+
+
+def test_sink_is_an_extra_zero_value_key():
+    """digest 模块 D: exp(z'_h) joins the denominator only -- the same as one
+    more key with logit z'_h and a zero value vector."""
+    nh, N, c = 4, 7, 5
+    q, keys, z = rnd(61, nh, c), rnd(62, N, c), rnd(63, nh) * 2
+    scale = 0.4
+    out = O.core_attention(q, keys, scale, z)
+    qa = np.concatenate([q * scale, np.ones((nh, 1))], axis=1)[:, None, :]     # [nh, 1, c+1]
+    Ka = np.zeros((nh, N + 1, c + 1))
+    Ka[:, :N, :c] = keys
+    Ka[:, N, c] = z
+    Va = np.zeros((nh, N + 1, c))
+    Va[:, :N] = keys
+    ref = sdpa(qa, Ka, Va, np.ones((1, N + 1), dtype=bool), 1.0)[:, 0]
+    assert np.allclose(out, ref, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    nh, N, c = 3, 9, 6
+    keys, z = rnd(64, N, c), rnd(65, nh)
+    mean = keys.mean(axis=0)
+    out = O.core_attention(np.zeros((nh, c)), keys, 1.0, None)
+    assert np.allclose(out, mean[None])
+    out = O.core_attention(np.zeros((nh, c)), keys, 1.0, z)
+    assert np.allclose(out, mean[None] * (N / (N + np.exp(z)))[:, None])
+    one = keys[:1]
+    assert np.allclose(O.core_attention(rnd(66, nh, c), one, 1.0, None), np.broadcast_to(one, (nh, c)))
+    assert np.array_equal(O.core_attention(rnd(67, nh, c), keys[:0], 1.0, z), np.zeros((nh, c)))
+
+
+def test_sparse_index_permutation_and_padding_invariance():
+    S, nh, c = 30, 4, 6
+    q, C, R = rnd(68, 1, nh, c), rnd(69, S, c), rnd(70, 50, c)
+    idx = np.array([[3, 17, 29, 0, 8]], dtype=np.int32)
+    a = O.sparse_mqa(q, C, idx, R, 10, 8, [40], rnd(71, nh), 0.3)
+    b = O.sparse_mqa(q, C, idx[:, ::-1].copy(), R, 10, 8, [40], rnd(71, nh), 0.3)
+    c2 = O.sparse_mqa(q, C, np.array([[3, -1, 17, 29, -1, 0, 8, -1]], np.int32), R, 10, 8, [40],
+                      rnd(71, nh), 0.3)
+    assert np.allclose(a, b, atol=1e-13) and np.allclose(a, c2, atol=1e-13)
+
+
+def test_window_must_be_covered():
+    with pytest.raises(ValueError):
+        O.window_rows(np.zeros((10, 2)), 5, 4, 7)      # needs position 4
+    with pytest.raises(ValueError):
+        O.window_rows(np.zeros((10, 2)), 0, 4, 10)     # position 10 not stored
+    assert O.window_rows(np.zeros((10, 2)), 0, 4, 2).shape == (3, 2)
