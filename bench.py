@@ -1,0 +1,176 @@
+"""Benchmark: query tokens/s of the interleaved CSA + HCA layer pair at 1M context.
+
+Workload (one step = every call of the hot path once): an 8192-token chunk
+at positions [2^20, 2^20 + 8192) against caches prefilled with 2^20 tokens
+(262144 CSA entries, 8192 HCA entries, 128-row SWA tails); bf16 activations,
+fp8 + bf16-RoPE KV rows, MXFP4 indexer keys, d = 4096, c = 512, 64 heads,
+top-k 1024, window 128.  Inputs are seeded synthetic data resident in HBM
+before the timed region.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+
+Prints one JSON line.  Per-call durations come from HIP events recorded on the
+stream the library launches on; the roofline is reported for the call that
+takes the most time, from the algorithmic work of one launch.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s for CSA+HCA layer at 1M ctx; % of HBM/MFMA roofline"
+PEAK = {"mfma": 2500.0, "hbm": 8000.0}    # MI355X: dense bf16 TFLOP/s, HBM GB/s
+CALLS = ["csa_compress", "indexer", "topk", "sparse", "hca_compress", "hca_dense"]
+
+
+def algorithmic_work(cfg, P, S0, Sh0):
+    """Algorithmic FLOPs / bytes of each call for one step (visible work only)."""
+    n, d, c, m, mp, cI, hI, k, nw, nh = (cfg[x] for x in ("n", "d", "c", "m", "mp", "cI", "hI", "k", "n_win", "nh"))
+    t = np.arange(n, dtype=np.int64)
+    S = S0 + n // m
+    Sh = Sh0 + n // mp
+    nvis = np.minimum(S, (P + t + 1) // m)
+    nvis_h = np.minimum(Sh, (P + t + 1) // mp)
+    row = c + 64                                               # fp8 + bf16-RoPE row bytes
+    w = {}
+    w["csa_compress"] = dict(flop=2.0 * (n + cfg["n_left"]) * d * (4 * c + 4 * cI), bound="mfma")
+    w["indexer"] = dict(flop=2.0 * float(nvis.sum()) * hI * cI, bound="mfma",
+                        bytes=float(n) * S * 4 + S * (cI // 2 + cI // 32) + n * hI * (2 * cI + 4))
+    w["topk"] = dict(bytes=float(nvis.sum()) * 4 + n * k * 4, bound="hbm")
+    keys_sparse = float(n) * (k + nw)
+    w["sparse"] = dict(flop=4.0 * keys_sparse * nh * c, bound="mfma",
+                       bytes=2.0 * n * nh * c * 2 + S * row + n * k * 4)
+    w["hca_compress"] = dict(flop=2.0 * n * d * 2 * c, bound="mfma")
+    keys_dense = float((nvis_h + nw).sum())
+    w["hca_dense"] = dict(flop=4.0 * keys_dense * nh * c, bound="mfma", bytes=2.0 * n * nh * c * 2 + Sh * row)
+    return w
+
+
+def cpu_baseline(inp, rows_n=16, seed=4):
+    """The float64 oracle on a bounded sample: the three compressors in full,
+    then the per-query steps (index scores, top-k, sparse MQA, dense MQA) for
+    `rows_n` seeded query rows.  Returns query tokens/s with the compress cost
+    amortised over the chunk."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle as O
+    from oracle import codecs as K
+    cfg = inp["cfg"]
+    n, c, m, mp, k, nw, nl = (cfg[x] for x in ("n", "c", "m", "mp", "k", "n_win", "n_left"))
+    P, S0, Sh0 = int(inp["q_pos0"][0]), inp["S0"], inp["Sh0"]
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        dec = lambda x: K.bf16_decode(x)
+        H = dec(inp["H"])
+        t0 = time.perf_counter()
+        comp, raw = O.csa_compress(H, dec(inp["W_kv"]), inp["B_kv"], m, block0=S0, n_left=nl)
+        ki, _ = O.csa_compress(H, dec(inp["W_ki"]), inp["B_ki"], m, block0=S0, n_left=nl)
+        hca, hraw = O.hca_compress(H[nl:], dec(inp["W_hca"]), inp["B_hca"], mp)
+        t_comp = time.perf_counter() - t0
+        kv_all = np.concatenate([K.decode_rows(inp["kv_cache"][:S0], 2, c), K.round_rows(comp, 2)])
+        ki_all = np.concatenate([K.mxfp4_decode(inp["ki_codes"][:S0], inp["ki_scales"][:S0]), K.round_rows(ki, 3)])
+        hc_all = np.concatenate([K.decode_rows(inp["hca_cache"][:Sh0], 2, c), K.round_rows(hca, 2)])
+        wk = np.concatenate([K.decode_rows(inp["kv_win"][:nw], 2, c), K.round_rows(raw, 2)])
+        wh = np.concatenate([K.decode_rows(inp["hca_win"][:nw], 2, c), K.round_rows(hraw, 2)])
+        rows = np.sort(np.random.default_rng(seed).choice(n, size=rows_n, replace=False))
+        pos = P + rows
+        qI, wI = dec(inp["qI"])[rows], inp["wI"][rows].astype(np.float64)
+        q, qh = dec(inp["q"])[rows], dec(inp["q_hca"])[rows]
+        t0 = time.perf_counter()
+        I = O.indexer_score(qI, wI, ki_all, m, pos)
+        idx = O.topk_select(I, m, pos, k)
+        O.sparse_mqa(q, kv_all, idx, wk, P - nw, nw, pos, inp["sink"].astype(np.float64), 1 / math.sqrt(c))
+        O.hca_dense(qh, hc_all, mp, wh, P - nw, nw, pos, inp["sink_hca"].astype(np.float64), 1 / math.sqrt(c))
+        t_rows = time.perf_counter() - t0
+    per_token = t_comp / n + t_rows / rows_n
+    return {"value": 1.0 / per_token, "unit": "query tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": "float64 numpy oracle: the three compressors over the full 8192-token chunk (%.1f s, "
+                      "amortised per token) + index scores, top-k, sparse and dense MQA for %d seeded query "
+                      "rows (%.1f s); host cores available %d" % (t_comp, rows_n, t_rows, cores)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported (multi-GPU sharding is a "
+              "design note only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_attention_08_amd.layer import pair_from_arrays
+    from synth import gen as G
+
+    inp = G.make(5)
+    cfg = inp["cfg"]
+    layer = pair_from_arrays(inp)
+    stream = torch.cuda.current_stream()
+    fns = [layer.csa_compress, layer.indexer, layer.topk, layer.sparse, layer.hca_compress, layer.hca_dense]
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(CALLS)}
+    ms_step = wall * 1e3 / args.steps
+    value = cfg["n"] * args.steps / wall
+
+    work = algorithmic_work(cfg, int(inp["q_pos0"][0]), inp["S0"], inp["Sh0"])
+    calls = {}
+    for name in CALLS:
+        w, t = work[name], per_call[name] * 1e-3
+        ent = {"ms": round(per_call[name], 4)}
+        if "flop" in w:
+            ent["tflops"] = round(w["flop"] / t / 1e12, 2)
+        if "bytes" in w:
+            ent["gbps"] = round(w["bytes"] / t / 1e9, 1)
+        b = w["bound"]
+        ach = w["flop"] / t / 1e12 if b == "mfma" else w["bytes"] / t / 1e9
+        ent["frac_" + b] = round(ach / PEAK[b], 4)
+        calls[name] = ent
+    dom = max(CALLS, key=lambda x: per_call[x])
+    w = work[dom]
+    b = w["bound"]
+    ach = (w["flop"] / (per_call[dom] * 1e-3) / 1e12) if b == "mfma" else (w["bytes"] / (per_call[dom] * 1e-3) / 1e9)
+    roof = {"kernel": dom, "bound": b, "achieved": round(ach, 2), "peak": PEAK[b],
+            "unit": "TFLOP/s" if b == "mfma" else "GB/s", "frac": round(ach / PEAK[b], 4), "traffic": None,
+            "work_per_launch": w.get("flop") if b == "mfma" else w.get("bytes")}
+
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg["name"], "chunk_tokens": cfg["n"], "context": cfg["ctx"], "d": cfg["d"],
+                       "c": cfg["c"], "heads": cfg["nh"], "m": cfg["m"], "m_prime": cfg["mp"], "top_k": cfg["k"],
+                       "window": cfg["n_win"], "kv": "fp8_e4m3+bf16_rope", "indexer_keys": "mxfp4"},
+            "roofline": roof, "calls": calls}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * libdsv4attn -- the CSA / HCA attention hot path of DeepSeek-V4 for AMD
+ * Instinct MI355X (gfx950), as a plain C ABI.
+ *
+ * Sources (cited by page title and section):
+ *   digest = ai-papers-daily page "DeepSeek-V4: Towards Highly Efficient
+ *            Million-Token Context Intelligence", 子模块实现, 模块 B (CSA,
+ *            eq 9-19), 模块 C (HCA, eq 20-26), 模块 D (sliding window,
+ *            attention sink), 模块 F (KV precisions, FP4 indexer).
+ *   blog   = jsqmd page "DeepSeek V4大模型算法解析", 二、核心算法, 1.) CSA
+ *            (第一/二/三阶段) and 2.) HCA.
+ *   news   = 智能計算芯世界 page on DeepSeek-V4, 三、全棧基建優化 (batch-invariant,
+ *            deterministic kernels).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer unless it is marked "host".
+ *     The caller owns every buffer (inputs, outputs, workspaces); the library
+ *     allocates nothing and keeps no mutable global state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every kernel is
+ *     enqueued on it and the call returns without synchronising.
+ *   - Return value: DSV4_OK, or an error status.  Argument checks run on the
+ *     host before any HIP call; on any error nothing is launched and no output
+ *     is written.  dsv4_last_error() gives a message for the calling thread.
+ *   - Tensors are row-major, last dimension contiguous.  Weights use the
+ *     [out, in] layout, so a projection is C = H W^T.
+ *   - Positions: query i of batch b sits at absolute position q_pos0[b] + i.
+ *     Compressed-cache row s of a batch is absolute block s.  Entry s is
+ *     visible to position p iff ratio*(s+1) <= p+1 (every token it pools is at
+ *     or before p; digest 模块 D: a query attends only to earlier blocks).
+ *   - Results are deterministic and batch invariant: a sequence's outputs do
+ *     not depend on the batch it is in, and repeated calls are bitwise equal
+ *     (news, 批不變 + 確定性內核).
+ */
+#ifndef DSV4ATTN_H
+#define DSV4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DSV4_OK                   0
+#define DSV4_ERR_INVALID_ARG      1 /* null pointer, bad size, uncovered window ... */
+#define DSV4_ERR_UNSUPPORTED      2 /* dtype / layout / shape combination not built */
+#define DSV4_ERR_HIP              3 /* a HIP launch failed */
+#define DSV4_ERR_WORKSPACE        4 /* workspace smaller than the size query returns */
+
+/* activation dtypes (hidden states, queries, weights, attention outputs) */
+#define DSV4_F32                  0
+#define DSV4_BF16                 1
+
+/* row layouts of compressed entries, window rows and indexer keys.
+ * ROW_FP8_ROPE_BF16: dims [0, c-64) as OCP E4M3 bytes (no scale) followed by
+ *   dims [c-64, c) as bf16 -- the last 64 dims carry RoPE and stay bf16
+ *   (digest 模块 D partial RoPE, 模块 F mixed-precision KV); c + 64 bytes.
+ * ROW_MXFP4: c/2 bytes of OCP E2M1 codes (element 2j in the low nibble of byte
+ *   j) plus a separate scales array of c/32 E8M0 bytes per row (one per 32
+ *   consecutive dims); used for the indexer keys (digest 模块 F FP4 indexer). */
+#define DSV4_ROW_F32              0
+#define DSV4_ROW_BF16             1
+#define DSV4_ROW_FP8_ROPE_BF16    2
+#define DSV4_ROW_MXFP4            3
+
+/* Bytes of one stored row of width c in `layout` (MXFP4: codes only). 0 if invalid. */
+size_t dsv4_row_bytes(int layout, int c);
+
+/*
+ * CSA token-level compressor (digest 模块 B eq 9-12; blog 第一阶段).
+ *   C^a, C^b, Z^a, Z^b = H W_{aKV}^T, H W_{bKV}^T, H W_{aZ}^T, H W_{bZ}^T.
+ *   Entry i, channel j: softmax over the logits Z^a[m i + r, j] + B^a[r, j] and
+ *   Z^b[m (i-1) + r, j] + B^b[r, j] (r < m; the b-part is absent for entry 0),
+ *   then the matching weighted sum of C^a / C^b rows.  Windows of successive
+ *   entries overlap by m tokens.
+ *
+ * H        [n_left + n, d] act_dtype.  Row n_left is the token at absolute
+ *          position m*block0; the n_left rows before it are left context.
+ * W        [4c, d] act_dtype = W_aKV | W_bKV | W_aZ | W_bZ stacked by rows.
+ * bias_ab  [2, m, c] float = B^a, B^b.
+ * block0   absolute index of the first emitted entry.  If block0 > 0 the first
+ *          entry's b-window needs n_left >= m (else DSV4_ERR_INVALID_ARG).
+ * comp_out [n/m rows] in comp_layout (F32, BF16, FP8_ROPE_BF16 or MXFP4);
+ *          comp_scales [n/m, c/32] bytes for MXFP4, else ignored (may be NULL).
+ *          An incomplete final block (n % m tokens) emits no entry.
+ * raw_out  [n rows] of C^a in raw_layout (F32, BF16 or FP8_ROPE_BF16), the
+ *          uncompressed sliding-window KV of the chunk; NULL to skip.
+ * Row layouts FP8_ROPE_BF16 need c >= 64 and c % 32 == 0; MXFP4 needs c % 32 == 0.
+ */
+int dsv4_csa_compress(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype,
+                      const void* W, const float* bias_ab, int m, int c, int64_t block0,
+                      void* comp_out, void* comp_scales, int comp_layout,
+                      void* raw_out, int raw_layout, void* stream);
+
+/*
+ * HCA compressor (digest 模块 C eq 20-23; blog 2.) HCA): C = H W_KV^T,
+ * Z = H W_Z^T; entry i, channel j = softmax_r(Z[m' i + r, j] + B[r, j]) weighted
+ * sum of C[m' i + r, j] over r < m' (no overlap).
+ * H [n, d]; W [2c, d] = W_KV | W_Z; bias [m', c] float.
+ * comp_out [n/m' rows] in comp_layout; raw_out [n rows] of C in raw_layout or NULL.
+ */
+int dsv4_hca_compress(const void* H, int64_t n, int64_t d, int act_dtype,
+                      const void* W, const float* bias, int m_prime, int c,
+                      void* comp_out, void* comp_scales, int comp_layout,
+                      void* raw_out, int raw_layout, void* stream);
+
+/*
+ * Lightning-indexer scores (digest 模块 B eq 16; blog 第二阶段):
+ *   I[b, t, s] = sum_h wI[b, t, h] * ReLU(qI[b, t, h, :] . K[b, s, :])
+ * for entries visible to the query (m*(s+1) <= p+1), -inf otherwise.  No scale.
+ * qI     [B, nq, hI, cI] q_dtype;  wI [B, nq, hI] float.
+ * keys   [B, S, row] in k_layout (F32, BF16 or MXFP4); k_scales [B, S, cI/32]
+ *        bytes for MXFP4 (else ignored).
+ * q_pos0 host [B].   scores [B, nq, S] float (output).
+ * The float accumulation is fp32; bf16 and MXFP4 inputs are decoded exactly.
+ */
+int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
+                       const void* keys, const uint8_t* k_scales, int k_layout,
+                       int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                       const int64_t* q_pos0, float* scores, void* stream);
+
+/*
+ * Top-k selector (digest 模块 B eq 17; blog 第二阶段 Top-k稀疏选择).
+ * For each row (b, t): the k visible entries with the largest score; ties go
+ * to the lower index; order (score descending, index ascending); fewer than
+ * k visible entries -> all of them, then -1 padding.  Only entries with
+ * m*(s+1) <= p+1 and s < S are candidates (the score values of other entries
+ * are never read).  -0.0 and +0.0 compare equal.  Scores must not be NaN.
+ * scores [B, nq, S] float; idx_out [B, nq, k] int32.  k <= 4096.
+ * ws: workspace of dsv4_topk_workspace_size() bytes (may be 0 -> NULL ok).
+ */
+size_t dsv4_topk_workspace_size(int64_t B, int64_t nq, int64_t S, int k);
+int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                     const int64_t* q_pos0, int k, int32_t* idx_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * CSA core: shared-KV multi-query attention over the selected compressed
+ * entries plus the sliding window, with an attention sink (digest 模块 B
+ * eq 18-19, 模块 D; blog 第三阶段).  For query (b, t) at position p and head h:
+ *   keys = { kv_comp[b, s] : s in idx[b, t], 0 <= s < S }  ++
+ *          { window row of position u : max(0, p-n_win+1) <= u <= p }
+ *   l_x = scale * q[b,t,h] . key_x;  M = max(max_x l_x, sink[h])
+ *   out[b,t,h] = sum_x e^{l_x-M} key_x / (sum_x e^{l_x-M} + e^{sink[h]-M})
+ * Each key is also its value.  Entries of idx outside [0, S) are padding.
+ * sink NULL -> no sink term.  An empty key set gives a zero output.
+ * q [B, nq, nh, c] q_dtype; out the same shape and dtype.
+ * kv_comp [B, S, row] and kv_win [B, W, row] in kv_layout (F32 with F32
+ * queries; BF16 or FP8_ROPE_BF16 with BF16 queries).  Window row w of batch b
+ * holds position win_pos0[b] + w (host array); every query's window must be
+ * covered, else DSV4_ERR_INVALID_ARG.  idx [B, nq, k] int32.
+ * ws: workspace of dsv4_attn_workspace_size() bytes, where dense is 0 for this
+ * call and 1 for dsv4_hca_dense_fwd, and max_keys bounds the compressed
+ * entries plus window rows of any query (k + n_win here; S + n_win for HCA).
+ */
+size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c, int64_t max_keys);
+int dsv4_sparse_mqa_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                        const void* kv_comp, int kv_layout, int64_t S,
+                        const int32_t* idx, int k,
+                        const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                        const int64_t* q_pos0, const float* sink, float scale,
+                        void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * HCA core: as dsv4_sparse_mqa_fwd but over every visible compressed entry
+ * (m'*(s+1) <= p+1, s < S) instead of an index list (digest 模块 C eq 24-26;
+ * blog 2.) HCA 融合与计算).
+ */
+int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                       const void* kv_comp, int kv_layout, int64_t S, int m_prime,
+                       const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                       const int64_t* q_pos0, const float* sink, float scale,
+                       void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Status text, and the last error message of the calling thread. */
+const char* dsv4_status_string(int status);
+const char* dsv4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSV4ATTN_H */

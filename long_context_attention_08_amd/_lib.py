@@ -1,0 +1,174 @@
+"""ctypes binding of libdsv4attn (the C ABI in include/dsv4attn.h).
+
+Argument marshalling only: every step runs in the HIP library.  torch supplies
+device memory and the current stream.  Importing this module raises if the
+built library is missing -- there is no fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsv4attn.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
+
+EXPORTS = [
+    "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
+    "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
+    "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libdsv4attn.so is not built (run `python long_context_attention_08_amd/build.py`)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_P64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def _sig(name, res, args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("dsv4_row_bytes", _sz, [_int, _int])
+_sig("dsv4_status_string", ctypes.c_char_p, [_int])
+_sig("dsv4_last_error", ctypes.c_char_p, [])
+_sig("dsv4_csa_compress", _int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _int, _int, _i64,
+                                 _vp, _vp, _int, _vp, _int, _vp])
+_sig("dsv4_hca_compress", _int, [_vp, _i64, _i64, _int, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _int, _vp])
+_sig("dsv4_indexer_score", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _i64, _int,
+                                  _P64, _vp, _vp])
+_sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
+_sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
+_sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
+_sig("dsv4_sparse_mqa_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _vp, _int,
+                                   _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
+_sig("dsv4_hca_dense_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _int,
+                                  _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
+
+
+class Dsv4Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (%d): %s" % (lib.dsv4_status_string(status).decode(), status, msg))
+        self.status = status
+
+
+def _check(status):
+    if status != OK:
+        raise Dsv4Error(status, lib.dsv4_last_error().decode())
+
+
+def row_bytes(layout, c):
+    return int(lib.dsv4_row_bytes(layout, c))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor, got %r" % type(t))
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _act(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _host_i64(vals):
+    arr = (ctypes.c_int64 * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+# --------------------------------------------------------------------- the six calls
+
+def csa_compress(H, W, bias_ab, m, c, comp_out, comp_layout, *, n_left=0, block0=0,
+                 comp_scales=None, raw_out=None, raw_layout=ROW_F32, stream=None):
+    """CSA compressor.  H [n_left + n, d]; W [4c, d]; bias_ab [2, m, c] float32."""
+    n = H.shape[0] - n_left
+    _check(lib.dsv4_csa_compress(_ptr(H), n_left, n, H.shape[1], _act(H), _ptr(W), _ptr(bias_ab), m, c,
+                                 block0, _ptr(comp_out), _ptr(comp_scales), comp_layout,
+                                 _ptr(raw_out), raw_layout, _stream(stream)))
+
+
+def hca_compress(H, W, bias, m_prime, c, comp_out, comp_layout, *, comp_scales=None,
+                 raw_out=None, raw_layout=ROW_F32, stream=None):
+    """HCA compressor.  H [n, d]; W [2c, d]; bias [m', c] float32."""
+    _check(lib.dsv4_hca_compress(_ptr(H), H.shape[0], H.shape[1], _act(H), _ptr(W), _ptr(bias), m_prime, c,
+                                 _ptr(comp_out), _ptr(comp_scales), comp_layout, _ptr(raw_out), raw_layout,
+                                 _stream(stream)))
+
+
+def indexer_score(qI, wI, keys, k_layout, m, q_pos0, scores, *, k_scales=None, S=None, stream=None):
+    """Index scores.  qI [B, nq, hI, cI]; wI [B, nq, hI]; keys [B, S, ...]; scores [B, nq, S]."""
+    B, nq, hI, cI = qI.shape
+    S = scores.shape[2] if S is None else S
+    _check(lib.dsv4_indexer_score(_ptr(qI), _act(qI), _ptr(wI), _ptr(keys), _ptr(k_scales), k_layout,
+                                  B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores), _stream(stream)))
+
+
+def topk_workspace_size(B, nq, S, k):
+    return int(lib.dsv4_topk_workspace_size(B, nq, S, k))
+
+
+def topk_select(scores, m, q_pos0, k, idx_out, ws=None, *, stream=None):
+    """Top-k.  scores [B, nq, S] float32 -> idx_out [B, nq, k] int32."""
+    B, nq, S = scores.shape
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv4_topk_select(_ptr(scores), B, nq, S, m, _host_i64(q_pos0), k, _ptr(idx_out),
+                                _ptr(ws), wsb, _stream(stream)))
+
+
+def attn_workspace_size(dense, B, nq, nh, c, max_keys):
+    return int(lib.dsv4_attn_workspace_size(1 if dense else 0, B, nq, nh, c, max_keys))
+
+
+def sparse_mqa_fwd(q, kv_comp, kv_layout, idx, kv_win, win_pos0, n_win, q_pos0, sink, scale, out,
+                   ws=None, *, S=None, W=None, stream=None):
+    """CSA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; idx [B, nq, k]; kv_win [B, W, row]."""
+    B, nq, nh, c = q.shape
+    S = kv_comp.shape[1] if S is None else S
+    W = kv_win.shape[1] if (W is None and kv_win is not None) else (W or 0)
+    k = idx.shape[2] if idx is not None else 0
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv4_sparse_mqa_fwd(_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, _ptr(idx), k,
+                                   _ptr(kv_win), W, _host_i64(win_pos0), n_win, _host_i64(q_pos0),
+                                   _ptr(sink), float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream)))
+
+
+def hca_dense_fwd(q, kv_comp, kv_layout, m_prime, kv_win, win_pos0, n_win, q_pos0, sink, scale, out,
+                  ws=None, *, S=None, W=None, stream=None):
+    """HCA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; kv_win [B, W, row]."""
+    B, nq, nh, c = q.shape
+    S = kv_comp.shape[1] if S is None else S
+    W = kv_win.shape[1] if (W is None and kv_win is not None) else (W or 0)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv4_hca_dense_fwd(_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, m_prime,
+                                  _ptr(kv_win), W, _host_i64(win_pos0), n_win, _host_i64(q_pos0),
+                                  _ptr(sink), float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream)))

@@ -1,0 +1,274 @@
+// C ABI of libdsv4attn: argument validation (host only, before any HIP call),
+// dispatch to the launchers, status strings.  See include/dsv4attn.h.
+#include "../../include/dsv4attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "dsv4_common.h"
+#include "dsv4_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DSV4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSV4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool act_ok(int dt) { return dt == DSV4_F32 || dt == DSV4_BF16; }
+
+// layouts usable for KV rows (compressed entries and window rows)
+bool kv_layout_ok(int layout, int c) {
+  if (layout == DSV4_ROW_F32 || layout == DSV4_ROW_BF16) return c >= 1;
+  if (layout == DSV4_ROW_FP8_ROPE_BF16) return c >= 64 && c % 16 == 0;
+  return false;
+}
+
+int check_ptrs16(const char* fn, std::initializer_list<std::pair<const void*, const char*>> ps) {
+  for (auto& p : ps) {
+    if (!p.first) return fail(DSV4_ERR_INVALID_ARG, "%s: %s is NULL", fn, p.second);
+    if (!aligned16(p.first)) return fail(DSV4_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, p.second);
+  }
+  return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsv4_row_bytes(int layout, int c) {
+  if (c <= 0) return 0;
+  switch (layout) {
+    case DSV4_ROW_F32: return (size_t)4 * c;
+    case DSV4_ROW_BF16: return (size_t)2 * c;
+    case DSV4_ROW_FP8_ROPE_BF16: return c >= 64 ? (size_t)c + 64 : 0;
+    case DSV4_ROW_MXFP4: return c % 32 == 0 ? (size_t)c / 2 : 0;
+    default: return 0;
+  }
+}
+
+const char* dsv4_status_string(int status) {
+  switch (status) {
+    case DSV4_OK: return "ok";
+    case DSV4_ERR_INVALID_ARG: return "invalid argument";
+    case DSV4_ERR_UNSUPPORTED: return "unsupported dtype/layout/shape combination";
+    case DSV4_ERR_HIP: return "HIP launch error";
+    case DSV4_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* dsv4_last_error(void) { return g_err; }
+
+// --------------------------------------------------------------------------- compressors
+
+static int check_compress(const char* fn, const void* H, int64_t n_left, int64_t n, int64_t d, int act,
+                          const void* W, const float* bias, int m, int c, void* comp, void* scales,
+                          int comp_layout, void* raw, int raw_layout) {
+  if (n_left < 0 || n < 0 || d <= 0 || c <= 0 || m <= 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes (n_left=%lld n=%lld d=%lld m=%d c=%d)", fn,
+                (long long)n_left, (long long)n, (long long)d, m, c);
+  if (!act_ok(act)) return fail(DSV4_ERR_UNSUPPORTED, "%s: act_dtype %d", fn, act);
+  if (comp_layout == DSV4_ROW_MXFP4) {
+    if (c % 32) return fail(DSV4_ERR_UNSUPPORTED, "%s: MXFP4 output needs c %% 32 == 0 (c=%d)", fn, c);
+  } else if (!kv_layout_ok(comp_layout, c)) {
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: comp_layout %d with c=%d", fn, comp_layout, c);
+  }
+  if (raw && !kv_layout_ok(raw_layout, c)) return fail(DSV4_ERR_UNSUPPORTED, "%s: raw_layout %d with c=%d", fn, raw_layout, c);
+  if (n_left + n == 0) return DSV4_OK;
+  int r = check_ptrs16(fn, {{H, "H"}, {W, "W"}});
+  if (r) return r;
+  if (!bias) return fail(DSV4_ERR_INVALID_ARG, "%s: bias is NULL", fn);
+  if (n / m > 0) {
+    r = check_ptrs16(fn, {{comp, "comp_out"}});
+    if (r) return r;
+    if (comp_layout == DSV4_ROW_MXFP4 && !scales) return fail(DSV4_ERR_INVALID_ARG, "%s: comp_scales is NULL", fn);
+  }
+  if (raw && !aligned16(raw)) return fail(DSV4_ERR_INVALID_ARG, "%s: raw_out is not 16-byte aligned", fn);
+  if (act == DSV4_BF16 && d % 8) return fail(DSV4_ERR_UNSUPPORTED, "%s: bf16 needs d %% 8 == 0", fn);
+  return DSV4_OK;
+}
+
+int dsv4_csa_compress(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype,
+                      const void* W, const float* bias_ab, int m, int c, int64_t block0,
+                      void* comp_out, void* comp_scales, int comp_layout,
+                      void* raw_out, int raw_layout, void* stream) {
+  const char* fn = "dsv4_csa_compress";
+  int r = check_compress(fn, H, n_left, n, d, act_dtype, W, bias_ab, m, c, comp_out, comp_scales,
+                         comp_layout, raw_out, raw_layout);
+  if (r) return r;
+  if (m > 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: m=%d > 64", fn, m);
+  if (block0 < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: block0 < 0", fn);
+  if (block0 >= 1 && n >= m && n_left < m)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: entry %lld needs %d rows of left context, got n_left=%lld", fn,
+                (long long)block0, m, (long long)n_left);
+  if (n == 0) return ok();
+  dsv4::CompressArgs a{H, n_left, n, d, act_dtype, W, bias_ab, m, c, block0, comp_out,
+                       reinterpret_cast<uint8_t*>(comp_scales), comp_layout, raw_out, raw_layout};
+  return hip_status(dsv4::launch_csa_compress(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_hca_compress(const void* H, int64_t n, int64_t d, int act_dtype,
+                      const void* W, const float* bias, int m_prime, int c,
+                      void* comp_out, void* comp_scales, int comp_layout,
+                      void* raw_out, int raw_layout, void* stream) {
+  const char* fn = "dsv4_hca_compress";
+  int r = check_compress(fn, H, 0, n, d, act_dtype, W, bias, m_prime, c, comp_out, comp_scales,
+                         comp_layout, raw_out, raw_layout);
+  if (r) return r;
+  if (n == 0) return ok();
+  dsv4::CompressArgs a{H, 0, n, d, act_dtype, W, bias, m_prime, c, 0, comp_out,
+                       reinterpret_cast<uint8_t*>(comp_scales), comp_layout, raw_out, raw_layout};
+  return hip_status(dsv4::launch_hca_compress(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+// --------------------------------------------------------------------------- indexer
+
+int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
+                       const void* keys, const uint8_t* k_scales, int k_layout,
+                       int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                       const int64_t* q_pos0, float* scores, void* stream) {
+  const char* fn = "dsv4_indexer_score";
+  if (B < 0 || nq < 0 || S < 0 || hI <= 0 || cI <= 0 || m <= 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
+  if (k_layout != DSV4_ROW_F32 && k_layout != DSV4_ROW_BF16 && k_layout != DSV4_ROW_MXFP4)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: k_layout %d", fn, k_layout);
+  if (k_layout == DSV4_ROW_MXFP4 && cI % 32) return fail(DSV4_ERR_UNSUPPORTED, "%s: MXFP4 keys need cI %% 32 == 0", fn);
+  if (B == 0 || nq == 0 || S == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  for (int64_t b = 0; b < B; ++b)
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+  int r = check_ptrs16(fn, {{qI, "qI"}, {keys, "keys"}, {scores, "scores"}});
+  if (r) return r;
+  if (!wI) return fail(DSV4_ERR_INVALID_ARG, "%s: wI is NULL", fn);
+  if (k_layout == DSV4_ROW_MXFP4 && !k_scales) return fail(DSV4_ERR_INVALID_ARG, "%s: k_scales is NULL", fn);
+  dsv4::IndexerArgs a{qI, q_dtype, wI, keys, k_scales, k_layout, B, nq, hI, cI, S, m, scores};
+  return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+// --------------------------------------------------------------------------- top-k
+
+size_t dsv4_topk_workspace_size(int64_t B, int64_t nq, int64_t S, int k) {
+  if (B <= 0 || nq <= 0 || S <= 0 || k <= 0) return 0;
+  return dsv4::topk_workspace_bytes(B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq, S, k);
+}
+
+int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                     const int64_t* q_pos0, int k, int32_t* idx_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_topk_select";
+  if (B < 0 || nq < 0 || S < 0 || m <= 0 || k <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "%s: k=%d > 4096", fn, k);
+  if (B == 0 || nq == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  for (int64_t b = 0; b < B; ++b)
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+  if (!idx_out) return fail(DSV4_ERR_INVALID_ARG, "%s: idx_out is NULL", fn);
+  if (S > 0 && !scores) return fail(DSV4_ERR_INVALID_ARG, "%s: scores is NULL", fn);
+  if (S >= (int64_t)1 << 31) return fail(DSV4_ERR_UNSUPPORTED, "%s: S >= 2^31", fn);
+  const int64_t rows = B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq;
+  if (!dsv4::topk_supported(rows, S > 0 ? S : 1, k)) return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
+  const size_t need = dsv4::topk_workspace_bytes(rows, S > 0 ? S : 1, k);
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  return hip_status(dsv4::launch_topk(scores, B, nq, S, m, q_pos0, k, idx_out, ws,
+                                      reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+// --------------------------------------------------------------------------- attention
+
+size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c, int64_t max_keys) {
+  if (B <= 0 || nq <= 0 || nh <= 0 || c <= 0) return 0;
+  return dsv4::attn_workspace_bytes(B, nq, nh, c, max_keys + 64, dense != 0);
+}
+
+static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, int64_t B, int64_t nq, int nh,
+                       int c, const void* kv_comp, int kv_layout, int64_t S, const int32_t* idx, int k,
+                       int ratio, const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                       const int64_t* q_pos0, const float* sink, float scale, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (B < 0 || nq < 0 || nh <= 0 || c <= 0 || S < 0 || W < 0 || n_win < 0 || k < 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (dense && ratio <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: m_prime <= 0", fn);
+  if (c > 1024) return fail(DSV4_ERR_UNSUPPORTED, "%s: c=%d > 1024", fn, c);
+  if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
+  if (!kv_layout_ok(kv_layout, c)) return fail(DSV4_ERR_UNSUPPORTED, "%s: kv_layout %d with c=%d", fn, kv_layout, c);
+  if (!std::isfinite(scale)) return fail(DSV4_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (B == 0 || nq == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  int r = check_ptrs16(fn, {{q, "q"}, {out, "out"}});
+  if (r) return r;
+  if ((S > 0 && (dense || k > 0)) && (r = check_ptrs16(fn, {{kv_comp, "kv_comp"}}))) return r;
+  if (!dense && k > 0 && !idx) return fail(DSV4_ERR_INVALID_ARG, "%s: idx is NULL", fn);
+  if (n_win > 0) {
+    if ((r = check_ptrs16(fn, {{kv_win, "kv_win"}}))) return r;
+    if (!win_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: win_pos0 is NULL", fn);
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+    if (q_pos0[b] + nq >= ((int64_t)1 << 31)) return fail(DSV4_ERR_UNSUPPORTED, "%s: positions >= 2^31", fn);
+    if (n_win > 0) {
+      const int64_t p_first = q_pos0[b], p_last = q_pos0[b] + nq - 1;
+      const int64_t lo = p_first - n_win + 1 > 0 ? p_first - n_win + 1 : 0;
+      if (lo < win_pos0[b] || p_last >= win_pos0[b] + W)
+        return fail(DSV4_ERR_INVALID_ARG,
+                    "%s: batch %lld: window positions [%lld, %lld] not covered by kv_win rows [%lld, %lld)", fn,
+                    (long long)b, (long long)lo, (long long)p_last, (long long)win_pos0[b],
+                    (long long)(win_pos0[b] + W));
+    }
+  }
+  int64_t max_keys = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t nc = dense ? dsv4::visible_count(q_pos0[b] + nq - 1, ratio, S) : k;
+    const int64_t kk = nc + (n_win > 0 ? n_win + 3 : 0);
+    max_keys = kk > max_keys ? kk : max_keys;
+  }
+  const size_t need = dsv4::attn_workspace_bytes(B, nq, nh, c, max_keys, dense);
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  dsv4::AttnArgs a{q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, dense ? nullptr : idx, dense ? 0 : k,
+                   dense ? ratio : 1, kv_win, W, n_win, sink, scale, out, ws, ws_bytes};
+  return hip_status(dsv4::launch_attn(a, q_pos0, win_pos0, dense, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_sparse_mqa_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                        const void* kv_comp, int kv_layout, int64_t S,
+                        const int32_t* idx, int k,
+                        const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                        const int64_t* q_pos0, const float* sink, float scale,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common("dsv4_sparse_mqa_fwd", false, q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, idx, k, 1,
+                     kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream);
+}
+
+int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                       const void* kv_comp, int kv_layout, int64_t S, int m_prime,
+                       const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                       const int64_t* q_pos0, const float* sink, float scale,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common("dsv4_hca_dense_fwd", true, q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, nullptr, 0,
+                     m_prime, kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

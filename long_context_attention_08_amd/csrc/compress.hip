@@ -1,0 +1,426 @@
+// Token-level KV compressors of CSA and HCA (DeepSeek-V4 digest, 模块 B eq 9-12
+// and 模块 C eq 20-23; jsqmd blog 第一阶段).
+//
+// CSA entry i, channel j: per-channel softmax over the logits
+//   Z^a[m i + r, j] + B^a[r, j]   and   Z^b[m (i-1) + r, j] + B^b[r, j]   (r < m)
+// (the b-part is absent for absolute entry 0), then the weighted sum of the
+// matching C^a / C^b values, with C^x = H W_x^T and Z^x = H W_x^T.
+// HCA entry i: softmax over Z[m' i + r, j] + B[r, j], weighted sum of C.
+//
+// Two paths:
+//   * generic: one thread per (entry, channel) computing its dot products in
+//     fp32 -- any m, c, d, either activation dtype (small or odd shapes);
+//   * MFMA (bf16, CSA m = 4 / HCA m' = 128, c % 32 == 0, d % 64 == 0): the
+//     projection GEMM on v_mfma_f32_16x16x32_bf16 with the pooling softmax,
+//     the window-row export and the storage packing fused in the epilogue, so
+//     C and Z never touch HBM.
+#include "dsv4_common.h"
+#include "dsv4_internal.h"
+
+namespace dsv4 {
+
+// ------------------------------------------------------------------------
+// shared epilogue: pack a pooled fp32 tile row (32 channels of one entry,
+// channels [j0, j0+32)) into the output layout.  Called by a 32-lane group
+// holding one channel each (lane32 = channel offset).
+// ------------------------------------------------------------------------
+__device__ __forceinline__ void pack32(float v, int lane32, uint8_t* row, uint8_t* scale_row,
+                                       int layout, int c, int j0) {
+  const int j = j0 + lane32;
+  if (layout != ROW_MXFP4) {
+    store_row_elem(row, layout, c, j, v);
+    return;
+  }
+  float amax = fabsf(v);
+  for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  const uint32_t E = mx_scale_code(amax);
+  const float inv = ldexpf(1.0f, 127 - (int)E);
+  uint32_t code = E ? f32_to_e2m1(v * inv) : 0u;
+  uint32_t partner = __shfl_xor(code, 1, 32);
+  if ((lane32 & 1) == 0) row[j >> 1] = (uint8_t)(code | (partner << 4));
+  if (lane32 == 0) scale_row[j0 >> 5] = (uint8_t)E;
+}
+
+// ------------------------------------------------------------------------
+// generic path
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float dot_row(const void* H, int act, int64_t hrow, const void* W,
+                                         int64_t wrow, int64_t d) {
+  float acc = 0.0f;
+  if (act == ACT_F32) {
+    const float* h = reinterpret_cast<const float*>(H) + hrow * d;
+    const float* w = reinterpret_cast<const float*>(W) + wrow * d;
+    for (int64_t k = 0; k < d; ++k) acc = fmaf(h[k], w[k], acc);
+  } else {
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(H) + hrow * d;
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(W) + wrow * d;
+    for (int64_t k = 0; k < d; ++k) acc = fmaf(bf16_to_f32(h[k]), bf16_to_f32(w[k]), acc);
+  }
+  return acc;
+}
+
+// threads: (entry slot e in [0, ceil(n/m)), channel j); c % 32 == 0 is not
+// required except for MXFP4 output (32 consecutive lanes = one block).
+__global__ void csa_compress_generic(CompressArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int c = a.c, m = a.m;
+  const int64_t n_slots = (a.n + m - 1) / m;
+  const int64_t e = t / c;
+  const int j = (int)(t % c);
+  if (e >= n_slots) return;
+  const int64_t a0 = a.n_left + (int64_t)m * e;     // H row of the first a-token
+  const int rb = row_bytes(a.comp_layout, c);
+  const int rrb = row_bytes(a.raw_layout, c);
+  float La[64], Ca[64];
+  float mx = -INFINITY;
+  int na = 0;
+  for (int r = 0; r < m; ++r) {
+    const int64_t tok = (int64_t)m * e + r;
+    if (tok >= a.n) break;
+    Ca[r] = dot_row(a.H, a.act, a0 + r, a.W, j, a.d);
+    if (a.raw) store_row_elem(reinterpret_cast<uint8_t*>(a.raw) + tok * rrb, a.raw_layout, c, j, Ca[r]);
+    La[r] = dot_row(a.H, a.act, a0 + r, a.W, 2 * c + j, a.d) + a.bias[r * c + j];
+    mx = fmaxf(mx, La[r]);
+    ++na;
+  }
+  const bool complete = (na == m);
+  const bool has_b = (a.block0 + e) >= 1;
+  float Cb[64], Lb[64];
+  if (complete && has_b) {
+    for (int r = 0; r < m; ++r) {
+      Cb[r] = dot_row(a.H, a.act, a0 - m + r, a.W, c + j, a.d);
+      Lb[r] = dot_row(a.H, a.act, a0 - m + r, a.W, 3 * c + j, a.d) + a.bias[(m + r) * c + j];
+      mx = fmaxf(mx, Lb[r]);
+    }
+  }
+  float v = 0.0f;
+  if (complete) {
+    float num = 0.0f, den = 0.0f;
+    for (int r = 0; r < m; ++r) {
+      const float w = __expf(La[r] - mx);
+      num = fmaf(w, Ca[r], num);
+      den += w;
+    }
+    if (has_b)
+      for (int r = 0; r < m; ++r) {
+        const float w = __expf(Lb[r] - mx);
+        num = fmaf(w, Cb[r], num);
+        den += w;
+      }
+    v = num / den;
+  }
+  // full 32-lane groups must reach the MXFP4 shuffles: every lane of a
+  // complete entry participates (entries are uniform across a block of 32
+  // channels because c % 32 == 0 for MXFP4)
+  if (!complete) return;
+  uint8_t* row = reinterpret_cast<uint8_t*>(a.comp) + e * rb;
+  if (a.comp_layout == ROW_MXFP4)
+    pack32(v, j & 31, row, a.comp_scales + e * (c / 32), ROW_MXFP4, c, j & ~31);
+  else
+    store_row_elem(row, a.comp_layout, c, j, v);
+}
+
+__global__ void hca_compress_generic(CompressArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int c = a.c, m = a.m;
+  const int64_t n_slots = (a.n + m - 1) / m;
+  const int64_t e = t / c;
+  const int j = (int)(t % c);
+  if (e >= n_slots) return;
+  const int rb = row_bytes(a.comp_layout, c);
+  const int rrb = row_bytes(a.raw_layout, c);
+  const bool complete = (int64_t)m * (e + 1) <= a.n;
+  // two passes over the block: max of the logits, then the weighted sums
+  float mx = -INFINITY;
+  for (int r = 0; r < m; ++r) {
+    const int64_t tok = (int64_t)m * e + r;
+    if (tok >= a.n) break;
+    const float C = dot_row(a.H, a.act, tok, a.W, j, a.d);
+    if (a.raw) store_row_elem(reinterpret_cast<uint8_t*>(a.raw) + tok * rrb, a.raw_layout, c, j, C);
+    if (complete) mx = fmaxf(mx, dot_row(a.H, a.act, tok, a.W, c + j, a.d) + a.bias[r * c + j]);
+  }
+  if (!complete) return;
+  float num = 0.0f, den = 0.0f;
+  for (int r = 0; r < m; ++r) {
+    const int64_t tok = (int64_t)m * e + r;
+    const float w = __expf(dot_row(a.H, a.act, tok, a.W, c + j, a.d) + a.bias[r * c + j] - mx);
+    num = fmaf(w, dot_row(a.H, a.act, tok, a.W, j, a.d), num);
+    den += w;
+  }
+  const float v = num / den;
+  uint8_t* row = reinterpret_cast<uint8_t*>(a.comp) + e * rb;
+  if (a.comp_layout == ROW_MXFP4)
+    pack32(v, j & 31, row, a.comp_scales + e * (c / 32), ROW_MXFP4, c, j & ~31);
+  else
+    store_row_elem(row, a.comp_layout, c, j, v);
+}
+
+// ------------------------------------------------------------------------
+// MFMA path (bf16)
+// ------------------------------------------------------------------------
+constexpr int KSTEP = 64;          // d elements staged per LDS round
+constexpr int LDK = KSTEP + 8;     // padded LDS row (bf16 elements)
+
+// Copy `rows` rows of KSTEP bf16 each (global row stride `ld` elements, first
+// column k0) into LDS; rows with a negative or out-of-range global index are
+// zero.  256 threads, 16-byte chunks.
+__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* g, int64_t row0,
+                                           int rows, int64_t row_lo, int64_t row_hi,
+                                           int64_t ld, int64_t k0) {
+  constexpr int CH = KSTEP / 8;    // 16-byte chunks per row
+  for (int i = threadIdx.x; i < rows * CH; i += 256) {
+    const int r = i / CH, cc = i % CH;
+    const int64_t gr = row0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (gr >= row_lo && gr < row_hi)
+      v = *reinterpret_cast<const u32x4*>(g + gr * ld + k0 + cc * 8);
+    *reinterpret_cast<u32x4*>(lds + r * LDK + cc * 8) = v;
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int col) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + row * LDK + col));
+}
+
+// CSA, m = 4.  Block: 64 tokens x 32 channels (16 entries); wave w owns
+// tokens [16w, 16w+16) = entries [4w, 4w+4).  In the 16x16 MFMA output a lane
+// holds 4 consecutive rows of one column, i.e. exactly the 4 a-tokens (or
+// b-tokens) of one entry for one channel, so the pooling runs in registers.
+__global__ __launch_bounds__(256) void csa_compress_mfma(CompressArgs a) {
+  __shared__ uint16_t As[68 * LDK];    // tokens T0-4 .. T0+63
+  __shared__ uint16_t Bs[128 * LDK];   // 4 matrices x 32 channels
+  __shared__ float Ps[16][33];
+  const int c = a.c;
+  const int64_t T0 = (int64_t)blockIdx.x * 64;      // chunk-local token
+  const int j0 = blockIdx.y * 32;
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, col = l & 15;
+  const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[q][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t k0 = 0; k0 < a.d; k0 += KSTEP) {
+    // H rows: local token t sits at H row n_left + t; valid rows [0, n_left + n)
+    stage_rows(As, H, a.n_left + T0 - 4, 68, 0, a.n_left + a.n, a.d, k0);
+    for (int i = threadIdx.x; i < 128 * (KSTEP / 8); i += 256) {
+      const int r = i / (KSTEP / 8), cc = i % (KSTEP / 8);
+      const int q = r >> 5, jj = r & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(W + (int64_t)(q * c + j0 + jj) * a.d + k0 + cc * 8);
+      *reinterpret_cast<u32x4*>(Bs + r * LDK + cc * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KSTEP; kk += 32) {
+      const bf16x8 fa = lds_frag(As, 16 * wv + 4 + col, kk + 8 * g);   // a-tokens
+      const bf16x8 fb = lds_frag(As, 16 * wv + col, kk + 8 * g);       // b-tokens (shifted by -m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 fw = lds_frag(Bs, 32 * q + 16 * h + col, kk + 8 * g);
+          acc[q][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((q & 1) ? fb : fa, fw, acc[q][h], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds tokens T0 + 16w + 4g + i (i < 4) = entry e of channel j
+  const int64_t e = blockIdx.x * 16 + 4 * wv + g;          // chunk-local entry
+  const int64_t n_ent = a.n / 4;
+  const bool has_b = (a.block0 + e) >= 1;
+  const int rrb = row_bytes(a.raw_layout, c);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = j0 + 16 * h + col;
+    float La[4], Lb[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      La[i] = acc[2][h][i] + a.bias[i * c + j];
+      Lb[i] = acc[3][h][i] + a.bias[(4 + i) * c + j];
+      mx = fmaxf(mx, La[i]);
+      if (has_b) mx = fmaxf(mx, Lb[i]);
+    }
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float w = __expf(La[i] - mx);
+      num = fmaf(w, acc[0][h][i], num);
+      den += w;
+    }
+    if (has_b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w = __expf(Lb[i] - mx);
+        num = fmaf(w, acc[1][h][i], num);
+        den += w;
+      }
+    }
+    Ps[4 * wv + g][16 * h + col] = num / den;
+    if (a.raw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tok = T0 + 16 * wv + 4 * g + i;
+        if (tok < a.n)
+          store_row_elem(reinterpret_cast<uint8_t*>(a.raw) + tok * rrb, a.raw_layout, c, j, acc[0][h][i]);
+      }
+    }
+  }
+  __syncthreads();
+  // pack: 16 entries x 32 channels; a 32-lane group per entry, two passes
+  const int rb = row_bytes(a.comp_layout, c);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int el = pass * 8 + (threadIdx.x >> 5);
+    const int64_t ee = blockIdx.x * 16 + el;
+    if (ee < n_ent)   // uniform across the 32-lane group
+      pack32(Ps[el][threadIdx.x & 31], threadIdx.x & 31,
+             reinterpret_cast<uint8_t*>(a.comp) + ee * rb,
+             a.comp_scales ? a.comp_scales + ee * (c / 32) : nullptr, a.comp_layout, c, j0);
+  }
+}
+
+// HCA, m' = 128.  Block: one entry (128 tokens) x 32 channels; wave w owns
+// tokens [32w, 32w+32) as two 16-row MFMA tiles.  The per-channel softmax
+// over 128 rows reduces within lanes, across the 4 lane groups and across
+// the 4 waves.
+__global__ __launch_bounds__(256) void hca_compress_mfma(CompressArgs a) {
+  __shared__ uint16_t As[128 * LDK];
+  __shared__ uint16_t Bs[64 * LDK];
+  __shared__ float red[4][32];
+  __shared__ float red2[4][32];
+  __shared__ float Ps[32];
+  const int c = a.c;
+  const int64_t T0 = (int64_t)blockIdx.x * 128;
+  const int j0 = blockIdx.y * 32;
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, col = l & 15;
+  const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
+
+  f32x4 acc[2][2][2];   // [mtile][KV/Z][channel half]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[t][q][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t k0 = 0; k0 < a.d; k0 += KSTEP) {
+    stage_rows(As, H, T0, 128, 0, a.n, a.d, k0);
+    for (int i = threadIdx.x; i < 64 * (KSTEP / 8); i += 256) {
+      const int r = i / (KSTEP / 8), cc = i % (KSTEP / 8);
+      const int q = r >> 5, jj = r & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(W + (int64_t)(q * c + j0 + jj) * a.d + k0 + cc * 8);
+      *reinterpret_cast<u32x4*>(Bs + r * LDK + cc * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KSTEP; kk += 32) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 fa = lds_frag(As, 32 * wv + 16 * t + col, kk + 8 * g);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[t][q][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fa, lds_frag(Bs, 32 * q + 16 * h + col, kk + 8 * g), acc[t][q][h], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  const bool complete = T0 + 128 <= a.n;
+  const int rrb = row_bytes(a.raw_layout, c);
+  float M[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = j0 + 16 * h + col;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wv + 16 * t + 4 * g + i;
+        acc[t][1][h][i] += a.bias[r * c + j];          // logit Z + B
+        mx = fmaxf(mx, acc[t][1][h][i]);
+        if (a.raw && T0 + r < a.n)
+          store_row_elem(reinterpret_cast<uint8_t*>(a.raw) + (T0 + r) * rrb, a.raw_layout, c, j,
+                         acc[t][0][h][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) red[wv][16 * h + col] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = 16 * h + col;
+    M[h] = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w = __expf(acc[t][1][h][i] - M[h]);
+        num = fmaf(w, acc[t][0][h][i], num);
+        den += w;
+      }
+    num += __shfl_xor(num, 16);
+    num += __shfl_xor(num, 32);
+    den += __shfl_xor(den, 16);
+    den += __shfl_xor(den, 32);
+    __syncthreads();   // red is reused below
+    if (g == 0) { red[wv][cc] = num; red2[wv][cc] = den; }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      const int c2 = 16 * h + threadIdx.x;
+      Ps[c2] = ((red[0][c2] + red[1][c2]) + (red[2][c2] + red[3][c2])) /
+               ((red2[0][c2] + red2[1][c2]) + (red2[2][c2] + red2[3][c2]));
+    }
+  }
+  __syncthreads();
+  if (complete && threadIdx.x < 32) {
+    const int rb = row_bytes(a.comp_layout, c);
+    pack32(Ps[threadIdx.x], threadIdx.x, reinterpret_cast<uint8_t*>(a.comp) + blockIdx.x * rb,
+           a.comp_scales ? a.comp_scales + blockIdx.x * (c / 32) : nullptr, a.comp_layout, c, j0);
+  }
+}
+
+// ------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------
+static bool mfma_ok(const CompressArgs& a, int want_m) {
+  return a.act == ACT_BF16 && a.m == want_m && a.c % 32 == 0 && a.d % KSTEP == 0 && a.n > 0;
+}
+
+hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  if (mfma_ok(a, 4)) {
+    dim3 grid((unsigned)((a.n + 63) / 64), (unsigned)(a.c / 32));
+    hipLaunchKernelGGL(csa_compress_mfma, grid, dim3(256), 0, s, a);
+  } else {
+    const int64_t slots = (a.n + a.m - 1) / a.m;
+    const int64_t threads = slots * a.c;
+    hipLaunchKernelGGL(csa_compress_generic, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hca_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  if (mfma_ok(a, 128)) {
+    dim3 grid((unsigned)((a.n + 127) / 128), (unsigned)(a.c / 32));
+    hipLaunchKernelGGL(hca_compress_mfma, grid, dim3(256), 0, s, a);
+  } else {
+    const int64_t slots = (a.n + a.m - 1) / a.m;
+    const int64_t threads = slots * a.c;
+    hipLaunchKernelGGL(hca_compress_generic, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsv4

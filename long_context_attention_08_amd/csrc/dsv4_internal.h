@@ -1,0 +1,83 @@
+// Host-side launchers of the libdsv4attn kernels (internal; the public C ABI
+// is include/dsv4attn.h).  Every launcher assumes validated arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+struct CompressArgs {
+  const void* H;        // [n_left + n, d]
+  int64_t n_left, n, d;
+  int act;              // ACT_F32 / ACT_BF16
+  const void* W;        // [nmat * c, d]
+  const float* bias;    // CSA [2, m, c]; HCA [m', c]
+  int m, c;
+  int64_t block0;       // CSA: absolute index of the first emitted entry
+  void* comp;           // [n/m rows]
+  uint8_t* comp_scales; // MXFP4 scales [n/m, c/32]
+  int comp_layout;
+  void* raw;            // [n rows] or null
+  int raw_layout;
+};
+
+hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_hca_compress(const CompressArgs& a, hipStream_t s);
+
+struct IndexerArgs {
+  const void* qI;       // [B, nq, hI, cI]
+  int q_dtype;
+  const float* wI;      // [B, nq, hI]
+  const void* keys;     // [B, S, row]
+  const uint8_t* k_scales;
+  int k_layout;
+  int64_t B, nq;
+  int hI, cI;
+  int64_t S;
+  int m;
+  float* scores;        // [B, nq, S]
+};
+
+// Per-batch absolute positions travel to the kernels by value: a launch covers
+// at most MAXB batch entries (launchers loop over larger batches).
+constexpr int MAXB = 64;
+struct PosTable {
+  int64_t q_pos0[MAXB];
+  int64_t win_pos0[MAXB];
+};
+
+// q_pos0: host array [B]
+hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s);
+
+size_t topk_workspace_bytes(int64_t rows, int64_t S, int k);
+bool topk_supported(int64_t rows, int64_t S, int k);
+hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                       const int64_t* q_pos0, int k, int32_t* idx, void* ws, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;        // [B, nq, nh, c]
+  int q_dtype;
+  int64_t B, nq;
+  int nh, c;
+  const void* kv_comp;  // [B, S, row]
+  int kv_layout;
+  int64_t S;
+  const int32_t* idx;   // sparse: [B, nq, k]; dense: null
+  int k;
+  int ratio;            // dense: m'
+  const void* kv_win;   // [B, W, row]
+  int64_t W;
+  int n_win;
+  const float* sink;    // [nh] or null
+  float scale;
+  void* out;            // [B, nq, nh, c]
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense);
+hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0,
+                       bool dense, hipStream_t s);
+
+}  // namespace dsv4

@@ -1,0 +1,243 @@
+// Lightning-indexer scores (DeepSeek-V4 digest, 模块 B eq 16; jsqmd blog 第二阶段):
+//   I[b, t, s] = sum_h wI[b, t, h] * ReLU(qI[b, t, h, :] . K[b, s, :])
+// for compressed entries visible to the query (m (s+1) <= p+1), -inf otherwise.
+//
+// MFMA path (bf16 queries, BF16 or MXFP4 keys, hI = 32, cI in {32, 64, 128}):
+// the 32 heads of a query are the M dimension of v_mfma_f32_32x32x16_bf16 and
+// 32 keys its N dimension.  Query fragments stay in registers for the whole
+// key loop; a 256-key tile is decoded once into LDS as bf16 (MXFP4 through the
+// gfx950 scaled fp4->bf16 conversion, which is exact) and shared by the four
+// waves.  The head reduction sum_h w_h ReLU(acc) runs on the accumulator
+// registers: 16 heads per lane plus one cross-lane add.
+#include "dsv4_common.h"
+#include "dsv4_internal.h"
+
+namespace dsv4 {
+
+// ------------------------------------------------------------------ generic
+__device__ __forceinline__ float key_elem(const IndexerArgs& a, int64_t b, int64_t s, int j) {
+  const int64_t row = b * a.S + s;
+  if (a.k_layout == ROW_MXFP4) {
+    const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys) + row * (a.cI / 2);
+    const uint32_t byte = codes[j >> 1];
+    const uint32_t nib = (j & 1) ? (byte >> 4) : (byte & 15u);
+    const uint32_t E = a.k_scales[row * (a.cI / 32) + (j >> 5)];
+    return e2m1_to_f32(nib) * e8m0_to_f32(E);
+  }
+  const uint8_t* r = reinterpret_cast<const uint8_t*>(a.keys) + row * row_bytes(a.k_layout, a.cI);
+  return load_row_elem(r, a.k_layout, a.cI, j);
+}
+
+__global__ void indexer_generic(IndexerArgs a, PosTable pt, int b0, int nb) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_b = a.nq * a.S;
+  if (gid >= per_b * nb) return;
+  const int64_t bl = gid / per_b;
+  const int64_t b = b0 + bl;
+  const int64_t t = (gid % per_b) / a.S;
+  const int64_t s = gid % a.S;
+  const int64_t p = pt.q_pos0[bl] + t;
+  float* out = a.scores + (b * a.nq + t) * a.S + s;
+  if (s >= visible_count(p, a.m, a.S)) { *out = -INFINITY; return; }
+  float score = 0.0f;
+  for (int h = 0; h < a.hI; ++h) {
+    const int64_t qbase = ((b * a.nq + t) * a.hI + h) * a.cI;
+    float dot = 0.0f;
+    for (int j = 0; j < a.cI; ++j) dot = fmaf(load_act(a.qI, a.q_dtype, qbase + j), key_elem(a, b, s, j), dot);
+    score = fmaf(a.wI[(b * a.nq + t) * a.hI + h], fmaxf(dot, 0.0f), score);
+  }
+  *out = score;
+}
+
+// ------------------------------------------------------------------ MFMA path
+constexpr int KT = 256;   // keys per LDS tile
+
+// WQ waves split the queries, 4/WQ waves split the 8 n-tiles of a key tile;
+// each wave holds QPW queries.
+template <int CI, int KL, int WQ, int QPW>
+__global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable pt, int b0,
+                                                        int qblocks, int tiles_per_split) {
+  constexpr int WK = 4 / WQ;          // waves along the key tile
+  constexpr int QB = WQ * QPW;        // queries per block
+  constexpr int NTW = 8 / WK;         // 32-key n-tiles per wave
+  constexpr int KS = CI / 16;         // MFMA k-steps
+  constexpr int LDK = CI + 8;
+  __shared__ uint16_t Ks[KT * LDK];
+
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int wq = wv / WK, wk = wv % WK;
+  const int bl = blockIdx.x / qblocks;
+  const int64_t b = b0 + bl;
+  const int64_t t0 = (int64_t)(blockIdx.x % qblocks) * QB;
+  const int64_t S = a.S;
+  const int64_t ntiles = (S + KT - 1) / KT;
+  const int64_t tile_lo = (int64_t)blockIdx.y * tiles_per_split;
+  const int64_t tile_hi = tile_lo + tiles_per_split < ntiles ? tile_lo + tiles_per_split : ntiles;
+  if (tile_lo >= tile_hi) return;
+
+  // query fragments (B operand is the key; A operand is the 32 heads x cI)
+  bf16x8 qf[QPW][KS];
+  float wh[QPW][16];
+  int64_t nvis[QPW];
+  bool qvalid[QPW];
+  int64_t nvis_max = 0;
+  for (int qi = 0; qi < QB; ++qi) {           // block-wide maximum (uniform)
+    const int64_t t = t0 + qi;
+    if (t < a.nq) {
+      const int64_t v = visible_count(pt.q_pos0[bl] + t, a.m, S);
+      nvis_max = v > nvis_max ? v : nvis_max;
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    const int64_t t = t0 + wq * QPW + qi;
+    qvalid[qi] = t < a.nq;
+    const int64_t tt = qvalid[qi] ? t : a.nq - 1;
+    nvis[qi] = qvalid[qi] ? visible_count(pt.q_pos0[bl] + t, a.m, S) : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.qI) + ((b * a.nq + tt) * 32 + (l & 31)) * CI;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qf[qi][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * (l >> 5)));
+    const float* wrow = a.wI + (b * a.nq + tt) * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wh[qi][r] = wrow[(r >> 2) * 8 + 4 * (l >> 5) + (r & 3)];
+  }
+
+  for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
+    const int64_t s0 = tile * KT;
+    if (s0 >= nvis_max) {
+      // nothing visible to any query of the block: -inf only
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (!qvalid[qi]) continue;
+        float* orow = a.scores + (b * a.nq + t0 + wq * QPW + qi) * S;
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int64_t s = s0 + (wk * NTW + nt) * 32 + (l & 31);
+          if (l < 32 && s < S) orow[s] = -INFINITY;
+        }
+      }
+      continue;
+    }
+    // ---- decode the key tile into LDS (bf16)
+    if (KL == ROW_MXFP4) {
+      constexpr int CB = CI / 2;            // code bytes per key
+      constexpr int NB = CI / 32;           // scale bytes per key
+      const int64_t s = s0 + threadIdx.x;
+      uint32_t out[CI / 2];
+      if (s < S) {
+        const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + (b * S + s) * CB;
+        const uint8_t* sr = a.k_scales + (b * S + s) * NB;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          const float sc = e8m0_to_f32(sr[blk]);
+          const u32x4 w = *reinterpret_cast<const u32x4*>(cr + 16 * blk);
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+#pragma unroll
+            for (int by = 0; by < 4; ++by) out[blk * 16 + dw * 4 + by] = fp4x2_to_bf16x2(w[dw], by, sc);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CI / 2; ++i) out[i] = 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < CI / 8; ++i)
+        *reinterpret_cast<u32x4*>(Ks + threadIdx.x * LDK + 8 * i) =
+            (u32x4){out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+    } else {   // BF16 keys
+      constexpr int CH = CI / 8;            // 16-byte chunks per key
+      for (int i = threadIdx.x; i < KT * CH; i += 256) {
+        const int kr = i / CH, cc = i % CH;
+        const int64_t s = s0 + kr;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (s < S) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.keys) + (b * S + s) * CI + 8 * cc);
+        *reinterpret_cast<u32x4*>(Ks + kr * LDK + 8 * cc) = v;
+      }
+    }
+    __syncthreads();
+    // ---- scores
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int ntile = wk * NTW + nt;
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (ntile * 32 + (l & 31)) * LDK + 16 * kk + 8 * (l >> 5)));
+      const int64_t s = s0 + ntile * 32 + (l & 31);
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][kk], kf[kk], acc, 0, 0, 0);
+        float sc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc = fmaf(wh[qi][r], fmaxf(acc[r], 0.0f), sc);
+        sc += __shfl_xor(sc, 32);
+        if (qvalid[qi] && l < 32 && s < S)
+          a.scores[(b * a.nq + t0 + wq * QPW + qi) * S + s] = s < nvis[qi] ? sc : -INFINITY;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int CI, int KL>
+static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
+  const int64_t ntiles = (a.S + KT - 1) / KT;
+  if (a.nq >= 16) {
+    constexpr int WQ = 4, QPW = 4;
+    const int qblocks = (int)((a.nq + WQ * QPW - 1) / (WQ * QPW));
+    int64_t units = (int64_t)qblocks * nb;
+    int64_t splits = (4096 + units - 1) / units;
+    if (splits > ntiles) splits = ntiles;
+    if (splits < 1) splits = 1;
+    const int tps = (int)((ntiles + splits - 1) / splits);
+    splits = (ntiles + tps - 1) / tps;
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+                       a, pt, b0, qblocks, tps);
+  } else {
+    constexpr int WQ = 1, QPW = 1;
+    const int qblocks = (int)a.nq;
+    int64_t units = (int64_t)qblocks * nb;
+    int64_t splits = (2048 + units - 1) / units;
+    if (splits > ntiles) splits = ntiles;
+    if (splits < 1) splits = 1;
+    const int tps = (int)((ntiles + splits - 1) / splits);
+    splits = (ntiles + tps - 1) / tps;
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+                       a, pt, b0, qblocks, tps);
+  }
+}
+
+static bool indexer_mfma_ok(const IndexerArgs& a) {
+  return a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 32 || a.cI == 64 || a.cI == 128) &&
+         (a.k_layout == ROW_BF16 || a.k_layout == ROW_MXFP4);
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s) {
+  if (a.nq <= 0 || a.S <= 0 || a.B <= 0) return hipSuccess;
+  for (int64_t b0 = 0; b0 < a.B; b0 += MAXB) {
+    const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
+    PosTable pt;
+    for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
+    if (indexer_mfma_ok(a)) {
+      const bool mx = a.k_layout == ROW_MXFP4;
+      switch (a.cI) {
+        case 32: mx ? launch_mfma_variant<32, ROW_MXFP4>(a, pt, (int)b0, nb, s) : launch_mfma_variant<32, ROW_BF16>(a, pt, (int)b0, nb, s); break;
+        case 64: mx ? launch_mfma_variant<64, ROW_MXFP4>(a, pt, (int)b0, nb, s) : launch_mfma_variant<64, ROW_BF16>(a, pt, (int)b0, nb, s); break;
+        default: mx ? launch_mfma_variant<128, ROW_MXFP4>(a, pt, (int)b0, nb, s) : launch_mfma_variant<128, ROW_BF16>(a, pt, (int)b0, nb, s); break;
+      }
+    } else {
+      const int64_t total = a.nq * a.S * nb;
+      hipLaunchKernelGGL(indexer_generic, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pt, (int)b0, nb);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dsv4

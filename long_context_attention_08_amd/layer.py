@@ -1,0 +1,114 @@
+"""Interleaved CSA + HCA layer pair over one chunk of a chunked prefill.
+
+DeepSeek-V4 digest (ai-papers-daily page "DeepSeek-V4: Towards Highly
+Efficient Million-Token Context Intelligence"): CSA and HCA layers alternate
+layer by layer (核心思路); the compressed entries of a prefix are cached and
+reused, and only complete blocks produce entries (模块 F).
+
+One `step()` enqueues, on one stream, the seven calls of the pair:
+  CSA: compress KV (appended to the KV cache, window rows to the CSA window
+       buffer), compress indexer keys (appended), index scores, top-k,
+       sparse MQA;
+  HCA: compress (appended, window rows to the HCA window buffer), dense MQA.
+Buffers are torch tensors owned by the caller; nothing is allocated in step().
+"""
+import math
+
+from . import _lib as L
+
+
+class PairLayer:
+    def __init__(self, *, H, n_left, m, mp, c, cI, hI, nh, k, n_win,
+                 W_kv, B_kv, W_ki, B_ki, W_hca, B_hca,
+                 kv_cache, S0, ki_codes, ki_scales, hca_cache, Sh0, kv_win, hca_win, win_pos0,
+                 q, qI, wI, q_hca, sink, sink_hca, q_pos0, kv_layout, key_layout):
+        import torch
+        self.__dict__.update(locals())
+        del self.__dict__["self"]
+        self.n = H.shape[0] - n_left
+        n = self.n
+        self.scale = 1.0 / math.sqrt(c)
+        self.S = S0 + n // m
+        self.Sh = Sh0 + n // mp
+        dev = H.device
+        self.scores = torch.empty((1, n, self.S), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((1, n, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q)
+        self.out_hca = torch.empty_like(q_hca)
+        nb = L.topk_workspace_size(1, n, self.S, k)
+        self.ws_topk = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        nb = max(L.attn_workspace_size(False, 1, n, nh, c, k + n_win),
+                 L.attn_workspace_size(True, 1, n, nh, c, self.Sh + n_win))
+        self.ws_attn = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        rb = L.row_bytes(kv_layout, c)
+        self.kv_new = kv_cache[S0:self.S]
+        self.kv_win_new = kv_win[n_win:n_win + n]
+        self.ki_new = ki_codes[S0:self.S]
+        self.ki_sc_new = ki_scales[S0:self.S]
+        self.hca_new = hca_cache[Sh0:self.Sh]
+        self.hca_win_new = hca_win[n_win:n_win + n]
+        assert kv_cache.shape[1] == rb and hca_cache.shape[1] == rb
+
+    # the CSA and HCA halves are separate so that each can be timed
+    def csa_compress(self, stream=None):
+        L.csa_compress(self.H, self.W_kv, self.B_kv, self.m, self.c, self.kv_new, self.kv_layout,
+                       n_left=self.n_left, block0=self.S0, raw_out=self.kv_win_new, raw_layout=self.kv_layout,
+                       stream=stream)
+        L.csa_compress(self.H, self.W_ki, self.B_ki, self.m, self.cI, self.ki_new, self.key_layout,
+                       n_left=self.n_left, block0=self.S0, comp_scales=self.ki_sc_new, stream=stream)
+
+    def indexer(self, stream=None):
+        L.indexer_score(self.qI.view(1, self.n, self.hI, self.cI), self.wI.view(1, self.n, self.hI),
+                        self.ki_codes[:self.S].view(1, self.S, -1), self.key_layout, self.m, self.q_pos0,
+                        self.scores, k_scales=self.ki_scales[:self.S].view(1, self.S, -1), stream=stream)
+
+    def topk(self, stream=None):
+        L.topk_select(self.scores, self.m, self.q_pos0, self.k, self.idx, self.ws_topk, stream=stream)
+
+    def sparse(self, stream=None):
+        L.sparse_mqa_fwd(self.q.view(1, self.n, self.nh, self.c), self.kv_cache[:self.S].view(1, self.S, -1),
+                         self.kv_layout, self.idx, self.kv_win.view(1, -1, self.kv_win.shape[1]), self.win_pos0,
+                         self.n_win, self.q_pos0, self.sink, self.scale, self.out.view(1, self.n, self.nh, self.c),
+                         self.ws_attn, stream=stream)
+
+    def hca_compress(self, stream=None):
+        L.hca_compress(self.H[self.n_left:], self.W_hca, self.B_hca, self.mp, self.c, self.hca_new,
+                       self.kv_layout, raw_out=self.hca_win_new, raw_layout=self.kv_layout, stream=stream)
+
+    def hca_dense(self, stream=None):
+        L.hca_dense_fwd(self.q_hca.view(1, self.n, self.nh, self.c), self.hca_cache[:self.Sh].view(1, self.Sh, -1),
+                        self.kv_layout, self.mp, self.hca_win.view(1, -1, self.hca_win.shape[1]), self.win_pos0,
+                        self.n_win, self.q_pos0, self.sink_hca, self.scale,
+                        self.out_hca.view(1, self.n, self.nh, self.c), self.ws_attn, stream=stream)
+
+    def step(self, stream=None):
+        self.csa_compress(stream)
+        self.indexer(stream)
+        self.topk(stream)
+        self.sparse(stream)
+        self.hca_compress(stream)
+        self.hca_dense(stream)
+
+
+def pair_from_arrays(inp, device="cuda"):
+    """Upload the stored numpy arrays of a layer-pair workload and build the layer."""
+    import numpy as np
+    import torch
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(x).to(device)
+
+    cfg = inp["cfg"]
+    n, nh, c, hI, cI = cfg["n"], cfg["nh"], cfg["c"], cfg["hI"], cfg["cI"]
+    return PairLayer(
+        H=up(inp["H"]), n_left=cfg["n_left"], m=cfg["m"], mp=cfg["mp"], c=c, cI=cI, hI=hI, nh=nh, k=cfg["k"],
+        n_win=cfg["n_win"], W_kv=up(inp["W_kv"]), B_kv=up(inp["B_kv"]), W_ki=up(inp["W_ki"]),
+        B_ki=up(inp["B_ki"]), W_hca=up(inp["W_hca"]), B_hca=up(inp["B_hca"]),
+        kv_cache=up(inp["kv_cache"]), S0=inp["S0"], ki_codes=up(inp["ki_codes"]), ki_scales=up(inp["ki_scales"]),
+        hca_cache=up(inp["hca_cache"]), Sh0=inp["Sh0"], kv_win=up(inp["kv_win"]), hca_win=up(inp["hca_win"]),
+        win_pos0=[int(inp["win_pos0"][0])], q=up(inp["q"]).view(n, nh, c), qI=up(inp["qI"]), wI=up(inp["wI"]),
+        q_hca=up(inp["q_hca"]).view(n, nh, c), sink=up(inp["sink"]), sink_hca=up(inp["sink_hca"]),
+        q_pos0=[int(inp["q_pos0"][0])], kv_layout=cfg["kv_layout"], key_layout=cfg["key_layout"])

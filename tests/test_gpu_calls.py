@@ -1,0 +1,329 @@
+"""Per-call parity of the HIP library against the float64 oracle on seeded
+inputs, at sizes that span several tiles and a ragged tail, through the C ABI.
+Both kernel paths of each call are exercised: the MFMA path (bf16, the
+configuration shapes) and the generic fp32-math path (fp32 or odd shapes)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codecs as K
+import oracle as O
+from synth import gen as G
+from tests.dsv4_testlib import (ROW_BF16, ROW_F32, ROW_FP8, ROW_MXFP4, assert_close, assert_quantized, decode_act,
+                                dev, empty_rows, host, rows_to_f64, stored_rows_f64, topk_sets_match)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_attention_08_amd as lib
+    return lib
+
+
+def act_arr(seed, stream, shape, std, dtype):
+    x = G.normal(seed, stream, shape, std)
+    return G.to_bf16(x) if dtype == "bf16" else x
+
+
+# ====================================================================== compressors
+
+CSA_CASES = [
+    # (dtype, n, d, c, m, block0, n_left, comp_layout, raw_layout)
+    ("f32", 61, 24, 8, 4, 0, 0, ROW_F32, ROW_F32),                # generic, ragged tail
+    ("f32", 40, 16, 6, 2, 3, 2, ROW_F32, ROW_F32),                # generic, chunk with left context
+    ("bf16", 200, 128, 64, 4, 0, 0, ROW_F32, ROW_F32),            # MFMA, ragged
+    ("bf16", 256, 192, 128, 4, 0, 0, ROW_BF16, ROW_BF16),         # MFMA, bf16 outputs
+    ("bf16", 128, 128, 128, 4, 17, 4, ROW_FP8, ROW_FP8),          # MFMA, fp8 rows, chunked
+    ("bf16", 96, 64, 64, 4, 5, 4, ROW_MXFP4, ROW_F32),            # MFMA, MXFP4 keys
+    ("bf16", 64, 40, 32, 4, 0, 0, ROW_MXFP4, ROW_BF16),           # generic (d % 64 != 0), MXFP4
+    ("bf16", 36, 64, 64, 1, 0, 0, ROW_F32, ROW_F32),              # generic, m = 1
+]
+
+
+@pytest.mark.parametrize("case", CSA_CASES, ids=[str(i) for i in range(len(CSA_CASES))])
+def test_csa_compress(L, case):
+    import torch
+    dt, n, d, c, m, block0, n_left, cl, rl = case
+    seed = 100 + n + d + c
+    H = act_arr(seed, "H", (n_left + n, d), 1.0, dt)
+    W = act_arr(seed, "W_kv", (4 * c, d), 2.0 / math.sqrt(d), dt)   # larger Z logits exercise the softmax
+    B = G.normal(seed, "B_kv", (2, m, c), 0.5)
+    S = n // m
+    comp = empty_rows(max(S, 1), cl, c)
+    sc = torch.zeros((max(S, 1), c // 32), dtype=torch.uint8, device="cuda") if cl == ROW_MXFP4 else None
+    raw = empty_rows(n, rl, c)
+    L.csa_compress(dev(H), dev(W), dev(B), m, c, comp, cl, n_left=n_left, block0=block0, comp_scales=sc,
+                   raw_out=raw, raw_layout=rl)
+    torch.cuda.synchronize()
+    ref, ref_raw = O.csa_compress(decode_act(H), decode_act(W), B, m, block0, n_left)
+    got = rows_to_f64(comp[:S], cl, c, sc[:S] if sc is not None else None)
+    got_raw = rows_to_f64(raw, rl, c)
+    for g_, r_, lay, what in ((got, ref, cl, "comp"), (got_raw, ref_raw, rl, "raw")):
+        if lay == ROW_F32:
+            assert_close(g_, r_, fp32=True, tol=1e-4 * max(1.0, np.abs(r_).max()), what=what)
+        else:
+            assert_quantized(g_, r_, lay, what=what)
+
+
+HCA_CASES = [
+    ("f32", 70, 16, 8, 8, ROW_F32, ROW_F32),          # generic, ragged
+    ("bf16", 300, 128, 64, 128, ROW_F32, ROW_F32),    # MFMA, ragged tail
+    ("bf16", 512, 64, 128, 128, ROW_BF16, ROW_BF16),  # MFMA
+    ("bf16", 256, 128, 512, 128, ROW_FP8, ROW_FP8),   # MFMA, fp8 rows at c = 512
+    ("bf16", 64, 64, 32, 16, ROW_MXFP4, ROW_F32),     # generic, MXFP4
+]
+
+
+@pytest.mark.parametrize("case", HCA_CASES, ids=[str(i) for i in range(len(HCA_CASES))])
+def test_hca_compress(L, case):
+    import torch
+    dt, n, d, c, mp, cl, rl = case
+    seed = 200 + n + c
+    H = act_arr(seed, "H", (n, d), 1.0, dt)
+    W = act_arr(seed, "W_hca", (2 * c, d), 2.0 / math.sqrt(d), dt)
+    B = G.normal(seed, "B_hca", (mp, c), 0.5)
+    S = n // mp
+    comp = empty_rows(max(S, 1), cl, c)
+    sc = torch.zeros((max(S, 1), c // 32), dtype=torch.uint8, device="cuda") if cl == ROW_MXFP4 else None
+    raw = empty_rows(n, rl, c)
+    L.hca_compress(dev(H), dev(W), dev(B), mp, c, comp, cl, comp_scales=sc, raw_out=raw, raw_layout=rl)
+    torch.cuda.synchronize()
+    ref, ref_raw = O.hca_compress(decode_act(H), decode_act(W), B, mp)
+    got = rows_to_f64(comp[:S], cl, c, sc[:S] if sc is not None else None)
+    got_raw = rows_to_f64(raw, rl, c)
+    for g_, r_, lay, what in ((got, ref, cl, "comp"), (got_raw, ref_raw, rl, "raw")):
+        if lay == ROW_F32:
+            assert_close(g_, r_, fp32=True, tol=1e-4 * max(1.0, np.abs(r_).max()), what=what)
+        else:
+            assert_quantized(g_, r_, lay, what=what)
+
+
+def test_compress_validation_errors(L):
+    import torch
+    H = torch.zeros((16, 8), dtype=torch.float32, device="cuda")
+    W = torch.zeros((32, 8), dtype=torch.float32, device="cuda")
+    B = torch.zeros((2, 4, 8), dtype=torch.float32, device="cuda")
+    out = torch.zeros((4, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(L.Dsv4Error) as e:
+        L.csa_compress(H, W, B, 4, 8, out, ROW_F32, block0=2)          # no left context
+    assert e.value.status == 1
+    with pytest.raises(L.Dsv4Error) as e:
+        L.csa_compress(H, W, B, 4, 8, out, ROW_MXFP4)                 # c % 32 != 0
+    assert e.value.status == 2
+
+
+# ====================================================================== indexer
+
+IDX_CASES = [
+    # (q dtype, key layout, B, nq, hI, cI, S, m, pos0 list)
+    ("f32", ROW_F32, 2, 37, 4, 32, 70, 4, [0, 200]),            # generic
+    ("bf16", ROW_BF16, 1, 100, 32, 64, 600, 4, [1700]),         # MFMA prefill, ragged key tiles
+    ("bf16", ROW_MXFP4, 2, 40, 32, 64, 1000, 4, [3, 3900]),     # MFMA prefill, MXFP4, causal boundary
+    ("bf16", ROW_MXFP4, 3, 1, 32, 64, 5000, 4, [19999, 10000, 3]),   # MFMA decode mode
+    ("bf16", ROW_BF16, 1, 20, 32, 128, 300, 4, [1199]),         # MFMA, cI = 128
+    ("bf16", ROW_BF16, 1, 9, 16, 64, 50, 1, [30]),              # generic (hI = 16), m = 1
+]
+
+
+@pytest.mark.parametrize("case", IDX_CASES, ids=[str(i) for i in range(len(IDX_CASES))])
+def test_indexer_score(L, case):
+    import torch
+    qd, kl, B, nq, hI, cI, S, m, pos = case
+    seed = 300 + S + nq
+    qI = act_arr(seed, "qI", (B, nq, hI, cI), 0.5, qd)
+    wI = G.normal(seed, "wI", (B, nq, hI))
+    kx = G.normal(seed, "cache_ki", (B, S, cI))
+    keys, ksc = G.store(kx, kl) if kl != ROW_F32 else (kx, None)
+    scores = torch.full((B, nq, S), float("nan"), dtype=torch.float32, device="cuda")
+    L.indexer_score(dev(qI), dev(wI), dev(keys), kl, m, pos, scores, k_scales=dev(ksc) if ksc is not None else None)
+    got = host(scores)
+    for b in range(B):
+        kf = stored_rows_f64(keys[b], kl, cI, ksc[b] if ksc is not None else None)
+        ref = O.indexer_score(decode_act(qI[b]), wI[b].astype(np.float64), kf, m, pos[b] + np.arange(nq))
+        vis = np.isfinite(ref)
+        assert np.array_equal(np.isneginf(got[b]), ~vis), "visibility mask"
+        if vis.any():
+            scale = np.abs(ref[vis]).max()
+            err = np.abs(got[b][vis] - ref[vis]).max() / scale
+            assert err < 2e-5, "normalised score error %.3g" % err
+
+
+def test_indexer_small_integers_bit_exact(L):
+    """Small-integer queries/keys (E2M1 values) and weights in {+-1, +-2} make
+    every partial sum an exactly representable integer, so any accumulation
+    order gives the oracle's value bit for bit."""
+    import torch
+    rng = np.random.default_rng(7)
+    B, nq, hI, cI, S, m = 1, 48, 32, 64, 700, 4
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6], dtype=np.float32)
+    q = vals[rng.integers(0, len(vals), (B, nq, hI, cI))] * 2
+    kx = vals[rng.integers(0, len(vals), (B, S, cI))]
+    w = rng.choice(np.array([-2, -1, 1, 2], dtype=np.float32), (B, nq, hI))
+    for kl in (ROW_BF16, ROW_MXFP4):
+        keys, ksc = G.store(kx, kl)
+        kf = stored_rows_f64(keys[0], kl, cI, ksc[0] if ksc is not None else None)
+        scores = torch.empty((B, nq, S), dtype=torch.float32, device="cuda")
+        L.indexer_score(dev(G.to_bf16(q)), dev(w), dev(keys), kl, m, [2000], scores,
+                        k_scales=dev(ksc) if ksc is not None else None)
+        ref = O.indexer_score(q[0].astype(np.float64), w[0].astype(np.float64), kf, m, 2000 + np.arange(nq))
+        assert np.array_equal(host(scores)[0], ref.astype(np.float32))
+
+
+# ====================================================================== top-k
+
+TOPK_CASES = [
+    # (rows B, nq, S, k, m, pos0 list, value kind)
+    (1, 50, 256, 16, 4, [0], "int"),          # prefill causal, ties
+    (2, 30, 16384, 512, 4, [40000, 100], "normal"),
+    (1, 20, 40000, 1024, 4, [200000], "int"),  # two parts
+    (16, 1, 262144, 1024, 4, [1 << 20] * 16, "normal"),   # decode shape: 16 parts + merge
+    (1, 8, 300, 64, 1, [290], "zeros"),       # all ties incl. -0.0
+    (1, 4, 5000, 4096, 4, [30000], "normal"), # large k
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[str(i) for i in range(len(TOPK_CASES))])
+def test_topk_select_bit_exact(L, case):
+    import torch
+    B, nq, S, k, m, pos, kind = case
+    rng = np.random.default_rng(S + k)
+    if kind == "int":
+        sc = rng.integers(-20, 20, (B, nq, S)).astype(np.float32)
+    elif kind == "zeros":
+        sc = np.where(rng.random((B, nq, S)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        sc[..., ::7] = 1.0
+    else:
+        sc = G.normal(S, "extra", (B, nq, S), 10.0)
+    scores = dev(sc)
+    idx = torch.empty((B, nq, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, L.topk_workspace_size(B, nq, S, k)), dtype=torch.uint8, device="cuda")
+    L.topk_select(scores, m, pos, k, idx, ws)
+    got = host(idx)
+    for b in range(B):
+        ref = O.topk_select(sc[b].astype(np.float64), m, pos[b] + np.arange(nq), k)
+        assert np.array_equal(got[b], ref)
+
+
+# ====================================================================== attention cores
+
+def make_rows(seed, stream, shape, layout):
+    x = G.normal(seed, stream, shape)
+    st, _ = G.store(x, layout)
+    return st
+
+
+SPARSE_CASES = [
+    # (q dtype, layout, B, nq, nh, c, S, k, n_win, W, pos0, sink)
+    ("f32", ROW_F32, 2, 20, 8, 64, 40, 16, 64, 300, [100, 230], True),       # generic
+    ("bf16", ROW_BF16, 1, 40, 64, 128, 300, 64, 128, 1400, [1200], True),    # MFMA no split
+    ("bf16", ROW_FP8, 3, 2, 64, 512, 2000, 200, 128, 300, [250, 160, 130], True),   # MFMA split (decode)
+    ("bf16", ROW_FP8, 1, 33, 64, 512, 500, 100, 0, 0, [4000], False),        # no window
+    ("bf16", ROW_BF16, 1, 5, 64, 128, 50, 0, 16, 40, [20], True),            # k = 0: window only
+    ("bf16", ROW_BF16, 1, 6, 16, 128, 50, 8, 16, 40, [20], True),            # generic (nh = 16 sparse)
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[str(i) for i in range(len(SPARSE_CASES))])
+def test_sparse_mqa(L, case):
+    import torch
+    qd, lay, B, nq, nh, c, S, k, nw, W, pos, use_sink = case
+    seed = 500 + S + c + nq
+    rng = np.random.default_rng(seed)
+    q = act_arr(seed, "q", (B, nq, nh, c), 1.0, qd)
+    kv = make_rows(seed, "cache_kv", (B, S, c), lay)
+    win = make_rows(seed, "win_kv", (B, max(W, 1), c), lay)
+    wpos = [max(0, p - nw + 1) for p in pos]
+    idx = np.full((B, nq, max(k, 1)), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(nq):
+            sel = rng.choice(S, size=min(k, S), replace=False)
+            keep = rng.random(sel.size) > 0.1                       # some padding slots
+            idx[b, t, :sel.size] = np.where(keep, sel, -1)
+    if k == 0:
+        idx = idx[:, :, :0]
+    sink = G.normal(seed, "sink", (nh,), 0.5)
+    scale = 1 / math.sqrt(c)
+    qt = dev(q)
+    out = torch.empty_like(qt)
+    ws = torch.empty(max(1, L.attn_workspace_size(False, B, nq, nh, c, k + nw)), dtype=torch.uint8, device="cuda")
+    L.sparse_mqa_fwd(qt, dev(kv), lay, dev(idx) if k > 0 else None, dev(win) if nw > 0 else None, wpos, nw, pos,
+                     dev(sink) if use_sink else None, scale, out, ws, W=W)
+    got = host(out)
+    got = decode_act(got)
+    for b in range(B):
+        kvf = stored_rows_f64(kv[b], lay, c)
+        winf = stored_rows_f64(win[b], lay, c)[:W]
+        ref = O.sparse_mqa(decode_act(q[b]), kvf, idx[b], winf, wpos[b], nw, pos[b] + np.arange(nq),
+                           sink.astype(np.float64) if use_sink else None, scale)
+        assert_close(got[b], ref, fp32=(qd == "f32"), what="sparse b=%d" % b)
+
+
+DENSE_CASES = [
+    # (q dtype, layout, B, nq, nh, c, S, mp, n_win, pos0, sink)
+    ("f32", ROW_F32, 1, 30, 4, 64, 20, 8, 16, [120], True),                  # generic
+    ("bf16", ROW_BF16, 1, 70, 16, 128, 40, 128, 128, [4000], True),          # MFMA, 4 queries per block
+    ("bf16", ROW_FP8, 1, 40, 64, 512, 200, 128, 128, [20000], True),         # MFMA, c = 512
+    ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 128, [1 << 16, 30000], True), # decode: split + combine
+    ("bf16", ROW_BF16, 1, 37, 32, 128, 10, 16, 0, [100], False),             # 2 queries per block, no window
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[str(i) for i in range(len(DENSE_CASES))])
+def test_hca_dense(L, case):
+    import torch
+    qd, lay, B, nq, nh, c, S, mp, nw, pos, use_sink = case
+    seed = 600 + S + c + nq
+    q = act_arr(seed, "q", (B, nq, nh, c), 1.0, qd)
+    kv = make_rows(seed, "cache_hca", (B, S, c), lay)
+    wpos = [max(0, p - nw + 1) for p in pos]
+    W = nq + nw
+    win = make_rows(seed, "win_hca", (B, W, c), lay)
+    sink = G.normal(seed, "sink", (nh,), 0.5)
+    scale = 1 / math.sqrt(c)
+    qt = dev(q)
+    out = torch.empty_like(qt)
+    ws = torch.empty(max(1, L.attn_workspace_size(True, B, nq, nh, c, S + nw)), dtype=torch.uint8, device="cuda")
+    L.hca_dense_fwd(qt, dev(kv), lay, mp, dev(win), wpos, nw, pos, dev(sink) if use_sink else None, scale, out, ws)
+    got = decode_act(host(out))
+    for b in range(B):
+        ref = O.hca_dense(decode_act(q[b]), stored_rows_f64(kv[b], lay, c), mp, stored_rows_f64(win[b], lay, c),
+                          wpos[b], nw, pos[b] + np.arange(nq), sink.astype(np.float64) if use_sink else None, scale)
+        assert_close(got[b], ref, fp32=(qd == "f32"), what="dense b=%d" % b)
+
+
+def test_attention_decodes_every_fp8_code(L):
+    """q = 0 and a single key: the output is that key, so each stored E4M3 code
+    (all 254 finite ones) and the bf16 RoPE dims come back exactly."""
+    import torch
+    c, nh = 512, 64
+    codes = np.array([x for x in range(256) if x & 0x7F != 0x7F], dtype=np.uint8)
+    row = np.zeros((1, 1, c + 64), np.uint8)
+    row[0, 0, :254] = codes
+    row[0, 0, 254:448] = codes[:194]
+    row[0, 0, 448:] = G.to_bf16(G.normal(1, "extra", (64,))).view(np.uint8)
+    q = torch.zeros((1, 1, nh, c), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    idx = torch.zeros((1, 1, 1), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, L.attn_workspace_size(False, 1, 1, nh, c, 1)), dtype=torch.uint8, device="cuda")
+    L.sparse_mqa_fwd(q, dev(row), ROW_FP8, idx, None, [0], 0, [10], None, 0.1, out, ws)
+    got = decode_act(host(out))[0, 0]
+    want = K.decode_rows(row[0, 0], ROW_FP8, c)
+    # the output is stored as bf16: every E4M3 value and every bf16 value is exact in bf16
+    assert np.array_equal(got, np.broadcast_to(want, (nh, c)))
+
+
+def test_attention_window_must_be_covered(L):
+    import torch
+    q = torch.zeros((1, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    win = torch.zeros((1, 10, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    idx = torch.zeros((1, 4, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(L.Dsv4Error) as e:   # query 103 needs position 103 but rows cover [90, 100)
+        L.sparse_mqa_fwd(q, kv, ROW_BF16, idx, win, [90], 8, [100], None, 1.0, out, None)
+    assert e.value.status == 1
