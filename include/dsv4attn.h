@@ -144,6 +144,7 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
  *   l_x = scale * q[b,t,h] . key_x;  M = max(max_x l_x, sink[h])
  *   out[b,t,h] = sum_x e^{l_x-M} key_x / (sum_x e^{l_x-M} + e^{sink[h]-M})
  * Each key is also its value.  Entries of idx outside [0, S) are padding.
+ * scale must be finite and > 0 (1/sqrt(c) in the pages' reading).
  * sink NULL -> no sink term.  An empty key set gives a zero output.
  * q [B, nq, nh, c] q_dtype; out the same shape and dtype.
  * kv_comp [B, S, row] and kv_win [B, W, row] in kv_layout (F32 with F32

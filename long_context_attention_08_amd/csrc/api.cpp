@@ -214,7 +214,7 @@ static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, i
   if (c > 1024) return fail(DSV4_ERR_UNSUPPORTED, "%s: c=%d > 1024", fn, c);
   if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
   if (!kv_layout_ok(kv_layout, c)) return fail(DSV4_ERR_UNSUPPORTED, "%s: kv_layout %d with c=%d", fn, kv_layout, c);
-  if (!std::isfinite(scale)) return fail(DSV4_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(DSV4_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (B == 0 || nq == 0) return ok();
   if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
   int r = check_ptrs16(fn, {{q, "q"}, {out, "out"}});
@@ -241,7 +241,7 @@ static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, i
   int64_t max_keys = 0;
   for (int64_t b = 0; b < B; ++b) {
     const int64_t nc = dense ? dsv4::visible_count(q_pos0[b] + nq - 1, ratio, S) : k;
-    const int64_t kk = nc + (n_win > 0 ? n_win + 3 : 0);
+    const int64_t kk = nc + (n_win > 0 ? n_win + 7 : 0);
     max_keys = kk > max_keys ? kk : max_keys;
   }
   const size_t need = dsv4::attn_workspace_bytes(B, nq, nh, c, max_keys, dense);

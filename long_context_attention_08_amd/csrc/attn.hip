@@ -9,15 +9,11 @@
 //   out = sum_x e^{l_x - M} key_x / (sum_x e^{l_x - M} + e^{z'_h - M}),
 //   l_x = scale * q_h . key_x,   M = max(max_x l_x, z'_h).
 //
-// MFMA path (bf16 queries, BF16 or FP8+bf16-RoPE rows, c in {128, 512}, 64
-// head rows per block): each wave owns 16 heads of one query.  A 32-key tile is
-// gathered, decoded once to bf16 and written to LDS twice: row-major (keys) and
-// transposed (values).  Scores are computed transposed, S^T = K Q^T, so the
-// 16x16 MFMA output gives each lane the logits of ONE head; the online-softmax
-// state, the rescaling and the P^T operand of O^T = V^T P^T are then lane-local.
-// The running maximum is only raised when a tile exceeds it by 2^8 (exact in
-// the final normalisation, and bf16 P stays well inside range).  Short key
-// sets with few queries are split across blocks and merged in a fixed order.
+// MFMA path (bf16 queries, BF16 or FP8+bf16-RoPE rows, c in {128, 512}): see
+// the comment above attn_mfma.  The running maximum is only raised when a tile
+// exceeds it by 2^8 (exact after the final normalisation; bf16 P stays well
+// inside range).  Short key sets with few queries are split across blocks and
+// merged in a fixed order.
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
@@ -161,26 +157,69 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a, PosTable pt, int
 }
 
 // ------------------------------------------------------------------ MFMA path
-constexpr int TS = 32;       // key slots per tile
-constexpr int VTP = TS + 4;  // padded transposed row
+// Rows are (query, head) pairs.  A block owns R = 32*NRG rows (one query for
+// the sparse core; queries that share their keys for the dense core) and
+// streams its key slots in tiles of 32:
+//   * the raw stored rows of a tile are copied global -> LDS with
+//     global_load_lds_dwordx4 two tiles ahead (double-buffered stage, no
+//     registers held while the copies are in flight);
+//   * the stage is decoded once into a bf16 key tile [32][c] whose 16-byte
+//     chunks are XOR-swizzled by row, so that both the row reads of S^T and
+//     the transposed reads of V^T are free of bank conflicts;
+//   * wave (rg, ch) owns the 32 rows of row group rg and channel slice ch: it
+//     keeps Q^T and O^T of that slice in registers, computes the partial
+//     S^T = K Q^T with v_mfma_f32_32x32x16_bf16 and adds the partner slice's
+//     partial through LDS; each lane then owns the logits of one row for half
+//     of the tile's keys (the other half is in lane ^ 32);
+//   * O^T += V^T P^T takes its V^T operand straight from the row-major key
+//     tile with ds_read_b64_tr_b16 (K = V).
+constexpr int TS = 32;           // key slots per tile
+constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LDS
 
-template <int C>
-struct AttnLds {
-  uint16_t Ks[TS * (C + 8)];
-  uint16_t Vt[C * VTP];
-  int64_t pos[TS];
-  int win[TS];
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// the global->LDS copies still in flight (their completion is waited for
+// explicitly with vmcnt before the stage is read).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
+// 16-byte chunk swizzle of the bf16 key tile: chunk j of row r is stored at
+// chunk j ^ sw(r); sw takes 8 distinct values over 8 consecutive rows and 4
+// distinct even parts over 4 consecutive rows
+__device__ __forceinline__ int ksw(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+template <int C, int KVL, int CS, int NRG>
+struct AttnCfg {
+  static constexpr int NW = NRG * CS;
+  static constexpr int NT = 64 * NW;
+  static constexpr int R = 32 * NRG;
+  static constexpr int CH = C / CS;                 // channels per wave
+  static constexpr int KQ = CH / 16;                // S^T k-steps per wave
+  static constexpr int MO = CH / 32;                // O^T m-tiles per wave
+  static constexpr int RB = KVL == ROW_FP8 ? C + ROPE_DIMS : 2 * C;   // stored row bytes
+  static constexpr int NP = RB / 16;                // 16-byte pieces per stored row
+  static constexpr int NF8 = KVL == ROW_FP8 ? (C - ROPE_DIMS) / 16 : 0;   // fp8 pieces (16 channels each)
+  static constexpr int NDMA = TS * NP / 64;         // wave copies per tile
+  static constexpr int STAGE = TS * RB;             // bytes per stage buffer
 };
 
-template <int C, int KVL>
-__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
-  constexpr int LDK = C + 8;
-  constexpr int KK = C / 32;      // k-steps of S^T
-  constexpr int MO = C / 16;      // O^T m-tiles
-  __shared__ AttnLds<C> sm;
-  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, col = l & 15;
-  const int wpq = a.nh / 16;               // waves per query
-  const int qw = wv / wpq, hb = wv % wpq;
+template <int C, int KVL, int CS, int NRG>
+__global__ __launch_bounds__(64 * NRG * CS)
+__attribute__((amdgpu_waves_per_eu(C >= 512 ? 1 : 2, C >= 512 ? 1 : 2)))
+void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
+  using Cf = AttnCfg<C, KVL, CS, NRG>;
+  constexpr int KQ = Cf::KQ, MO = Cf::MO, CH = Cf::CH, NP = Cf::NP, RB = Cf::RB;
+  // separate LDS objects, so that alias analysis can tell the in-flight
+  // global->LDS copies (stage) from every other LDS access
+  __shared__ __align__(16) uint8_t s_stage[2][Cf::STAGE];   // piece-major: [piece][slot][16 B]
+  __shared__ __align__(16) uint16_t s_K[TS * C];             // bf16, chunk-swizzled
+  __shared__ __align__(16) float s_xb[CS > 1 ? NRG * CS * 4 * 64 * 4 : 4];   // [wave][r/4][lane][4]
+  __shared__ uint32_t s_vmask[8];                            // per query: visible slots of the tile
+  __shared__ int s_nvisq[8];
+  __shared__ int s_sidx[SIDX_CAP];
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, G = l >> 5, col = l & 31;
+  const int rg = wv / CS, ch = wv % CS;
   const int64_t bl = blockIdx.x / pl.units_per_b, u = blockIdx.x % pl.units_per_b;
   const int64_t b = b0 + bl;
   const int64_t p0 = pt.q_pos0[bl], wpos0 = pt.win_pos0[bl];
@@ -188,133 +227,238 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, PosTable pt, int
   const int64_t nsplit = pl.max_splits == 1 ? 1 : (ui.total + pl.chunk - 1) / pl.chunk;
   const int split = blockIdx.y;
   if (split > 0 && split >= nsplit) return;
-  const int64_t slot_lo = (int64_t)split * pl.chunk;
-  const int64_t slot_hi = pl.max_splits == 1 ? ui.total : (slot_lo + pl.chunk < ui.total ? slot_lo + pl.chunk : ui.total);
-  const int rb = row_bytes(KVL, C);
+  const int slot_lo = split * pl.chunk;
+  const int slot_hi = (int)(pl.max_splits == 1 ? ui.total : (slot_lo + pl.chunk < ui.total ? slot_lo + pl.chunk : ui.total));
+  const int ncomp = (int)ui.ncomp;
+  const uint8_t* comp_base = reinterpret_cast<const uint8_t*>(a.kv_comp) + b * a.S * (int64_t)RB;
+  const uint8_t* win_base = reinterpret_cast<const uint8_t*>(a.kv_win) + (b * a.W + (ui.wlo - wpos0)) * (int64_t)RB;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);     // any readable address
+  const int nq_blk = (int)(ui.tl - ui.t0 + 1);
+  const int pfirst = (int)(p0 + ui.t0);
+  const int ntiles = slot_hi > slot_lo ? (slot_hi - slot_lo + TS - 1) / TS : 0;
 
-  const int64_t t = ui.t0 + qw;
+  // block-level tables: visible compressed entries per query, cached index list
+  if (threadIdx.x < 8) s_nvisq[threadIdx.x] = pl.dense ? (int)visible_count(pfirst + threadIdx.x, a.ratio, a.S) : (int)a.S;
+  if (a.idx) {
+    const int32_t* irow = a.idx + (b * a.nq + ui.t0) * a.k;
+    const int n_i = (ncomp < slot_hi ? ncomp : slot_hi) - slot_lo;
+    for (int i = threadIdx.x; i < n_i; i += Cf::NT) s_sidx[i] = irow[slot_lo + i];
+  }
+  __syncthreads();
+
+  // the row this lane owns: (query t, head h)
+  const int row = 32 * rg + col;
+  const int qloc = row / a.nh;
+  const int h = row % a.nh;
+  const int64_t t = ui.t0 + qloc;
   const bool qvalid = t <= ui.tl;
   const int64_t tq = qvalid ? t : ui.tl;
-  const int64_t p = p0 + tq;
-  const int64_t nvis = pl.dense ? visible_count(p, a.ratio, a.S) : a.S;
-  const int h = 16 * hb + col;             // the head this lane owns
 
-  // Q^T fragments: lane holds q[h][32 kk + 8 g .. + 8]
-  bf16x8 qf[KK];
+  bf16x8 qf[KQ];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C + ch * CH;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g));
+    for (int kk = 0; kk < KQ; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * G));
   }
-  f32x4 acc[MO];
+  f32x16 acc[MO];
 #pragma unroll
-  for (int i = 0; i < MO; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MO; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float sl = pl.scale_log2;     // > 0
 
-  // loader mapping: 4 slots x 16 channels per thread
-  const int kg = threadIdx.x & 7, cs = threadIdx.x >> 3;
+  // stored row of slot s, or nullptr for padding; *pos, *win describe it
+  auto slot_src = [&](int s, int* pos, bool* win) -> const uint8_t* {
+    if (s < ncomp) {
+      *win = false;
+      const int e = a.idx ? s_sidx[s - slot_lo] : s;
+      *pos = e;
+      if (e < 0 || e >= a.S) return nullptr;
+      return comp_base + (int64_t)e * RB;
+    }
+    *win = true;
+    *pos = (int)ui.wlo + (s - ncomp);
+    return win_base + (int64_t)(s - ncomp) * RB;
+  };
 
-  for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += TS) {
-    if (cs < C / 16) {
-      uint32_t v[4][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t slot = s0 + 4 * kg + j;
-        int64_t pos = -1;
-        bool win = false;
-        const uint8_t* row = nullptr;
-        if (slot < slot_hi) row = slot_row(a, b, ui.t0, ui, wpos0, slot, rb, &pos, &win);
-        if (cs == 0) { sm.pos[4 * kg + j] = row ? pos : -1; sm.win[4 * kg + j] = win ? 1 : 0; }
-        if (!row) {
-#pragma unroll
-          for (int d = 0; d < 8; ++d) v[j][d] = 0u;
-        } else if (KVL == ROW_FP8 && 16 * cs < C - ROPE_DIMS) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(row + 16 * cs);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            v[j][2 * d] = e4m3x2_to_bf16x2(w[d], false);
-            v[j][2 * d + 1] = e4m3x2_to_bf16x2(w[d], true);
-          }
-        } else {
-          const uint8_t* src = KVL == ROW_FP8 ? row + (C - ROPE_DIMS) + 2 * (16 * cs - (C - ROPE_DIMS))
-                                              : row + 32 * cs;
-          const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
-          const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 16);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) { v[j][d] = w0[d]; v[j][4 + d] = w1[d]; }
+  // copies of tile `it` into stage buffer `buf`: wave copy q covers stage
+  // pieces [64 q, 64 q + 64); stage piece P = piece * TS + slot
+  auto issue = [&](int it, int buf) {
+    const int s0 = slot_lo + it * TS;
+    for (int q = wv; q < Cf::NDMA; q += Cf::NW) {
+      const int P = q * 64 + l;
+      const int piece = P / TS, sl_ = P % TS;
+      int pos;
+      bool win;
+      const uint8_t* src = (s0 + sl_ < slot_hi) ? slot_src(s0 + sl_, &pos, &win) : nullptr;
+      src = src ? src + 16 * piece : dummy;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_stage[buf] + q * 1024), 16, 0, 0);
+    }
+  };
+  // copies per wave and tile: waves below NDMA % NW issue one more
+  const int my_dma = Cf::NDMA / Cf::NW + (wv < Cf::NDMA % Cf::NW ? 1 : 0);
+
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  for (int it = 0; it < ntiles; ++it) {
+    const int s0 = slot_lo + it * TS;
+    const int buf = it & 1;
+    // wait for this wave's copies of tile `it` (those of tile it+1 may stay in flight)
+    if (it + 1 < ntiles) {
+      switch (my_dma) {
+        case 0: break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;   // vmcnt(1)
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+    }
+    lds_barrier();
+    // ---- decode the stage into the bf16 key tile
+    {
+      const uint8_t* st8 = s_stage[buf];
+      for (int un = threadIdx.x; un < TS * NP; un += Cf::NT) {
+        const int piece = un / TS, ks = un % TS;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st8 + (piece * TS + ks) * 16);
+        uint16_t* krow = s_K + ks * C;
+        if (piece < Cf::NF8) {              // 16 E4M3 channels -> two 16-byte chunks
+          const u32x4 lo = {e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
+                            e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
+          const u32x4 hi = {e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
+                            e4m3x2_to_bf16x2(w[3], false), e4m3x2_to_bf16x2(w[3], true)};
+          *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece) ^ ksw(ks))) = lo;
+          *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece + 1) ^ ksw(ks))) = hi;
+        } else {                            // 8 bf16 channels -> one chunk
+          const int chunk = 2 * Cf::NF8 + (piece - Cf::NF8);
+          *reinterpret_cast<u32x4*>(krow + 8 * (chunk ^ ksw(ks))) = w;
         }
-        uint16_t* kd = sm.Ks + (4 * kg + j) * LDK + 16 * cs;
-        *reinterpret_cast<u32x4*>(kd) = (u32x4){v[j][0], v[j][1], v[j][2], v[j][3]};
-        *reinterpret_cast<u32x4*>(kd + 8) = (u32x4){v[j][4], v[j][5], v[j][6], v[j][7]};
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t lo0 = (v[0][d] & 0xFFFFu) | (v[1][d] << 16);
-        const uint32_t lo1 = (v[2][d] & 0xFFFFu) | (v[3][d] << 16);
-        const uint32_t hi0 = (v[0][d] >> 16) | (v[1][d] & 0xFFFF0000u);
-        const uint32_t hi1 = (v[2][d] >> 16) | (v[3][d] & 0xFFFF0000u);
-        *reinterpret_cast<u32x2*>(sm.Vt + (16 * cs + 2 * d) * VTP + 4 * kg) = (u32x2){lo0, lo1};
-        *reinterpret_cast<u32x2*>(sm.Vt + (16 * cs + 2 * d + 1) * VTP + 4 * kg) = (u32x2){hi0, hi1};
       }
     }
-    __syncthreads();
+    if (wv == 0) {
+      uint32_t vbits = 0;
+      const int slot = s0 + l;
+      if (l < TS && slot < slot_hi) {
+        int pos;
+        bool win;
+        if (slot_src(slot, &pos, &win)) {
+          for (int q = 0; q < nq_blk; ++q) {
+            const int pq = pfirst + q;
+            const bool ok = win ? (pos <= pq && pos >= pq - a.n_win + 1) : (pos < s_nvisq[q]);
+            vbits |= (ok ? 1u : 0u) << q;
+          }
+        }
+      }
+      for (int q = 0; q < nq_blk; ++q) {
+        const uint64_t bal = __ballot((vbits >> q) & 1u);
+        if (l == 0) s_vmask[q] = (uint32_t)bal;
+      }
+    }
+    lds_barrier();
 
-    // S^T[key][head] for 32 keys (two 16-row tiles)
-    f32x4 st[2];
+    // ---- partial S^T[32 keys][32 rows] over this wave's channel slice, two chains
+    f32x16 st, st1;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      st[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 16; ++r) { st[r] = 0.f; st1[r] = 0.f; }
+    {
+      const uint16_t* krow = s_K + col * C;
+      const int swz = ksw(col);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(sm.Ks + (16 * mt + col) * LDK + 32 * kk + 8 * g));
-        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], st[mt], 0, 0, 0);
+      for (int kk = 0; kk < KQ; kk += 2) {
+        const int c0 = (ch * CH + 16 * kk + 8 * G) >> 3;          // logical chunk
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * (c0 ^ swz))), qf[kk], st, 0, 0, 0);
+        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * ((c0 + 2) ^ swz))), qf[kk + 1], st1, 0, 0, 0);
       }
     }
-    float x[2][4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] += st1[r];
+    if (CS > 1) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<f32x4*>(s_xb + ((wv * 4 + rr) * 64 + l) * 4) =
+            (f32x4){st[4 * rr], st[4 * rr + 1], st[4 * rr + 2], st[4 * rr + 3]};
+      lds_barrier();
+      const int pw = rg * CS + (ch ^ 1);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(s_xb + ((pw * 4 + rr) * 64 + l) * 4);
+        st[4 * rr] += o[0]; st[4 * rr + 1] += o[1]; st[4 * rr + 2] += o[2]; st[4 * rr + 3] += o[3];
+      }
+    }
+    // the copies of tile it+2 go out now (stage `buf` is free since its decode)
+    // and overlap the softmax, the PV MFMAs and the next tile's decode
+    if (it + 2 < ntiles) issue(it + 2, buf);
+    // ---- online softmax: register r holds key slot 8 (r/4) + 4 G + r%4 of this lane's row
+    const uint32_t m16 = (s_vmask[qloc] >> (4 * G)) & 0x0F0F0F0Fu;
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sl = 16 * mt + 4 * g + i;
-        const bool ok = sm.pos[sl] >= 0 && slot_visible(sm.win[sl] != 0, sm.pos[sl], p, nvis, a.n_win);
-        x[mt][i] = ok ? st[mt][i] * pl.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[mt][i]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    for (int r = 0; r < 16; ++r) {
+      st[r] = ((m16 >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] : -INFINITY;
+      tmax = fmaxf(tmax, st[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl;
     if (tmax > m_run + 8.0f) {
       const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - tmax);
       m_run = tmax;
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < MO; ++i) acc[i] *= alpha;
+      for (int i = 0; i < MO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
     }
-    float pr[2][4];
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    uint32_t pk[8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int r = 0; r < 16; r += 2) {
+      const float e0 = exp2f(fmaf(st[r], sl, mneg));
+      const float e1 = exp2f(fmaf(st[r + 1], sl, mneg));
+      l_run += e0 + e1;
+      pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
+    }
+    // ---- O^T[c][row] += V^T[c][keys] P^T[keys][row].  MFMA s covers key slots
+    // [16s + 4G, +4) and [16s + 8 + 4G, +4) in its eight k-slots; each half
+    // comes from one transposed read: lane (lambda = l % 16) of a 16-lane group
+    // addresses key row key0 + lambda/4, channels c0 + 4 (lambda % 4) .. + 4,
+    // and receives channel c0 + lambda of keys key0 .. key0 + 3.
+    {
+      const int lam = l & 15, grp = (l >> 4) & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[mt][i] = (x[mt][i] == -INFINITY) ? 0.f : exp2f(x[mt][i] - m_run);
-        l_run += pr[mt][i];
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 pf = as_bf16x8((u32x4){pk[4 * s], pk[4 * s + 1], pk[4 * s + 2], pk[4 * s + 3]});
+#pragma unroll
+        for (int mo = 0; mo < MO; ++mo) {
+          const int c0 = ch * CH + 32 * mo + 16 * grp + 4 * (lam & 3);   // element offset of this lane's read
+          const int e8 = c0 >> 2;                                         // 8-byte chunk
+          uint32_t hv[4];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int kr = 16 * s + 8 * hf + 4 * G + (lam >> 2);
+            const uint16_t* ad = s_K + kr * C + 8 * ((e8 >> 1) ^ ksw(kr)) + 4 * (e8 & 1);
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            const v4s tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)ad);
+            const u32x2 tw = __builtin_bit_cast(u32x2, tv);
+            hv[2 * hf] = tw[0];
+            hv[2 * hf + 1] = tw[1];
+          }
+          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){hv[0], hv[1], hv[2], hv[3]}), pf,
+                                                            acc[mo], 0, 0, 0);
+        }
       }
-    const u32x4 pw = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
-                      pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
-    const bf16x8 pf = as_bf16x8(pw);
-#pragma unroll
-    for (int mo = 0; mo < MO; ++mo) {
-      const uint16_t* vr = sm.Vt + (16 * mo + col) * VTP;
-      const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr + 4 * g);
-      const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * g);
-      const bf16x8 vf = as_bf16x8((u32x4){v0[0], v0[1], v1[0], v1[1]});
-      acc[mo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[mo], 0, 0, 0);
     }
-    __syncthreads();
   }
 
-  l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (!qvalid) return;
+  // register r of m-tile mo holds channel ch*CH + 32 mo + 8 (r/4) + 4 G + r%4 of this lane's row
   if (pl.max_splits == 1) {
     float f = m_run == -INFINITY ? 0.f : 1.f, den = l_run;
     if (a.sink) {
@@ -324,24 +468,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, PosTable pt, int
       den = l_run * f + exp2f(z - M);
     }
     const float inv = den > 0.f ? f / den : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C;
-#pragma unroll
-    for (int mo = 0; mo < MO; ++mo) {
-      const u32x2 w = {pack_bf16x2(acc[mo][0] * inv, acc[mo][1] * inv), pack_bf16x2(acc[mo][2] * inv, acc[mo][3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 16 * mo + 4 * g) = w;
-    }
-  } else {
-    // partials: [unit][split][qpw*nh] {m, l} and [unit][split][qpw*nh][C]
-    const int64_t unit = blockIdx.x;
-    const int64_t rows = (int64_t)pl.qpw * a.nh;
-    const int64_t r = (int64_t)qw * a.nh + h;
-    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + r) * 2;
-    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + r) * C;
-    if (g == 0) { ml[0] = m_run; ml[1] = l_run; }
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + ch * CH;
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
-      *reinterpret_cast<f32x4*>(ow + 16 * mo + 4 * g) = acc[mo];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = {__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j] * inv), (__bf16)(acc[mo][4 * j + 1] * inv)}),
+                         __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j + 2] * inv), (__bf16)(acc[mo][4 * j + 3] * inv)})};
+        *reinterpret_cast<u32x2*>(orow + 32 * mo + 8 * j + 4 * G) = w;
+      }
+  } else {
+    // partials: [unit][split][R rows] {m, l} and [unit][split][R rows][C]
+    const int64_t unit = blockIdx.x;
+    const int64_t rows = Cf::R;
+    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
+    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
+                ((unit * pl.max_splits + split) * rows + row) * C + ch * CH;
+    if (G == 0 && ch == 0) { ml[0] = m_run; ml[1] = l_run; }
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
+            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
   }
 }
 
@@ -383,16 +532,26 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
 // ------------------------------------------------------------------ planning and launch
 static bool attn_mfma_ok(const AttnArgs& a, bool dense) {
   if (a.q_dtype != ACT_BF16 || (a.kv_layout != ROW_BF16 && a.kv_layout != ROW_FP8)) return false;
-  if (a.c != 128 && a.c != 512) return false;
-  if (dense) return a.nh == 16 || a.nh == 32 || a.nh == 64;
-  return a.nh == 64;
+  if (!dense && a.k > SIDX_CAP) return false;
+  if (a.c == 512) return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
+  if (a.c == 128) return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64 || a.nh == 128)
+                               : (a.nh == 32 || a.nh == 64 || a.nh == 128);
+  return false;
+}
+
+// rows per block: one query (sparse) or 128 rows of queries sharing their keys (dense)
+// (c = 512 keeps one query per block: its Q^T and O^T slices already fill the register file)
+static int rows_per_block(const AttnArgs& a, bool dense) {
+  if (!dense) return a.nh;
+  if (a.c >= 512) return a.nh < 64 ? 64 : a.nh;
+  return a.nh > 128 ? a.nh : 128;
 }
 
 static AttnPlan make_plan(const AttnArgs& a, bool dense, int64_t max_keys) {
   AttnPlan pl;
   pl.dense = dense ? 1 : 0;
   pl.scale_log2 = a.scale * LOG2E;
-  pl.qpw = dense ? 64 / a.nh : 1;
+  pl.qpw = rows_per_block(a, dense) / a.nh;
   if (pl.qpw < 1) pl.qpw = 1;
   pl.units_per_b = (a.nq + pl.qpw - 1) / pl.qpw;
   // split the keys only when a sequence has few query groups; the split size
@@ -417,31 +576,45 @@ size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_ke
   return (size_t)units * pl.max_splits * pl.qpw * nh * (c + 2) * sizeof(float);
 }
 
+template <int C, int KVL, int CS>
+static void launch_mfma_c(const AttnArgs& a, dim3 grid, int nrg, const PosTable& pt, int b0, const AttnPlan& pl,
+                          hipStream_t s) {
+  constexpr int NRG_MAX = C >= 512 ? 2 : 4;     // c = 512 blocks hold at most 64 rows
+  switch (nrg) {
+    case 1: hipLaunchKernelGGL((attn_mfma<C, KVL, CS, 1>), grid, dim3(64 * 1 * CS), 0, s, a, pt, b0, pl); break;
+    case 2: hipLaunchKernelGGL((attn_mfma<C, KVL, CS, 2>), grid, dim3(64 * 2 * CS), 0, s, a, pt, b0, pl); break;
+    default:
+      hipLaunchKernelGGL((attn_mfma<C, KVL, CS, NRG_MAX>), grid, dim3(64 * NRG_MAX * CS), 0, s, a, pt, b0, pl);
+      break;
+  }
+}
+
 hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0, bool dense, hipStream_t s) {
   if (a.B <= 0 || a.nq <= 0) return hipSuccess;
   const bool mf = attn_mfma_ok(a, dense);
+  const int qpw = mf ? rows_per_block(a, dense) / a.nh : 1;
   // most key slots any group can have
   int64_t max_keys = 0;
   for (int64_t b = 0; b < a.B; ++b) {
     const int64_t pl_ = q_pos0[b] + a.nq - 1;
     const int64_t ncomp = dense ? visible_count(pl_, a.ratio, a.S) : a.k;
-    const int64_t qpw = mf && dense ? 64 / a.nh : 1;
-    const int64_t wl = a.n_win > 0 ? a.n_win + qpw - 1 : 0;
+    const int64_t wl = a.n_win > 0 ? a.n_win + (qpw < a.nq ? qpw : a.nq) - 1 : 0;
     max_keys = ncomp + wl > max_keys ? ncomp + wl : max_keys;
   }
   for (int64_t b0 = 0; b0 < a.B; b0 += MAXB) {
     const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
     PosTable pt;
-    for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = win_pos0[b0 + i]; }
+    for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = win_pos0 ? win_pos0[b0 + i] : 0; }
     if (mf) {
       AttnPlan pl = make_plan(a, dense, max_keys);
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
+      const int nrg = rows_per_block(a, dense) / 32;
       if (a.c == 512) {
-        if (a.kv_layout == ROW_FP8) hipLaunchKernelGGL((attn_mfma<512, ROW_FP8>), grid, dim3(256), 0, s, a, pt, (int)b0, pl);
-        else hipLaunchKernelGGL((attn_mfma<512, ROW_BF16>), grid, dim3(256), 0, s, a, pt, (int)b0, pl);
+        if (a.kv_layout == ROW_FP8) launch_mfma_c<512, ROW_FP8, 2>(a, grid, nrg, pt, (int)b0, pl, s);
+        else launch_mfma_c<512, ROW_BF16, 2>(a, grid, nrg, pt, (int)b0, pl, s);
       } else {
-        if (a.kv_layout == ROW_FP8) hipLaunchKernelGGL((attn_mfma<128, ROW_FP8>), grid, dim3(256), 0, s, a, pt, (int)b0, pl);
-        else hipLaunchKernelGGL((attn_mfma<128, ROW_BF16>), grid, dim3(256), 0, s, a, pt, (int)b0, pl);
+        if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1>(a, grid, nrg, pt, (int)b0, pl, s);
+        else launch_mfma_c<128, ROW_BF16, 1>(a, grid, nrg, pt, (int)b0, pl, s);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

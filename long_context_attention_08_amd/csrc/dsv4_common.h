@@ -46,9 +46,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi_word) {
   bf16x2 r = hi_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  uint32_t u;
-  __builtin_memcpy(&u, &r, 4);
-  return u;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // f32 -> E4M3, round to nearest even, saturating at +-448 (finite inputs).
@@ -80,9 +78,7 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t byte_word, int byte
     case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte_word, scale, 2); break;
     default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte_word, scale, 3); break;
   }
-  uint32_t u;
-  __builtin_memcpy(&u, &r, 4);
-  return u;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t E) {
@@ -159,11 +155,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // position of the first entry NOT visible at position p for ratio m: entries
 // s < floor((p+1)/m) satisfy m*(s+1) <= p+1
