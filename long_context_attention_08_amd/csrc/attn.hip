@@ -176,6 +176,16 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a, PosTable pt, int
 constexpr int TS = 32;           // key slots per tile
 constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LDS
 
+// 16-byte global -> LDS copy of every lane: lane l's bytes land at LDS address
+// lds_base + 16 l (lds_base wave-uniform).  Written as a two-instruction asm
+// block (M0 set in the same block) so that the compiler does not track it:
+// the kernel waits for these copies itself (vmcnt) before reading the stage.
+// The instruction has no register results, so nothing is written back into
+// VGPRs while it is in flight.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds_base) : "memory", "m0");
+}
+
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // the global->LDS copies still in flight (their completion is waited for
 // explicitly with vmcnt before the stage is read).
@@ -184,10 +194,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// 16-byte chunk swizzle of the bf16 key tile: chunk j of row r is stored at
-// chunk j ^ sw(r); sw takes 8 distinct values over 8 consecutive rows and 4
-// distinct even parts over 4 consecutive rows
-__device__ __forceinline__ int ksw(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// Layout of the bf16 key tile: rows of C + 16 elements (a stride of 32 bytes
+// mod 128), and 16-byte chunk j of row r stored at chunk j ^ ksw(r) with
+// ksw(r) = (r >> 2) & 3.  Eight consecutive rows then cover 8 distinct
+// 16-byte bank groups (row reads of S^T, the decode writes), and 4 consecutive
+// rows x 32 bytes cover all 32 banks (transposed reads of V^T).  The XOR only
+// touches the two low chunk bits, so every loop-varying part of an address is
+// an immediate offset.
+constexpr int KPAD = 16;
+__device__ __forceinline__ int ksw(int r) { return (r >> 2) & 3; }
 
 template <int C, int KVL, int CS, int NRG>
 struct AttnCfg {
@@ -212,13 +227,16 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   constexpr int KQ = Cf::KQ, MO = Cf::MO, CH = Cf::CH, NP = Cf::NP, RB = Cf::RB;
   // separate LDS objects, so that alias analysis can tell the in-flight
   // global->LDS copies (stage) from every other LDS access
-  __shared__ __align__(16) uint8_t s_stage[2][Cf::STAGE];   // piece-major: [piece][slot][16 B]
-  __shared__ __align__(16) uint16_t s_K[TS * C];             // bf16, chunk-swizzled
+  __shared__ __align__(16) uint8_t s_stage0[Cf::STAGE];     // piece-major: [piece][slot][16 B]
+  __shared__ __align__(16) uint8_t s_stage1[Cf::STAGE];
+  __shared__ __align__(16) uint16_t s_K[TS * (C + KPAD)];    // bf16, chunk-swizzled
   __shared__ __align__(16) float s_xb[CS > 1 ? NRG * CS * 4 * 64 * 4 : 4];   // [wave][r/4][lane][4]
   __shared__ uint32_t s_vmask[8];                            // per query: visible slots of the tile
+  __shared__ uint32_t s_vall;                                // AND of s_vmask over the block's queries
   __shared__ int s_nvisq[8];
   __shared__ int s_sidx[SIDX_CAP];
-  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, G = l >> 5, col = l & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
   const int rg = wv / CS, ch = wv % CS;
   const int64_t bl = blockIdx.x / pl.units_per_b, u = blockIdx.x % pl.units_per_b;
   const int64_t b = b0 + bl;
@@ -259,6 +277,9 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C + ch * CH;
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * G));
+    // land the query fragments before the tile copies start: a later wait for
+    // them would also wait for every copy issued after them
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   }
   f32x16 acc[MO];
 #pragma unroll
@@ -284,7 +305,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 
   // copies of tile `it` into stage buffer `buf`: wave copy q covers stage
   // pieces [64 q, 64 q + 64); stage piece P = piece * TS + slot
-  auto issue = [&](int it, int buf) {
+  auto issue = [&](int it, uint8_t* stg) {
     const int s0 = slot_lo + it * TS;
     for (int q = wv; q < Cf::NDMA; q += Cf::NW) {
       const int P = q * 64 + l;
@@ -293,17 +314,21 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
       bool win;
       const uint8_t* src = (s0 + sl_ < slot_hi) ? slot_src(s0 + sl_, &pos, &win) : nullptr;
       src = src ? src + 16 * piece : dummy;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_stage[buf] + q * 1024), 16, 0, 0);
+      const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + q * 1024);
+      dma16(src, __builtin_amdgcn_readfirstlane(lds));
     }
   };
   // copies per wave and tile: waves below NDMA % NW issue one more
   const int my_dma = Cf::NDMA / Cf::NW + (wv < Cf::NDMA % Cf::NW ? 1 : 0);
 
-  if (ntiles > 0) issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
-  for (int it = 0; it < ntiles; ++it) {
+  // a tile in two halves.  score(): wait for its copies, decode the stage,
+  // S^T, mask, tile maximum; returns whether some row must raise its running
+  // maximum.  accumulate(): P, O^T += V^T P^T, and the copies of tile it+2
+  // into the stage just decoded.
+  f32x16 st;
+  float tmax;
+  auto score = [&](int it, uint8_t* stg) -> bool {
     const int s0 = slot_lo + it * TS;
-    const int buf = it & 1;
     // wait for this wave's copies of tile `it` (those of tile it+1 may stay in flight)
     if (it + 1 < ntiles) {
       switch (my_dma) {
@@ -316,29 +341,56 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
         case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
         case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+        case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+        case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
         default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
       }
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
     }
     lds_barrier();
-    // ---- decode the stage into the bf16 key tile
+    // ---- decode the stage into the bf16 key tile.  Stage unit un (16 bytes)
+    // is piece un / TS of slot un % TS; the E4M3 units come first.  Fixed trip
+    // counts with all stage reads issued before the conversions; the guards
+    // are uniform per wave (NT is a multiple of 64 and so are the unit counts).
     {
-      const uint8_t* st8 = s_stage[buf];
-      for (int un = threadIdx.x; un < TS * NP; un += Cf::NT) {
-        const int piece = un / TS, ks = un % TS;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(st8 + (piece * TS + ks) * 16);
-        uint16_t* krow = s_K + ks * C;
-        if (piece < Cf::NF8) {              // 16 E4M3 channels -> two 16-byte chunks
+      constexpr int U8 = Cf::NF8 * TS, UB = (NP - Cf::NF8) * TS;
+      constexpr int N8 = (U8 + Cf::NT - 1) / Cf::NT, NB = (UB + Cf::NT - 1) / Cf::NT;
+      u32x4 w8[N8 > 0 ? N8 : 1], wb[NB > 0 ? NB : 1];
+#pragma unroll
+      for (int j = 0; j < N8; ++j) {
+        const int un = threadIdx.x + Cf::NT * j;
+        if (Cf::NT * (j + 1) <= U8 || un < U8) w8[j] = *reinterpret_cast<const u32x4*>(stg + un * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int un = U8 + threadIdx.x + Cf::NT * j;
+        if (Cf::NT * (j + 1) <= UB || un < U8 + UB) wb[j] = *reinterpret_cast<const u32x4*>(stg + un * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < N8; ++j) {
+        const int un = threadIdx.x + Cf::NT * j;
+        if (Cf::NT * (j + 1) <= U8 || un < U8) {   // 16 E4M3 channels -> two 16-byte chunks
+          const int piece = un / TS, ks = un % TS;
+          const u32x4 w = w8[j];
+          uint16_t* krow = s_K + ks * (C + KPAD);
           const u32x4 lo = {e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
                             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
           const u32x4 hi = {e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
                             e4m3x2_to_bf16x2(w[3], false), e4m3x2_to_bf16x2(w[3], true)};
           *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece) ^ ksw(ks))) = lo;
           *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece + 1) ^ ksw(ks))) = hi;
-        } else {                            // 8 bf16 channels -> one chunk
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int un = U8 + threadIdx.x + Cf::NT * j;
+        if (Cf::NT * (j + 1) <= UB || un < U8 + UB) {   // 8 bf16 channels -> one chunk
+          const int piece = un / TS, ks = un % TS;
           const int chunk = 2 * Cf::NF8 + (piece - Cf::NF8);
-          *reinterpret_cast<u32x4*>(krow + 8 * (chunk ^ ksw(ks))) = w;
+          *reinterpret_cast<u32x4*>(s_K + ks * (C + KPAD) + 8 * (chunk ^ ksw(ks))) = wb[j];
         }
       }
     }
@@ -356,27 +408,34 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
           }
         }
       }
+      uint32_t vall = 0xFFFFFFFFu;
       for (int q = 0; q < nq_blk; ++q) {
-        const uint64_t bal = __ballot((vbits >> q) & 1u);
-        if (l == 0) s_vmask[q] = (uint32_t)bal;
+        const uint32_t bal = (uint32_t)__ballot((vbits >> q) & 1u);
+        vall &= bal;
+        if (l == 0) s_vmask[q] = bal;
       }
+      if (l == 0) s_vall = vall;
     }
     lds_barrier();
 
     // ---- partial S^T[32 keys][32 rows] over this wave's channel slice, two chains
-    f32x16 st, st1;
+    f32x16 st1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { st[r] = 0.f; st1[r] = 0.f; }
     {
-      const uint16_t* krow = s_K + col * C;
-      const int swz = ksw(col);
+      // logical chunk of k-step kk: ch*CH/8 + 2 kk + G; only its two low bits
+      // meet the swizzle, so even and odd kk each get one base address
+      const uint16_t* krow = s_K + col * (C + KPAD);
+      const int x0 = ch * (CH / 8) + G;
+      const uint16_t* kb0 = krow + 8 * (x0 ^ ksw(col));          // kk = 0 (mod 4 chunks)
+      const uint16_t* kb1 = krow + 8 * ((x0 + 2) ^ ksw(col));    // kk = 1
 #pragma unroll
       for (int kk = 0; kk < KQ; kk += 2) {
-        const int c0 = (ch * CH + 16 * kk + 8 * G) >> 3;          // logical chunk
+        const int hop = 8 * 4 * (kk >> 1);                       // 4 chunks per kk pair
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * (c0 ^ swz))), qf[kk], st, 0, 0, 0);
+            as_bf16x8(*reinterpret_cast<const u32x4*>(kb0 + hop)), qf[kk], st, 0, 0, 0);
         st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * ((c0 + 2) ^ swz))), qf[kk + 1], st1, 0, 0, 0);
+            as_bf16x8(*reinterpret_cast<const u32x4*>(kb1 + hop)), qf[kk + 1], st1, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -394,33 +453,43 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         st[4 * rr] += o[0]; st[4 * rr + 1] += o[1]; st[4 * rr + 2] += o[2]; st[4 * rr + 3] += o[3];
       }
     }
-    // the copies of tile it+2 go out now (stage `buf` is free since its decode)
-    // and overlap the softmax, the PV MFMAs and the next tile's decode
-    if (it + 2 < ntiles) issue(it + 2, buf);
     // ---- online softmax: register r holds key slot 8 (r/4) + 4 G + r%4 of this lane's row
-    const uint32_t m16 = (s_vmask[qloc] >> (4 * G)) & 0x0F0F0F0Fu;
-    float tmax = -INFINITY;
+    // (tiles that every query of the block sees whole skip the mask)
+    if (__builtin_amdgcn_readfirstlane(s_vall) != 0xFFFFFFFFu) {
+      const uint32_t m16 = (s_vmask[qloc] >> (4 * G)) & 0x0F0F0F0Fu;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      st[r] = ((m16 >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] : -INFINITY;
-      tmax = fmaxf(tmax, st[r]);
+      for (int r = 0; r < 16; ++r) st[r] = ((m16 >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] : -INFINITY;
     }
+    tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl;
+    // the running maximum is raised only when a row's tile maximum passes it
+    // by more than 8 (log2 units)
+    return __builtin_amdgcn_ballot_w64(tmax > m_run + 8.0f) != 0;
+  };
+  // rescale O^T and l for rows whose maximum rises (the whole wave runs it)
+  auto raise_max = [&]() {
+    float alpha = 1.f;
     if (tmax > m_run + 8.0f) {
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - tmax);
+      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - tmax);
       m_run = tmax;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < MO; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
     }
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < MO; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+  };
+  auto accumulate = [&](int it, uint8_t* stg) {
     const float mneg = m_run == -INFINITY ? 0.f : -m_run;
     uint32_t pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float e0 = exp2f(fmaf(st[r], sl, mneg));
-      const float e1 = exp2f(fmaf(st[r + 1], sl, mneg));
+      // v_exp_f32 directly: results below 2^-126 flush to zero, which leaves
+      // the normalised output unchanged at fp32 resolution
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(st[r], sl, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(st[r + 1], sl, mneg));
       l_run += e0 + e1;
       pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
     }
@@ -431,28 +500,47 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     // and receives channel c0 + lambda of keys key0 .. key0 + 3.
     {
       const int lam = l & 15, grp = (l >> 4) & 1;
+      // key row 16 s + 8 hf + 4 G + lam/4 has ksw = (2 hf + G) & 3; the
+      // channel part 4 mo of the 16-byte chunk index sits above the XOR bits
+      const int e8 = (ch * CH + 16 * grp + 4 * (lam & 3)) >> 2;      // 8-byte chunk for mo = 0
+      const int rowl = 4 * G + (lam >> 2);
+      const uint16_t* tb0 = s_K + rowl * (C + KPAD) + 8 * ((e8 >> 1) ^ ((0 + G) & 3)) + 4 * (e8 & 1);
+      const uint16_t* tb1 = s_K + (rowl + 8) * (C + KPAD) + 8 * ((e8 >> 1) ^ ((2 + G) & 3)) + 4 * (e8 & 1);
+      typedef short v4s __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 pf = as_bf16x8((u32x4){pk[4 * s], pk[4 * s + 1], pk[4 * s + 2], pk[4 * s + 3]});
+      for (int sk = 0; sk < 2; ++sk) {
+        const bf16x8 pf = as_bf16x8((u32x4){pk[4 * sk], pk[4 * sk + 1], pk[4 * sk + 2], pk[4 * sk + 3]});
 #pragma unroll
         for (int mo = 0; mo < MO; ++mo) {
-          const int c0 = ch * CH + 32 * mo + 16 * grp + 4 * (lam & 3);   // element offset of this lane's read
-          const int e8 = c0 >> 2;                                         // 8-byte chunk
-          uint32_t hv[4];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int kr = 16 * s + 8 * hf + 4 * G + (lam >> 2);
-            const uint16_t* ad = s_K + kr * C + 8 * ((e8 >> 1) ^ ksw(kr)) + 4 * (e8 & 1);
-            typedef short v4s __attribute__((ext_vector_type(4)));
-            const v4s tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)ad);
-            const u32x2 tw = __builtin_bit_cast(u32x2, tv);
-            hv[2 * hf] = tw[0];
-            hv[2 * hf + 1] = tw[1];
-          }
-          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){hv[0], hv[1], hv[2], hv[3]}), pf,
+          const int off = 16 * sk * (C + KPAD) + 32 * mo;                  // rows 16 sk, chunks 4 mo
+          const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb0 + off));
+          const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb1 + off));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf,
                                                             acc[mo], 0, 0, 0);
         }
       }
+    }
+      if (it + 2 < ntiles) issue(it + 2, stg);
+  };
+
+  if (ntiles > 0) issue(0, s_stage0);
+  if (ntiles > 1) issue(1, s_stage1);
+  // The inner loop holds no rescale code, so the accumulator stays in the
+  // MFMA registers across it; a tile that raises a maximum leaves it, is
+  // rescaled and finished here, and the inner loop resumes.
+  for (int it = 0; it < ntiles;) {
+    bool up = false;
+    for (; it < ntiles; ++it) {
+      uint8_t* stg = (it & 1) ? s_stage1 : s_stage0;
+      up = score(it, stg);
+      if (up) break;
+      accumulate(it, stg);
+    }
+    if (up) {
+      raise_max();
+      accumulate(it, (it & 1) ? s_stage1 : s_stage0);
+      ++it;
     }
   }
 
