@@ -202,6 +202,7 @@ __device__ __forceinline__ void lds_barrier() {
 // touches the two low chunk bits, so every loop-varying part of an address is
 // an immediate offset.
 constexpr int KPAD = 16;
+template <int V> struct Par { static constexpr int value = V; };   // a buffer parity known at compile time
 __device__ __forceinline__ int ksw(int r) { return (r >> 2) & 3; }
 
 template <int C, int KVL, int CS, int NRG>
@@ -225,14 +226,16 @@ __attribute__((amdgpu_waves_per_eu(C >= 512 ? 1 : 2, C >= 512 ? 1 : 2)))
 void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   using Cf = AttnCfg<C, KVL, CS, NRG>;
   constexpr int KQ = Cf::KQ, MO = Cf::MO, CH = Cf::CH, NP = Cf::NP, RB = Cf::RB;
+  constexpr int KT = TS * (C + KPAD);     // elements of one key tile
   // separate LDS objects, so that alias analysis can tell the in-flight
   // global->LDS copies (stage) from every other LDS access
-  __shared__ __align__(16) uint8_t s_stage0[Cf::STAGE];     // piece-major: [piece][slot][16 B]
-  __shared__ __align__(16) uint8_t s_stage1[Cf::STAGE];
-  __shared__ __align__(16) uint16_t s_K[TS * (C + KPAD)];    // bf16, chunk-swizzled
+  // two stage buffers (piece-major: [piece][slot][16 B]) and two bf16 key
+  // tiles (chunk-swizzled), even tiles in the first; a buffer is chosen at
+  // compile time so that its offset folds into the LDS instructions
+  __shared__ __align__(16) uint8_t s_stage[2 * Cf::STAGE];
+  __shared__ __align__(16) uint16_t s_K[2 * KT];
   __shared__ __align__(16) float s_xb[CS > 1 ? NRG * CS * 4 * 64 * 4 : 4];   // [wave][r/4][lane][4]
-  __shared__ uint32_t s_vmask[8];                            // per query: visible slots of the tile
-  __shared__ uint32_t s_vall;                                // AND of s_vmask over the block's queries
+  __shared__ uint32_t s_vmask[2][8];                         // per buffer and query: visible slots of the tile
   __shared__ int s_nvisq[8];
   __shared__ int s_sidx[SIDX_CAP];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -257,12 +260,19 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 
   // block-level tables: visible compressed entries per query, cached index list
   if (threadIdx.x < 8) s_nvisq[threadIdx.x] = pl.dense ? (int)visible_count(pfirst + threadIdx.x, a.ratio, a.S) : (int)a.S;
+  int bad_idx = 0;      // an index outside [0, S) in this block's list
   if (a.idx) {
     const int32_t* irow = a.idx + (b * a.nq + ui.t0) * a.k;
     const int n_i = (ncomp < slot_hi ? ncomp : slot_hi) - slot_lo;
-    for (int i = threadIdx.x; i < n_i; i += Cf::NT) s_sidx[i] = irow[slot_lo + i];
+    for (int i = threadIdx.x; i < n_i; i += Cf::NT) {
+      const int e = irow[slot_lo + i];
+      s_sidx[i] = e;
+      bad_idx |= (e < 0 || e >= a.S) ? 1 : 0;
+    }
   }
-  __syncthreads();
+  const bool idx_ok = !__syncthreads_or(bad_idx);
+  const int plast = (int)(p0 + ui.tl);
+  const int nvis_first = pl.dense ? (int)visible_count(pfirst, a.ratio, a.S) : (int)a.S;
 
   // the row this lane owns: (query t, head h)
   const int row = 32 * rg + col;
@@ -320,38 +330,68 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   };
   // copies per wave and tile: waves below NDMA % NW issue one more
   const int my_dma = Cf::NDMA / Cf::NW + (wv < Cf::NDMA % Cf::NW ? 1 : 0);
-
-  // a tile in two halves.  score(): wait for its copies, decode the stage,
-  // S^T, mask, tile maximum; returns whether some row must raise its running
-  // maximum.  accumulate(): P, O^T += V^T P^T, and the copies of tile it+2
-  // into the stage just decoded.
-  f32x16 st;
-  float tmax;
-  auto score = [&](int it, uint8_t* stg) -> bool {
-    const int s0 = slot_lo + it * TS;
-    // wait for this wave's copies of tile `it` (those of tile it+1 may stay in flight)
-    if (it + 1 < ntiles) {
-      switch (my_dma) {
-        case 0: break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;   // vmcnt(1)
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-        case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-        case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-      }
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+  // wait until at most n of this wave's tile copies are still in flight
+  auto wait_copies = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // vmcnt(0)
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+      case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+      case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+      case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+      case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
-    lds_barrier();
-    // ---- decode the stage into the bf16 key tile.  Stage unit un (16 bytes)
+  };
+
+  // Is every slot of tile `it` visible to every query of the block?  Scalar
+  // arithmetic: the first query sees the fewest compressed entries, the first
+  // query's position bounds the window from above and the last query's window
+  // start bounds it from below; an index list is all visible when every
+  // entry lies in [0, S).
+  auto tile_full = [&](int it) -> bool {
+    const int s0 = slot_lo + it * TS, s1 = s0 + TS;
+    if (s1 > slot_hi) return false;
+    if (s0 < ncomp) {
+      if (a.idx ? !idx_ok : (s1 < ncomp ? s1 : ncomp) > nvis_first) return false;
+    }
+    if (s1 > ncomp) {
+      const int lo = (int)ui.wlo + ((s0 > ncomp ? s0 : ncomp) - ncomp), hi = (int)ui.wlo + (s1 - 1 - ncomp);
+      if (hi > pfirst || lo < plast - a.n_win + 1) return false;
+    }
+    return true;
+  };
+  // per-query visibility bits of a tile that is not full (wave 0)
+  auto masks = [&](int it, int buf) {
+    if (wv != 0 || tile_full(it)) return;
+    const int s0 = slot_lo + it * TS;
+    uint32_t vbits = 0;
+    const int slot = s0 + l;
+    if (l < TS && slot < slot_hi) {
+      int pos;
+      bool win;
+      if (slot_src(slot, &pos, &win)) {
+        for (int q = 0; q < nq_blk; ++q) {
+          const int pq = pfirst + q;
+          const bool ok = win ? (pos <= pq && pos >= pq - a.n_win + 1) : (pos < s_nvisq[q]);
+          vbits |= (ok ? 1u : 0u) << q;
+        }
+      }
+    }
+    for (int q = 0; q < nq_blk; ++q) {
+      const uint32_t bal = (uint32_t)__ballot((vbits >> q) & 1u);
+      if (l == 0) s_vmask[buf][q] = bal;
+    }
+  };
+
+  auto decode = [&](const uint8_t* stg, uint16_t* kt) {
+    // decode a stage into a bf16 key tile.  Stage unit un (16 bytes)
     // is piece un / TS of slot un % TS; the E4M3 units come first.  Fixed trip
     // counts with all stage reads issued before the conversions; the guards
     // are uniform per wave (NT is a multiple of 64 and so are the unit counts).
@@ -375,7 +415,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         if (Cf::NT * (j + 1) <= U8 || un < U8) {   // 16 E4M3 channels -> two 16-byte chunks
           const int piece = un / TS, ks = un % TS;
           const u32x4 w = w8[j];
-          uint16_t* krow = s_K + ks * (C + KPAD);
+          uint16_t* krow = kt + ks * (C + KPAD);
           const u32x4 lo = {e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
                             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
           const u32x4 hi = {e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
@@ -390,34 +430,23 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         if (Cf::NT * (j + 1) <= UB || un < U8 + UB) {   // 8 bf16 channels -> one chunk
           const int piece = un / TS, ks = un % TS;
           const int chunk = 2 * Cf::NF8 + (piece - Cf::NF8);
-          *reinterpret_cast<u32x4*>(s_K + ks * (C + KPAD) + 8 * (chunk ^ ksw(ks))) = wb[j];
+          *reinterpret_cast<u32x4*>(kt + ks * (C + KPAD) + 8 * (chunk ^ ksw(ks))) = wb[j];
         }
       }
     }
-    if (wv == 0) {
-      uint32_t vbits = 0;
-      const int slot = s0 + l;
-      if (l < TS && slot < slot_hi) {
-        int pos;
-        bool win;
-        if (slot_src(slot, &pos, &win)) {
-          for (int q = 0; q < nq_blk; ++q) {
-            const int pq = pfirst + q;
-            const bool ok = win ? (pos <= pq && pos >= pq - a.n_win + 1) : (pos < s_nvisq[q]);
-            vbits |= (ok ? 1u : 0u) << q;
-          }
-        }
-      }
-      uint32_t vall = 0xFFFFFFFFu;
-      for (int q = 0; q < nq_blk; ++q) {
-        const uint32_t bal = (uint32_t)__ballot((vbits >> q) & 1u);
-        vall &= bal;
-        if (l == 0) s_vmask[q] = bal;
-      }
-      if (l == 0) s_vall = vall;
-    }
-    lds_barrier();
+  };
 
+  // A tile in two halves around the rescale.  Per tile two block barriers:
+  // B3 (partial scores visible, every wave's copies of the next tile landed)
+  // and B4 (this tile's PV done, next tile decoded after it).  Stage it&1 is refilled
+  // with tile it+2 at the start of tile it: its last reader, the decode of
+  // tile it, finished before the previous B4.
+  f32x16 st;
+  float tmax;
+  auto score = [&](auto par, int it) -> bool {
+    constexpr int PB = decltype(par)::value;   // it & 1
+    const uint16_t* kt = s_K + PB * KT;
+    if (it + 2 < ntiles) issue(it + 2, s_stage + PB * Cf::STAGE);
     // ---- partial S^T[32 keys][32 rows] over this wave's channel slice, two chains
     f32x16 st1;
 #pragma unroll
@@ -425,7 +454,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     {
       // logical chunk of k-step kk: ch*CH/8 + 2 kk + G; only its two low bits
       // meet the swizzle, so even and odd kk each get one base address
-      const uint16_t* krow = s_K + col * (C + KPAD);
+      const uint16_t* krow = kt + col * (C + KPAD);
       const int x0 = ch * (CH / 8) + G;
       const uint16_t* kb0 = krow + 8 * (x0 ^ ksw(col));          // kk = 0 (mod 4 chunks)
       const uint16_t* kb1 = krow + 8 * ((x0 + 2) ^ ksw(col));    // kk = 1
@@ -445,7 +474,11 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
       for (int rr = 0; rr < 4; ++rr)
         *reinterpret_cast<f32x4*>(s_xb + ((wv * 4 + rr) * 64 + l) * 4) =
             (f32x4){st[4 * rr], st[4 * rr + 1], st[4 * rr + 2], st[4 * rr + 3]};
-      lds_barrier();
+    }
+    // this wave's copies of tile it+1 have landed once at most those of it+2 remain
+    if (it + 1 < ntiles) wait_copies(it + 2 < ntiles ? my_dma : 0);
+    lds_barrier();                                                    // B3
+    if (CS > 1) {
       const int pw = rg * CS + (ch ^ 1);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -454,9 +487,8 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
       }
     }
     // ---- online softmax: register r holds key slot 8 (r/4) + 4 G + r%4 of this lane's row
-    // (tiles that every query of the block sees whole skip the mask)
-    if (__builtin_amdgcn_readfirstlane(s_vall) != 0xFFFFFFFFu) {
-      const uint32_t m16 = (s_vmask[qloc] >> (4 * G)) & 0x0F0F0F0Fu;
+    if (!tile_full(it)) {
+      const uint32_t m16 = (s_vmask[PB][qloc] >> (4 * G)) & 0x0F0F0F0Fu;
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = ((m16 >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] : -INFINITY;
     }
@@ -481,7 +513,9 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
   };
-  auto accumulate = [&](int it, uint8_t* stg) {
+  auto accumulate = [&](auto par, int it) {
+    constexpr int PB = decltype(par)::value;   // it & 1
+    const uint16_t* kt = s_K + PB * KT;
     const float mneg = m_run == -INFINITY ? 0.f : -m_run;
     uint32_t pk[8];
 #pragma unroll
@@ -504,8 +538,8 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
       // channel part 4 mo of the 16-byte chunk index sits above the XOR bits
       const int e8 = (ch * CH + 16 * grp + 4 * (lam & 3)) >> 2;      // 8-byte chunk for mo = 0
       const int rowl = 4 * G + (lam >> 2);
-      const uint16_t* tb0 = s_K + rowl * (C + KPAD) + 8 * ((e8 >> 1) ^ ((0 + G) & 3)) + 4 * (e8 & 1);
-      const uint16_t* tb1 = s_K + (rowl + 8) * (C + KPAD) + 8 * ((e8 >> 1) ^ ((2 + G) & 3)) + 4 * (e8 & 1);
+      const uint16_t* tb0 = kt + rowl * (C + KPAD) + 8 * ((e8 >> 1) ^ ((0 + G) & 3)) + 4 * (e8 & 1);
+      const uint16_t* tb1 = kt + (rowl + 8) * (C + KPAD) + 8 * ((e8 >> 1) ^ ((2 + G) & 3)) + 4 * (e8 & 1);
       typedef short v4s __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
@@ -521,25 +555,48 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         }
       }
     }
-      if (it + 2 < ntiles) issue(it + 2, stg);
+    // decode tile it+1 (its copies landed before B3) into the other key tile
+    if (it + 1 < ntiles) {
+      decode(s_stage + (1 - PB) * Cf::STAGE, s_K + (1 - PB) * KT);
+      masks(it + 1, 1 - PB);
+    }
+    lds_barrier();                                                    // B4
   };
 
-  if (ntiles > 0) issue(0, s_stage0);
-  if (ntiles > 1) issue(1, s_stage1);
+  // prologue: tiles 0 and 1 in flight, tile 0 decoded
+  if (ntiles > 0) {
+    issue(0, s_stage);
+    if (ntiles > 1) issue(1, s_stage + Cf::STAGE);
+    wait_copies(ntiles > 1 ? my_dma : 0);
+    lds_barrier();
+    decode(s_stage, s_K);
+    masks(0, 0);
+    lds_barrier();
+  }
   // The inner loop holds no rescale code, so the accumulator stays in the
   // MFMA registers across it; a tile that raises a maximum leaves it, is
-  // rescaled and finished here, and the inner loop resumes.
+  // rescaled and finished here, and the inner loop resumes (at either
+  // parity: the even half is skipped when it is odd).
+  const Par<0> even;
+  const Par<1> odd;
   for (int it = 0; it < ntiles;) {
     bool up = false;
-    for (; it < ntiles; ++it) {
-      uint8_t* stg = (it & 1) ? s_stage1 : s_stage0;
-      up = score(it, stg);
+    for (;;) {
+      if (!(it & 1)) {
+        up = score(even, it);
+        if (up) break;
+        accumulate(even, it);
+        if (++it >= ntiles) break;
+      }
+      up = score(odd, it);
       if (up) break;
-      accumulate(it, stg);
+      accumulate(odd, it);
+      if (++it >= ntiles) break;
     }
     if (up) {
       raise_max();
-      accumulate(it, (it & 1) ? s_stage1 : s_stage0);
+      if (it & 1) accumulate(odd, it);
+      else accumulate(even, it);
       ++it;
     }
   }
