@@ -8,13 +8,20 @@
 // digits, stopping as soon as a whole bin is taken), the winners are gathered
 // and bitonic-sorted in LDS.
 //
-// Stage 1: one block per (row, part); a part is up to PART visible scores of
-//          the row, staged once in LDS.  With one part the block writes the
-//          final sorted indices; otherwise its k best composites go to the
-//          workspace.
-// Stage 2: one block per row merges the parts' candidates (at most 16384).
-// Everything is exact integer work, so the result is bit-identical for any
-// decomposition.
+// k <= 1024, streaming: one block per (row, part) reads its scores once from
+//          HBM.  A running threshold tau (a composite no larger than the k-th
+//          largest seen so far) rejects almost every score with one float
+//          compare; the survivors go to an LDS candidate buffer, which is cut
+//          back to its k largest (exact radix select, first digit at the
+//          highest bit where the candidates differ) whenever a step could
+//          overflow it.  A rejected score is below k kept ones, so it cannot
+//          be selected.
+// k > 1024: stage 1, one block per (row, part); a part is up to PART visible
+//          scores staged once in LDS and radix-selected there.
+// Either way, with one part the block writes the final sorted indices;
+// otherwise its k best composites go to the workspace and stage 2 (one block
+// per row) merges the parts' candidates (at most 16384).  Everything is exact
+// integer work, so the result is bit-identical for any decomposition.
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
@@ -118,11 +125,12 @@ __device__ uint64_t radix_threshold(Get get, int N, uint32_t need, uint32_t* his
   return st->prefix;
 }
 
-// descending bitonic sort of n (power of two) composites in LDS
+// descending bitonic sort of n (power of two) composites in LDS, NT threads
+template <int NT = TK_THREADS>
 __device__ void bitonic_desc(uint64_t* buf, int n) {
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += TK_THREADS) {
+      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
         const int pos = 2 * i - (i & (stride - 1));
         const int par = pos + stride;
         const bool desc = (pos & size) == 0;
@@ -242,7 +250,256 @@ __global__ __launch_bounds__(TK_THREADS) void topk_stage2(TopkArgs a, PosTable p
     a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)out[i]) : -1;
 }
 
+// ------------------------------------------------------------------ streaming select (k <= 1024)
+
+constexpr int SK_NT = 256;                  // threads per block
+constexpr int SK_U = 4;                     // float4 loads per thread and step
+constexpr int SK_STEP = SK_NT * 4 * SK_U;   // scores per step
+constexpr int SK_CAP = 6144;                // candidate slots (>= SK_STEP + k)
+constexpr int SK_BIN = 2048;                // 11-bit digits
+constexpr int SK_KMAX = 1024;
+
+struct SkShared {
+  uint64_t cand[SK_CAP];
+  uint64_t out[SK_KMAX];
+  uint32_t hist[SK_BIN];
+  uint64_t rmin[SK_NT / 64], rmax[SK_NT / 64];
+  uint32_t wsum[SK_NT / 64];
+  uint32_t cnt, cnt2;
+  uint32_t sel_bin, sel_above, sel_cnt;
+};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// exclusive prefix over the SK_NT threads of a per-thread count; *total gets the sum
+__device__ __forceinline__ uint32_t sk_scan_excl(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(x, o);
+    if (lane >= o) x += n;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < SK_NT / 64; ++i) {
+    const uint32_t ws = wsum[i];
+    before += i < w ? ws : 0u;
+    all += ws;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// the composite T with #{cand[i] >= T, i < n} == need (1 <= need <= n, unique, non-zero)
+__device__ uint64_t sk_select(SkShared& sh, int n, uint32_t need) {
+  uint64_t mn = ~0ull, mx = 0;
+  for (int i = threadIdx.x; i < n; i += SK_NT) {
+    const uint64_t x = sh.cand[i];
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t a = shfl_xor_u64(mn, o), b = shfl_xor_u64(mx, o);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if ((threadIdx.x & 63) == 0) { sh.rmin[threadIdx.x >> 6] = mn; sh.rmax[threadIdx.x >> 6] = mx; }
+  __syncthreads();
+  mn = sh.rmin[0];
+  mx = sh.rmax[0];
+#pragma unroll
+  for (int i = 1; i < SK_NT / 64; ++i) {
+    mn = sh.rmin[i] < mn ? sh.rmin[i] : mn;
+    mx = sh.rmax[i] > mx ? sh.rmax[i] : mx;
+  }
+  if (need >= (uint32_t)n) return mn;          // everything is taken
+  // bits above the highest differing one are common to all candidates
+  const int hb = 63 - __clzll(mn ^ mx);
+  int shift = hb + 1;
+  uint64_t prefix = shift >= 64 ? 0ull : (mn >> shift) << shift;
+  uint32_t remaining = need;
+  for (;;) {
+    const int width = shift < 11 ? shift : 11;
+    shift -= width;
+    const int top = shift + width;               // bits at and above `top` must match prefix
+    for (int i = threadIdx.x; i < SK_BIN; i += SK_NT) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += SK_NT) {
+      const uint64_t x = sh.cand[i];
+      if (top >= 64 || (x >> top) == (prefix >> top))
+        atomicAdd(&sh.hist[(uint32_t)(x >> shift) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    // thread t owns the 8 bins [SK_BIN - 8(t+1), SK_BIN - 8t), scanned from the top
+    constexpr int PER = SK_BIN / SK_NT;
+    uint32_t c[PER];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) { c[q] = sh.hist[SK_BIN - 1 - (PER * threadIdx.x + q)]; loc += c[q]; }
+    uint32_t total;
+    uint32_t above = sk_scan_excl(loc, sh.wsum, &total);
+    if (above < remaining && remaining <= above + loc) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        if (above < remaining && remaining <= above + c[q]) {
+          sh.sel_bin = SK_BIN - 1 - (PER * threadIdx.x + q);
+          sh.sel_above = above;
+          sh.sel_cnt = c[q];
+        }
+        above += c[q];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sh.sel_bin, ab = sh.sel_above, cb = sh.sel_cnt;
+    __syncthreads();
+    prefix |= (uint64_t)bin << shift;
+    remaining -= ab;
+    if (cb == remaining || shift == 0) return prefix;   // the whole bin is taken
+  }
+}
+
+// keep the `need` candidates >= T in sh.out (any order); returns through sh.out
+__device__ void sk_gather(SkShared& sh, int n, uint64_t T) {
+  if (threadIdx.x == 0) sh.cnt2 = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += SK_NT) {
+    const uint64_t x = sh.cand[i];
+    if (x >= T) {
+      const uint32_t at = atomicAdd(&sh.cnt2, 1u);
+      if (at < SK_KMAX) sh.out[at] = x;
+    }
+  }
+  __syncthreads();
+}
+
+// dynamic LDS: sizeof(SkShared)
+__global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, int b0) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
+  const int64_t row = (int64_t)blockIdx.x;         // row within this launch's batch slice
+  const int pidx = blockIdx.y;
+  const int64_t bl = row / a.nq, t = row % a.nq;
+  const int64_t grow = (b0 + bl) * a.nq + t;       // global row
+  const int64_t nv = visible_count(pt.q_pos0[bl] + t, a.m, a.S);
+  const int64_t lo = (int64_t)pidx * a.part;
+  const int N = (int)(nv - lo < 0 ? 0 : (nv - lo < a.part ? nv - lo : a.part));
+  const uint32_t need = (uint32_t)(N < a.k ? N : a.k);
+  const float* src = a.scores + grow * a.S + lo;
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  if (threadIdx.x == 0) sh.cnt = 0;
+
+  uint64_t tau = 0;                  // composites must exceed tau to enter
+  float tauf = __uint_as_float(0xFFFFFFFFu);   // score of tau's key (NaN while tau = 0)
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  auto load = [&](int i0, f4 (&d)[SK_U]) {
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+      const int e = i0 + (u * SK_NT + (int)threadIdx.x) * 4;
+      if (vec && e + 4 <= N) {
+        d[u] = *reinterpret_cast<const f4*>(src + e);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[u][j] = e + j < N ? src[e + j] : 0.f;
+      }
+    }
+  };
+  // cut the buffer back to its `need` largest and raise tau
+  auto compact = [&]() {
+    const int n = (int)sh.cnt;
+    const uint64_t T = sk_select(sh, n, need);
+    sk_gather(sh, n, T);
+    for (int i = threadIdx.x; i < (int)need; i += SK_NT) sh.cand[i] = sh.out[i];
+    if (threadIdx.x == 0) sh.cnt = need;
+    __syncthreads();
+    tau = T;
+    const uint32_t th = (uint32_t)(T >> 32);
+    tauf = __uint_as_float((th & 0x80000000u) ? (th ^ 0x80000000u) : ~th);
+  };
+  auto process = [&](int i0, const f4 (&d)[SK_U]) {
+    __syncthreads();                                   // sh.cnt is stable
+    if (sh.cnt > (uint32_t)(SK_CAP - SK_STEP)) compact();
+    // survivors of this thread: scores not below tauf, then the exact composite test
+    uint64_t keep[SK_U * 4];
+    uint32_t nk = 0;
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = i0 + (u * SK_NT + (int)threadIdx.x) * 4 + j;
+        const float x = d[u][j];
+        keep[u * 4 + j] = 0;
+        if (e < N && !(x < tauf)) {
+          const uint64_t c = composite(score_key(x), (uint32_t)(lo + e));
+          if (c > tau) keep[u * 4 + j] = c;
+        }
+        nk += keep[u * 4 + j] != 0 ? 1u : 0u;
+      }
+    if (__syncthreads_or(nk != 0)) {
+      uint32_t total;
+      uint32_t at = sk_scan_excl(nk, sh.wsum, &total);
+      const uint32_t base = sh.cnt;
+      at += base;
+#pragma unroll
+      for (int i = 0; i < SK_U * 4; ++i)
+        if (keep[i] != 0) sh.cand[at++] = keep[i];
+      __syncthreads();
+      if (threadIdx.x == 0) sh.cnt = base + total;
+    }
+  };
+
+  f4 A[SK_U], B[SK_U];
+  if (N > 0) load(0, A);
+  for (int i0 = 0; i0 < N; i0 += 2 * SK_STEP) {
+    if (i0 + SK_STEP < N) load(i0 + SK_STEP, B);
+    process(i0, A);
+    if (i0 + SK_STEP >= N) break;
+    if (i0 + 2 * SK_STEP < N) load(i0 + 2 * SK_STEP, A);
+    process(i0 + SK_STEP, B);
+  }
+  __syncthreads();
+  // final selection of the `need` largest, sorted descending
+  const int n = (int)sh.cnt;
+  if (need > 0) {
+    const uint64_t T = sk_select(sh, n, need);
+    sk_gather(sh, n, T);
+  }
+  if (a.nparts == 1) {
+    const int n2 = pow2_ceil(a.k);
+    for (int i = need + threadIdx.x; i < n2; i += SK_NT) sh.out[i] = 0;
+    __syncthreads();
+    bitonic_desc<SK_NT>(sh.out, n2);
+    for (int i = threadIdx.x; i < a.k; i += SK_NT)
+      a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
+  } else {
+    uint64_t* dst = a.cand + (row * a.nparts + pidx) * a.k;   // launch-local row
+    for (int i = threadIdx.x; i < a.k; i += SK_NT) dst[i] = i < (int)need ? sh.out[i] : 0;
+  }
+}
+
 static void topk_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
+  if (k <= SK_KMAX) {
+    // streaming: whole rows when there are enough of them, else up to 16
+    // parts of at least 16384 scores so that some 512 blocks run
+    int np = 1;
+    if (rows < 512 && S > 16384) {
+      np = (int)((512 + rows - 1) / rows);
+      const int64_t by_len = S / 16384;
+      if (np > by_len) np = (int)by_len;
+      if (np > 16) np = 16;
+      if (np < 1) np = 1;
+    }
+    int64_t p = (S + np - 1) / np;
+    p = (p + 3) / 4 * 4;                       // parts start 16-byte aligned in aligned rows
+    *part = (int)p;
+    *nparts = (int)((S + p - 1) / p);
+    return;
+  }
   int p = k <= 1024 ? 32768 : 16384;
   if (rows < 256 && S > 16384 && k <= 1024) p = 16384;   // more blocks for few rows
   int fit = 4096;                                         // short rows: a smaller LDS stage
@@ -272,9 +529,11 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
   topk_plan((B < MAXB ? B : MAXB) * nq, S, k, &a.part, &a.nparts);
   a.cand = reinterpret_cast<uint64_t*>(ws);
   const int n2 = [&] { int p = 1; while (p < k) p <<= 1; return p; }();
-  const size_t lds1 = (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
+  const bool stream = k <= SK_KMAX;
+  const size_t lds1 = stream ? sizeof(SkShared) : (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
   const size_t lds2 = (size_t)a.nparts * k * 8 + NBIN * 4 + (size_t)n2 * 8;
-  hipError_t e = hipFuncSetAttribute((const void*)topk_stage1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  hipError_t e = hipFuncSetAttribute(stream ? (const void*)topk_stream : (const void*)topk_stage1,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
   if (a.nparts > 1) {
     e = hipFuncSetAttribute((const void*)topk_stage2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
@@ -284,8 +543,12 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
     const int nb = (int)(B - b0 < MAXB ? B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
-    hipLaunchKernelGGL(topk_stage1, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(TK_THREADS), lds1, s,
-                       a, pt, (int)b0);
+    if (stream)
+      hipLaunchKernelGGL(topk_stream, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
+                         a, pt, (int)b0);
+    else
+      hipLaunchKernelGGL(topk_stage1, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(TK_THREADS), lds1, s,
+                         a, pt, (int)b0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nparts > 1) {

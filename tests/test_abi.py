@@ -91,7 +91,8 @@ def test_topk_validation(L):
     f = L.lib.dsv4_topk_select
     assert f(FAKE, 1, 4, 100, 4, pos(0), 5000, FAKE, None, 0, None) == 2                     # k > 4096
     assert f(FAKE, 1, 4, 100, 4, pos(0), 0, FAKE, None, 0, None) == 1                        # k = 0
-    assert f(FAKE, 16, 1, 1 << 21, 4, pos(*[0] * 16), 1024, FAKE, None, 0, None) == 2        # too many parts
+    assert f(FAKE, 16, 1, 1 << 21, 4, pos(*[0] * 16), 4096, FAKE, None, 0, None) == 2        # too many parts
+    assert f(FAKE, 16, 1, 1 << 21, 4, pos(*[0] * 16), 1024, FAKE, None, 0, None) == 4        # needs a workspace
     need = L.lib.dsv4_topk_workspace_size(16, 1, 262144, 1024)
     assert need > 0
     assert f(FAKE, 16, 1, 262144, 4, pos(*[0] * 16), 1024, FAKE, None, 0, None) == 4         # workspace

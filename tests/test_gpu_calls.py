@@ -184,6 +184,10 @@ TOPK_CASES = [
     (16, 1, 262144, 1024, 4, [1 << 20] * 16, "normal"),   # decode shape: 16 parts + merge
     (1, 8, 300, 64, 1, [290], "zeros"),       # all ties incl. -0.0
     (1, 4, 5000, 4096, 4, [30000], "normal"), # large k
+    (1, 3, 65536, 1024, 4, [300000], "asc"),  # every score beats the running threshold
+    (1, 3, 65536, 1024, 4, [300000], "desc"), # the first scores are the answer
+    (1, 6, 50001, 512, 4, [250000], "normal"), # rows not 16-byte aligned
+    (1, 8, 100000, 1024, 1, [200000], "int"),  # long rows, heavy ties at the threshold
 ]
 
 
@@ -197,6 +201,9 @@ def test_topk_select_bit_exact(L, case):
     elif kind == "zeros":
         sc = np.where(rng.random((B, nq, S)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
         sc[..., ::7] = 1.0
+    elif kind in ("asc", "desc"):
+        ramp = np.linspace(-3.0, 5.0, S, dtype=np.float32)
+        sc = np.broadcast_to(ramp if kind == "asc" else ramp[::-1], (B, nq, S)).copy()
     else:
         sc = G.normal(S, "extra", (B, nq, S), 10.0)
     scores = dev(sc)
