@@ -255,19 +255,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_stage2(TopkArgs a, PosTable p
 constexpr int SK_NT = 256;                  // threads per block
 constexpr int SK_U = 4;                     // float4 loads per thread and step
 constexpr int SK_STEP = SK_NT * 4 * SK_U;   // scores per step
-constexpr int SK_CAP = 6144;                // candidate slots (>= SK_STEP + k)
+constexpr int SK_CAP = 8192;                // candidate slots (>= SK_STEP + k)
 constexpr int SK_BIN = 2048;                // 11-bit digits
 constexpr int SK_KMAX = 1024;
 
 struct SkShared {
   uint64_t cand[SK_CAP];
-  uint64_t out[SK_KMAX];
-  uint32_t hist[SK_BIN];
+  union {                                   // the histogram is dead once the gather starts
+    uint64_t out[SK_KMAX];
+    uint32_t hist[SK_BIN];
+  };
   uint64_t rmin[SK_NT / 64], rmax[SK_NT / 64];
   uint32_t wsum[SK_NT / 64];
   uint32_t cnt, cnt2;
   uint32_t sel_bin, sel_above, sel_cnt;
 };
+
+// Barrier for LDS traffic only (waits for this wave's LDS operations): unlike
+// __syncthreads() it carries no memory fence, so score loads in flight stay
+// in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
@@ -378,7 +388,10 @@ __device__ void sk_gather(SkShared& sh, int n, uint64_t T) {
   __syncthreads();
 }
 
-// dynamic LDS: sizeof(SkShared)
+// dynamic LDS: sizeof(SkShared).  VEC: every part starts 16-byte aligned, so
+// whole steps are read with float4 loads (the last, partial step with
+// clamped scalar loads).
+template <bool VEC>
 __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, int b0) {
   extern __shared__ __align__(16) uint8_t smem[];
   SkShared& sh = *reinterpret_cast<SkShared*>(smem);
@@ -391,23 +404,29 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
   const int N = (int)(nv - lo < 0 ? 0 : (nv - lo < a.part ? nv - lo : a.part));
   const uint32_t need = (uint32_t)(N < a.k ? N : a.k);
   const float* src = a.scores + grow * a.S + lo;
-  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
   if (threadIdx.x == 0) sh.cnt = 0;
 
   uint64_t tau = 0;                  // composites must exceed tau to enter
   float tauf = __uint_as_float(0xFFFFFFFFu);   // score of tau's key (NaN while tau = 0)
   typedef float f4 __attribute__((ext_vector_type(4)));
-  auto load = [&](int i0, f4 (&d)[SK_U]) {
+  // loads without per-lane branches, so that the compiler's waits stay per buffer
+  auto load_vec = [&](int i0, f4 (&d)[SK_U]) {     // a whole step, i0 + SK_STEP <= N
 #pragma unroll
-    for (int u = 0; u < SK_U; ++u) {
-      const int e = i0 + (u * SK_NT + (int)threadIdx.x) * 4;
-      if (vec && e + 4 <= N) {
-        d[u] = *reinterpret_cast<const f4*>(src + e);
-      } else {
+    for (int u = 0; u < SK_U; ++u)
+      d[u] = *reinterpret_cast<const f4*>(src + i0 + (u * SK_NT + (int)threadIdx.x) * 4);
+  };
+  auto load_sca = [&](int i0, f4 (&d)[SK_U]) {     // indices past N read element N-1 (masked later)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d[u][j] = e + j < N ? src[e + j] : 0.f;
+    for (int u = 0; u < SK_U; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = i0 + (u * SK_NT + (int)threadIdx.x) * 4 + j;
+        d[u][j] = src[e < N ? e : N - 1];
       }
-    }
+  };
+  auto load = [&](int i0, f4 (&d)[SK_U]) {
+    if (VEC) load_vec(i0, d);
+    else load_sca(i0, d);
   };
   // cut the buffer back to its `need` largest and raise tau
   auto compact = [&]() {
@@ -422,11 +441,11 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
     tauf = __uint_as_float((th & 0x80000000u) ? (th ^ 0x80000000u) : ~th);
   };
   auto process = [&](int i0, const f4 (&d)[SK_U]) {
-    __syncthreads();                                   // sh.cnt is stable
+    lds_barrier();                                     // every append of the last step is in
     if (sh.cnt > (uint32_t)(SK_CAP - SK_STEP)) compact();
-    // survivors of this thread: scores not below tauf, then the exact composite test
+    // survivors: scores not below tauf, then the exact composite test
     uint64_t keep[SK_U * 4];
-    uint32_t nk = 0;
+    bool anyk = false;
 #pragma unroll
     for (int u = 0; u < SK_U; ++u)
 #pragma unroll
@@ -438,29 +457,59 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
           const uint64_t c = composite(score_key(x), (uint32_t)(lo + e));
           if (c > tau) keep[u * 4 + j] = c;
         }
-        nk += keep[u * 4 + j] != 0 ? 1u : 0u;
+        anyk |= keep[u * 4 + j] != 0;
       }
-    if (__syncthreads_or(nk != 0)) {
-      uint32_t total;
-      uint32_t at = sk_scan_excl(nk, sh.wsum, &total);
-      const uint32_t base = sh.cnt;
-      at += base;
+    // wave-local append: one LDS atomic per wave, positions from ballots
+    if (__ballot(anyk) != 0) {
+      uint64_t bal[SK_U * 4];
+      uint32_t total = 0;
 #pragma unroll
-      for (int i = 0; i < SK_U * 4; ++i)
-        if (keep[i] != 0) sh.cand[at++] = keep[i];
-      __syncthreads();
-      if (threadIdx.x == 0) sh.cnt = base + total;
+      for (int i = 0; i < SK_U * 4; ++i) {
+        bal[i] = __ballot(keep[i] != 0);
+        total += (uint32_t)__popcll(bal[i]);
+      }
+      uint32_t base = 0;
+      if ((threadIdx.x & 63) == 0) base = atomicAdd(&sh.cnt, total);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int i = 0; i < SK_U * 4; ++i) {
+        if (keep[i] != 0)
+          sh.cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u))] = keep[i];
+        base += (uint32_t)__popcll(bal[i]);
+      }
     }
   };
 
-  f4 A[SK_U], B[SK_U];
-  if (N > 0) load(0, A);
-  for (int i0 = 0; i0 < N; i0 += 2 * SK_STEP) {
-    if (i0 + SK_STEP < N) load(i0 + SK_STEP, B);
-    process(i0, A);
-    if (i0 + SK_STEP >= N) break;
-    if (i0 + 2 * SK_STEP < N) load(i0 + 2 * SK_STEP, A);
-    process(i0 + SK_STEP, B);
+  // four register buffers in rotation: three steps of loads in flight; a
+  // partial last step follows with scalar loads.
+  // Every load is issued unconditionally (steps past the end re-read the last
+  // whole step, never processed twice), so the compiler's per-buffer wait
+  // counts stay exact.  The rotation covers whole steps only.
+  constexpr int ST = SK_STEP;
+  const int NM = N / ST * ST;
+  if (NM > 0) {
+    const int last = NM - ST;
+    auto cl = [&](int i) { return i < last ? i : last; };
+    f4 A[SK_U], B[SK_U], C[SK_U], D[SK_U];
+    load(0, A);
+    load(cl(ST), B);
+    load(cl(2 * ST), C);
+    for (int i0 = 0; i0 < NM; i0 += 4 * ST) {
+      load(cl(i0 + 3 * ST), D);
+      process(i0, A);
+      load(cl(i0 + 4 * ST), A);
+      if (i0 + ST < NM) process(i0 + ST, B);
+      load(cl(i0 + 5 * ST), B);
+      if (i0 + 2 * ST < NM) process(i0 + 2 * ST, C);
+      load(cl(i0 + 6 * ST), C);
+      if (i0 + 3 * ST < NM) process(i0 + 3 * ST, D);
+    }
+  }
+  if (NM < N) {
+    f4 T[SK_U];
+    load_sca(NM, T);
+    process(NM, T);
   }
   __syncthreads();
   // final selection of the `need` largest, sorted descending
@@ -532,8 +581,10 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
   const bool stream = k <= SK_KMAX;
   const size_t lds1 = stream ? sizeof(SkShared) : (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
   const size_t lds2 = (size_t)a.nparts * k * 8 + NBIN * 4 + (size_t)n2 * 8;
-  hipError_t e = hipFuncSetAttribute(stream ? (const void*)topk_stream : (const void*)topk_stage1,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && S % 4 == 0 && a.part % 4 == 0;
+  const void* k1 = !stream ? (const void*)topk_stage1
+                           : vec ? (const void*)topk_stream<true> : (const void*)topk_stream<false>;
+  hipError_t e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
   if (a.nparts > 1) {
     e = hipFuncSetAttribute((const void*)topk_stage2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
@@ -543,8 +594,11 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
     const int nb = (int)(B - b0 < MAXB ? B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
-    if (stream)
-      hipLaunchKernelGGL(topk_stream, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
+    if (stream && vec)
+      hipLaunchKernelGGL(topk_stream<true>, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
+                         a, pt, (int)b0);
+    else if (stream)
+      hipLaunchKernelGGL(topk_stream<false>, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
                          a, pt, (int)b0);
     else
       hipLaunchKernelGGL(topk_stage1, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(TK_THREADS), lds1, s,
