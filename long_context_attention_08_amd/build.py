@@ -26,6 +26,12 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The indexer's ReLU epilogue is the bulk of its VALU
+# work; with IEEE mode off a max needs no operand quieting first (its inputs
+# are finite MFMA results), which halves the epilogue.
+FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _hipcc():
     h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(h):
@@ -35,7 +41,7 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [_hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + FLAGS + FILE_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

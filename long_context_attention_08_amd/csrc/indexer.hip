@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   float wh[QPW][16];
   int64_t nvis[QPW];
   bool qvalid[QPW];
+  float* orow[QPW];                  // output row of each query (clamped for invalid ones)
   int64_t nvis_max = 0;
   for (int qi = 0; qi < QB; ++qi) {           // block-wide maximum (uniform)
     const int64_t t = t0 + qi;
@@ -94,6 +95,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     qvalid[qi] = t < a.nq;
     const int64_t tt = qvalid[qi] ? t : a.nq - 1;
     nvis[qi] = qvalid[qi] ? visible_count(pt.q_pos0[bl] + t, a.m, S) : 0;
+    orow[qi] = a.scores + (b * a.nq + tt) * S;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.qI) + ((b * a.nq + tt) * 32 + (l & 31)) * CI;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
@@ -165,6 +167,8 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
       for (int kk = 0; kk < KS; ++kk)
         kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (ntile * 32 + (l & 31)) * LDK + 16 * kk + 8 * (l >> 5)));
       const int64_t s = s0 + ntile * 32 + (l & 31);
+      // lane half G holds heads 8 (r/4) + 4 G + r%4 of key s: partial sums
+      float part[QPW];
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
         f32x16 acc;
@@ -172,12 +176,24 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][kk], kf[kk], acc, 0, 0, 0);
+        // (this file is built with IEEE mode off: the max is one instruction)
         float sc = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc = fmaf(wh[qi][r], fmaxf(acc[r], 0.0f), sc);
-        sc += __shfl_xor(sc, 32);
-        if (qvalid[qi] && l < 32 && s < S)
-          a.scores[(b * a.nq + t0 + wq * QPW + qi) * S + s] = s < nvis[qi] ? sc : -INFINITY;
+        part[qi] = sc;
+      }
+      // queries in pairs: the lower half finishes query qa, the upper half qb,
+      // each taking the other half's partial; one 64-lane store per pair
+#pragma unroll
+      for (int qa = 0; qa < QPW; qa += 2) {
+        const int qb = QPW > 1 ? qa + 1 : qa;
+        const bool hi = l >= 32;
+        const float mine = hi ? part[qb] : part[qa];
+        const float total = mine + __shfl_xor(hi ? part[qa] : part[qb], 32);
+        const int q = hi ? qb : qa;
+        const bool ok = (QPW > 1 || !hi) && (hi ? qvalid[qb] : qvalid[qa]) && s < S;
+        if (ok) (hi ? orow[qb] : orow[qa])[s] = s < (hi ? nvis[qb] : nvis[qa]) ? total : -INFINITY;
+        (void)q;
       }
     }
     __syncthreads();
