@@ -174,17 +174,43 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a, PosTable pt, int
 //   * O^T += V^T P^T takes its V^T operand straight from the row-major key
 //     tile with ds_read_b64_tr_b16 (K = V).
 constexpr int TS = 32;           // key slots per tile
+
+// A zero row (at least as long as any stored row, 2 c bytes at c = 512):
+// padding key slots are copied from it, so their keys and values are exactly
+// zero (their logits are masked; a zero value keeps P = 0 from meeting a
+// non-finite byte pattern in PV).  Read-only; zero-initialised at load.
+__device__ __align__(16) uint8_t g_zero_row[1024];
 constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LDS
 
-// 16-byte global -> LDS copy of every lane: lane l's bytes land at LDS address
-// lds_base + 16 l (lds_base wave-uniform).  Written as a two-instruction asm
+// 16-byte global -> LDS copy of every lane: lane l's bytes from gsrc + OFF land
+// at LDS address lds_base + 16 l (lds_base wave-uniform).  The instruction's
+// immediate offset is added to the LDS address as well as to the global one,
+// so M0 is set to lds_base - OFF.  Written as a two-instruction asm
 // block (M0 set in the same block) so that the compiler does not track it:
 // the kernel waits for these copies itself (vmcnt) before reading the stage.
 // The instruction has no register results, so nothing is written back into
 // VGPRs while it is in flight.
+template <int OFF>
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds_base) : "memory", "m0");
+  static_assert(OFF >= 0 && OFF < 4096, "global offset is a 13-bit signed immediate");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               : : "v"(gsrc), "s"(lds_base - (uint32_t)OFF), "i"(OFF) : "memory", "m0");
 }
+
+// The copies of one wave for one tile: copy q = wv + NW i (q < NDMA) takes
+// bytes 32 q + 16 G of each lane's row (offset 32 NW i from `base`, which
+// already holds 32 wv + 16 G) into stage bytes [1024 q, 1024 q + 1024).
+template <int I, int N, int NW, int NDMA>
+struct DmaCopies {
+  __device__ __forceinline__ static void run(const uint8_t* base, uint32_t lds0, int wv) {
+    if (wv + NW * I < NDMA) dma16<32 * NW * I>(base, lds0 + 1024 * NW * I);
+    DmaCopies<I + 1, N, NW, NDMA>::run(base, lds0, wv);
+  }
+};
+template <int N, int NW, int NDMA>
+struct DmaCopies<N, N, NW, NDMA> {
+  __device__ __forceinline__ static void run(const uint8_t*, uint32_t, int) {}
+};
 
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // the global->LDS copies still in flight (their completion is waited for
@@ -253,7 +279,8 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   const int ncomp = (int)ui.ncomp;
   const uint8_t* comp_base = reinterpret_cast<const uint8_t*>(a.kv_comp) + b * a.S * (int64_t)RB;
   const uint8_t* win_base = reinterpret_cast<const uint8_t*>(a.kv_win) + (b * a.W + (ui.wlo - wpos0)) * (int64_t)RB;
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);     // any readable address
+  static_assert(Cf::RB <= (int)sizeof(g_zero_row), "zero row shorter than a stored row");
+  const uint8_t* dummy = g_zero_row;                                 // padding slots
   const int nq_blk = (int)(ui.tl - ui.t0 + 1);
   const int pfirst = (int)(p0 + ui.t0);
   const int ntiles = slot_hi > slot_lo ? (slot_hi - slot_lo + TS - 1) / TS : 0;
@@ -313,20 +340,20 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     return win_base + (int64_t)(s - ncomp) * RB;
   };
 
-  // copies of tile `it` into stage buffer `buf`: wave copy q covers stage
-  // pieces [64 q, 64 q + 64); stage piece P = piece * TS + slot
+  // copies of tile `it` into a stage buffer.  Stage piece P = piece * TS +
+  // slot and wave copy q covers P in [64 q, 64 q + 64): lane l always serves
+  // slot s0 + l % 32 (piece 2 q + l / 32), so its row address is found once
+  // per tile and the copies differ by immediate offsets.  Padding slots copy
+  // the zero row.
   auto issue = [&](int it, uint8_t* stg) {
-    const int s0 = slot_lo + it * TS;
-    for (int q = wv; q < Cf::NDMA; q += Cf::NW) {
-      const int P = q * 64 + l;
-      const int piece = P / TS, sl_ = P % TS;
-      int pos;
-      bool win;
-      const uint8_t* src = (s0 + sl_ < slot_hi) ? slot_src(s0 + sl_, &pos, &win) : nullptr;
-      src = src ? src + 16 * piece : dummy;
-      const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + q * 1024);
-      dma16(src, __builtin_amdgcn_readfirstlane(lds));
-    }
+    const int slot = slot_lo + it * TS + (l & 31);
+    int pos;
+    bool win;
+    const uint8_t* row = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
+    const uint8_t* base = (row ? row : dummy) + 16 * G + 32 * wv;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + wv * 1024));
+    DmaCopies<0, (Cf::NDMA + Cf::NW - 1) / Cf::NW, Cf::NW, Cf::NDMA>::run(base, lds0, wv);
   };
   // copies per wave and tile: waves below NDMA % NW issue one more
   const int my_dma = Cf::NDMA / Cf::NW + (wv < Cf::NDMA % Cf::NW ? 1 : 0);
