@@ -253,15 +253,21 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   using Cf = AttnCfg<C, KVL, CS, NRG>;
   constexpr int KQ = Cf::KQ, MO = Cf::MO, CH = Cf::CH, NP = Cf::NP, RB = Cf::RB;
   constexpr int KT = TS * (C + KPAD);     // elements of one key tile
-  // separate LDS objects, so that alias analysis can tell the in-flight
-  // global->LDS copies (stage) from every other LDS access
-  // two stage buffers (piece-major: [piece][slot][16 B]) and two bf16 key
-  // tiles (chunk-swizzled), even tiles in the first; a buffer is chosen at
-  // compile time so that its offset folds into the LDS instructions
+  // two stage buffers (raw rows, piece-major: [piece][slot][16 B]) and three
+  // bf16 key tiles (chunk-swizzled); tile t lives in key tile t % 3, chosen at
+  // compile time (separate objects: addresses fold into the LDS instructions
+  // and alias analysis keeps the tiles apart)
+  constexpr int HK = CS > 1 ? 8 : 16;     // score registers a wave keeps per tile: its key half
   __shared__ __align__(16) uint8_t s_stage[2 * Cf::STAGE];
-  __shared__ __align__(16) uint16_t s_K[2 * KT];
-  __shared__ __align__(16) float s_xb[CS > 1 ? NRG * CS * 4 * 64 * 4 : 4];   // [wave][r/4][lane][4]
-  __shared__ uint32_t s_vmask[2][8];                         // per buffer and query: visible slots of the tile
+  __shared__ __align__(16) uint16_t s_K0[KT];
+  __shared__ __align__(16) uint16_t s_K1[KT];
+  __shared__ __align__(16) uint16_t s_K2[KT];
+  // exchange within a channel pair: the partner's half of the partial scores,
+  // this wave's half of P (bf16 pairs), its per-row half maximum
+  __shared__ __align__(16) float s_xs[CS > 1 ? Cf::NW * 2 * 64 * 4 : 4];   // [wave][r/4][lane][4]
+  __shared__ __align__(16) uint32_t s_xp[CS > 1 ? Cf::NW * 64 * 4 : 4];   // [wave][lane][4]
+  __shared__ float s_xm[CS > 1 ? Cf::NW * 64 : 1];                        // [wave][lane]
+  __shared__ uint32_t s_vmask[3][8];                         // per key tile and query: visible slots
   __shared__ int s_nvisq[8];
   __shared__ int s_sidx[SIDX_CAP];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -463,71 +469,123 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     }
   };
 
-  // A tile in two halves around the rescale.  Per tile two block barriers:
-  // B3 (partial scores visible, every wave's copies of the next tile landed)
-  // and B4 (this tile's PV done, next tile decoded after it).  Stage it&1 is refilled
-  // with tile it+2 at the start of tile it: its last reader, the decode of
-  // tile it, finished before the previous B4.
-  f32x16 st;
-  float tmax;
-  auto score = [&](auto par, int it) -> bool {
-    constexpr int PB = decltype(par)::value;   // it & 1
-    const uint16_t* kt = s_K + PB * KT;
-    if (it + 2 < ntiles) issue(it + 2, s_stage + PB * Cf::STAGE);
-    // ---- partial S^T[32 keys][32 rows] over this wave's channel slice, two chains
-    f32x16 st1;
+  auto ktile = [&](auto kbc) -> uint16_t* {
+    constexpr int KB = decltype(kbc)::value;
+    if constexpr (KB == 0) return s_K0;
+    else if constexpr (KB == 1) return s_K1;
+    else return s_K2;
+  };
+  // ---- pieces of the pipeline
+  // partial S^T[32 keys][32 rows] of the tile in key tile KB over this wave's
+  // channel slice: register r holds key slot 8 (r/4) + 4 G + r%4 of row col
+  auto score_tile = [&](auto kbc) -> f32x16 {
+    const uint16_t* kt = ktile(kbc);
+    f32x16 s0, s1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { st[r] = 0.f; st1[r] = 0.f; }
-    {
-      // logical chunk of k-step kk: ch*CH/8 + 2 kk + G; only its two low bits
-      // meet the swizzle, so even and odd kk each get one base address
-      const uint16_t* krow = kt + col * (C + KPAD);
-      const int x0 = ch * (CH / 8) + G;
-      const uint16_t* kb0 = krow + 8 * (x0 ^ ksw(col));          // kk = 0 (mod 4 chunks)
-      const uint16_t* kb1 = krow + 8 * ((x0 + 2) ^ ksw(col));    // kk = 1
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+    // logical chunk of k-step kk: ch*CH/8 + 2 kk + G; only its two low bits
+    // meet the swizzle, so even and odd kk each get one base address
+    const uint16_t* krow = kt + col * (C + KPAD);
+    const int x0 = ch * (CH / 8) + G;
+    const uint16_t* kb0 = krow + 8 * (x0 ^ ksw(col));
+    const uint16_t* kb1 = krow + 8 * ((x0 + 2) ^ ksw(col));
 #pragma unroll
-      for (int kk = 0; kk < KQ; kk += 2) {
-        const int hop = 8 * 4 * (kk >> 1);                       // 4 chunks per kk pair
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const u32x4*>(kb0 + hop)), qf[kk], st, 0, 0, 0);
-        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const u32x4*>(kb1 + hop)), qf[kk + 1], st1, 0, 0, 0);
+    for (int kk = 0; kk < KQ; kk += 2) {
+      const int hop = 8 * 4 * (kk >> 1);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kb0 + hop)), qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kb1 + hop)), qf[kk + 1], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] += s1[r];
+    return s0;
+  };
+  const int partner = wv ^ 1;                       // CS == 2: the wave with the other channel half
+  // the partner's key half of a partial S^T goes to LDS
+  auto put_partial = [&](const f32x16& sp) {
+    const bool lo = ch != 0;                        // partner owns keys 0..15 (registers 0..7)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+      *reinterpret_cast<f32x4*>(s_xs + ((wv * 2 + rr) * 64 + l) * 4) =
+          (f32x4){lo ? sp[4 * rr] : sp[8 + 4 * rr], lo ? sp[4 * rr + 1] : sp[8 + 4 * rr + 1],
+                  lo ? sp[4 * rr + 2] : sp[8 + 4 * rr + 2], lo ? sp[4 * rr + 3] : sp[8 + 4 * rr + 3]};
+  };
+  // this wave's key half of the full scores: own registers 8 ch .. 8 ch + 7 plus the partner's
+  auto take_half = [&](const f32x16& sp, float (&hn)[HK]) {
+    if constexpr (CS > 1) {
+      const bool hi = ch != 0;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(s_xs + ((partner * 2 + rr) * 64 + l) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hn[4 * rr + j] = (hi ? sp[8 + 4 * rr + j] : sp[4 * rr + j]) + o[j];
       }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hn[r] = sp[r];
     }
+  };
+  // mask a tile's half scores (tiles not seen whole by every query) and
+  // return this lane's row maximum over the half (both lane halves)
+  auto mask_max = [&](int t, int kbuf, float (&hn)[HK]) -> float {
+    if (!tile_full(t)) {
+      const uint32_t m16 = (s_vmask[kbuf][qloc] >> (4 * G)) & 0x0F0F0F0Fu;
+      const uint32_t mh = CS > 1 ? m16 >> (16 * ch) : m16;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] += st1[r];
-    if (CS > 1) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<f32x4*>(s_xb + ((wv * 4 + rr) * 64 + l) * 4) =
-            (f32x4){st[4 * rr], st[4 * rr + 1], st[4 * rr + 2], st[4 * rr + 3]};
+      for (int i = 0; i < HK; ++i) hn[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? hn[i] : -INFINITY;
     }
-    // this wave's copies of tile it+1 have landed once at most those of it+2 remain
-    if (it + 1 < ntiles) wait_copies(it + 2 < ntiles ? my_dma : 0);
-    lds_barrier();                                                    // B3
-    if (CS > 1) {
-      const int pw = rg * CS + (ch ^ 1);
+    float mx = -INFINITY;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(s_xb + ((pw * 4 + rr) * 64 + l) * 4);
-        st[4 * rr] += o[0]; st[4 * rr + 1] += o[1]; st[4 * rr + 2] += o[2]; st[4 * rr + 3] += o[3];
-      }
+    for (int i = 0; i < HK; ++i) mx = fmaxf(mx, hn[i]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+
+  // PV of the tile in key tile KB: O^T[c][row] += V^T[c][keys] P^T[keys][row].
+  // MFMA over key half s covers slots [16s + 4G, +4) and [16s + 8 + 4G, +4);
+  // each half of its A operand comes from one transposed read: lane (lambda =
+  // l % 16) of a 16-lane group addresses key row key0 + lambda/4, channels
+  // c0 + 4 (lambda % 4) .. + 4, and receives channel c0 + lambda of keys
+  // key0 .. key0 + 3.  Key rows 16 s + 8 hf + 4 G + lambda/4 have the swizzle
+  // (2 hf + G) & 3 for either s, so a half only moves the base by 16 rows.
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int lam = l & 15, grp = (l >> 4) & 1;
+  const int e8 = (ch * CH + 16 * grp + 4 * (lam & 3)) >> 2;            // 8-byte chunk for mo = 0
+  const int rowl = 4 * G + (lam >> 2);
+  const int tb0 = rowl * (C + KPAD) + 8 * ((e8 >> 1) ^ ((0 + G) & 3)) + 4 * (e8 & 1);
+  const int tb1 = (rowl + 8) * (C + KPAD) + 8 * ((e8 >> 1) ^ ((2 + G) & 3)) + 4 * (e8 & 1);
+  auto pv_half = [&](const uint16_t* kt, int half, const bf16x8& pf) {
+    const uint16_t* t0p = kt + 16 * half * (C + KPAD) + tb0;
+    const uint16_t* t1p = kt + 16 * half * (C + KPAD) + tb1;
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo) {
+      const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(t0p + 32 * mo));
+      const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(t1p + 32 * mo));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+      acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf,
+                                                        acc[mo], 0, 0, 0);
     }
-    // ---- online softmax: register r holds key slot 8 (r/4) + 4 G + r%4 of this lane's row
-    if (!tile_full(it)) {
-      const uint32_t m16 = (s_vmask[PB][qloc] >> (4 * G)) & 0x0F0F0F0Fu;
+  };
+
+  // Software pipeline, two block barriers per tile.  Iteration it (tile it's
+  // scores of this wave's key half, hc, and its row maximum are in registers):
+  //   copies of tile it+3 go out (into the stage tile it+1 was decoded from);
+  //   P of tile it, next to the S^T MFMAs of tile it+1;
+  //   partner exchange of partial scores (tile it+1) and P (tile it);
+  //   [wait for this wave's copies of tile it+2]  B_a;
+  //   scores of tile it+1 completed, masked, half maximum published;
+  //   PV of tile it, next to the decode of tile it+2 (key tile (it+2) % 3,
+  //   last read by PV of tile it-1);  B_b.
+  // The running maximum is raised only when a row's tile maximum passes it by
+  // more than 8 (log2 units); that rescale sits outside the inner loop, which
+  // keeps the O^T accumulator in place.
+  float hc[HK];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = ((m16 >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] : -INFINITY;
-    }
-    tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl;
-    // the running maximum is raised only when a row's tile maximum passes it
-    // by more than 8 (log2 units)
+  for (int i = 0; i < HK; ++i) hc[i] = -INFINITY;
+  float hmc = -INFINITY, tmax = -INFINITY;
+  auto check = [&]() -> bool {
+    const float pm = CS > 1 ? s_xm[partner * 64 + l] : -INFINITY;
+    tmax = fmaxf(hmc, pm) * sl;
     return __builtin_amdgcn_ballot_w64(tmax > m_run + 8.0f) != 0;
   };
-  // rescale O^T and l for rows whose maximum rises (the whole wave runs it)
   auto raise_max = [&]() {
     float alpha = 1.f;
     if (tmax > m_run + 8.0f) {
@@ -540,95 +598,119 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
   };
-  auto accumulate = [&](auto par, int it) {
-    constexpr int PB = decltype(par)::value;   // it & 1
-    const uint16_t* kt = s_K + PB * KT;
+  // The two overlapped stretches (P of tile it with the S^T MFMAs of tile it+1;
+  // PV of tile it with the decode of tile it+2) are branch-free so that the
+  // scheduler can interleave them: past the last tile they run on key tiles
+  // and stages nobody reads again.
+  auto finish = [&](auto kbc, int it) {
+    constexpr int KB = decltype(kbc)::value;
+    const Par<(KB + 1) % 3> kb1;
+    const Par<(KB + 2) % 3> kb2;
+    if (it + 3 < ntiles) issue(it + 3, s_stage + ((it + 1) & 1) * Cf::STAGE);
+    // P of tile it over this wave's key half; l accumulates over it
     const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-    uint32_t pk[8];
+    uint32_t pk[HK / 2];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
+    for (int i = 0; i < HK; i += 2) {
       // v_exp_f32 directly: results below 2^-126 flush to zero, which leaves
       // the normalised output unchanged at fp32 resolution
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(st[r], sl, mneg));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(st[r + 1], sl, mneg));
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(hc[i], sl, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(hc[i + 1], sl, mneg));
       l_run += e0 + e1;
-      pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
+      pk[i >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
     }
-    // ---- O^T[c][row] += V^T[c][keys] P^T[keys][row].  MFMA s covers key slots
-    // [16s + 4G, +4) and [16s + 8 + 4G, +4) in its eight k-slots; each half
-    // comes from one transposed read: lane (lambda = l % 16) of a 16-lane group
-    // addresses key row key0 + lambda/4, channels c0 + 4 (lambda % 4) .. + 4,
-    // and receives channel c0 + lambda of keys key0 .. key0 + 3.
-    {
-      const int lam = l & 15, grp = (l >> 4) & 1;
-      // key row 16 s + 8 hf + 4 G + lam/4 has ksw = (2 hf + G) & 3; the
-      // channel part 4 mo of the 16-byte chunk index sits above the XOR bits
-      const int e8 = (ch * CH + 16 * grp + 4 * (lam & 3)) >> 2;      // 8-byte chunk for mo = 0
-      const int rowl = 4 * G + (lam >> 2);
-      const uint16_t* tb0 = kt + rowl * (C + KPAD) + 8 * ((e8 >> 1) ^ ((0 + G) & 3)) + 4 * (e8 & 1);
-      const uint16_t* tb1 = kt + (rowl + 8) * (C + KPAD) + 8 * ((e8 >> 1) ^ ((2 + G) & 3)) + 4 * (e8 & 1);
-      typedef short v4s __attribute__((ext_vector_type(4)));
+    const f32x16 sn = score_tile(kb1);
+    if constexpr (CS > 1) {
+      put_partial(sn);
+      *reinterpret_cast<u32x4*>(s_xp + (wv * 64 + l) * 4) = (u32x4){pk[0], pk[1], pk[2], pk[3]};
+    }
+    // this wave's copies of tile it+2 have landed once at most those of it+3 remain
+    wait_copies(it + 3 < ntiles ? my_dma : 0);
+    lds_barrier();                                                    // B_a
+    float hn[HK];
+    take_half(sn, hn);
+    const float hmn = mask_max(it + 1, (KB + 1) % 3, hn);
+    if constexpr (CS > 1) s_xm[wv * 64 + l] = hmn;
+    const uint16_t* kt = ktile(kbc);
+    if constexpr (CS > 1) {
+      const u32x4 pp = *reinterpret_cast<const u32x4*>(s_xp + (partner * 64 + l) * 4);
+      pv_half(kt, ch, as_bf16x8((u32x4){pk[0], pk[1], pk[2], pk[3]}));
+      pv_half(kt, ch ^ 1, as_bf16x8(pp));
+    } else {
+      pv_half(kt, 0, as_bf16x8((u32x4){pk[0], pk[1], pk[2], pk[3]}));
+      pv_half(kt, 1, as_bf16x8((u32x4){pk[4], pk[5], pk[6], pk[7]}));
+    }
+    decode(s_stage + (it & 1) * Cf::STAGE, ktile(kb2));
+    masks(it + 2, (KB + 2) % 3);
+    lds_barrier();                                                    // B_b
 #pragma unroll
-      for (int sk = 0; sk < 2; ++sk) {
-        const bf16x8 pf = as_bf16x8((u32x4){pk[4 * sk], pk[4 * sk + 1], pk[4 * sk + 2], pk[4 * sk + 3]});
-#pragma unroll
-        for (int mo = 0; mo < MO; ++mo) {
-          const int off = 16 * sk * (C + KPAD) + 32 * mo;                  // rows 16 sk, chunks 4 mo
-          const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb0 + off));
-          const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb1 + off));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
-          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf,
-                                                            acc[mo], 0, 0, 0);
-        }
-      }
-    }
-    // decode tile it+1 (its copies landed before B3) into the other key tile
-    if (it + 1 < ntiles) {
-      decode(s_stage + (1 - PB) * Cf::STAGE, s_K + (1 - PB) * KT);
-      masks(it + 1, 1 - PB);
-    }
-    lds_barrier();                                                    // B4
+    for (int i = 0; i < HK; ++i) hc[i] = hn[i];
+    hmc = hmn;
   };
 
-  // prologue: tiles 0 and 1 in flight, tile 0 decoded
+  // prologue: tiles 0 and 1 decoded, tile 2 in flight, scores of tile 0 ready
   if (ntiles > 0) {
     issue(0, s_stage);
     if (ntiles > 1) issue(1, s_stage + Cf::STAGE);
     wait_copies(ntiles > 1 ? my_dma : 0);
-    lds_barrier();
-    decode(s_stage, s_K);
+    lds_barrier();                                   // copies of tile 0 visible
+    decode(s_stage, s_K0);
     masks(0, 0);
-    lds_barrier();
+    wait_copies(0);
+    lds_barrier();                                   // key tile 0 complete, copies of tile 1 visible
+    if (ntiles > 2) issue(2, s_stage);
+    if (ntiles > 1) {
+      decode(s_stage + Cf::STAGE, s_K1);
+      masks(1, 1);
+    }
+    const f32x16 s0v = score_tile(Par<0>());
+    if constexpr (CS > 1) put_partial(s0v);
+    lds_barrier();                                   // partials of tile 0, key tile 1 complete
+    take_half(s0v, hc);
+    hmc = mask_max(0, 0, hc);
+    if constexpr (CS > 1) s_xm[wv * 64 + l] = hmc;
+    lds_barrier();                                   // half maxima of tile 0
   }
-  // The inner loop holds no rescale code, so the accumulator stays in the
-  // MFMA registers across it; a tile that raises a maximum leaves it, is
-  // rescaled and finished here, and the inner loop resumes (at either
-  // parity: the even half is skipped when it is odd).
-  const Par<0> even;
-  const Par<1> odd;
+  // inner loop unrolled by three (key tile it % 3 known at compile time); it
+  // resumes at any phase after a rescale
   for (int it = 0; it < ntiles;) {
     bool up = false;
     for (;;) {
-      if (!(it & 1)) {
-        up = score(even, it);
+      const int ph = it % 3;
+      if (ph == 0) {
+        up = check();
         if (up) break;
-        accumulate(even, it);
+        finish(Par<0>(), it);
         if (++it >= ntiles) break;
       }
-      up = score(odd, it);
+      if (ph <= 1) {
+        up = check();
+        if (up) break;
+        finish(Par<1>(), it);
+        if (++it >= ntiles) break;
+      }
+      up = check();
       if (up) break;
-      accumulate(odd, it);
+      finish(Par<2>(), it);
       if (++it >= ntiles) break;
     }
     if (up) {
       raise_max();
-      if (it & 1) accumulate(odd, it);
-      else accumulate(even, it);
+      switch (it % 3) {
+        case 0: finish(Par<0>(), it); break;
+        case 1: finish(Par<1>(), it); break;
+        default: finish(Par<2>(), it); break;
+      }
       ++it;
     }
   }
 
   l_run += __shfl_xor(l_run, 32);
+  if constexpr (CS > 1) {            // each wave of a pair summed P over its own key half
+    s_xm[wv * 64 + l] = l_run;
+    lds_barrier();
+    l_run += s_xm[partner * 64 + l];
+  }
   if (!qvalid) return;
   // register r of m-tile mo holds channel ch*CH + 32 mo + 8 (r/4) + 4 G + r%4 of this lane's row
   if (pl.max_splits == 1) {
@@ -705,7 +787,12 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
 static bool attn_mfma_ok(const AttnArgs& a, bool dense) {
   if (a.q_dtype != ACT_BF16 || (a.kv_layout != ROW_BF16 && a.kv_layout != ROW_FP8)) return false;
   if (!dense && a.k > SIDX_CAP) return false;
-  if (a.c == 512) return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
+  // c = 512 with bf16 rows: two 32 KB stages and three key tiles exceed the
+  // 160 KB of LDS, so that layout takes the generic kernel
+  if (a.c == 512) {
+    if (a.kv_layout != ROW_FP8) return false;
+    return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
+  }
   if (a.c == 128) return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64 || a.nh == 128)
                                : (a.nh == 32 || a.nh == 64 || a.nh == 128);
   return false;
@@ -782,8 +869,7 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
       const int nrg = rows_per_block(a, dense) / 32;
       if (a.c == 512) {
-        if (a.kv_layout == ROW_FP8) launch_mfma_c<512, ROW_FP8, 2>(a, grid, nrg, pt, (int)b0, pl, s);
-        else launch_mfma_c<512, ROW_BF16, 2>(a, grid, nrg, pt, (int)b0, pl, s);
+        launch_mfma_c<512, ROW_FP8, 2>(a, grid, nrg, pt, (int)b0, pl, s);
       } else {
         if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1>(a, grid, nrg, pt, (int)b0, pl, s);
         else launch_mfma_c<128, ROW_BF16, 1>(a, grid, nrg, pt, (int)b0, pl, s);
