@@ -203,7 +203,7 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
 template <int I, int N, int NW, int NDMA>
 struct DmaCopies {
   __device__ __forceinline__ static void run(const uint8_t* base, uint32_t lds0, int wv) {
-    if (wv + NW * I < NDMA) dma16<32 * NW * I>(base, lds0 + 1024 * NW * I);
+    if (NW * (I + 1) <= NDMA || wv + NW * I < NDMA) dma16<32 * NW * I>(base, lds0 + 1024 * NW * I);
     DmaCopies<I + 1, N, NW, NDMA>::run(base, lds0, wv);
   }
 };
@@ -423,51 +423,55 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     }
   };
 
-  auto decode = [&](const uint8_t* stg, uint16_t* kt) {
-    // decode a stage into a bf16 key tile.  Stage unit un (16 bytes)
-    // is piece un / TS of slot un % TS; the E4M3 units come first.  Fixed trip
-    // counts with all stage reads issued before the conversions; the guards
-    // are uniform per wave (NT is a multiple of 64 and so are the unit counts).
-    {
-      constexpr int U8 = Cf::NF8 * TS, UB = (NP - Cf::NF8) * TS;
-      constexpr int N8 = (U8 + Cf::NT - 1) / Cf::NT, NB = (UB + Cf::NT - 1) / Cf::NT;
-      u32x4 w8[N8 > 0 ? N8 : 1], wb[NB > 0 ? NB : 1];
+  // Decode of a stage into a bf16 key tile, as a load step and a convert-and-
+  // store step, both free of branches.  Stage unit un (16 bytes) is piece
+  // un / TS of slot un % TS, E4M3 units first.  Each thread takes F8 whole
+  // E4M3 units, then (when the E4M3 units leave half a round) half of one
+  // more E4M3 unit, then FB bf16 units.
+  constexpr int U8 = Cf::NF8 * TS, UB = (NP - Cf::NF8) * TS;
+  constexpr int F8 = U8 / Cf::NT, R8 = U8 % Cf::NT, FB = UB / Cf::NT;
+  static_assert((R8 == 0 || 2 * R8 == Cf::NT) && UB % Cf::NT == 0, "decode work splits evenly");
+  constexpr bool HALF = R8 != 0;
+  struct DecRegs {
+    u32x4 w8[F8 > 0 ? F8 : 1];
+    u32x2 wh;
+    u32x4 wb[FB > 0 ? FB : 1];
+  };
+  const int tid = threadIdx.x;
+  auto dec_load = [&](const uint8_t* stg) -> DecRegs {
+    DecRegs d;
 #pragma unroll
-      for (int j = 0; j < N8; ++j) {
-        const int un = threadIdx.x + Cf::NT * j;
-        if (Cf::NT * (j + 1) <= U8 || un < U8) w8[j] = *reinterpret_cast<const u32x4*>(stg + un * 16);
-      }
+    for (int j = 0; j < F8; ++j) d.w8[j] = *reinterpret_cast<const u32x4*>(stg + (tid + Cf::NT * j) * 16);
+    if constexpr (HALF) d.wh = *reinterpret_cast<const u32x2*>(stg + (F8 * Cf::NT + (tid >> 1)) * 16 + 8 * (tid & 1));
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int un = U8 + threadIdx.x + Cf::NT * j;
-        if (Cf::NT * (j + 1) <= UB || un < U8 + UB) wb[j] = *reinterpret_cast<const u32x4*>(stg + un * 16);
-      }
+    for (int j = 0; j < FB; ++j) d.wb[j] = *reinterpret_cast<const u32x4*>(stg + (U8 + tid + Cf::NT * j) * 16);
+    return d;
+  };
+  // 8 E4M3 bytes -> one 16-byte bf16 chunk
+  auto e4m3x8 = [](u32x2 w) -> u32x4 {
+    return (u32x4){e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
+                   e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
+  };
+  auto dec_store = [&](const DecRegs& d, uint16_t* kt) {
 #pragma unroll
-      for (int j = 0; j < N8; ++j) {
-        const int un = threadIdx.x + Cf::NT * j;
-        if (Cf::NT * (j + 1) <= U8 || un < U8) {   // 16 E4M3 channels -> two 16-byte chunks
-          const int piece = un / TS, ks = un % TS;
-          const u32x4 w = w8[j];
-          uint16_t* krow = kt + ks * (C + KPAD);
-          const u32x4 lo = {e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
-                            e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
-          const u32x4 hi = {e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
-                            e4m3x2_to_bf16x2(w[3], false), e4m3x2_to_bf16x2(w[3], true)};
-          *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece) ^ ksw(ks))) = lo;
-          *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece + 1) ^ ksw(ks))) = hi;
-        }
-      }
+    for (int j = 0; j < F8; ++j) {               // 16 E4M3 channels -> chunks 2 piece, 2 piece + 1
+      const int un = tid + Cf::NT * j, piece = un / TS, ks = un % TS;
+      uint16_t* krow = kt + ks * (C + KPAD);
+      *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece) ^ ksw(ks))) = e4m3x8((u32x2){d.w8[j][0], d.w8[j][1]});
+      *reinterpret_cast<u32x4*>(krow + 8 * ((2 * piece + 1) ^ ksw(ks))) = e4m3x8((u32x2){d.w8[j][2], d.w8[j][3]});
+    }
+    if constexpr (HALF) {                        // 8 E4M3 channels -> chunk 2 piece + half
+      const int un = F8 * Cf::NT + (tid >> 1), piece = un / TS, ks = un % TS;
+      *reinterpret_cast<u32x4*>(kt + ks * (C + KPAD) + 8 * ((2 * piece + (tid & 1)) ^ ksw(ks))) = e4m3x8(d.wh);
+    }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int un = U8 + threadIdx.x + Cf::NT * j;
-        if (Cf::NT * (j + 1) <= UB || un < U8 + UB) {   // 8 bf16 channels -> one chunk
-          const int piece = un / TS, ks = un % TS;
-          const int chunk = 2 * Cf::NF8 + (piece - Cf::NF8);
-          *reinterpret_cast<u32x4*>(kt + ks * (C + KPAD) + 8 * (chunk ^ ksw(ks))) = wb[j];
-        }
-      }
+    for (int j = 0; j < FB; ++j) {               // 8 bf16 channels -> one chunk
+      const int un = U8 + tid + Cf::NT * j, piece = un / TS, ks = un % TS;
+      const int chunk = 2 * Cf::NF8 + (piece - Cf::NF8);
+      *reinterpret_cast<u32x4*>(kt + ks * (C + KPAD) + 8 * (chunk ^ ksw(ks))) = d.wb[j];
     }
   };
+  auto decode = [&](const uint8_t* stg, uint16_t* kt) { dec_store(dec_load(stg), kt); };
 
   auto ktile = [&](auto kbc) -> uint16_t* {
     constexpr int KB = decltype(kbc)::value;
@@ -627,6 +631,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     // this wave's copies of tile it+2 have landed once at most those of it+3 remain
     wait_copies(it + 3 < ntiles ? my_dma : 0);
     lds_barrier();                                                    // B_a
+    const DecRegs dr = dec_load(s_stage + (it & 1) * Cf::STAGE);     // tile it+2
     float hn[HK];
     take_half(sn, hn);
     const float hmn = mask_max(it + 1, (KB + 1) % 3, hn);
@@ -640,7 +645,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
       pv_half(kt, 0, as_bf16x8((u32x4){pk[0], pk[1], pk[2], pk[3]}));
       pv_half(kt, 1, as_bf16x8((u32x4){pk[4], pk[5], pk[6], pk[7]}));
     }
-    decode(s_stage + (it & 1) * Cf::STAGE, ktile(kb2));
+    dec_store(dr, ktile(kb2));
     masks(it + 2, (KB + 2) % 3);
     lds_barrier();                                                    // B_b
 #pragma unroll
