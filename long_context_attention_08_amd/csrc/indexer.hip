@@ -9,6 +9,8 @@
 // gfx950 scaled fp4->bf16 conversion, which is exact) and shared by the four
 // waves.  The head reduction sum_h w_h ReLU(acc) runs on the accumulator
 // registers: 16 heads per lane plus one cross-lane add.
+#include <type_traits>
+
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
@@ -105,6 +107,22 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     for (int r = 0; r < 16; ++r) wh[qi][r] = wrow[(r >> 2) * 8 + 4 * (l >> 5) + (r & 3)];
   }
 
+  // query pairs: lane half G finishes query 2 p + G of pair p (one query per
+  // pair when QPW = 1, upper half idle); per-lane row, visible count, validity
+  constexpr int NPAIR = QPW > 1 ? QPW / 2 : 1;
+  float* prow[NPAIR];
+  int pvis[NPAIR];
+  bool pok[NPAIR];
+  const bool hi = l >= 32;
+#pragma unroll
+  for (int pp = 0; pp < NPAIR; ++pp) {
+    const int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
+    prow[pp] = hi ? orow[qb] : orow[qa];
+    pvis[pp] = (int)(hi ? nvis[qb] : nvis[qa]);
+    pok[pp] = (hi ? qvalid[qb] : qvalid[qa]) && (QPW > 1 || !hi);
+  }
+  const int S32 = (int)S;
+
   for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
     const int64_t s0 = tile * KT;
     if (s0 >= nvis_max) {
@@ -182,19 +200,19 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         for (int r = 0; r < 16; ++r) sc = fmaf(wh[qi][r], fmaxf(acc[r], 0.0f), sc);
         part[qi] = sc;
       }
-      // queries in pairs: the lower half finishes query qa, the upper half qb,
-      // each taking the other half's partial; one 64-lane store per pair
-#pragma unroll
-      for (int qa = 0; qa < QPW; qa += 2) {
-        const int qb = QPW > 1 ? qa + 1 : qa;
-        const bool hi = l >= 32;
-        const float mine = hi ? part[qb] : part[qa];
-        const float total = mine + __shfl_xor(hi ? part[qa] : part[qb], 32);
-        const int q = hi ? qb : qa;
-        const bool ok = (QPW > 1 || !hi) && (hi ? qvalid[qb] : qvalid[qa]) && s < S;
-        if (ok) (hi ? orow[qb] : orow[qa])[s] = s < (hi ? nvis[qb] : nvis[qa]) ? total : -INFINITY;
-        (void)q;
-      }
+      // queries in pairs: the lower half finishes query 2 p, the upper half
+      // 2 p + 1, each taking the other half's partial; one 64-lane store per pair
+      const int s32 = (int)s;
+      auto finish_pair = [&](auto ppc) {
+        constexpr int pp = decltype(ppc)::value;
+        constexpr int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
+        const float keep = hi ? part[qb] : part[qa];
+        const float total = keep + __shfl_xor(hi ? part[qa] : part[qb], 32);
+        if (pok[pp] && s32 < S32) prow[pp][s32] = s32 < pvis[pp] ? total : -INFINITY;
+      };
+      finish_pair(std::integral_constant<int, 0>());
+      if constexpr (NPAIR > 1) finish_pair(std::integral_constant<int, 1>());
+      static_assert(NPAIR <= 2, "pairs");
     }
     __syncthreads();
   }
@@ -230,6 +248,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
 
 static bool indexer_mfma_ok(const IndexerArgs& a) {
   return a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 32 || a.cI == 64 || a.cI == 128) &&
+         a.S < ((int64_t)1 << 31) &&                 // key positions fit 32-bit store offsets
          (a.k_layout == ROW_BF16 || a.k_layout == ROW_MXFP4);
 }
 
