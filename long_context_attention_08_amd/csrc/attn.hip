@@ -185,7 +185,8 @@ constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LD
 // 16-byte global -> LDS copy of every lane: lane l's bytes from gsrc + OFF land
 // at LDS address lds_base + 16 l (lds_base wave-uniform).  The instruction's
 // immediate offset is added to the LDS address as well as to the global one,
-// so M0 is set to lds_base - OFF.  Written as a two-instruction asm
+// so M0 is set to lds_base - OFF (one wait state between the M0 write and the
+// copy that reads it).  Written as a three-instruction asm
 // block (M0 set in the same block) so that the compiler does not track it:
 // the kernel waits for these copies itself (vmcnt) before reading the stage.
 // The instruction has no register results, so nothing is written back into
@@ -193,7 +194,7 @@ constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LD
 template <int OFF>
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "global offset is a 13-bit signed immediate");
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                : : "v"(gsrc), "s"(lds_base - (uint32_t)OFF), "i"(OFF) : "memory", "m0");
 }
 
@@ -803,8 +804,10 @@ static bool attn_mfma_ok(const AttnArgs& a, bool dense) {
   return false;
 }
 
-// rows per block: one query (sparse) or 128 rows of queries sharing their keys (dense)
-// (c = 512 keeps one query per block: its Q^T and O^T slices already fill the register file)
+// rows per block: one query (sparse) or 128 rows of queries sharing their keys
+// (dense); c = 512 keeps 64 rows per block: Q^T and O^T of 32 rows x 256
+// channels already take 192 registers per wave (all 512 channels of 32 rows
+// in one wave would need 384 and spill)
 static int rows_per_block(const AttnArgs& a, bool dense) {
   if (!dense) return a.nh;
   if (a.c >= 512) return a.nh < 64 ? 64 : a.nh;
@@ -840,10 +843,9 @@ size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_ke
   return (size_t)units * pl.max_splits * pl.qpw * nh * (c + 2) * sizeof(float);
 }
 
-template <int C, int KVL, int CS>
+template <int C, int KVL, int CS, int NRG_MAX>
 static void launch_mfma_c(const AttnArgs& a, dim3 grid, int nrg, const PosTable& pt, int b0, const AttnPlan& pl,
                           hipStream_t s) {
-  constexpr int NRG_MAX = C >= 512 ? 2 : 4;     // c = 512 blocks hold at most 64 rows
   switch (nrg) {
     case 1: hipLaunchKernelGGL((attn_mfma<C, KVL, CS, 1>), grid, dim3(64 * 1 * CS), 0, s, a, pt, b0, pl); break;
     case 2: hipLaunchKernelGGL((attn_mfma<C, KVL, CS, 2>), grid, dim3(64 * 2 * CS), 0, s, a, pt, b0, pl); break;
@@ -874,10 +876,10 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
       const int nrg = rows_per_block(a, dense) / 32;
       if (a.c == 512) {
-        launch_mfma_c<512, ROW_FP8, 2>(a, grid, nrg, pt, (int)b0, pl, s);
+        launch_mfma_c<512, ROW_FP8, 2, 2>(a, grid, nrg, pt, (int)b0, pl, s);
       } else {
-        if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1>(a, grid, nrg, pt, (int)b0, pl, s);
-        else launch_mfma_c<128, ROW_BF16, 1>(a, grid, nrg, pt, (int)b0, pl, s);
+        if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
+        else launch_mfma_c<128, ROW_BF16, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
