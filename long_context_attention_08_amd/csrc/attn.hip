@@ -821,13 +821,17 @@ static AttnPlan make_plan(const AttnArgs& a, bool dense, int64_t max_keys) {
   pl.qpw = rows_per_block(a, dense) / a.nh;
   if (pl.qpw < 1) pl.qpw = 1;
   pl.units_per_b = (a.nq + pl.qpw - 1) / pl.qpw;
-  // split the keys only when a sequence has few query groups; the split size
-  // depends on the sequence alone, so results do not depend on the batch
+  // split the keys only when a sequence has few query groups.  The split size
+  // depends on the key bound alone (never on the batch), so a sequence's
+  // results do not depend on the batch: about 16 splits of at least 256 slots,
+  // so that a split's fp32 partial (rows x c) stays small next to the rows it reads
   if (pl.units_per_b >= 32) {
     pl.chunk = 1 << 30;
     pl.max_splits = 1;
   } else {
-    pl.chunk = 64;
+    int64_t ch = (max_keys + 15) / 16;
+    ch = ch < 256 ? 256 : ch;
+    pl.chunk = (int)((ch + 31) / 32 * 32);
     int64_t ms = (max_keys + pl.chunk - 1) / pl.chunk;
     pl.max_splits = (int)(ms < 1 ? 1 : ms);
   }
