@@ -754,38 +754,66 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   }
 }
 
-// merge of the split partials, splits in increasing order (deterministic)
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int b0, AttnPlan pl, int c) {
+// Merge of the split partials, splits in increasing order (deterministic).
+// A block takes 4 rows of one unit; each row's 64 threads own CPT = c / 64
+// consecutive channels and read every split's partial for them with vector
+// loads.
+template <int CPT>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   const int64_t unit = blockIdx.x;
   const int64_t bl = unit / pl.units_per_b, u = unit % pl.units_per_b;
   const int64_t b = b0 + bl;
   const UnitInfo ui = unit_info(a, pl, pt.q_pos0[bl], u);
   const int64_t nsplit = (ui.total + pl.chunk - 1) / pl.chunk;
   const int64_t rows = (int64_t)pl.qpw * a.nh;
+  const int64_t r = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = CPT * 64;
+  if (r >= rows) return;
+  const int qw = (int)(r / a.nh), h = (int)(r % a.nh);
+  const int64_t t = ui.t0 + qw;
+  if (t > ui.tl) return;
   const float* mlb = reinterpret_cast<const float*>(a.ws);
   const float* owb = mlb + (int64_t)gridDim.x * pl.max_splits * rows * 2;
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const int qw = (int)(r / a.nh), h = (int)(r % a.nh);
-    const int64_t t = ui.t0 + qw;
-    if (t > ui.tl) continue;
-    float M = -INFINITY;
-    for (int64_t s = 0; s < nsplit; ++s) M = fmaxf(M, mlb[((unit * pl.max_splits + s) * rows + r) * 2]);
-    const float z = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-    const float Mt = fmaxf(M, z);
-    float den = a.sink ? exp2f(z - Mt) : 0.f;
-    for (int64_t s = 0; s < nsplit; ++s) {
-      const float ms = mlb[((unit * pl.max_splits + s) * rows + r) * 2];
-      if (ms != -INFINITY) den += mlb[((unit * pl.max_splits + s) * rows + r) * 2 + 1] * exp2f(ms - Mt);
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int j = threadIdx.x; j < c; j += 256) {
-      float o = 0.f;
-      for (int64_t s = 0; s < nsplit; ++s) {
-        const float ms = mlb[((unit * pl.max_splits + s) * rows + r) * 2];
-        if (ms != -INFINITY) o = fmaf(owb[((unit * pl.max_splits + s) * rows + r) * c + j], exp2f(ms - Mt), o);
+  const float* ml = mlb + (unit * pl.max_splits * rows + r) * 2;          // split s at + 2 s rows
+  float M = -INFINITY;
+  for (int64_t sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[sp * rows * 2]);
+  const float z = a.sink ? a.sink[h] * LOG2E : -INFINITY;
+  const float Mt = fmaxf(M, z);
+  float den = a.sink ? exp2f(z - Mt) : 0.f;
+  float o[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) o[j] = 0.f;
+  const float* ow = owb + (unit * pl.max_splits * rows + r) * (int64_t)c + lane * CPT;   // split s at + s rows c
+  for (int64_t sp = 0; sp < nsplit; ++sp) {
+    const float ms = ml[sp * rows * 2];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - Mt);
+    den = fmaf(ml[sp * rows * 2 + 1], w, den);
+    const float* src = ow + sp * rows * (int64_t)c;
+    if constexpr (CPT % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < CPT; j += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
+        o[j] = fmaf(v[0], w, o[j]); o[j + 1] = fmaf(v[1], w, o[j + 1]);
+        o[j + 2] = fmaf(v[2], w, o[j + 2]); o[j + 3] = fmaf(v[3], w, o[j + 3]);
       }
-      store_act(a.out, a.q_dtype, ((b * a.nq + t) * a.nh + h) * c + j, o * inv);
+    } else {
+      static_assert(CPT % 2 == 0, "channels per thread");
+#pragma unroll
+      for (int j = 0; j < CPT; j += 2) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 v = *reinterpret_cast<const f32x2*>(src + j);
+        o[j] = fmaf(v[0], w, o[j]); o[j + 1] = fmaf(v[1], w, o[j + 1]);
+      }
     }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int64_t obase = ((b * a.nq + t) * a.nh + h) * c + lane * CPT;
+#pragma unroll
+  for (int j = 0; j < CPT; j += 2) {
+    const uint32_t w2 = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(o[j] * inv), (__bf16)(o[j + 1] * inv)});
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + obase + j) = w2;
   }
 }
 
@@ -889,8 +917,9 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
       if (e != hipSuccess) return e;
       if (pl.max_splits > 1) {
         const int rows = pl.qpw * a.nh;
-        hipLaunchKernelGGL(attn_combine, dim3((unsigned)(nb * pl.units_per_b), (unsigned)(rows < 64 ? rows : 64)),
-                           dim3(256), 0, s, a, pt, (int)b0, pl, a.c);
+        const dim3 cg((unsigned)(nb * pl.units_per_b), (unsigned)((rows + 3) / 4));
+        if (a.c == 512) hipLaunchKernelGGL(attn_combine<8>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
+        else hipLaunchKernelGGL(attn_combine<2>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
       }
     } else {
       AttnPlan pl = {};
