@@ -135,6 +135,36 @@ def cpu_baseline(inp, rows_n=16, seed=4):
                       "rows (%.1f s); host cores available %d" % (t_comp, rows_n, t_rows, cores)}
 
 
+def fp4_indexer_report(layer, flop, steps, stream, rows_n=256):
+    """Time the FP4-query indexer on the same chunk and measure the recall of
+    its top-k against the bf16-query top-k on rows_n evenly spaced rows."""
+    import torch
+    layer.indexer()
+    layer.topk()
+    torch.cuda.synchronize()
+    ref = layer.idx[0].cpu().numpy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    layer.indexer_fp4q()
+    e0.record(stream)
+    for _ in range(steps):
+        layer.indexer_fp4q()
+    e1.record(stream)
+    layer.topk()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    got = layer.idx[0].cpu().numpy()
+    rows = np.linspace(0, ref.shape[0] - 1, rows_n).astype(np.int64)
+    rec = []
+    for r in rows:
+        a, b = set(ref[r][ref[r] >= 0].tolist()), set(got[r][got[r] >= 0].tolist())
+        if a:
+            rec.append(len(a & b) / len(a))
+    layer.indexer()          # leave the bf16 scores in place
+    torch.cuda.synchronize()
+    return {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "recall_at_k_vs_bf16_query": round(float(np.mean(rec)), 4), "recall_rows": len(rec)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +241,7 @@ def main():
                        "c": cfg["c"], "heads": cfg["nh"], "m": cfg["m"], "m_prime": cfg["mp"], "top_k": cfg["k"],
                        "window": cfg["n_win"], "kv": "fp8_e4m3+bf16_rope", "indexer_keys": "mxfp4"},
             "roofline": roof, "calls": calls}
+    line["fp4_indexer"] = fp4_indexer_report(layer, work["indexer"]["flop"], args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
     print(json.dumps(line), flush=True)

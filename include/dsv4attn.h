@@ -121,6 +121,23 @@ int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
                        const int64_t* q_pos0, float* scores, void* stream);
 
 /*
+ * Index scores with the indexer's QK product in FP4 (digest 模块 F: the
+ * lightning indexer computes its attention in FP4).  Each query head's c_I
+ * values are quantised to MXFP4 exactly as the keys are stored (blocks of 32
+ * along c_I, E8M0 scale 2^(floor(log2 amax) - 2), E2M1 elements rounded to
+ * nearest even, saturating), then
+ *   I[b, t, s] = sum_h wI[b, t, h] * ReLU(Q4[b, t, h, :] . K4[b, s, :])
+ * for visible entries, -inf otherwise, with the products of FP4 values exact
+ * and the sums in fp32.  Same arguments as dsv4_indexer_score with MXFP4 keys:
+ * k_codes [B, S, cI/2] (element 2j in the low nibble of byte j), k_scales
+ * [B, S, cI/32].  cI must be a multiple of 32.
+ */
+int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
+                            const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                            const int64_t* q_pos0, float* scores, void* stream);
+
+/*
  * Top-k selector (digest 模块 B eq 17; blog 第二阶段 Top-k稀疏选择).
  * For each row (b, t): the k visible entries with the largest score; ties go
  * to the lower index; order (score descending, index ascending); fewer than

@@ -16,6 +16,7 @@ ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
     "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
+    "dsv4_indexer_score_fp4q",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
 ]
@@ -44,6 +45,8 @@ _sig("dsv4_csa_compress", _int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _int, _i
 _sig("dsv4_hca_compress", _int, [_vp, _i64, _i64, _int, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _int, _vp])
 _sig("dsv4_indexer_score", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _i64, _int,
                                   _P64, _vp, _vp])
+_sig("dsv4_indexer_score_fp4q", _int, [_vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _int, _i64, _int,
+                                       _P64, _vp, _vp])
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
@@ -131,6 +134,17 @@ def indexer_score(qI, wI, keys, k_layout, m, q_pos0, scores, *, k_scales=None, S
     S = scores.shape[2] if S is None else S
     _check(lib.dsv4_indexer_score(_ptr(qI), _act(qI), _ptr(wI), _ptr(keys), _ptr(k_scales), k_layout,
                                   B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores), _stream(stream)))
+
+
+def indexer_score_fp4q(qI, wI, k_codes, k_scales, m, q_pos0, scores, *, S=None, stream=None):
+    """Index scores of the FP4 indexer: the query heads are rounded to MXFP4 and
+    multiplied with the MXFP4 keys.  qI [B, nq, hI, cI]; wI [B, nq, hI];
+    k_codes [B, S, cI/2]; k_scales [B, S, cI/32]; scores [B, nq, S]."""
+    B, nq, hI, cI = qI.shape
+    S = scores.shape[2] if S is None else S
+    _check(lib.dsv4_indexer_score_fp4q(_ptr(qI), _act(qI), _ptr(wI), _ptr(k_codes), _ptr(k_scales),
+                                       B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores),
+                                       _stream(stream)))
 
 
 def topk_workspace_size(B, nq, S, k):

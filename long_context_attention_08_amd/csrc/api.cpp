@@ -163,7 +163,28 @@ int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
   if (r) return r;
   if (!wI) return fail(DSV4_ERR_INVALID_ARG, "%s: wI is NULL", fn);
   if (k_layout == DSV4_ROW_MXFP4 && !k_scales) return fail(DSV4_ERR_INVALID_ARG, "%s: k_scales is NULL", fn);
-  dsv4::IndexerArgs a{qI, q_dtype, wI, keys, k_scales, k_layout, B, nq, hI, cI, S, m, scores};
+  dsv4::IndexerArgs a{qI, q_dtype, wI, keys, k_scales, k_layout, B, nq, hI, cI, S, m, scores, 0};
+  return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
+                            const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                            const int64_t* q_pos0, float* scores, void* stream) {
+  const char* fn = "dsv4_indexer_score_fp4q";
+  if (B < 0 || nq < 0 || S < 0 || hI <= 0 || cI <= 0 || m <= 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
+  if (cI % 32) return fail(DSV4_ERR_UNSUPPORTED, "%s: cI %% 32 != 0", fn);
+  if (B == 0 || nq == 0 || S == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  for (int64_t b = 0; b < B; ++b)
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+  int r = check_ptrs16(fn, {{qI, "qI"}, {k_codes, "k_codes"}, {scores, "scores"}});
+  if (r) return r;
+  if (!wI) return fail(DSV4_ERR_INVALID_ARG, "%s: wI is NULL", fn);
+  if (!k_scales) return fail(DSV4_ERR_INVALID_ARG, "%s: k_scales is NULL", fn);
+  dsv4::IndexerArgs a{qI, q_dtype, wI, k_codes, k_scales, DSV4_ROW_MXFP4, B, nq, hI, cI, S, m, scores, 1};
   return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

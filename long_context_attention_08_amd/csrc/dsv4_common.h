@@ -92,11 +92,14 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
   return (nib & 8u) ? -v : v;
 }
 
-// |y| -> E2M1 magnitude code, round to nearest even, saturating at 6.
+// y -> E2M1 code (sign bit 3), round to nearest even, saturating at 6.  The
+// magnitude code counts the rounding boundaries |y| lies beyond; a boundary
+// that is a tie belongs to the even code below or above it (branch-free).
 __device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
-  float a = fabsf(y);
-  uint32_t m = a > 5.0f ? 7u : a >= 3.5f ? 6u : a > 2.5f ? 5u : a >= 1.75f ? 4u
-             : a > 1.25f ? 3u : a >= 0.75f ? 2u : a > 0.25f ? 1u : 0u;
+  const float a = fabsf(y);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
   return m | ((__float_as_uint(y) >> 28) & 8u);
 }
 

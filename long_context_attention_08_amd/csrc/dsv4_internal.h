@@ -37,6 +37,7 @@ struct IndexerArgs {
   int64_t S;
   int m;
   float* scores;        // [B, nq, S]
+  int q4;               // 1: the queries are quantised to MXFP4 (keys MXFP4 too)
 };
 
 // Per-batch absolute positions travel to the kernels by value: a launch covers

@@ -51,20 +51,81 @@ __global__ void indexer_generic(IndexerArgs a, PosTable pt, int b0, int nb) {
   *out = score;
 }
 
+// value of element j of a query head quantised to MXFP4 (its 32-element block
+// scaled by 2^(floor(log2 amax) - 2), elements rounded to E2M1)
+__device__ __forceinline__ float q4_elem(const IndexerArgs& a, int64_t qbase, int j) {
+  const int j0 = j & ~31;
+  float amax = 0.f;
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_act(a.qI, a.q_dtype, qbase + j0 + i)));
+  const uint32_t E = mx_scale_code(amax);
+  const float inv = __uint_as_float((254u - E) << 23);            // 2^(127 - E)
+  return e2m1_to_f32(f32_to_e2m1(load_act(a.qI, a.q_dtype, qbase + j) * inv)) * e8m0_to_f32(E);
+}
+
+// generic path of the FP4-query scores: one thread per (b, t, s)
+__global__ void indexer_generic_q4(IndexerArgs a, PosTable pt, int b0, int nb) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_b = a.nq * a.S;
+  if (gid >= per_b * nb) return;
+  const int64_t bl = gid / per_b;
+  const int64_t b = b0 + bl;
+  const int64_t t = (gid % per_b) / a.S;
+  const int64_t s = gid % a.S;
+  const int64_t p = pt.q_pos0[bl] + t;
+  float* out = a.scores + (b * a.nq + t) * a.S + s;
+  if (s >= visible_count(p, a.m, a.S)) { *out = -INFINITY; return; }
+  float score = 0.0f;
+  for (int h = 0; h < a.hI; ++h) {
+    const int64_t qbase = ((b * a.nq + t) * a.hI + h) * a.cI;
+    float dot = 0.0f;
+    for (int j = 0; j < a.cI; ++j) dot = fmaf(q4_elem(a, qbase, j), key_elem(a, b, s, j), dot);
+    score = fmaf(a.wI[(b * a.nq + t) * a.hI + h], fmaxf(dot, 0.0f), score);
+  }
+  *out = score;
+}
+
+// 32 values -> one MXFP4 block: 16 bytes of E2M1 codes (element 2j in the low
+// nibble of byte j) and the E8M0 scale code
+__device__ __forceinline__ void mxfp4_block(const float (&x)[32], u32x4& codes, uint32_t& E) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  E = mx_scale_code(amax);
+  const float inv = __uint_as_float((254u - E) << 23);            // 2^(127 - E)
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= f32_to_e2m1(x[8 * d + e] * inv) << (4 * e);
+    codes[d] = w;
+  }
+}
+
 // ------------------------------------------------------------------ MFMA path
 constexpr int KT = 256;   // keys per LDS tile
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // WQ waves split the queries, 4/WQ waves split the 8 n-tiles of a key tile;
-// each wave holds QPW queries.
-template <int CI, int KL, int WQ, int QPW>
+// each wave holds QPW queries.  Q4: the queries are quantised to MXFP4 in
+// registers and the MXFP4 key tile stays in its stored form in LDS; each
+// 64-channel k-step is one v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands
+// with their E8M0 block scales (lane l of either operand holds row/column
+// l % 32, channels 32 (l / 32) .. + 32, as 16 code bytes plus one scale).
+template <int CI, int KL, int WQ, int QPW, bool Q4>
 __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable pt, int b0,
                                                         int qblocks, int tiles_per_split) {
   constexpr int WK = 4 / WQ;          // waves along the key tile
   constexpr int QB = WQ * QPW;        // queries per block
   constexpr int NTW = 8 / WK;         // 32-key n-tiles per wave
-  constexpr int KS = CI / 16;         // MFMA k-steps
+  constexpr int KS = CI / 16;         // bf16 MFMA k-steps
+  constexpr int K4 = CI / 64;         // scaled-MFMA k-steps (Q4)
   constexpr int LDK = CI + 8;
-  __shared__ uint16_t Ks[KT * LDK];
+  constexpr int CB = CI / 2, NBS = CI / 32;              // MXFP4 code / scale bytes per key
+  constexpr int LDC = CB + (CI >= 128 ? 16 : 0);         // LDS code row stride (bytes)
+  static_assert(!Q4 || (KL == ROW_MXFP4 && CI % 64 == 0), "FP4 queries need MXFP4 keys, cI % 64 == 0");
+  __shared__ uint16_t Ks[Q4 ? 8 : KT * LDK];
+  __shared__ __align__(16) uint8_t Kc[Q4 ? KT * LDC : 16];
+  __shared__ uint8_t Kscl[Q4 ? KT * NBS : 4];
 
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int wq = wv / WK, wk = wv % WK;
@@ -78,7 +139,9 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   if (tile_lo >= tile_hi) return;
 
   // query fragments (B operand is the key; A operand is the 32 heads x cI)
-  bf16x8 qf[QPW][KS];
+  bf16x8 qf[QPW][Q4 ? 1 : KS];
+  u32x4 q4c[QPW][Q4 ? K4 : 1];
+  uint32_t q4s[QPW][Q4 ? K4 : 1];
   float wh[QPW][16];
   int64_t nvis[QPW];
   bool qvalid[QPW];
@@ -99,9 +162,26 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     nvis[qi] = qvalid[qi] ? visible_count(pt.q_pos0[bl] + t, a.m, S) : 0;
     orow[qi] = a.scores + (b * a.nq + tt) * S;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.qI) + ((b * a.nq + tt) * 32 + (l & 31)) * CI;
+    if constexpr (Q4) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      qf[qi][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * (l >> 5)));
+      for (int k4 = 0; k4 < K4; ++k4) {
+        float x[32];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * k4 + 32 * (l >> 5) + 8 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * v + 2 * e] = __uint_as_float(w[e] << 16);
+            x[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        }
+        mxfp4_block(x, q4c[qi][k4], q4s[qi][k4]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        qf[qi][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * (l >> 5)));
+    }
     const float* wrow = a.wI + (b * a.nq + tt) * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) wh[qi][r] = wrow[(r >> 2) * 8 + 4 * (l >> 5) + (r & 3)];
@@ -138,8 +218,21 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
       }
       continue;
     }
-    // ---- decode the key tile into LDS (bf16)
-    if (KL == ROW_MXFP4) {
+    // ---- the key tile into LDS: stored MXFP4 bytes (Q4), else decoded to bf16
+    if constexpr (Q4) {
+      const int64_t s = s0 + threadIdx.x;
+      const bool in = s < S;
+      const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + (b * S + (in ? s : 0)) * CB;
+      const uint8_t* sr = a.k_scales + (b * S + (in ? s : 0)) * NBS;
+#pragma unroll
+      for (int i = 0; i < CB / 16; ++i) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(cr + 16 * i);
+        if (!in) v = (u32x4){0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(Kc + threadIdx.x * LDC + 16 * i) = v;
+      }
+#pragma unroll
+      for (int i = 0; i < NBS; ++i) Kscl[threadIdx.x * NBS + i] = in ? sr[i] : (uint8_t)0;
+    } else if (KL == ROW_MXFP4) {
       constexpr int CB = CI / 2;            // code bytes per key
       constexpr int NB = CI / 32;           // scale bytes per key
       const int64_t s = s0 + threadIdx.x;
@@ -180,10 +273,21 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int ntile = wk * NTW + nt;
-      bf16x8 kf[KS];
+      bf16x8 kf[Q4 ? 1 : KS];
+      i32x8 k4c[Q4 ? K4 : 1];
+      int k4s[Q4 ? K4 : 1];
+      if constexpr (Q4) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (ntile * 32 + (l & 31)) * LDK + 16 * kk + 8 * (l >> 5)));
+        for (int k4 = 0; k4 < K4; ++k4) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(Kc + (ntile * 32 + (l & 31)) * LDC + 32 * k4 + 16 * (l >> 5));
+          k4c[k4] = (i32x8){(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+          k4s[k4] = Kscl[(ntile * 32 + (l & 31)) * NBS + 2 * k4 + (l >> 5)];
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (ntile * 32 + (l & 31)) * LDK + 16 * kk + 8 * (l >> 5)));
+      }
       const int64_t s = s0 + ntile * 32 + (l & 31);
       // lane half G holds heads 8 (r/4) + 4 G + r%4 of key s: partial sums
       float part[QPW];
@@ -192,8 +296,18 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        if constexpr (Q4) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][kk], kf[kk], acc, 0, 0, 0);
+          for (int k4 = 0; k4 < K4; ++k4) {
+            const u32x4 qc = q4c[qi][k4];
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                (i32x8){(int)qc[0], (int)qc[1], (int)qc[2], (int)qc[3], 0, 0, 0, 0}, k4c[k4], acc,
+                4, 4, 0, (int)q4s[qi][k4], 0, k4s[k4]);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][kk], kf[kk], acc, 0, 0, 0);
+        }
         // (this file is built with IEEE mode off: the max is one instruction)
         float sc = 0.0f;
 #pragma unroll
@@ -218,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   }
 }
 
-template <int CI, int KL>
+template <int CI, int KL, bool Q4 = false>
 static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
   const int64_t ntiles = (a.S + KT - 1) / KT;
   if (a.nq >= 16) {
@@ -230,7 +344,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
     if (splits < 1) splits = 1;
     const int tps = (int)((ntiles + splits - 1) / splits);
     splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, Q4>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
                        a, pt, b0, qblocks, tps);
   } else {
     constexpr int WQ = 1, QPW = 1;
@@ -241,7 +355,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
     if (splits < 1) splits = 1;
     const int tps = (int)((ntiles + splits - 1) / splits);
     splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, Q4>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
                        a, pt, b0, qblocks, tps);
   }
 }
@@ -258,7 +372,15 @@ hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream
     const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
-    if (indexer_mfma_ok(a)) {
+    if (a.q4) {
+      if (a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 64 || a.cI == 128) && a.S < ((int64_t)1 << 31)) {
+        if (a.cI == 64) launch_mfma_variant<64, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
+        else launch_mfma_variant<128, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
+      } else {
+        const int64_t total = a.nq * a.S * nb;
+        hipLaunchKernelGGL(indexer_generic_q4, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pt, (int)b0, nb);
+      }
+    } else if (indexer_mfma_ok(a)) {
       const bool mx = a.k_layout == ROW_MXFP4;
       switch (a.cI) {
         case 32: mx ? launch_mfma_variant<32, ROW_MXFP4>(a, pt, (int)b0, nb, s) : launch_mfma_variant<32, ROW_BF16>(a, pt, (int)b0, nb, s); break;

@@ -5,9 +5,9 @@ benchmark's CPU-baseline leg, never by the library or its binding.
 """
 from . import codecs
 from .dsv4 import (softmax_pool, csa_compress, csa_pool_weights, hca_compress,
-                   visible_count, indexer_score, topk_select, core_attention,
+                   visible_count, indexer_score, indexer_score_fp4q, topk_select, core_attention,
                    window_rows, sparse_mqa, hca_dense)
 
 __all__ = ["codecs", "softmax_pool", "csa_compress", "csa_pool_weights", "hca_compress",
-           "visible_count", "indexer_score", "topk_select", "core_attention",
+           "visible_count", "indexer_score", "indexer_score_fp4q", "topk_select", "core_attention",
            "window_rows", "sparse_mqa", "hca_dense"]

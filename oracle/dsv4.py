@@ -36,9 +36,14 @@ reason, in the design notes of the repository):
   R13 a selected entry is both key and value (K = V);
   R14 logits are scale * q.k with the scale passed in (1/sqrt(c) by default);
   R15 the sink adds exp(z'_h) to the softmax denominator only;
-  R16 an empty key set gives a zero output.
+  R16 an empty key set gives a zero output;
+  R19b the FP4 indexer rounds each query head q^I[t, h] to MXFP4 (blocks of
+      32 consecutive c_I dims, the key encoder) before eq 16; the keys are the
+      stored MXFP4 rows, decoded.
 """
 import numpy as np
+
+from . import codecs as _codecs
 
 
 # ---------------------------------------------------------------------------
@@ -162,6 +167,16 @@ def indexer_score(qI, wI, KI, m, q_pos):
         dots = qI[t] @ KI[:nv].T              # [hI, nv]
         out[t, :nv] = wI[t] @ np.maximum(dots, 0.0)
     return out
+
+
+def indexer_score_fp4q(qI, wI, KI, m, q_pos):
+    """Index scores of the FP4 lightning indexer (digest 模块 F: the indexer's
+    attention runs in FP4): eq 16 over the query heads rounded to MXFP4 along
+    c_I (R19b).  qI [nq, hI, cI] with cI a multiple of 32; KI [S, cI] are the
+    decoded MXFP4 keys."""
+    qI = np.asarray(qI, dtype=np.float64)
+    codes, scales = _codecs.mxfp4_encode(qI)
+    return indexer_score(_codecs.mxfp4_decode(codes, scales), wI, KI, m, q_pos)
 
 
 def topk_select(I, m, q_pos, k):

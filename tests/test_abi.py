@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 12
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -85,6 +85,15 @@ def test_indexer_validation(L):
     assert f(FAKE, 1, FAKE, FAKE, None, 1, 1, 4, 32, 64, 100, 4, pos(-5), FAKE, None) == 1   # negative pos
     assert f(FAKE, 1, FAKE, FAKE, None, 1, 1, 4, 32, 64, 100, 0, pos(0), FAKE, None) == 1    # m = 0
     assert f(FAKE, 1, FAKE, FAKE, None, 1, 0, 4, 32, 64, 100, 4, None, FAKE, None) == 0      # B = 0 no-op
+
+
+def test_indexer_fp4q_validation(L):
+    f = L.lib.dsv4_indexer_score_fp4q
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 1, 4, 32, 48, 100, 4, pos(0), FAKE, None) == 2       # cI % 32
+    assert f(FAKE, 1, FAKE, FAKE, None, 1, 4, 32, 64, 100, 4, pos(0), FAKE, None) == 1       # no scales
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 1, 4, 32, 64, 100, 4, pos(-1), FAKE, None) == 1      # negative pos
+    assert f(FAKE, 7, FAKE, FAKE, FAKE, 1, 4, 32, 64, 100, 4, pos(0), FAKE, None) == 2       # q dtype
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 0, 4, 32, 64, 100, 4, None, FAKE, None) == 0         # B = 0 no-op
 
 
 def test_topk_validation(L):

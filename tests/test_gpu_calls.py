@@ -174,6 +174,62 @@ def test_indexer_small_integers_bit_exact(L):
         assert np.array_equal(host(scores)[0], ref.astype(np.float32))
 
 
+IDX4_CASES = [
+    # (q dtype, B, nq, hI, cI, S, m, pos0 list)
+    ("bf16", 2, 40, 32, 64, 1000, 4, [3, 3900]),      # scaled-MFMA prefill, causal boundary, ragged tile
+    ("bf16", 3, 1, 32, 64, 5000, 4, [19999, 10000, 3]),   # scaled-MFMA decode mode
+    ("bf16", 1, 20, 32, 128, 300, 4, [1199]),         # scaled-MFMA, cI = 128
+    ("f32", 2, 37, 4, 32, 70, 4, [0, 200]),           # generic (f32 query, cI = 32)
+    ("bf16", 1, 9, 16, 64, 50, 1, [30]),              # generic (hI = 16), m = 1
+]
+
+
+@pytest.mark.parametrize("case", IDX4_CASES, ids=[str(i) for i in range(len(IDX4_CASES))])
+def test_indexer_score_fp4q(L, case):
+    """FP4 indexer: the library rounds the query to MXFP4 itself; the oracle
+    rounds the same stored query; the rounding decisions are exact on both
+    sides (power-of-two scaling of the same bf16/f32 values), so only the
+    summation order differs."""
+    import torch
+    qd, B, nq, hI, cI, S, m, pos = case
+    seed = 700 + S + nq
+    qI = act_arr(seed, "qI", (B, nq, hI, cI), 0.5, qd)
+    wI = G.normal(seed, "wI", (B, nq, hI))
+    kx = G.normal(seed, "cache_ki", (B, S, cI))
+    codes, ksc = G.store(kx, ROW_MXFP4)
+    scores = torch.full((B, nq, S), float("nan"), dtype=torch.float32, device="cuda")
+    L.indexer_score_fp4q(dev(qI), dev(wI), dev(codes), dev(ksc), m, pos, scores)
+    got = host(scores)
+    for b in range(B):
+        kf = stored_rows_f64(codes[b], ROW_MXFP4, cI, ksc[b])
+        ref = O.indexer_score_fp4q(decode_act(qI[b]), wI[b].astype(np.float64), kf, m, pos[b] + np.arange(nq))
+        vis = np.isfinite(ref)
+        assert np.array_equal(np.isneginf(got[b]), ~vis), "visibility mask"
+        if vis.any():
+            scale = np.abs(ref[vis]).max()
+            err = np.abs(got[b][vis] - ref[vis]).max() / scale
+            assert err < 2e-5, "normalised score error %.3g" % err
+
+
+def test_indexer_fp4q_small_integers_bit_exact(L):
+    """Queries on the E2M1 grid (times 2) round to themselves, and every product
+    and partial sum is a multiple of 1/2 below 2^24: any accumulation order
+    gives the oracle's value bit for bit."""
+    import torch
+    rng = np.random.default_rng(8)
+    B, nq, hI, cI, S, m = 1, 48, 32, 128, 700, 4
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6], dtype=np.float32)
+    q = vals[rng.integers(0, len(vals), (B, nq, hI, cI))] * 2
+    kx = vals[rng.integers(0, len(vals), (B, S, cI))]
+    w = rng.choice(np.array([-2, -1, 1, 2], dtype=np.float32), (B, nq, hI))
+    codes, ksc = G.store(kx, ROW_MXFP4)
+    kf = stored_rows_f64(codes[0], ROW_MXFP4, cI, ksc[0])
+    scores = torch.empty((B, nq, S), dtype=torch.float32, device="cuda")
+    L.indexer_score_fp4q(dev(G.to_bf16(q)), dev(w), dev(codes), dev(ksc), m, [2000], scores)
+    ref = O.indexer_score_fp4q(q[0].astype(np.float64), w[0].astype(np.float64), kf, m, 2000 + np.arange(nq))
+    assert np.array_equal(host(scores)[0], ref.astype(np.float32))
+
+
 # ====================================================================== top-k
 
 TOPK_CASES = [

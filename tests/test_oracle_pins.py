@@ -262,6 +262,63 @@ def test_indexer_visibility_boundary(p, nvis):
     assert np.isneginf(I[0, nvis:]).all()
 
 
+# ----------------------------------------------------------------------
+# FP4 lightning indexer (digest 模块 F; reading R19b: q^I rounded to MXFP4
+# per head in blocks of 32 along c_I, then eq 16)
+# ----------------------------------------------------------------------
+
+def test_indexer_fp4q_hand_example():
+    """Scores worked by hand on basis keys.  Head 0, block 0: amax 5.5 gives
+    scale 2^0, so 5.5 -> 6 (beyond the 5 boundary), 1.3 -> 1.5, 0.2 -> 0,
+    -2.75 -> -3.  Head 0, block 1: amax 0.1 gives scale 2^-6, 0.1 -> 6 * 2^-6
+    (saturated), 0.03 -> 2 * 2^-6.  Head 1, block 0: amax 0.75 gives scale 2^-3;
+    the ties 0.3125 = 2.5 * 2^-3 and 0.15625 = 1.25 * 2^-3 go to the even codes
+    2 and 1."""
+    q = np.zeros((1, 2, 64))
+    q[0, 0, [0, 1, 2, 3, 32, 33]] = [5.5, 1.3, 0.2, -2.75, 0.1, 0.03]
+    q[0, 1, [0, 1, 2]] = [0.75, 0.3125, 0.15625]
+    w = np.array([[1.0, 10.0]])
+    I = O.indexer_score_fp4q(q, w, np.eye(64), 1, [63])
+    want = np.zeros(64)
+    want[[0, 1, 2, 32, 33]] = [6 + 10 * 0.75, 1.5 + 10 * 0.25, 10 * 0.125, 6 * 2.0**-6, 2 * 2.0**-6]
+    assert np.array_equal(I[0], want)
+    # the unrounded query scores differently (13 at key 0), so rounding is applied
+    assert O.indexer_score(q, w, np.eye(64), 1, [63])[0, 0] == 13.0
+
+
+def test_indexer_fp4q_grid_query_equals_plain_scores():
+    """A query already on the MXFP4 grid (each 32-block holds a +-6 element, so
+    its scale is its own) rounds to itself: the FP4 scores equal eq 16."""
+    rng = np.random.default_rng(90)
+    nq, hI, cI, S = 3, 4, 64, 40
+    codes = rng.integers(0, 256, (nq, hI, cI // 2)).astype(np.uint8)
+    codes[..., 0] = (codes[..., 0] & 0xF0) | 0x7          # element 0 of block 0 = +6
+    codes[..., 16] = (codes[..., 16] & 0xF0) | 0xF        # element 0 of block 1 = -6
+    scales = rng.integers(118, 136, (nq, hI, cI // 32)).astype(np.uint8)
+    q = O.codecs.mxfp4_decode(codes, scales)
+    K = rnd(91, S, cI)
+    w = rnd(92, nq, hI)
+    pos = [39, 20, 5]
+    assert np.array_equal(O.indexer_score_fp4q(q, w, K, 1, pos), O.indexer_score(q, w, K, 1, pos))
+
+
+def test_indexer_fp4q_blocks_are_per_head():
+    """Scaling one head by 2^20 (and its weight by 2^-20) leaves every score
+    unchanged: MXFP4 rounding is equivariant under powers of two and the blocks
+    never span heads; a scale shared across heads would flush head 0 to zero."""
+    q = rnd(93, 2, 3, 64)
+    w = rnd(94, 2, 3)
+    K = rnd(95, 30, 64)
+    pos = [29, 12]
+    base = O.indexer_score_fp4q(q, w, K, 1, pos)
+    q2, w2 = q.copy(), w.copy()
+    q2[:, 1] *= 2.0**20
+    w2[:, 1] *= 2.0**-20
+    assert np.array_equal(O.indexer_score_fp4q(q2, w2, K, 1, pos), base)
+    assert np.array_equal(O.indexer_score_fp4q(q * 2.0**-7, w, K, 1, pos)[np.isfinite(base)],
+                          base[np.isfinite(base)] * 2.0**-7)
+
+
 # ======================================================================
 # Top-k selector (digest 模块 B eq 17)
 # ======================================================================
