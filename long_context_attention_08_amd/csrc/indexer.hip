@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   float wh[QPW][16];
   int64_t nvis[QPW];
   bool qvalid[QPW];
-  float* orow[QPW];                  // output row of each query (clamped for invalid ones)
   int64_t nvis_max = 0;
   for (int qi = 0; qi < QB; ++qi) {           // block-wide maximum (uniform)
     const int64_t t = t0 + qi;
@@ -160,7 +159,6 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     qvalid[qi] = t < a.nq;
     const int64_t tt = qvalid[qi] ? t : a.nq - 1;
     nvis[qi] = qvalid[qi] ? visible_count(pt.q_pos0[bl] + t, a.m, S) : 0;
-    orow[qi] = a.scores + (b * a.nq + tt) * S;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.qI) + ((b * a.nq + tt) * 32 + (l & 31)) * CI;
     if constexpr (Q4) {
 #pragma unroll
@@ -190,14 +188,25 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   // query pairs: lane half G finishes query 2 p + G of pair p (one query per
   // pair when QPW = 1, upper half idle); per-lane row, visible count, validity
   constexpr int NPAIR = QPW > 1 ? QPW / 2 : 1;
-  float* prow[NPAIR];
+  // Scores go out through a buffer resource over the block's valid query
+  // rows: a lane whose key is past S, or that finishes no query, gets an
+  // offset beyond the range and the hardware drops its store, so the store
+  // needs no branch and the unrolled n-tile loop stays one scheduling region.
+  const int64_t nrows = a.nq - t0 < QB ? a.nq - t0 : QB;
+  const uint64_t sbase = reinterpret_cast<uint64_t>(a.scores + (b * a.nq + t0) * S);
+  const uint32_t sb_lo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
+  const uint32_t sb_hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<float*>(((uint64_t)sb_hi << 32) | sb_lo), (short)0,
+      __builtin_amdgcn_readfirstlane((int)(nrows * S * 4)), 0x00020000);
+  uint32_t prow[NPAIR];              // byte offset of the lane's output row
   int pvis[NPAIR];
   bool pok[NPAIR];
   const bool hi = l >= 32;
 #pragma unroll
   for (int pp = 0; pp < NPAIR; ++pp) {
     const int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
-    prow[pp] = hi ? orow[qb] : orow[qa];
+    prow[pp] = (uint32_t)((wq * QPW + (hi ? qb : qa)) * S) * 4u;
     pvis[pp] = (int)(hi ? nvis[qb] : nvis[qa]);
     pok[pp] = (hi ? qvalid[qb] : qvalid[qa]) && (QPW > 1 || !hi);
   }
@@ -322,7 +331,9 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         constexpr int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
         const float keep = hi ? part[qb] : part[qa];
         const float total = keep + __shfl_xor(hi ? part[qa] : part[qb], 32);
-        if (pok[pp] && s32 < S32) prow[pp][s32] = s32 < pvis[pp] ? total : -INFINITY;
+        const uint32_t off = pok[pp] && s32 < S32 ? prow[pp] + 4u * (uint32_t)s32 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32 < pvis[pp] ? total : -INFINITY), srsrc,
+                                              (int)off, 0, 0);
       };
       finish_pair(std::integral_constant<int, 0>());
       if constexpr (NPAIR > 1) finish_pair(std::integral_constant<int, 1>());
@@ -362,7 +373,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
 
 static bool indexer_mfma_ok(const IndexerArgs& a) {
   return a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 32 || a.cI == 64 || a.cI == 128) &&
-         a.S < ((int64_t)1 << 31) &&                 // key positions fit 32-bit store offsets
+         a.S < ((int64_t)1 << 25) &&                 // 16 score rows fit a buffer range below 2^31 bytes
          (a.k_layout == ROW_BF16 || a.k_layout == ROW_MXFP4);
 }
 
@@ -373,7 +384,7 @@ hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
     if (a.q4) {
-      if (a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 64 || a.cI == 128) && a.S < ((int64_t)1 << 31)) {
+      if (a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 64 || a.cI == 128) && a.S < ((int64_t)1 << 25)) {
         if (a.cI == 64) launch_mfma_variant<64, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
         else launch_mfma_variant<128, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
       } else {
