@@ -14,6 +14,8 @@
 // exceeds it by 2^8 (exact after the final normalisation; bf16 P stays well
 // inside range).  Short key sets with few queries are split across blocks and
 // merged in a fixed order.
+#include <type_traits>
+
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
@@ -754,6 +756,339 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   }
 }
 
+// ------------------------------------------------------------------ FP8 rows at c = 512
+// Two blocks per CU.  The decoded bf16 key tiles are gone: the MFMA operands
+// come straight from the raw stage (E4M3 bytes converted in registers, the 64
+// bf16 RoPE channels as they are), which halves the LDS bytes per MFMA and
+// leaves LDS for three stages of copies in flight.
+//   * wave (rg, ch) holds Q^T and O^T of 32 rows x 256 channels, as above;
+//   * S^T over the wave's channel half: A = K rows (ds_read_b64 of 8 E4M3
+//     bytes per lane, or ds_read_b128 of 8 bf16), B = Q^T;
+//   * both waves of a pair write their whole partial S^T and read the other's,
+//     so each holds the full scores of its 32 rows and computes the softmax of
+//     all 32 keys itself (no exchange of maxima or P);
+//   * O^T += V^T P^T with V^T from ds_read_b64_tr_b8: in a 16-lane group, lane
+//     s reads 8 bytes at key k0 + s/2, channels c0 + 8 (s % 2); lane i then
+//     holds channel c0 + i of keys k0 .. k0 + 7.  The stage keeps key j of a
+//     tile at slot kperm(j) (bits 2 and 3 of j swapped), so those 8 slots are
+//     the keys 16 s + 4 G + {0..3}, 16 s + 8 + 4 G + {0..3} that the P^T
+//     fragment of lane half G holds (registers 8 s .. 8 s + 7 of S^T);
+//   * per tile: [copies of tile it landed] barrier, copies of tile it+2, S^T,
+//     partial out, barrier, softmax, PV.
+constexpr int F8_NSTG = 3;
+__device__ __forceinline__ int kperm(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
+
+template <int NRG>
+__global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
+  constexpr int C = 512, CS = 2;
+  using Cf = AttnCfg<C, ROW_FP8, CS, NRG>;
+  constexpr int KQ = Cf::KQ, MO = Cf::MO, RB = Cf::RB, NF8 = Cf::NF8;   // 16, 8, 576, 28
+  static_assert(KQ == 16 && MO == 8 && NF8 == 28, "c = 512, FP8 + 64 bf16 RoPE dims");
+  __shared__ __align__(16) uint8_t s_stage[F8_NSTG * Cf::STAGE];
+  __shared__ __align__(16) float s_x[Cf::NW * 16 * 64];            // [wave][r/4][lane][4]
+  __shared__ uint32_t s_vmask[F8_NSTG][8];
+  __shared__ int s_nvisq[8];
+  __shared__ int s_sidx[SIDX_CAP];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
+  const int rg = wv / CS, ch = wv % CS;
+  const int64_t bl = blockIdx.x / pl.units_per_b, u = blockIdx.x % pl.units_per_b;
+  const int64_t b = b0 + bl;
+  const int64_t p0 = pt.q_pos0[bl], wpos0 = pt.win_pos0[bl];
+  const UnitInfo ui = unit_info(a, pl, p0, u);
+  const int64_t nsplit = pl.max_splits == 1 ? 1 : (ui.total + pl.chunk - 1) / pl.chunk;
+  const int split = blockIdx.y;
+  if (split > 0 && split >= nsplit) return;
+  const int slot_lo = split * pl.chunk;
+  const int slot_hi = (int)(pl.max_splits == 1 ? ui.total : (slot_lo + pl.chunk < ui.total ? slot_lo + pl.chunk : ui.total));
+  const int ncomp = (int)ui.ncomp;
+  const uint8_t* comp_base = reinterpret_cast<const uint8_t*>(a.kv_comp) + b * a.S * (int64_t)RB;
+  const uint8_t* win_base = reinterpret_cast<const uint8_t*>(a.kv_win) + (b * a.W + (ui.wlo - wpos0)) * (int64_t)RB;
+  static_assert(RB <= (int)sizeof(g_zero_row), "zero row shorter than a stored row");
+  const uint8_t* dummy = g_zero_row;
+  const int nq_blk = (int)(ui.tl - ui.t0 + 1);
+  const int pfirst = (int)(p0 + ui.t0);
+  const int ntiles = slot_hi > slot_lo ? (slot_hi - slot_lo + TS - 1) / TS : 0;
+
+  if (threadIdx.x < 8) s_nvisq[threadIdx.x] = pl.dense ? (int)visible_count(pfirst + threadIdx.x, a.ratio, a.S) : (int)a.S;
+  int bad_idx = 0;
+  if (a.idx) {
+    const int32_t* irow = a.idx + (b * a.nq + ui.t0) * a.k;
+    const int n_i = (ncomp < slot_hi ? ncomp : slot_hi) - slot_lo;
+    for (int i = threadIdx.x; i < n_i; i += Cf::NT) {
+      const int e = irow[slot_lo + i];
+      s_sidx[i] = e;
+      bad_idx |= (e < 0 || e >= a.S) ? 1 : 0;
+    }
+  }
+  const bool idx_ok = !__syncthreads_or(bad_idx);
+  const int plast = (int)(p0 + ui.tl);
+  const int nvis_first = pl.dense ? (int)visible_count(pfirst, a.ratio, a.S) : (int)a.S;
+
+  const int row = 32 * rg + col;
+  const int qloc = row / a.nh;
+  const int h = row % a.nh;
+  const int64_t t = ui.t0 + qloc;
+  const bool qvalid = t <= ui.tl;
+  const int64_t tq = qvalid ? t : ui.tl;
+
+  bf16x8 qf[KQ];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C + ch * 256;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * G));
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile copies are counted from here on
+  }
+  f32x16 acc[MO];
+#pragma unroll
+  for (int i = 0; i < MO; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl = pl.scale_log2;
+
+  auto slot_src = [&](int s, int* pos, bool* win) -> const uint8_t* {
+    if (s < ncomp) {
+      *win = false;
+      const int e = a.idx ? s_sidx[s - slot_lo] : s;
+      *pos = e;
+      if (e < 0 || e >= a.S) return nullptr;
+      return comp_base + (int64_t)e * RB;
+    }
+    *win = true;
+    *pos = (int)ui.wlo + (s - ncomp);
+    return win_base + (int64_t)(s - ncomp) * RB;
+  };
+  // copies of tile `it`: lane l serves stage slot l % 32, which holds key kperm(l % 32)
+  auto issue = [&](int it, uint8_t* stg) {
+    const int slot = slot_lo + it * TS + kperm(l & 31);
+    int pos;
+    bool win;
+    const uint8_t* rowp = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
+    const uint8_t* base = (rowp ? rowp : dummy) + 16 * G + 32 * wv;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + wv * 1024));
+    DmaCopies<0, (Cf::NDMA + Cf::NW - 1) / Cf::NW, Cf::NW, Cf::NDMA>::run(base, lds0, wv);
+  };
+  const int my_dma = Cf::NDMA / Cf::NW + (wv < Cf::NDMA % Cf::NW ? 1 : 0);
+  auto wait_copies = [&](int n) {
+    switch (n) {
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+      case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+      case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+  };
+  auto tile_full = [&](int it) -> bool {
+    const int s0 = slot_lo + it * TS, s1 = s0 + TS;
+    if (s1 > slot_hi) return false;
+    if (s0 < ncomp) {
+      if (a.idx ? !idx_ok : (s1 < ncomp ? s1 : ncomp) > nvis_first) return false;
+    }
+    if (s1 > ncomp) {
+      const int lo = (int)ui.wlo + ((s0 > ncomp ? s0 : ncomp) - ncomp), hi = (int)ui.wlo + (s1 - 1 - ncomp);
+      if (hi > pfirst || lo < plast - a.n_win + 1) return false;
+    }
+    return true;
+  };
+  // per-query visibility bits of a tile that is not full, in key order (wave 0)
+  auto masks = [&](int it, int buf) {
+    if (wv != 0 || tile_full(it)) return;
+    const int s0 = slot_lo + it * TS;
+    uint32_t vbits = 0;
+    const int slot = s0 + l;
+    if (l < TS && slot < slot_hi) {
+      int pos;
+      bool win;
+      if (slot_src(slot, &pos, &win)) {
+        for (int q = 0; q < nq_blk; ++q) {
+          const int pq = pfirst + q;
+          const bool ok = win ? (pos <= pq && pos >= pq - a.n_win + 1) : (pos < s_nvisq[q]);
+          vbits |= (ok ? 1u : 0u) << q;
+        }
+      }
+    }
+    for (int q = 0; q < nq_blk; ++q) {
+      const uint32_t bal = (uint32_t)__ballot((vbits >> q) & 1u);
+      if (l == 0) s_vmask[buf][q] = bal;
+    }
+  };
+
+  auto e4m3x8 = [](u32x2 w) -> bf16x8 {
+    return as_bf16x8((u32x4){e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
+                             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)});
+  };
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  // S^T operand: key m = l % 32 at stage slot kperm(m); channel half ch: E4M3
+  // pieces 16 ch + kk (kk < 16 - 4 ch), then bf16 pieces 28 + 2 (kk - 12) + G
+  const int kslot = kperm(col) * 16;
+  auto score_tile = [&](auto chc, const uint8_t* stg) -> f32x16 {
+    constexpr int CHW = decltype(chc)::value;
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    if constexpr (CHW == 0) {
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(stg + kk * (TS * 16) + kslot + 8 * G);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(w), qf[kk], sacc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 12; ++kk) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(stg + (16 + kk) * (TS * 16) + kslot + 8 * G);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(w), qf[kk], sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 12; kk < KQ; ++kk) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (NF8 + 2 * (kk - 12) + G) * (TS * 16) + kslot);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), qf[kk], sacc, 0, 0, 0);
+      }
+    }
+    return sacc;
+  };
+  // PV over key half s: lane l's 8-byte transposed read of m-tile mo
+  const int lam = l & 15, grp = (l >> 4) & 1;
+  auto pv_half = [&](auto chc, const uint8_t* stg, int s, const bf16x8& pf) {
+    constexpr int CHW = decltype(chc)::value;
+    const int slot8 = 16 * s + 8 * G;              // first of the 8 stage slots of this lane half
+    if constexpr (CHW == 0) {
+#pragma unroll
+      for (int mo = 0; mo < MO; ++mo) {            // E4M3 pieces 2 mo + grp
+        const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+            stg + ((2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int mo = 0; mo < 6; ++mo) {             // E4M3 pieces 16 + 2 mo + grp
+        const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+            stg + ((16 + 2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
+      }
+#pragma unroll
+      for (int mo = 6; mo < MO; ++mo) {            // bf16 channels 448 + 32 (mo - 6) + 16 grp + lam
+        const int piece = NF8 + 4 * (mo - 6) + 2 * grp + ((lam & 3) >> 1);
+        const uint8_t* p0 = stg + (piece * TS + slot8 + (lam >> 2)) * 16 + 8 * (lam & 1);
+        const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0));
+        const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * 16));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf,
+                                                          acc[mo], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: copies of tiles 0 and 1 in flight, their masks
+  if (ntiles > 0) issue(0, s_stage);
+  if (ntiles > 1) issue(1, s_stage + Cf::STAGE);
+  if (ntiles > 0) masks(0, 0);
+  if (ntiles > 1) masks(1, 1);
+  const int partner = wv ^ 1;
+  // the tile loop, compiled once per channel half (straight-line code for each)
+  auto tile_loop = [&](auto chc) {
+  constexpr int CHW = decltype(chc)::value;
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it % F8_NSTG;
+    const uint8_t* stg = s_stage + buf * Cf::STAGE;
+    wait_copies(it + 1 < ntiles ? my_dma : 0);      // this wave's copies of tile it have landed
+    lds_barrier();                                   // A: tile it visible, stage of it-1 and s_x free
+    if (it + 2 < ntiles) {
+      const int nb = (it + 2) % F8_NSTG;
+      issue(it + 2, s_stage + nb * Cf::STAGE);
+      masks(it + 2, nb);
+    }
+    f32x16 sc = score_tile(chc, stg);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      *reinterpret_cast<f32x4*>(s_x + ((wv * 4 + rr) * 64 + l) * 4) =
+          (f32x4){sc[4 * rr], sc[4 * rr + 1], sc[4 * rr + 2], sc[4 * rr + 3]};
+    lds_barrier();                                   // B: partials of tile it
+    // full scores: the channel-0 half plus the channel-1 half, in that order in
+    // both waves of the pair, so that both get the same sums
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(s_x + ((partner * 4 + rr) * 64 + l) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[4 * rr + j] = CHW == 0 ? sc[4 * rr + j] + o[j] : o[j] + sc[4 * rr + j];
+    }
+    if (!tile_full(it)) {
+      const uint32_t mk = s_vmask[buf][qloc] >> (4 * G);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = ((mk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sc[r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      float alpha = 1.f;
+      if (mx > m_run + 8.0f) {
+        alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+        m_run = mx;
+      }
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < MO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    }
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      // v_exp_f32 directly: results below 2^-126 flush to zero, which leaves
+      // the normalised output unchanged at fp32 resolution
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[r], sl, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], sl, mneg));
+      l_run += e0 + e1;
+      pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
+    }
+    pv_half(chc, stg, 0, as_bf16x8((u32x4){pk[0], pk[1], pk[2], pk[3]}));
+    pv_half(chc, stg, 1, as_bf16x8((u32x4){pk[4], pk[5], pk[6], pk[7]}));
+  }
+  };
+  if (ch == 0) tile_loop(std::integral_constant<int, 0>());
+  else tile_loop(std::integral_constant<int, 1>());
+
+  l_run += __shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  if (pl.max_splits == 1) {
+    float f = m_run == -INFINITY ? 0.f : 1.f, den = l_run;
+    if (a.sink) {
+      const float z = a.sink[h] * LOG2E;
+      const float M = fmaxf(m_run, z);
+      f = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+      den = l_run * f + exp2f(z - M);
+    }
+    const float inv = den > 0.f ? f / den : 0.f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + ch * 256;
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = {__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j] * inv), (__bf16)(acc[mo][4 * j + 1] * inv)}),
+                         __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j + 2] * inv), (__bf16)(acc[mo][4 * j + 3] * inv)})};
+        *reinterpret_cast<u32x2*>(orow + 32 * mo + 8 * j + 4 * G) = w;
+      }
+  } else {
+    const int64_t unit = blockIdx.x;
+    const int64_t rows = Cf::R;
+    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
+    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
+                ((unit * pl.max_splits + split) * rows + row) * C + ch * 256;
+    if (G == 0 && ch == 0) { ml[0] = m_run; ml[1] = l_run; }
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
+            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
+  }
+}
+
 // Merge of the split partials, splits in increasing order (deterministic).
 // A block takes 4 rows of one unit; each row's 64 threads own CPT = c / 64
 // consecutive channels and read every split's partial for them with vector
@@ -908,7 +1243,8 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
       const int nrg = rows_per_block(a, dense) / 32;
       if (a.c == 512) {
-        launch_mfma_c<512, ROW_FP8, 2, 2>(a, grid, nrg, pt, (int)b0, pl, s);
+        if (nrg == 1) hipLaunchKernelGGL(attn_f8<1>, grid, dim3(128), 0, s, a, pt, (int)b0, pl);
+        else hipLaunchKernelGGL(attn_f8<2>, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
       } else {
         if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
         else launch_mfma_c<128, ROW_BF16, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
