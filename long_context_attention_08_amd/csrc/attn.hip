@@ -832,11 +832,18 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   const bool qvalid = t <= ui.tl;
   const int64_t tq = qvalid ? t : ui.tl;
 
+  // Q^T in the contraction order of S^T: k-step 2 j + hh of lane half G takes
+  // channels 16 (2 j + G) + 8 hh .. + 8 of the wave's slice for the E4M3 part
+  // (12 or 16 k-steps), then 16 kk + 8 G .. + 8 for the bf16 part
   bf16x8 qf[KQ];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C + ch * 256;
+    const int nf8k = ch == 0 ? 16 : 12;
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * G));
+    for (int kk = 0; kk < KQ; ++kk) {
+      const int c8 = kk < nf8k ? 16 * (2 * (kk >> 1) + G) + 8 * (kk & 1) : 16 * kk + 8 * G;
+      qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + c8));
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile copies are counted from here on
   }
   f32x16 acc[MO];
@@ -929,17 +936,20 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     f32x16 sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    // one 16-byte unit (16 E4M3 channels of key m) per lane feeds two k-steps
     if constexpr (CHW == 0) {
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(stg + kk * (TS * 16) + kslot + 8 * G);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(w), qf[kk], sacc, 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (2 * j + G) * (TS * 16) + kslot);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], sacc, 0, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 12; ++kk) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(stg + (16 + kk) * (TS * 16) + kslot + 8 * G);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(w), qf[kk], sacc, 0, 0, 0);
+      for (int j = 0; j < 6; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (16 + 2 * j + G) * (TS * 16) + kslot);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int kk = 12; kk < KQ; ++kk) {
