@@ -142,6 +142,13 @@ __device__ void bitonic_desc(uint64_t* buf, int n) {
   }
 }
 
+struct HsMeta {
+  int bstar;         // threshold bin (-1: every visible score is taken)
+  uint32_t above;    // visible keys in bins above bstar (all winners)
+  uint32_t inbin;    // visible keys in bin bstar
+  uint32_t need;     // min(k, visible)
+};
+
 struct TopkArgs {
   const float* scores;
   int64_t nq, S;
@@ -150,6 +157,12 @@ struct TopkArgs {
   int nparts;
   int32_t* idx;      // [rows, k]
   uint64_t* cand;    // [rows, nparts, k] (nparts > 1)
+  // histogram select (few long rows)
+  uint32_t* hsuf;    // [rows, nparts, HS_BIN] suffix counts per part
+  uint32_t* hoff;    // [rows, nparts, 2] write offsets (winners, bin candidates)
+  HsMeta* hmeta;     // [rows]
+  uint64_t* hwin;    // [rows, k] winners above the threshold bin
+  uint64_t* hcand;   // [rows, SK_CAP] keys of the threshold bin
 };
 
 __device__ __forceinline__ int pow2_ceil(int x) {
@@ -282,6 +295,65 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of the 1024 composites in buf (LDS), SK_NT = 256
+// threads, element e = 4 t + j held in register j of thread t: strides 1 and
+// 2 compare within a thread, strides 4 .. 128 with the lane t ^ (stride / 4)
+// of the same wave, and only strides 256 and 512 go through LDS.  The result
+// is written back to buf in order.
+__device__ void bitonic1024_desc(uint64_t* buf) {
+  static_assert(SK_NT == 256, "4 elements per thread");
+  const int t = threadIdx.x;
+  uint64_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = buf[4 * t + j];
+  __syncthreads();
+  for (int size = 2; size <= 1024; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pj = j ^ stride;
+          if (pj > j) {
+            const int e = 4 * t + j;
+            const bool desc = (e & size) == 0;
+            const uint64_t x = v[j], y = v[pj];
+            if ((x < y) == desc) { v[j] = y; v[pj] = x; }
+          }
+        }
+      } else if (stride < 256) {
+        const int lo = stride >> 2;                  // partner lane distance
+        const bool lower = (t & lo) == 0;            // this thread holds the lower index of each pair
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * t + j;
+          const bool desc = (e & size) == 0;
+          const uint64_t y = shfl_xor_u64(v[j], lo);
+          const uint64_t mx = v[j] > y ? v[j] : y, mn = v[j] > y ? y : v[j];
+          v[j] = (lower == desc) ? mx : mn;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf[4 * t + j] = v[j];
+        __syncthreads();
+        const int pt = t ^ (stride >> 2);
+        const bool lower = (t & (stride >> 2)) == 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * t + j;
+          const bool desc = (e & size) == 0;
+          const uint64_t y = buf[4 * pt + j];
+          const uint64_t mx = v[j] > y ? v[j] : y, mn = v[j] > y ? y : v[j];
+          v[j] = (lower == desc) ? mx : mn;
+        }
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) buf[4 * t + j] = v[j];
+  __syncthreads();
 }
 
 // exclusive prefix over the SK_NT threads of a per-thread count; *total gets the sum
@@ -519,16 +591,307 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
     sk_gather(sh, n, T);
   }
   if (a.nparts == 1) {
-    const int n2 = pow2_ceil(a.k);
+    const int n2 = pow2_ceil(a.k) > 256 ? SK_KMAX : pow2_ceil(a.k);
     for (int i = need + threadIdx.x; i < n2; i += SK_NT) sh.out[i] = 0;
     __syncthreads();
-    bitonic_desc<SK_NT>(sh.out, n2);
+    if (n2 == SK_KMAX) bitonic1024_desc(sh.out);
+    else bitonic_desc<SK_NT>(sh.out, n2);
     for (int i = threadIdx.x; i < a.k; i += SK_NT)
       a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
   } else {
     uint64_t* dst = a.cand + (row * a.nparts + pidx) * a.k;   // launch-local row
     for (int i = threadIdx.x; i < a.k; i += SK_NT) dst[i] = i < (int)need ? sh.out[i] : 0;
   }
+}
+
+// ------------------------------------------------------------------ histogram select (few long rows, k <= 1024)
+// Decode has a handful of rows of 2^18 scores.  Each row is cut into parts and
+// processed in four launches, each a plain pass:
+//   1. per part: a 2048-bin histogram of the top 11 key bits, stored as suffix
+//      counts (keys at or above each bin);
+//   2. per row: the threshold bin b* (the highest bin whose suffix count
+//      reaches min(k, visible)), how many keys lie above it and in it, and
+//      every part's write offsets into the winner and candidate lists;
+//   3. per part: keys above b* go to the winner list, keys in b* to the
+//      candidate list, as composites;
+//   4. per row: the candidates are cut to the missing count by the exact
+//      radix select, and the k winners are bitonic-sorted.  When b* holds more
+//      keys than the candidate list (heavy ties), the select runs over the row
+//      in global memory instead.
+// The selected set is the same exact set as on every other path.
+constexpr int HS_BIN = 2048;
+constexpr int HS_PER = HS_BIN / SK_NT;     // bins per thread
+
+__device__ __forceinline__ int64_t hs_row(const TopkArgs& a, const PosTable& pt, int b0, int64_t row,
+                                          int64_t* nv) {
+  const int64_t bl = row / a.nq, t = row % a.nq;
+  *nv = visible_count(pt.q_pos0[bl] + t, a.m, a.S);
+  return (b0 + bl) * a.nq + t;
+}
+
+__global__ __launch_bounds__(SK_NT) void topk_h_hist(TopkArgs a, PosTable pt, int b0) {
+  __shared__ uint32_t h[HS_BIN];
+  __shared__ uint32_t wsum[SK_NT / 64];
+  const int64_t row = blockIdx.y;
+  const int p = blockIdx.x;
+  int64_t nv;
+  const int64_t grow = hs_row(a, pt, b0, row, &nv);
+  const int64_t s0 = (int64_t)p * a.part, s1 = s0 + a.part < nv ? s0 + a.part : nv;
+  for (int i = threadIdx.x; i < HS_BIN; i += SK_NT) h[i] = 0;
+  __syncthreads();
+  const float* src = a.scores + grow * a.S;
+  // eight loads in flight per thread (clamped indices, used only when in range)
+  for (int64_t base = s0; base < s1; base += 8 * SK_NT) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = base + u * SK_NT + threadIdx.x;
+      x[u] = src[s < s1 ? s : s1 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + u * SK_NT + threadIdx.x < s1) atomicAdd(&h[score_key(x[u]) >> 21], 1u);
+  }
+  __syncthreads();
+  uint32_t c[HS_PER];
+  uint32_t loc = 0;
+#pragma unroll
+  for (int q = 0; q < HS_PER; ++q) { c[q] = h[HS_PER * threadIdx.x + q]; loc += c[q]; }
+  uint32_t total;
+  const uint32_t before = sk_scan_excl(loc, wsum, &total);
+  uint32_t acc = total - before - loc;       // keys in the bins above this thread's range
+  uint32_t* dst = a.hsuf + (row * a.nparts + p) * HS_BIN + HS_PER * threadIdx.x;
+#pragma unroll
+  for (int q = HS_PER - 1; q >= 0; --q) {
+    acc += c[q];
+    dst[q] = acc;
+  }
+}
+
+__global__ __launch_bounds__(SK_NT) void topk_h_thresh(TopkArgs a, PosTable pt, int b0) {
+  __shared__ uint32_t wsum[SK_NT / 64];
+  __shared__ int s_b;
+  __shared__ uint32_t s_t0[SK_NT + 1];
+  static_assert(HS_PER == 8, "two 16-byte loads per part and thread");
+  const int64_t row = blockIdx.x;
+  int64_t nv;
+  hs_row(a, pt, b0, row, &nv);
+  const uint32_t need = (uint32_t)(nv < a.k ? nv : a.k);
+  const uint32_t* suf = a.hsuf + row * a.nparts * HS_BIN;
+  const bool cut = need < (uint64_t)nv;
+  // total suffix counts of this thread's 8 bins over all parts (loads in flight together)
+  uint32_t tot[HS_PER];
+#pragma unroll
+  for (int q = 0; q < HS_PER; ++q) tot[q] = 0;
+  if (cut) {
+    const u32x4* sp = reinterpret_cast<const u32x4*>(suf) + 2 * threadIdx.x;
+#pragma unroll 8
+    for (int pp = 0; pp < a.nparts; ++pp) {
+      const u32x4 x0 = sp[pp * (HS_BIN / 4)], x1 = sp[pp * (HS_BIN / 4) + 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { tot[q] += x0[q]; tot[4 + q] += x1[q]; }
+    }
+  }
+  s_t0[threadIdx.x] = tot[0];
+  if (threadIdx.x == 0) { s_t0[SK_NT] = 0; s_b = -1; }
+  __syncthreads();
+  if (cut) {
+    // exactly one bin has suffix >= need while the next one up has less
+    const uint32_t nxt = s_t0[threadIdx.x + 1];
+#pragma unroll
+    for (int q = 0; q < HS_PER; ++q) {
+      const uint32_t up = q + 1 < HS_PER ? tot[q + 1] : nxt;
+      if (tot[q] >= need && up < need) s_b = HS_PER * threadIdx.x + q;
+    }
+  }
+  __syncthreads();
+  const int bstar = s_b;
+  uint32_t ca = 0, cb = 0;
+  if ((int)threadIdx.x < a.nparts) {
+    const uint32_t* sp = suf + threadIdx.x * HS_BIN;
+    ca = bstar + 1 < HS_BIN ? sp[bstar + 1] : 0u;
+    cb = bstar >= 0 ? sp[bstar] - ca : 0u;
+  }
+  uint32_t ta, tb;
+  const uint32_t ea = sk_scan_excl(ca, wsum, &ta);
+  const uint32_t eb = sk_scan_excl(cb, wsum, &tb);
+  if ((int)threadIdx.x < a.nparts) {
+    a.hoff[(row * a.nparts + threadIdx.x) * 2] = ea;
+    a.hoff[(row * a.nparts + threadIdx.x) * 2 + 1] = eb;
+  }
+  if (threadIdx.x == 0) a.hmeta[row] = HsMeta{bstar, ta, tb, need};
+}
+
+__global__ __launch_bounds__(SK_NT) void topk_h_compact(TopkArgs a, PosTable pt, int b0) {
+  __shared__ uint32_t na, nb;
+  const int64_t row = blockIdx.y;
+  const int p = blockIdx.x;
+  int64_t nv;
+  const int64_t grow = hs_row(a, pt, b0, row, &nv);
+  const HsMeta mt = a.hmeta[row];
+  if (mt.need == 0) return;
+  const uint32_t offa = a.hoff[(row * a.nparts + p) * 2], offb = a.hoff[(row * a.nparts + p) * 2 + 1];
+  if (threadIdx.x == 0) { na = 0; nb = 0; }
+  __syncthreads();
+  const int64_t s0 = (int64_t)p * a.part, s1 = s0 + a.part < nv ? s0 + a.part : nv;
+  const float* src = a.scores + grow * a.S;
+  uint64_t* win = a.hwin + row * a.k;
+  uint64_t* cand = a.hcand + row * SK_CAP;
+  for (int64_t base = s0; base < s1; base += 8 * SK_NT) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = base + u * SK_NT + threadIdx.x;
+      x[u] = src[s < s1 ? s : s1 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = base + u * SK_NT + threadIdx.x;
+      if (s >= s1) continue;
+      const uint32_t key = score_key(x[u]);
+      const int bin = (int)(key >> 21);
+      if (bin > mt.bstar) {
+        win[offa + atomicAdd(&na, 1u)] = composite(key, (uint32_t)s);
+      } else if (bin == mt.bstar) {
+        const uint32_t at = offb + atomicAdd(&nb, 1u);
+        if (at < (uint32_t)SK_CAP) cand[at] = composite(key, (uint32_t)s);
+      }
+    }
+  }
+}
+
+// global -> LDS copy of n composites, eight loads in flight per thread
+__device__ __forceinline__ void hs_copy(uint64_t* dst, const uint64_t* src, uint32_t n) {
+  for (uint32_t base = 0; base < n; base += 8 * SK_NT) {
+    uint64_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = base + u * SK_NT + threadIdx.x;
+      x[u] = src[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = base + u * SK_NT + threadIdx.x;
+      if (i < n) dst[i] = x[u];
+    }
+  }
+}
+
+// dynamic LDS: sizeof(SkShared)
+__global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
+  const int64_t row = blockIdx.x;
+  int64_t nv;
+  const int64_t grow = hs_row(a, pt, b0, row, &nv);
+  const HsMeta mt = a.hmeta[row];
+  const uint32_t need = mt.need, nab = mt.above;
+  const uint32_t needb = need - nab;                 // to take from bin b*
+  const bool spill = mt.inbin > (uint32_t)SK_CAP;
+  const float* src = a.scores + grow * a.S;
+  const uint64_t pre = (uint64_t)(uint32_t)mt.bstar << 53;   // composites of bin b* start with it
+  uint64_t T = ~0ull;
+  if (needb > 0 && !spill) {
+    hs_copy(sh.cand, a.hcand + row * SK_CAP, mt.inbin);
+    __syncthreads();
+    T = sk_select(sh, (int)mt.inbin, needb);
+  } else if (needb > 0) {
+    // exact MSD radix select over the row's keys of bin b*, read from global memory
+    uint64_t prefix = pre;
+    uint32_t remaining = needb;
+    int shift = 53;
+    for (;;) {
+      const int width = shift < 11 ? shift : 11;
+      shift -= width;
+      const int top = shift + width;
+      for (int i = threadIdx.x; i < SK_BIN; i += SK_NT) sh.hist[i] = 0;
+      __syncthreads();
+      for (int64_t s = threadIdx.x; s < nv; s += SK_NT) {
+        const uint64_t x = composite(score_key(src[s]), (uint32_t)s);
+        if ((x >> top) == (prefix >> top)) atomicAdd(&sh.hist[(uint32_t)(x >> shift) & ((1u << width) - 1u)], 1u);
+      }
+      __syncthreads();
+      uint32_t c[HS_PER];
+      uint32_t loc = 0;
+#pragma unroll
+      for (int q = 0; q < HS_PER; ++q) { c[q] = sh.hist[SK_BIN - 1 - (HS_PER * threadIdx.x + q)]; loc += c[q]; }
+      uint32_t total;
+      uint32_t above = sk_scan_excl(loc, sh.wsum, &total);
+      if (above < remaining && remaining <= above + loc) {
+#pragma unroll
+        for (int q = 0; q < HS_PER; ++q) {
+          if (above < remaining && remaining <= above + c[q]) {
+            sh.sel_bin = SK_BIN - 1 - (HS_PER * threadIdx.x + q);
+            sh.sel_above = above;
+            sh.sel_cnt = c[q];
+          }
+          above += c[q];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = sh.sel_bin, ab = sh.sel_above, cb = sh.sel_cnt;
+      __syncthreads();
+      prefix |= (uint64_t)bin << shift;
+      remaining -= ab;
+      if (cb == remaining || shift == 0) break;
+    }
+    T = prefix;
+  }
+  __syncthreads();
+  // winners: the list above b*, then the bin's keys >= T
+  if (threadIdx.x == 0) sh.cnt2 = 0;
+  hs_copy(sh.out, a.hwin + row * a.k, nab);
+  __syncthreads();
+  if (needb > 0 && !spill) {
+    for (uint32_t i = threadIdx.x; i < mt.inbin; i += SK_NT) {
+      const uint64_t x = sh.cand[i];
+      if (x >= T) {
+        const uint32_t at = nab + atomicAdd(&sh.cnt2, 1u);
+        if (at < (uint32_t)SK_KMAX) sh.out[at] = x;
+      }
+    }
+  } else if (needb > 0) {
+    for (int64_t s = threadIdx.x; s < nv; s += SK_NT) {
+      const uint64_t x = composite(score_key(src[s]), (uint32_t)s);
+      if ((x >> 53) == (pre >> 53) && x >= T) {
+        const uint32_t at = nab + atomicAdd(&sh.cnt2, 1u);
+        if (at < (uint32_t)SK_KMAX) sh.out[at] = x;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = (int)need + threadIdx.x; i < SK_KMAX; i += SK_NT) sh.out[i] = 0;
+  __syncthreads();
+  bitonic1024_desc(sh.out);
+  for (int i = threadIdx.x; i < a.k; i += SK_NT)
+    a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
+}
+
+// bytes of the histogram-select workspace for `rows` rows of `nparts` parts
+static size_t hs_bytes(int64_t rows, int nparts, int k, size_t* o_suf, size_t* o_off, size_t* o_meta,
+                       size_t* o_win, size_t* o_cand) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t o = 0;
+  *o_suf = o; o = al(o + (size_t)rows * nparts * HS_BIN * 4);
+  *o_off = o; o = al(o + (size_t)rows * nparts * 2 * 4);
+  *o_meta = o; o = al(o + (size_t)rows * sizeof(HsMeta));
+  *o_win = o; o = al(o + (size_t)rows * k * 8);
+  *o_cand = o; o = al(o + (size_t)rows * SK_CAP * 8);
+  return o;
+}
+
+// histogram select for few long rows: parts of at least 8192 scores, at most 64
+static bool hs_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
+  if (k > SK_KMAX || rows >= 512 || S <= 16384) return false;
+  int64_t np = (512 + rows - 1) / rows;
+  const int64_t by_len = S / 8192;
+  if (np > by_len) np = by_len;
+  if (np > 64) np = 64;
+  if (np < 2) np = 2;
+  const int64_t p = (S + np - 1) / np;
+  *part = (int)p;
+  *nparts = (int)((S + p - 1) / p);
+  return true;
 }
 
 static void topk_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
@@ -560,12 +923,17 @@ static void topk_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
 
 size_t topk_workspace_bytes(int64_t rows, int64_t S, int k) {
   int part, nparts;
+  if (hs_plan(rows, S, k, &part, &nparts)) {
+    size_t o1, o2, o3, o4, o5;
+    return hs_bytes(rows, nparts, k, &o1, &o2, &o3, &o4, &o5);
+  }
   topk_plan(rows, S, k, &part, &nparts);
   return nparts > 1 ? (size_t)rows * nparts * k * sizeof(uint64_t) : 0;
 }
 
 bool topk_supported(int64_t rows, int64_t S, int k) {
   int part, nparts;
+  if (k >= 1 && hs_plan(rows, S, k, &part, &nparts)) return true;
   topk_plan(rows, S, k, &part, &nparts);
   return k >= 1 && k <= 4096 && (nparts == 1 || (int64_t)nparts * k <= MAX_CAND);
 }
@@ -573,9 +941,36 @@ bool topk_supported(int64_t rows, int64_t S, int k) {
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
                        const int64_t* q_pos0, int k, int32_t* idx, void* ws, hipStream_t s) {
   if (B <= 0 || nq <= 0) return hipSuccess;
-  TopkArgs a;
+  TopkArgs a = {};
   a.scores = scores; a.nq = nq; a.S = S; a.m = m; a.k = k; a.idx = idx;
-  topk_plan((B < MAXB ? B : MAXB) * nq, S, k, &a.part, &a.nparts);
+  const int64_t rows_l = (B < MAXB ? B : MAXB) * nq;
+  if (hs_plan(rows_l, S, k, &a.part, &a.nparts)) {
+    size_t o_suf, o_off, o_meta, o_win, o_cand;
+    hs_bytes(rows_l, a.nparts, k, &o_suf, &o_off, &o_meta, &o_win, &o_cand);
+    uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+    a.hsuf = reinterpret_cast<uint32_t*>(w + o_suf);
+    a.hoff = reinterpret_cast<uint32_t*>(w + o_off);
+    a.hmeta = reinterpret_cast<HsMeta*>(w + o_meta);
+    a.hwin = reinterpret_cast<uint64_t*>(w + o_win);
+    a.hcand = reinterpret_cast<uint64_t*>(w + o_cand);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_h_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(SkShared));
+    if (e != hipSuccess) return e;
+    for (int64_t b0 = 0; b0 < B; b0 += MAXB) {
+      const int nb = (int)(B - b0 < MAXB ? B - b0 : MAXB);
+      PosTable pt;
+      for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
+      const unsigned rows = (unsigned)(nb * nq);
+      hipLaunchKernelGGL(topk_h_hist, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
+      hipLaunchKernelGGL(topk_h_thresh, dim3(rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
+      hipLaunchKernelGGL(topk_h_compact, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
+      hipLaunchKernelGGL(topk_h_finish, dim3(rows), dim3(SK_NT), sizeof(SkShared), s, a, pt, (int)b0);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  topk_plan(rows_l, S, k, &a.part, &a.nparts);
   a.cand = reinterpret_cast<uint64_t*>(ws);
   const int n2 = [&] { int p = 1; while (p < k) p <<= 1; return p; }();
   const bool stream = k <= SK_KMAX;

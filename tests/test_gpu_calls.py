@@ -244,6 +244,8 @@ TOPK_CASES = [
     (1, 3, 65536, 1024, 4, [300000], "desc"), # the first scores are the answer
     (1, 6, 50001, 512, 4, [250000], "normal"), # rows not 16-byte aligned
     (1, 8, 100000, 1024, 1, [200000], "int"),  # long rows, heavy ties at the threshold
+    (1, 2, 70000, 512, 4, [300000], "zeros"),  # long rows: the threshold bin holds 10000 equal keys
+    (1, 3, 40000, 1024, 4, [1000], "normal"),  # long rows with fewer visible scores than k
 ]
 
 
