@@ -6,8 +6,10 @@ benchmark's CPU-baseline leg, never by the library or its binding.
 from . import codecs
 from .dsv4 import (softmax_pool, csa_compress, csa_pool_weights, hca_compress,
                    visible_count, indexer_score, indexer_score_fp4q, topk_select, core_attention,
-                   window_rows, sparse_mqa, hca_dense)
+                   window_rows, sparse_mqa, hca_dense, rmsnorm, rope_last, q_norm_rope,
+                   kv_norm_rope, entry_positions, out_rope)
 
 __all__ = ["codecs", "softmax_pool", "csa_compress", "csa_pool_weights", "hca_compress",
            "visible_count", "indexer_score", "indexer_score_fp4q", "topk_select", "core_attention",
-           "window_rows", "sparse_mqa", "hca_dense"]
+           "window_rows", "sparse_mqa", "hca_dense", "rmsnorm", "rope_last", "q_norm_rope",
+           "kv_norm_rope", "entry_positions", "out_rope"]

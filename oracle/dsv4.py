@@ -39,7 +39,19 @@ reason, in the design notes of the repository):
   R16 an empty key set gives a zero output;
   R19b the FP4 indexer rounds each query head q^I[t, h] to MXFP4 (blocks of
       32 consecutive c_I dims, the key encoder) before eq 16; the keys are the
-      stored MXFP4 rows, decoded.
+      stored MXFP4 rows, decoded;
+  R32 RMSNorm (digest 模块 D, Q/KV normalisation) of a vector x of width c is
+      x / sqrt(mean(x^2) + eps) * gamma, eps = 1e-6, gamma per channel; it is
+      applied to every query head and to every KV row that core attention
+      reads (compressed entries and window rows);
+  R33 partial RoPE (digest 模块 D) rotates the last 64 dims as interleaved
+      pairs (2j, 2j + 1), j < 32, by the angle pos * theta^(-2j/64),
+      theta = 10000, after the RMSNorm;
+  R34 positions: a query at its own position p; a window row at its token's
+      position; a compressed entry at the position of the newest token it
+      pools, m (s + 1) - 1 (HCA: m' (s + 1) - 1);
+  R35 the attention output's last 64 dims are rotated by -p (the query's
+      position), so that they carry relative positions.
 """
 import numpy as np
 
@@ -177,6 +189,51 @@ def indexer_score_fp4q(qI, wI, KI, m, q_pos):
     qI = np.asarray(qI, dtype=np.float64)
     codes, scales = _codecs.mxfp4_encode(qI)
     return indexer_score(_codecs.mxfp4_decode(codes, scales), wI, KI, m, q_pos)
+
+
+def rmsnorm(x, gamma, eps=1e-6):
+    """RMSNorm over the last axis (digest 模块 D; R32)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def rope_last(x, pos, theta=10000.0, rope_dims=64):
+    """Partial RoPE (digest 模块 D; R33): the last rope_dims dims of x [..., c]
+    rotated as interleaved pairs (2j, 2j+1) by pos * theta^(-2j/rope_dims);
+    pos broadcasts over the leading axes of x (one position per row)."""
+    x = np.array(x, dtype=np.float64)
+    c = x.shape[-1]
+    pos = np.asarray(pos, dtype=np.float64)[..., None]        # [..., 1]
+    j = np.arange(rope_dims // 2, dtype=np.float64)
+    ang = pos * theta ** (-2.0 * j / rope_dims)               # [..., rope_dims/2]
+    cs, sn = np.cos(ang), np.sin(ang)
+    a = x[..., c - rope_dims::2].copy()
+    b = x[..., c - rope_dims + 1::2].copy()
+    x[..., c - rope_dims::2] = a * cs - b * sn
+    x[..., c - rope_dims + 1::2] = a * sn + b * cs
+    return x
+
+
+def q_norm_rope(q, gamma, q_pos, eps=1e-6, theta=10000.0, rope_dims=64):
+    """Query preparation (R32, R33): q [nq, nh, c] at positions q_pos [nq]."""
+    y = rmsnorm(q, gamma, eps)
+    return rope_last(y, np.asarray(q_pos, dtype=np.float64)[:, None] * np.ones(y.shape[:-1]), theta, rope_dims)
+
+
+def kv_norm_rope(rows, gamma, pos, eps=1e-6, theta=10000.0, rope_dims=64):
+    """KV row preparation (R32-R34): rows [n, c] at positions pos [n]."""
+    return rope_last(rmsnorm(rows, gamma, eps), pos, theta, rope_dims)
+
+
+def entry_positions(m, s0, n):
+    """Positions of compressed entries s0 .. s0+n-1 (R34): the newest pooled token."""
+    return m * (np.arange(s0, s0 + n, dtype=np.int64) + 1) - 1
+
+
+def out_rope(o, q_pos, theta=10000.0, rope_dims=64):
+    """Output rotation (R35): o [nq, nh, c], last dims rotated by -q_pos."""
+    o = np.asarray(o, dtype=np.float64)
+    return rope_last(o, -np.asarray(q_pos, dtype=np.float64)[:, None] * np.ones(o.shape[:-1]), theta, rope_dims)
 
 
 def topk_select(I, m, q_pos, k):

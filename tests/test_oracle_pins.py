@@ -319,6 +319,89 @@ def test_indexer_fp4q_blocks_are_per_head():
                           base[np.isfinite(base)] * 2.0**-7)
 
 
+# ----------------------------------------------------------------------
+# Q/KV RMSNorm and partial RoPE (digest 模块 D; readings R32-R35)
+# ----------------------------------------------------------------------
+
+def test_rmsnorm_closed_forms():
+    """A constant vector a*1 normalises to a / sqrt(a^2 + eps) per channel,
+    times gamma; gamma scales channel by channel; the output's mean square is
+    ms / (ms + eps) for unit gamma."""
+    c, eps = 16, 1e-6
+    g = np.linspace(0.5, 2.0, c)
+    y = O.rmsnorm(np.full(c, 3.0), g, eps)
+    assert np.allclose(y, 3.0 / np.sqrt(9.0 + eps) * g, rtol=1e-15, atol=0)
+    x = rnd(60, 5, c)
+    ms = np.mean(x * x, axis=-1)
+    y1 = O.rmsnorm(x, np.ones(c), eps)
+    assert np.allclose(np.mean(y1 * y1, axis=-1), ms / (ms + eps), rtol=1e-13)
+    assert np.allclose(O.rmsnorm(x, g, eps), y1 * g, rtol=1e-15)
+
+
+def test_rope_hand_example_pins_interleaved_pairs():
+    """Pair j of the last 64 dims is (c-64+2j, c-64+2j+1), rotated by
+    pos * 10000^(-2j/64): at pos 1, (1, 0) in pair 0 becomes (cos 1, sin 1) and
+    (1, 0) in pair 1 becomes (cos a, sin a), a = 10000^(-1/32); earlier dims
+    are untouched (a half-split pairing would move dim c-32 instead)."""
+    c = 72
+    x = np.zeros(c)
+    x[c - 64] = 1.0
+    x[c - 62] = 1.0
+    x[3] = 7.0
+    y = O.rope_last(x[None], [1.0])[0]
+    a = 10000.0 ** (-1.0 / 32)
+    want = np.zeros(c)
+    want[3] = 7.0
+    want[c - 64], want[c - 63] = np.cos(1.0), np.sin(1.0)
+    want[c - 62], want[c - 61] = np.cos(a), np.sin(a)
+    assert np.allclose(y, want, rtol=0, atol=1e-15)
+
+
+def test_rope_rotation_identities():
+    """R(0) = I, each pair keeps its length, R(a) R(b) = R(a + b)."""
+    x = rnd(61, 4, 128)
+    assert np.array_equal(O.rope_last(x, np.zeros(4)), x)
+    y = O.rope_last(x, [5.0, -3.0, 1e6, 0.25])
+    n0 = x[:, 64::2] ** 2 + x[:, 65::2] ** 2
+    n1 = y[:, 64::2] ** 2 + y[:, 65::2] ** 2
+    assert np.allclose(n0, n1, rtol=1e-12)
+    ab = O.rope_last(O.rope_last(x, [2.0, 7.0, 11.0, 13.0]), [3.0, -7.0, 100.0, 0.5])
+    assert np.allclose(ab, O.rope_last(x, [5.0, 0.0, 111.0, 13.5]), rtol=0, atol=1e-12)
+
+
+def test_rope_chain_depends_only_on_relative_positions():
+    """Logits (R(p) q) . (R(s) k) and the rotated-back output R(-p) sum_s P_s
+    R(s) v_s are unchanged when every position moves by the same offset: the
+    reason the pages rotate the output by the query's position."""
+    c = 96
+    q = O.rmsnorm(rnd(62, 1, c), np.ones(c))
+    ks = O.rmsnorm(rnd(63, 9, c), np.ones(c))
+    p, s = 40.0, np.arange(20.0, 29.0)
+    def chain(shift):
+        qr = O.rope_last(q, [p + shift])
+        kr = O.rope_last(ks, s + shift)
+        lg = kr @ qr[0] / np.sqrt(c)
+        P = np.exp(lg - lg.max())
+        P /= P.sum()
+        o = (P[:, None] * kr).sum(axis=0)
+        return lg, O.out_rope(o[None, None], [p + shift])[0, 0]
+    l0, o0 = chain(0.0)
+    l1, o1 = chain(12345.0)
+    assert np.allclose(l0, l1, rtol=0, atol=1e-9)
+    assert np.allclose(o0, o1, rtol=0, atol=1e-9)
+
+
+def test_entry_positions_match_visibility():
+    """Entry s sits at the newest token it pools, m (s + 1) - 1, so it is visible
+    at position p exactly when its position is <= p (R5, R34)."""
+    for m in (1, 4, 128):
+        pos = O.entry_positions(m, 0, 50)
+        assert pos[0] == m - 1 and pos[2] == 3 * m - 1
+        for p in (0, m - 2, m - 1, 3 * m, 7 * m + 3):
+            assert (pos <= p).sum() == O.visible_count(p, m, 50)
+    assert np.array_equal(O.entry_positions(4, 10, 3), [43, 47, 51])
+
+
 # ======================================================================
 # Top-k selector (digest 模块 B eq 17)
 # ======================================================================
