@@ -165,6 +165,48 @@ def fp4_indexer_report(layer, flop, steps, stream, rows_n=256):
             "recall_at_k_vs_bf16_query": round(float(np.mean(rec)), 4), "recall_rows": len(rec)}
 
 
+def norm_rope_report(layer, steps, stream):
+    """Time the Q/KV RMSNorm + partial RoPE and the output rotation at the
+    chunk's shapes (outside the step: the six calls take their inputs already
+    normalised and rotated): every query head, the chunk's new compressed
+    entries and window rows, every output row."""
+    import torch
+    from long_context_attention_08_amd import _lib as L
+    n, nh, c = layer.n, layer.nh, layer.c
+    q = layer.q.view(1, n, nh, c)
+    qo = torch.empty_like(q)
+    o = layer.out.view(1, n, nh, c).clone()
+    g = torch.ones(c, dtype=torch.float32, device="cuda")
+    ncomp = n // layer.m
+    comp_in = torch.randn((1, ncomp, c), dtype=torch.float32, device="cuda")
+    comp_out = torch.empty((1, ncomp, c + 64), dtype=torch.uint8, device="cuda")
+    win_in = torch.randn((1, n, c), dtype=torch.bfloat16, device="cuda")
+    win_out = torch.empty((1, n, c + 64), dtype=torch.uint8, device="cuda")
+    p0 = layer.q_pos0
+    calls = {
+        "q_norm_rope": (lambda: L.q_norm_rope(q, g, p0, out=qo), 2 * q.numel() * 2),
+        "out_rope": (lambda: L.out_rope(o, p0), 2 * n * nh * 64 * 2),
+        "kv_norm_rope (entries + window rows)": (
+            lambda: (L.kv_norm_rope(comp_in, L.ROW_F32, c, g, [layer.m * (layer.S0 + 1) - 1], layer.m, comp_out,
+                                    L.ROW_FP8_ROPE_BF16),
+                     L.kv_norm_rope(win_in, L.ROW_BF16, c, g, p0, 1, win_out, L.ROW_FP8_ROPE_BF16)),
+            ncomp * (4 * c + c + 64) + n * (2 * c + c + 64)),
+    }
+    rep = {}
+    for name, (f, nbytes) in calls.items():
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rep[name] = {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK["hbm"], 4)}
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +284,7 @@ def main():
                        "window": cfg["n_win"], "kv": "fp8_e4m3+bf16_rope", "indexer_keys": "mxfp4"},
             "roofline": roof, "calls": calls}
     line["fp4_indexer"] = fp4_indexer_report(layer, work["indexer"]["flop"], args.steps, stream)
+    line["norm_rope"] = norm_rope_report(layer, args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
     print(json.dumps(line), flush=True)

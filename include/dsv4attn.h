@@ -191,6 +191,49 @@ int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh
                        const int64_t* q_pos0, const float* sink, float scale,
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Query-side RMSNorm and partial RoPE (digest 模块 D: each query head is
+ * RMS-normalised before core attention; RoPE acts on the last dims only).
+ * For every row x = q[b, t, h, :] of width c, at position p = q_pos0[b] + t:
+ *   y = x / sqrt(mean(x^2) + eps) * gamma          (gamma NULL: 1)
+ *   then the last rope_dims dims are rotated as interleaved pairs
+ *   (c - R + 2j, c - R + 2j + 1), j < R/2, by p * theta^(-2j/R).
+ * q and q_out [B, nq, nh, c] in q_dtype (F32 or BF16, 16-byte aligned); they
+ * may be the same buffer.  c a multiple of 8 up to 4096; rope_dims a multiple
+ * of 8 up to min(c, 512) (64 in the pages); eps >= 0 (1e-6 in this library's
+ * reading), theta > 0 (10000).  q_pos0: host array [B].
+ */
+int dsv4_q_norm_rope(const void* q, int q_dtype, void* q_out, int64_t B, int64_t nq, int nh, int c,
+                     const float* gamma, float eps, float theta, int rope_dims,
+                     const int64_t* q_pos0, void* stream);
+
+/*
+ * KV-side RMSNorm and partial RoPE, with the storage pack (digest 模块 D; 模块 F
+ * for the FP8 + bf16-RoPE rows).  Row i of batch entry b, rows[b, i, :] in
+ * in_layout (F32 or BF16), sits at position pos0[b] + pos_stride * i (host
+ * array pos0): window rows use their token positions (stride 1), compressed
+ * entries the newest token they pool, m (s + 1) - 1 (stride m).  The row is
+ * normalised and rotated as in dsv4_q_norm_rope and stored to rows_out[b, i]
+ * in out_layout (F32, BF16 or FP8_ROPE_BF16).  In place only when the two
+ * layouts have the same row size.  Same limits on c, rope_dims, eps and theta
+ * as dsv4_q_norm_rope; FP8 rows need c >= 64 and c % 16 == 0.
+ */
+int dsv4_kv_norm_rope(const void* rows, int in_layout, int64_t B, int64_t n, int c,
+                      const float* gamma, float eps, float theta, int rope_dims,
+                      const int64_t* pos0, int64_t pos_stride,
+                      void* rows_out, int out_layout, void* stream);
+
+/*
+ * Output rotation (digest 模块 D: since each KV entry is key and value, the
+ * output carries the entries' absolute positions; rotating it back by the
+ * query's position leaves relative ones).  In place on o [B, nq, nh, c]
+ * (F32 or BF16): the last rope_dims dims of row (b, t, h) are rotated by
+ * -(q_pos0[b] + t), as pairs like dsv4_q_norm_rope; the other dims are not
+ * touched.  rope_dims == 0 is a no-op.
+ */
+int dsv4_out_rope(void* o, int o_dtype, int64_t B, int64_t nq, int nh, int c, float theta, int rope_dims,
+                  const int64_t* q_pos0, void* stream);
+
 /* Status text, and the last error message of the calling thread. */
 const char* dsv4_status_string(int status);
 const char* dsv4_last_error(void);

@@ -16,7 +16,7 @@ ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
     "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
-    "dsv4_indexer_score_fp4q",
+    "dsv4_indexer_score_fp4q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
 ]
@@ -47,6 +47,9 @@ _sig("dsv4_indexer_score", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _i
                                   _P64, _vp, _vp])
 _sig("dsv4_indexer_score_fp4q", _int, [_vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _int, _i64, _int,
                                        _P64, _vp, _vp])
+_sig("dsv4_q_norm_rope", _int, [_vp, _int, _vp, _i64, _i64, _int, _int, _vp, _f32, _f32, _int, _P64, _vp])
+_sig("dsv4_kv_norm_rope", _int, [_vp, _int, _i64, _i64, _int, _vp, _f32, _f32, _int, _P64, _i64, _vp, _int, _vp])
+_sig("dsv4_out_rope", _int, [_vp, _int, _i64, _i64, _int, _int, _f32, _int, _P64, _vp])
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
@@ -186,3 +189,31 @@ def hca_dense_fwd(q, kv_comp, kv_layout, m_prime, kv_win, win_pos0, n_win, q_pos
     _check(lib.dsv4_hca_dense_fwd(_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, m_prime,
                                   _ptr(kv_win), W, _host_i64(win_pos0), n_win, _host_i64(q_pos0),
                                   _ptr(sink), float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream)))
+
+
+# --------------------------------------------------------------------- Q/KV norm and RoPE
+
+def q_norm_rope(q, gamma, q_pos0, *, out=None, eps=1e-6, theta=10000.0, rope_dims=64, stream=None):
+    """RMSNorm and partial RoPE of every query head.  q [B, nq, nh, c] float32 or
+    bfloat16; out (default: q, in place) of the same shape and dtype."""
+    B, nq, nh, c = q.shape
+    out = q if out is None else out
+    _check(lib.dsv4_q_norm_rope(_ptr(q), _act(q), _ptr(out), B, nq, nh, c, _ptr(gamma), eps, theta, rope_dims,
+                                _host_i64(q_pos0), _stream(stream)))
+
+
+def kv_norm_rope(rows, in_layout, c, gamma, pos0, pos_stride, rows_out, out_layout, *, eps=1e-6,
+                 theta=10000.0, rope_dims=64, stream=None):
+    """RMSNorm, partial RoPE and the storage pack of KV rows.  rows [B, n, row]
+    in in_layout; row i of batch entry b sits at pos0[b] + pos_stride * i;
+    rows_out [B, n, row] in out_layout."""
+    B, n = rows.shape[0], rows.shape[1]
+    _check(lib.dsv4_kv_norm_rope(_ptr(rows), in_layout, B, n, c, _ptr(gamma), eps, theta, rope_dims,
+                                 _host_i64(pos0), pos_stride, _ptr(rows_out), out_layout, _stream(stream)))
+
+
+def out_rope(o, q_pos0, *, theta=10000.0, rope_dims=64, stream=None):
+    """Rotate the last rope_dims dims of every output row o[b, t, h] (in place)
+    by -(q_pos0[b] + t)."""
+    B, nq, nh, c = o.shape
+    _check(lib.dsv4_out_rope(_ptr(o), _act(o), B, nq, nh, c, theta, rope_dims, _host_i64(q_pos0), _stream(stream)))

@@ -292,4 +292,69 @@ int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh
                      m_prime, kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream);
 }
 
+// --------------------------------------------------------------------------- Q/KV norm and RoPE
+
+static int rope_args_ok(const char* fn, int c, float eps, float theta, int rope_dims) {
+  if (c <= 0 || c % 8 || c > 4096) return fail(DSV4_ERR_UNSUPPORTED, "%s: c=%d (multiple of 8, <= 4096)", fn, c);
+  if (rope_dims < 0 || rope_dims > c || rope_dims % 8 || rope_dims > 512)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: rope_dims=%d (multiple of 8, <= min(c, 512))", fn, rope_dims);
+  if (!(eps >= 0.f) || !(theta > 0.f)) return fail(DSV4_ERR_INVALID_ARG, "%s: eps < 0 or theta <= 0", fn);
+  return 0;
+}
+
+int dsv4_q_norm_rope(const void* q, int q_dtype, void* q_out, int64_t B, int64_t nq, int nh, int c,
+                     const float* gamma, float eps, float theta, int rope_dims,
+                     const int64_t* q_pos0, void* stream) {
+  const char* fn = "dsv4_q_norm_rope";
+  if (B < 0 || nq < 0 || nh <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
+  int r = rope_args_ok(fn, c, eps, theta, rope_dims);
+  if (r) return r;
+  if (B == 0 || nq == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  r = check_ptrs16(fn, {{q, "q"}, {q_out, "q_out"}});
+  if (r) return r;
+  dsv4::QPrepArgs a{q, q_out, q_dtype, B, nq, nh, c, gamma, eps, theta, rope_dims, 0};
+  return hip_status(dsv4::launch_q_prep(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_kv_norm_rope(const void* rows, int in_layout, int64_t B, int64_t n, int c,
+                      const float* gamma, float eps, float theta, int rope_dims,
+                      const int64_t* pos0, int64_t pos_stride,
+                      void* rows_out, int out_layout, void* stream) {
+  const char* fn = "dsv4_kv_norm_rope";
+  if (B < 0 || n < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (in_layout != DSV4_ROW_F32 && in_layout != DSV4_ROW_BF16)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: in_layout %d", fn, in_layout);
+  if (out_layout != DSV4_ROW_F32 && out_layout != DSV4_ROW_BF16 && out_layout != DSV4_ROW_FP8_ROPE_BF16)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: out_layout %d", fn, out_layout);
+  int r = rope_args_ok(fn, c, eps, theta, rope_dims);
+  if (r) return r;
+  if (out_layout == DSV4_ROW_FP8_ROPE_BF16 && (c < 64 || c % 16))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: FP8 rows need c >= 64, c %% 16 == 0", fn);
+  if (B == 0 || n == 0) return ok();
+  if (!pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: pos0 is NULL", fn);
+  r = check_ptrs16(fn, {{rows, "rows"}, {rows_out, "rows_out"}});
+  if (r) return r;
+  if (rows == rows_out && dsv4_row_bytes(in_layout, c) != dsv4_row_bytes(out_layout, c))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: in place needs equal row sizes", fn);
+  dsv4::KvPrepArgs a{rows, in_layout, rows_out, out_layout, B, n, c, gamma, eps, theta, rope_dims, pos_stride};
+  return hip_status(dsv4::launch_kv_prep(a, pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_out_rope(void* o, int o_dtype, int64_t B, int64_t nq, int nh, int c, float theta, int rope_dims,
+                  const int64_t* q_pos0, void* stream) {
+  const char* fn = "dsv4_out_rope";
+  if (B < 0 || nq < 0 || nh <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!act_ok(o_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: o_dtype %d", fn, o_dtype);
+  int r = rope_args_ok(fn, c, 0.f, theta, rope_dims);
+  if (r) return r;
+  if (B == 0 || nq == 0 || rope_dims == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  r = check_ptrs16(fn, {{o, "o"}});
+  if (r) return r;
+  dsv4::QPrepArgs a{o, o, o_dtype, B, nq, nh, c, nullptr, 0.f, theta, rope_dims, 1};
+  return hip_status(dsv4::launch_q_prep(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -77,6 +77,33 @@ struct AttnArgs {
   size_t ws_bytes;
 };
 
+// Q/KV RMSNorm + partial RoPE, and the output rotation (normrope.hip)
+struct QPrepArgs {
+  const void* in;       // [B, nq, nh, c]
+  void* out;            // same shape and dtype (may alias in)
+  int dtype;            // ACT_F32 | ACT_BF16
+  int64_t B, nq;
+  int nh, c;
+  const float* gamma;   // [c] or null (1); unused for the output rotation
+  float eps, theta;
+  int R;                // rotated dims (the last R of each row)
+  int out_rot;          // 1: no norm, rotate by -position, write the rotated dims only
+};
+struct KvPrepArgs {
+  const void* in;       // [B, n, row] in ROW_F32 | ROW_BF16
+  int in_layout;
+  void* out;            // [B, n, row] in ROW_F32 | ROW_BF16 | ROW_FP8
+  int out_layout;
+  int64_t B, n;
+  int c;
+  const float* gamma;
+  float eps, theta;
+  int R;
+  int64_t pos_stride;   // row i of batch entry b sits at pos0[b] + pos_stride * i
+};
+hipError_t launch_q_prep(const QPrepArgs& a, const int64_t* q_pos0, hipStream_t s);
+hipError_t launch_kv_prep(const KvPrepArgs& a, const int64_t* pos0, hipStream_t s);
+
 size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense);
 hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0,
                        bool dense, hipStream_t s);

@@ -28,7 +28,8 @@ CHUNK = 1 << 22
 _POOL = ThreadPoolExecutor(max_workers=8)
 
 STREAMS = ["H", "W_kv", "W_ki", "W_hca", "B_kv", "B_ki", "B_hca", "q", "qI", "wI", "q_hca",
-           "sink", "sink_hca", "cache_kv", "cache_ki", "cache_hca", "win_kv", "win_hca", "extra"]
+           "sink", "sink_hca", "cache_kv", "cache_ki", "cache_hca", "win_kv", "win_hca", "extra",
+           "gamma", "o", "rows"]
 
 
 def normal(seed, stream, shape, std=1.0):

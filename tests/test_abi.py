@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 12
+    assert len(syms) == 15
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -94,6 +94,26 @@ def test_indexer_fp4q_validation(L):
     assert f(FAKE, 1, FAKE, FAKE, FAKE, 1, 4, 32, 64, 100, 4, pos(-1), FAKE, None) == 1      # negative pos
     assert f(FAKE, 7, FAKE, FAKE, FAKE, 1, 4, 32, 64, 100, 4, pos(0), FAKE, None) == 2       # q dtype
     assert f(FAKE, 1, FAKE, FAKE, FAKE, 0, 4, 32, 64, 100, 4, None, FAKE, None) == 0         # B = 0 no-op
+
+
+def test_norm_rope_validation(L):
+    f = L.lib.dsv4_q_norm_rope
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 100, None, 1e-6, 1e4, 64, pos(0), None) == 2     # c % 8
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 512, None, 1e-6, 1e4, 60, pos(0), None) == 2     # rope_dims % 8
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 64, None, 1e-6, 1e4, 72, pos(0), None) == 2      # rope_dims > c
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 512, None, -1.0, 1e4, 64, pos(0), None) == 1     # eps < 0
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 512, None, 1e-6, 0.0, 64, pos(0), None) == 1     # theta <= 0
+    assert f(FAKE, 1, FAKE, 1, 2, 4, 512, None, 1e-6, 1e4, 64, None, None) == 1       # no positions
+    assert f(FAKE, 1, FAKE, 0, 2, 4, 512, None, 1e-6, 1e4, 64, None, None) == 0       # B = 0 no-op
+    g = L.lib.dsv4_kv_norm_rope
+    assert g(FAKE, 2, 1, 8, 512, None, 1e-6, 1e4, 64, pos(0), 4, FAKE, 2, None) == 2  # FP8 input
+    assert g(FAKE, 1, 1, 8, 512, None, 1e-6, 1e4, 64, pos(0), 4, FAKE, 3, None) == 2  # MXFP4 output
+    assert g(FAKE, 1, 1, 8, 40, None, 1e-6, 1e4, 8, pos(0), 4, FAKE, 2, None) == 2    # FP8 rows need c >= 64
+    assert g(FAKE, 1, 1, 8, 512, None, 1e-6, 1e4, 64, pos(0), 4, FAKE, 2, None) == 1  # in place, sizes differ
+    assert g(FAKE, 1, 1, 0, 512, None, 1e-6, 1e4, 64, None, 4, FAKE, 2, None) == 0    # n = 0 no-op
+    h = L.lib.dsv4_out_rope
+    assert h(FAKE, 5, 1, 2, 4, 512, 1e4, 64, pos(0), None) == 2                       # dtype
+    assert h(FAKE, 1, 1, 2, 4, 512, 1e4, 0, None, None) == 0                          # rope_dims 0 no-op
 
 
 def test_topk_validation(L):

@@ -392,3 +392,85 @@ def test_attention_window_must_be_covered(L):
     with pytest.raises(L.Dsv4Error) as e:   # query 103 needs position 103 but rows cover [90, 100)
         L.sparse_mqa_fwd(q, kv, ROW_BF16, idx, win, [90], 8, [100], None, 1.0, out, None)
     assert e.value.status == 1
+
+
+# ====================================================================== Q/KV RMSNorm, partial RoPE, output rotation
+
+NRQ_CASES = [
+    # (dtype, B, nq, nh, c, rope_dims, pos0 list, gamma)
+    ("bf16", 2, 5, 64, 512, 64, [1 << 20, 17], True),    # the configs' shape, positions near 2^20
+    ("f32", 1, 3, 4, 128, 64, [5], True),
+    ("f32", 1, 2, 3, 1024, 64, [999999], False),         # two passes of 512 per row
+    ("bf16", 1, 2, 8, 64, 0, [3], True),                 # no rotated dims
+]
+
+
+def _gamma(seed, c):
+    return (1.0 + G.normal(seed, "gamma", (c,), 0.3)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", NRQ_CASES, ids=[str(i) for i in range(len(NRQ_CASES))])
+def test_q_norm_rope(L, case):
+    import torch
+    dt, B, nq, nh, c, R, pos, use_g = case
+    seed = 800 + c + nh
+    q = act_arr(seed, "q", (B, nq, nh, c), 2.0, dt)
+    g = _gamma(seed, c) if use_g else None
+    qd = dev(q)
+    out = torch.empty_like(qd)
+    L.q_norm_rope(qd, dev(g) if use_g else None, pos, out=out, rope_dims=R)
+    got = host(out)
+    for b in range(B):
+        ref = O.q_norm_rope(decode_act(q[b]), g if use_g else np.ones(c), pos[b] + np.arange(nq), rope_dims=R)
+        if dt == "f32":
+            assert_close(got[b], ref, fp32=True, tol=2e-5, what="q_norm_rope")
+        else:
+            assert_quantized(decode_act(got[b]), ref, ROW_BF16, rel=2e-6, what="q_norm_rope")
+    # in place gives the same bytes
+    L.q_norm_rope(qd, dev(g) if use_g else None, pos, rope_dims=R)
+    assert np.array_equal(host(qd), got)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_out_rope(L, dt):
+    B, nq, nh, c, pos = 2, 7, 64, 512, [1 << 20, 3]
+    o = act_arr(900, "o", (B, nq, nh, c), 1.0, dt)
+    od = dev(o)
+    L.out_rope(od, pos)
+    got = host(od)
+    assert np.array_equal(got[..., :c - 64], o[..., :c - 64]), "dims outside the rotated block changed"
+    for b in range(B):
+        ref = O.out_rope(decode_act(o[b]), pos[b] + np.arange(nq))
+        if dt == "f32":
+            assert_close(got[b], ref, fp32=True, tol=2e-6, what="out_rope")
+        else:
+            assert_quantized(decode_act(got[b]), ref, ROW_BF16, rel=2e-6, what="out_rope")
+
+
+NRKV_CASES = [
+    # (in layout, out layout, B, n, c, rope_dims, pos0 list, stride, gamma)
+    (ROW_F32, ROW_FP8, 2, 37, 512, 64, [4 * (262144 + 1) - 1, 7], 4, True),   # compressed entries -> cache rows
+    (ROW_BF16, ROW_BF16, 1, 130, 128, 64, [(1 << 20) - 127], 1, True),         # window rows
+    (ROW_F32, ROW_F32, 1, 9, 512, 64, [1023], 128, False),                     # in place, HCA entry stride
+]
+
+
+@pytest.mark.parametrize("case", NRKV_CASES, ids=[str(i) for i in range(len(NRKV_CASES))])
+def test_kv_norm_rope(L, case):
+    il, ol, B, n, c, R, pos0, stride, use_g = case
+    seed = 950 + n + c
+    x = G.normal(seed, "rows", (B, n, c), 1.5)
+    rows, _ = G.store(x, il)
+    g = _gamma(seed, c) if use_g else None
+    rd = dev(rows)
+    inplace = il == ol and il == ROW_F32
+    out = rd if inplace else empty_rows(B * n, ol, c).view(B, n, -1)
+    L.kv_norm_rope(rd, il, c, dev(g) if use_g else None, pos0, stride, out, ol, rope_dims=R)
+    for b in range(B):
+        xin = stored_rows_f64(rows[b], il, c)
+        ref = O.kv_norm_rope(xin, g if use_g else np.ones(c), pos0[b] + stride * np.arange(n), rope_dims=R)
+        got = rows_to_f64(out[b], ol, c)
+        if ol == ROW_F32:
+            assert_close(got, ref, fp32=True, tol=2e-5, what="kv_norm_rope")
+        else:
+            assert_quantized(got, ref, ol, rel=2e-6, what="kv_norm_rope")
