@@ -51,7 +51,12 @@ reason, in the design notes of the repository):
       position; a compressed entry at the position of the newest token it
       pools, m (s + 1) - 1 (HCA: m' (s + 1) - 1);
   R35 the attention output's last 64 dims are rotated by -p (the query's
-      position), so that they carry relative positions.
+      position), so that they carry relative positions;
+  R36 the low-rank latent c^Q and the grouped projection's intermediate z are
+      activations: stored in bf16 between their two products (as the
+      library's GEMMs do), the products themselves exact;
+  R37 output group j (of g) takes the consecutive heads [j nh/g, (j+1) nh/g),
+      flattened head-major, and fills columns [j d_g, (j+1) d_g) of z.
 """
 import numpy as np
 
@@ -234,6 +239,38 @@ def out_rope(o, q_pos, theta=10000.0, rope_dims=64):
     """Output rotation (R35): o [nq, nh, c], last dims rotated by -q_pos."""
     o = np.asarray(o, dtype=np.float64)
     return rope_last(o, -np.asarray(q_pos, dtype=np.float64)[:, None] * np.ones(o.shape[:-1]), theta, rope_dims)
+
+
+def _bf16(x):
+    return _codecs.bf16_round(x)
+
+
+def query_proj(h, W_DQ, W_UQ, W_IUQ, W_w, nh, c, hI, cI):
+    """Low-rank query path (digest 模块 B eq 13-15, 18; R36): c^Q = h W^DQ^T
+    (stored bf16), q = c^Q W^UQ^T, q^I = c^Q W^IUQ^T, w^I = h W^w^T.
+    h [n, d]; weights in the [out, in] layout.  Returns q [n, nh, c],
+    q^I [n, hI, cI] (both before their bf16 storage rounding) and w^I [n, hI]."""
+    h = np.asarray(h, dtype=np.float64)
+    cq = _bf16(h @ np.asarray(W_DQ, dtype=np.float64).T)
+    q = cq @ np.asarray(W_UQ, dtype=np.float64).T
+    qI = cq @ np.asarray(W_IUQ, dtype=np.float64).T
+    wI = h @ np.asarray(W_w, dtype=np.float64).T
+    n = h.shape[0]
+    return q.reshape(n, nh, c), qI.reshape(n, hI, cI), wI
+
+
+def output_proj(o, W_O1, W_O2, g):
+    """Grouped output projection (digest 模块 B, grouped output projection; R36,
+    R37): the nh head outputs o [n, nh, c] form g groups of consecutive heads;
+    group j's flattened rows are projected by W_O1[j] [d_g, (nh/g) c] into
+    columns [j d_g, (j+1) d_g) of z (stored bf16), then out = z W_O2^T with
+    W_O2 [d, g d_g]."""
+    o = np.asarray(o, dtype=np.float64)
+    n, nh, c = o.shape
+    W_O1 = np.asarray(W_O1, dtype=np.float64)
+    hg = nh // g
+    z = np.concatenate([o[:, j * hg:(j + 1) * hg, :].reshape(n, hg * c) @ W_O1[j].T for j in range(g)], axis=1)
+    return _bf16(z) @ np.asarray(W_O2, dtype=np.float64).T
 
 
 def topk_select(I, m, q_pos, k):

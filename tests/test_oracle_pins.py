@@ -402,6 +402,68 @@ def test_entry_positions_match_visibility():
     assert np.array_equal(O.entry_positions(4, 10, 3), [43, 47, 51])
 
 
+# ----------------------------------------------------------------------
+# Low-rank query path and grouped output projection (digest 模块 B eq 13-15,
+# 18 and the grouped output projection; readings R36, R37)
+# ----------------------------------------------------------------------
+
+def test_query_proj_orientation_and_head_layout():
+    """Selector and permutation weights: c^Q = h W^DQ^T picks h's first 4 dims,
+    q = c^Q W^UQ^T permutes them, and the result is split head-major
+    (q[t, h, :] = columns [h c, (h+1) c)).  Integer values stay exact in bf16."""
+    n, d, dc = 3, 8, 4
+    h = np.arange(n * d, dtype=np.float64).reshape(n, d) - 7.0
+    W_DQ = np.eye(dc, d)
+    P = np.eye(4)[[2, 0, 3, 1]]                       # q column i = c^Q column perm[i]
+    W_w = np.zeros((2, d))
+    W_w[0, 5], W_w[1, 7] = 1.0, -2.0
+    q, qI, wI = O.query_proj(h, W_DQ, P, np.eye(4)[::-1], W_w, nh=2, c=2, hI=1, cI=4)
+    cq = h[:, :4]
+    assert np.array_equal(q, cq[:, [2, 0, 3, 1]].reshape(n, 2, 2))
+    assert np.array_equal(qI, cq[:, ::-1].reshape(n, 1, 4))
+    assert np.array_equal(wI, np.stack([h[:, 5], -2.0 * h[:, 7]], axis=1))
+
+
+def test_query_proj_latent_is_stored_bf16():
+    """c^Q = 1 + 2^-10 is stored as 1.0 (below half an ulp of bf16), so
+    q = c^Q * 1 is exactly 1.0, while w^I, formed from h directly, keeps it."""
+    h = np.array([[1.0, 2.0 ** -10]])
+    q, qI, wI = O.query_proj(h, np.ones((1, 2)), np.ones((1, 1)), np.ones((1, 1)), np.ones((1, 2)),
+                             nh=1, c=1, hI=1, cI=1)
+    assert q[0, 0, 0] == 1.0 and qI[0, 0, 0] == 1.0
+    assert wI[0, 0] == 1.0 + 2.0 ** -10
+
+
+def test_output_proj_groups_are_consecutive_heads():
+    """With identity weights the grouped projection is the head-major flatten;
+    zeroing group 1's weights zeroes exactly columns [d_g, 2 d_g), the heads
+    2 and 3."""
+    n, nh, c, g = 2, 4, 2, 2
+    o = np.arange(n * nh * c, dtype=np.float64).reshape(n, nh, c) + 1.0
+    W1 = np.stack([np.eye(4), np.eye(4)])
+    out = O.output_proj(o, W1, np.eye(8), g)
+    assert np.array_equal(out, o.reshape(n, 8))
+    W1[1] = 0.0
+    out = O.output_proj(o, W1, np.eye(8), g)
+    assert np.array_equal(out[:, :4], o[:, :2].reshape(n, 4)) and not out[:, 4:].any()
+
+
+def test_projections_scale_by_powers_of_two_exactly():
+    """bf16 storage commutes with scaling by 2^k, so both paths are exactly
+    2^k-homogeneous."""
+    rng = np.random.default_rng(64)
+    o = rng.standard_normal((3, 4, 8))
+    W1 = rng.standard_normal((2, 5, 16))
+    W2 = rng.standard_normal((6, 10))
+    a = O.output_proj(o, W1, W2, 2)
+    assert np.array_equal(O.output_proj(o * 8.0, W1, W2, 2), a * 8.0)
+    h = rng.standard_normal((3, 8))
+    ws = [rng.standard_normal(sh) for sh in ((4, 8), (6, 4), (4, 4), (2, 8))]
+    q, qI, wI = O.query_proj(h, *ws, nh=2, c=3, hI=2, cI=2)
+    q2, qI2, wI2 = O.query_proj(h * 0.25, *ws, nh=2, c=3, hI=2, cI=2)
+    assert np.array_equal(q2, q * 0.25) and np.array_equal(qI2, qI * 0.25) and np.array_equal(wI2, wI * 0.25)
+
+
 # ======================================================================
 # Top-k selector (digest 模块 B eq 17)
 # ======================================================================
