@@ -207,6 +207,43 @@ def norm_rope_report(layer, steps, stream):
     return rep
 
 
+def projections_report(steps, stream, n=8192, d=4096, d_c=1024, nh=64, c=512, hI=32, cI=64, g=8, d_g=1024):
+    """Time the low-rank query path and the grouped output projection on the
+    bf16 GEMM at the chunk's shapes (weights N(0, 1/fan_in), synthetic)."""
+    import torch
+    from long_context_attention_08_amd import _lib as L
+    bf = torch.bfloat16
+    r = lambda *sh: (torch.randn(sh, device="cuda") * sh[-1] ** -0.5).to(bf)
+    h = torch.randn((n, d), device="cuda").to(bf)
+    W_DQ, W_UQ, W_IUQ, W_w = r(d_c, d), r(nh * c, d_c), r(hI * cI, d_c), r(hI, d)
+    q = torch.empty((n, nh, c), dtype=bf, device="cuda")
+    qI = torch.empty((n, hI, cI), dtype=bf, device="cuda")
+    wI = torch.empty((n, hI), dtype=torch.float32, device="cuda")
+    wsq = torch.empty(L.query_proj_workspace_size(n, d_c), dtype=torch.uint8, device="cuda")
+    o = torch.randn((n, nh, c), device="cuda").to(bf)
+    W1, W2 = r(g, d_g, nh // g * c), r(d, g * d_g)
+    out = torch.empty((n, d), dtype=bf, device="cuda")
+    wso = torch.empty(L.output_proj_workspace_size(n, g, d_g), dtype=torch.uint8, device="cuda")
+    fq = 2.0 * n * (d * d_c + d_c * nh * c + d_c * hI * cI + d * hI)
+    fo = 2.0 * n * (nh * c * d_g + g * d_g * d)
+    calls = {"query_proj": (lambda: L.query_proj(h, W_DQ, W_UQ, W_IUQ, W_w, nh=nh, c=c, hI=hI, cI=cI, q=q, qI=qI,
+                                                 wI=wI, ws=wsq), fq),
+             "output_proj": (lambda: L.output_proj(o, W1, W2, out, g=g, ws=wso), fo)}
+    rep = {}
+    for name, (f, flop) in calls.items():
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rep[name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK["mfma"], 4)}
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +322,7 @@ def main():
             "roofline": roof, "calls": calls}
     line["fp4_indexer"] = fp4_indexer_report(layer, work["indexer"]["flop"], args.steps, stream)
     line["norm_rope"] = norm_rope_report(layer, args.steps, stream)
+    line["projections"] = projections_report(args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -234,6 +234,47 @@ int dsv4_kv_norm_rope(const void* rows, int in_layout, int64_t B, int64_t n, int
 int dsv4_out_rope(void* o, int o_dtype, int64_t B, int64_t nq, int nh, int c, float theta, int rope_dims,
                   const int64_t* q_pos0, void* stream);
 
+/*
+ * bf16 GEMM, C = A B^T with fp32 accumulation, for the projections around the
+ * core (digest 模块 B: the low-rank query path and the grouped output
+ * projection).  A [M, K] and B [N, K] are bf16, K-contiguous with row strides
+ * lda, ldb (elements, multiples of 8, 16-byte aligned bases); C [M, N] in
+ * c_dtype (F32 or BF16, round to nearest even) with row stride ldc.  batch
+ * products run with element strides stride_a, stride_b, stride_c (multiples
+ * of 8 for A and B when batch > 1).  K a multiple of 64.
+ */
+int dsv4_gemm_bf16_nt(const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
+                      void* C, int c_dtype, int64_t ldc, int64_t stride_c, int64_t M, int64_t N, int64_t K,
+                      int64_t batch, void* stream);
+
+/*
+ * Low-rank query path (digest 模块 B eq 13-15 and 18): for h [n, d] bf16,
+ *   c^Q = h W_DQ^T          [n, d_c], stored bf16 in ws
+ *   q   = c^Q W_UQ^T        [n, nh * c]   bf16  (the heads of MQA)
+ *   q^I = c^Q W_IUQ^T       [n, hI * cI]  bf16  (the indexer heads)
+ *   w^I = h W_w^T           [n, hI]       fp32  (the indexer head weights)
+ * Weights in the [out, in] layout, bf16: W_DQ [d_c, d], W_UQ [nh c, d_c],
+ * W_IUQ [hI cI, d_c], W_w [hI, d].  q, qI or wI may be NULL to skip them (the
+ * HCA layer has no indexer).  d and d_c multiples of 64.  ws: at least
+ * dsv4_query_proj_workspace_size(n, d_c) bytes, 16-byte aligned.
+ */
+size_t dsv4_query_proj_workspace_size(int64_t n, int d_c);
+int dsv4_query_proj(const void* h, int64_t n, int d, const void* W_DQ, int d_c,
+                    const void* W_UQ, int nh, int c, const void* W_IUQ, int hI, int cI, const void* W_w,
+                    void* q, void* qI, float* wI, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped output projection (digest 模块 B): the nh head outputs o [n, nh, c]
+ * form g groups of consecutive heads; group j's rows (nh/g heads, flattened
+ * head-major) are projected by W_O1[j] [d_g, (nh/g) c] into columns
+ * [j d_g, (j+1) d_g) of z [n, g d_g] (stored bf16 in ws), then
+ * out = z W_O2^T [n, d] bf16 with W_O2 [d, g d_g].  All bf16; (nh/g) c and
+ * g d_g multiples of 64.  ws: dsv4_output_proj_workspace_size(n, g, d_g) bytes.
+ */
+size_t dsv4_output_proj_workspace_size(int64_t n, int g, int d_g);
+int dsv4_output_proj(const void* o, int64_t n, int nh, int c, int g, int d_g, const void* W_O1,
+                     const void* W_O2, int d, void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Status text, and the last error message of the calling thread. */
 const char* dsv4_status_string(int status);
 const char* dsv4_last_error(void);

@@ -17,6 +17,8 @@ ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 EXPORTS = [
     "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
     "dsv4_indexer_score_fp4q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
+    "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
+    "dsv4_output_proj_workspace_size", "dsv4_output_proj",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
 ]
@@ -50,6 +52,13 @@ _sig("dsv4_indexer_score_fp4q", _int, [_vp, _int, _vp, _vp, _vp, _i64, _i64, _in
 _sig("dsv4_q_norm_rope", _int, [_vp, _int, _vp, _i64, _i64, _int, _int, _vp, _f32, _f32, _int, _P64, _vp])
 _sig("dsv4_kv_norm_rope", _int, [_vp, _int, _i64, _i64, _int, _vp, _f32, _f32, _int, _P64, _i64, _vp, _int, _vp])
 _sig("dsv4_out_rope", _int, [_vp, _int, _i64, _i64, _int, _int, _f32, _int, _P64, _vp])
+_sig("dsv4_gemm_bf16_nt", _int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _int, _i64, _i64, _i64, _i64, _i64,
+                                 _i64, _vp])
+_sig("dsv4_query_proj_workspace_size", _sz, [_i64, _int])
+_sig("dsv4_query_proj", _int, [_vp, _i64, _int, _vp, _int, _vp, _int, _int, _vp, _int, _int, _vp,
+                               _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("dsv4_output_proj_workspace_size", _sz, [_i64, _int, _int])
+_sig("dsv4_output_proj", _int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
@@ -217,3 +226,48 @@ def out_rope(o, q_pos0, *, theta=10000.0, rope_dims=64, stream=None):
     by -(q_pos0[b] + t)."""
     B, nq, nh, c = o.shape
     _check(lib.dsv4_out_rope(_ptr(o), _act(o), B, nq, nh, c, theta, rope_dims, _host_i64(q_pos0), _stream(stream)))
+
+
+# --------------------------------------------------------------------- projections (bf16 GEMM)
+
+def gemm_bf16_nt(A, B, C, *, batch=1, stride_a=0, stride_b=0, stride_c=0, M=None, N=None, K=None,
+                 lda=None, ldb=None, ldc=None, stream=None):
+    """C = A B^T (bf16 A [M, K], B [N, K], fp32 accumulation, C bf16 or fp32).
+    Shapes default to the tensors' last two dims."""
+    M = A.shape[-2] if M is None else M
+    K = A.shape[-1] if K is None else K
+    N = B.shape[-2] if N is None else N
+    lda = A.shape[-1] if lda is None else lda
+    ldb = B.shape[-1] if ldb is None else ldb
+    ldc = C.shape[-1] if ldc is None else ldc
+    _check(lib.dsv4_gemm_bf16_nt(_ptr(A), lda, stride_a, _ptr(B), ldb, stride_b, _ptr(C), _act(C), ldc, stride_c,
+                                 M, N, K, batch, _stream(stream)))
+
+
+def query_proj_workspace_size(n, d_c):
+    return int(lib.dsv4_query_proj_workspace_size(n, d_c))
+
+
+def query_proj(h, W_DQ, W_UQ, W_IUQ, W_w, *, nh, c, hI, cI, q=None, qI=None, wI=None, ws=None, stream=None):
+    """Low-rank query path: q = (h W_DQ^T) W_UQ^T, q^I = (h W_DQ^T) W_IUQ^T,
+    w^I = h W_w^T.  h [n, d] bf16; outputs q [n, nh, c] / q^I [n, hI, cI] bf16,
+    w^I [n, hI] fp32 (any of them None to skip)."""
+    n, d = h.shape
+    d_c = W_DQ.shape[0]
+    _check(lib.dsv4_query_proj(_ptr(h), n, d, _ptr(W_DQ), d_c, _ptr(W_UQ), nh, c, _ptr(W_IUQ), hI, cI, _ptr(W_w),
+                               _ptr(q), _ptr(qI), _ptr(wI), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(stream)))
+
+
+def output_proj_workspace_size(n, g, d_g):
+    return int(lib.dsv4_output_proj_workspace_size(n, g, d_g))
+
+
+def output_proj(o, W_O1, W_O2, out, *, g, ws=None, stream=None):
+    """Grouped output projection: o [n, nh, c] bf16, W_O1 [g, d_g, (nh/g) c],
+    W_O2 [d, g d_g], out [n, d] bf16."""
+    n, nh, c = o.shape
+    d_g = W_O1.shape[1]
+    d = W_O2.shape[0]
+    _check(lib.dsv4_output_proj(_ptr(o), n, nh, c, g, d_g, _ptr(W_O1), _ptr(W_O2), d, _ptr(out), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))

@@ -357,4 +357,92 @@ int dsv4_out_rope(void* o, int o_dtype, int64_t B, int64_t nq, int nh, int c, fl
   return hip_status(dsv4::launch_q_prep(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+// --------------------------------------------------------------------------- projections (GEMM)
+
+static int gemm_check(const char* fn, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (K % 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: K=%lld (multiple of 64)", fn, (long long)K);
+  if (lda < K || ldb < K || ldc < N) return fail(DSV4_ERR_INVALID_ARG, "%s: leading dimension too small", fn);
+  if (lda % 8 || ldb % 8) return fail(DSV4_ERR_UNSUPPORTED, "%s: lda, ldb must be multiples of 8", fn);
+  if (M == 0 || N == 0) return 0;
+  return check_ptrs16(fn, {{A, "A"}, {B, "B"}, {C, "C"}});
+}
+
+int dsv4_gemm_bf16_nt(const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
+                      void* C, int c_dtype, int64_t ldc, int64_t stride_c, int64_t M, int64_t N, int64_t K,
+                      int64_t batch, void* stream) {
+  const char* fn = "dsv4_gemm_bf16_nt";
+  if (!act_ok(c_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: c_dtype %d", fn, c_dtype);
+  if (batch < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: batch < 0", fn);
+  int r = gemm_check(fn, A, lda, B, ldb, C, ldc, M, N, K);
+  if (r) return r;
+  if (M == 0 || N == 0 || batch == 0) return ok();
+  if (batch > 1 && (stride_a % 8 || stride_b % 8))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: batch strides of A and B must be multiples of 8", fn);
+  dsv4::GemmArgs a{A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, c_dtype == DSV4_F32 ? 1 : 0, M, N, K, batch};
+  return hip_status(dsv4::launch_gemm(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t dsv4_query_proj_workspace_size(int64_t n, int d_c) {
+  return n > 0 && d_c > 0 ? (size_t)n * d_c * 2 : 0;
+}
+
+int dsv4_query_proj(const void* h, int64_t n, int d, const void* W_DQ, int d_c,
+                    const void* W_UQ, int nh, int c, const void* W_IUQ, int hI, int cI, const void* W_w,
+                    void* q, void* qI, float* wI, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_query_proj";
+  if (n < 0 || d <= 0 || d_c <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (n == 0) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool need_cq = q || qI;
+  int r;
+  if (need_cq) {
+    if (ws_bytes < dsv4_query_proj_workspace_size(n, d_c) || !ws)
+      return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes,
+                  dsv4_query_proj_workspace_size(n, d_c));
+    if ((r = gemm_check(fn, h, d, W_DQ, d, ws, d_c, n, d_c, d))) return r;
+    if (q && (nh <= 0 || c <= 0 || (r = gemm_check(fn, ws, d_c, W_UQ, d_c, q, (int64_t)nh * c, n, (int64_t)nh * c, d_c))))
+      return r ? r : fail(DSV4_ERR_INVALID_ARG, "%s: nh, c", fn);
+    if (qI && (hI <= 0 || cI <= 0 ||
+               (r = gemm_check(fn, ws, d_c, W_IUQ, d_c, qI, (int64_t)hI * cI, n, (int64_t)hI * cI, d_c))))
+      return r ? r : fail(DSV4_ERR_INVALID_ARG, "%s: hI, cI", fn);
+  }
+  if (wI && (hI <= 0 || (r = gemm_check(fn, h, d, W_w, d, wI, hI, n, hI, d))))
+    return r ? r : fail(DSV4_ERR_INVALID_ARG, "%s: hI", fn);
+  hipError_t e = hipSuccess;
+  if (need_cq) {
+    e = dsv4::launch_gemm({h, d, 0, W_DQ, d, 0, ws, d_c, 0, 0, n, d_c, d, 1}, s);
+    if (e == hipSuccess && q)
+      e = dsv4::launch_gemm({ws, d_c, 0, W_UQ, d_c, 0, q, (int64_t)nh * c, 0, 0, n, (int64_t)nh * c, d_c, 1}, s);
+    if (e == hipSuccess && qI)
+      e = dsv4::launch_gemm({ws, d_c, 0, W_IUQ, d_c, 0, qI, (int64_t)hI * cI, 0, 0, n, (int64_t)hI * cI, d_c, 1}, s);
+  }
+  if (e == hipSuccess && wI) e = dsv4::launch_gemm({h, d, 0, W_w, d, 0, wI, hI, 0, 1, n, hI, d, 1}, s);
+  return hip_status(e, fn);
+}
+
+size_t dsv4_output_proj_workspace_size(int64_t n, int g, int d_g) {
+  return n > 0 && g > 0 && d_g > 0 ? (size_t)n * g * d_g * 2 : 0;
+}
+
+int dsv4_output_proj(const void* o, int64_t n, int nh, int c, int g, int d_g, const void* W_O1,
+                     const void* W_O2, int d, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_output_proj";
+  if (n < 0 || nh <= 0 || c <= 0 || g <= 0 || d_g <= 0 || d <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (nh % g) return fail(DSV4_ERR_INVALID_ARG, "%s: nh %% g != 0", fn);
+  if (n == 0) return ok();
+  if (ws_bytes < dsv4_output_proj_workspace_size(n, g, d_g) || !ws)
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes,
+                dsv4_output_proj_workspace_size(n, g, d_g));
+  const int64_t kg = (int64_t)(nh / g) * c, zw = (int64_t)g * d_g;
+  int r = gemm_check(fn, o, (int64_t)nh * c, W_O1, kg, ws, zw, n, d_g, kg);
+  if (r) return r;
+  if ((r = gemm_check(fn, ws, zw, W_O2, zw, out, d, n, d, zw))) return r;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dsv4::launch_gemm({o, (int64_t)nh * c, kg, W_O1, kg, (int64_t)d_g * kg, ws, zw, d_g, 0, n, d_g, kg, g}, s);
+  if (e == hipSuccess) e = dsv4::launch_gemm({ws, zw, 0, W_O2, zw, 0, out, d, 0, 0, n, d, zw, 1}, s);
+  return hip_status(e, fn);
+}
+
 }  // extern "C"

@@ -184,22 +184,6 @@ constexpr int TS = 32;           // key slots per tile
 __device__ __align__(16) uint8_t g_zero_row[1024];
 constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LDS
 
-// 16-byte global -> LDS copy of every lane: lane l's bytes from gsrc + OFF land
-// at LDS address lds_base + 16 l (lds_base wave-uniform).  The instruction's
-// immediate offset is added to the LDS address as well as to the global one,
-// so M0 is set to lds_base - OFF (one wait state between the M0 write and the
-// copy that reads it).  Written as a three-instruction asm
-// block (M0 set in the same block) so that the compiler does not track it:
-// the kernel waits for these copies itself (vmcnt) before reading the stage.
-// The instruction has no register results, so nothing is written back into
-// VGPRs while it is in flight.
-template <int OFF>
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  static_assert(OFF >= 0 && OFF < 4096, "global offset is a 13-bit signed immediate");
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
-               : : "v"(gsrc), "s"(lds_base - (uint32_t)OFF), "i"(OFF) : "memory", "m0");
-}
-
 // The copies of one wave for one tile: copy q = wv + NW i (q < NDMA) takes
 // bytes 32 q + 16 G of each lane's row (offset 32 NW i from `base`, which
 // already holds 32 wv + 16 G) into stage bytes [1024 q, 1024 q + 1024).

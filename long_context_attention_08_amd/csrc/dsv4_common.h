@@ -112,6 +112,28 @@ __device__ __forceinline__ uint32_t mx_scale_code(float amax) {
   return (uint32_t)(E < 0 ? 0 : (E > 254 ? 254 : E));
 }
 
+// ------------------------------------------------------------------ global -> LDS copies
+
+// 16-byte global -> LDS copy of every lane: lane l's bytes from gsrc + OFF land
+// at LDS address lds_base + 16 l (lds_base wave-uniform).  The instruction's
+// immediate offset is added to the LDS address as well as to the global one,
+// so M0 is set to lds_base - OFF (one wait state between the M0 write and the
+// copy that reads it).  Written as a three-instruction asm block (M0 set in the
+// same block) so that the compiler does not track it: callers wait for these
+// copies themselves (vmcnt) before reading the destination.  The instruction
+// has no register results, so nothing is written back into VGPRs while it is
+// in flight.
+template <int OFF>
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  static_assert(OFF >= 0 && OFF < 4096, "global offset is a 13-bit signed immediate");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               : : "v"(gsrc), "s"(lds_base - (uint32_t)OFF), "i"(OFF) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
+}
+
 // ------------------------------------------------------------------ generic row access
 
 __host__ __device__ __forceinline__ int row_bytes(int layout, int c) {

@@ -104,6 +104,19 @@ struct KvPrepArgs {
 hipError_t launch_q_prep(const QPrepArgs& a, const int64_t* q_pos0, hipStream_t s);
 hipError_t launch_kv_prep(const KvPrepArgs& a, const int64_t* pos0, hipStream_t s);
 
+// bf16 GEMM C = A B^T, fp32 accumulation (gemm.hip)
+struct GemmArgs {
+  const void* A;        // [M, K] bf16, row stride lda elements
+  int64_t lda, sA;      // sA: batch stride (elements)
+  const void* B;        // [N, K] bf16
+  int64_t ldb, sB;
+  void* C;              // [M, N] bf16 or fp32
+  int64_t ldc, sC;
+  int c_f32;
+  int64_t M, N, K, batch;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
 size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense);
 hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0,
                        bool dense, hipStream_t s);

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 20
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -114,6 +114,23 @@ def test_norm_rope_validation(L):
     h = L.lib.dsv4_out_rope
     assert h(FAKE, 5, 1, 2, 4, 512, 1e4, 64, pos(0), None) == 2                       # dtype
     assert h(FAKE, 1, 1, 2, 4, 512, 1e4, 0, None, None) == 0                          # rope_dims 0 no-op
+
+
+def test_projection_validation(L):
+    f = L.lib.dsv4_gemm_bf16_nt
+    assert f(FAKE, 100, 0, FAKE, 100, 0, FAKE, 1, 64, 0, 64, 64, 100, 1, None) == 2     # K % 64
+    assert f(FAKE, 64, 0, FAKE, 64, 0, FAKE, 1, 32, 0, 64, 64, 64, 1, None) == 1        # ldc < N
+    assert f(FAKE, 68, 0, FAKE, 64, 0, FAKE, 1, 64, 0, 64, 64, 64, 1, None) == 2        # lda % 8
+    assert f(FAKE, 64, 0, FAKE, 64, 0, FAKE, 7, 64, 0, 64, 64, 64, 1, None) == 2        # C dtype
+    assert f(FAKE, 64, 0, FAKE, 64, 0, FAKE, 1, 64, 0, 0, 64, 64, 1, None) == 0         # M = 0 no-op
+    assert L.lib.dsv4_query_proj_workspace_size(8192, 1024) == 8192 * 1024 * 2
+    g = L.lib.dsv4_query_proj
+    assert g(FAKE, 16, 256, FAKE, 128, FAKE, 2, 64, None, 0, 0, None, FAKE, None, None, None, 0, None) == 4
+    assert g(FAKE, 16, 250, FAKE, 128, FAKE, 2, 64, None, 0, 0, None, FAKE, None, None, FAKE, 4096, None) == 2
+    h = L.lib.dsv4_output_proj
+    assert h(FAKE, 16, 6, 64, 4, 64, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == 1   # nh % g
+    assert h(FAKE, 16, 8, 64, 4, 64, FAKE, FAKE, 128, FAKE, FAKE, 10, None) == 4        # workspace
+    assert L.lib.dsv4_output_proj_workspace_size(16, 4, 64) == 16 * 4 * 64 * 2
 
 
 def test_topk_validation(L):

@@ -474,3 +474,68 @@ def test_kv_norm_rope(L, case):
             assert_close(got, ref, fp32=True, tol=2e-5, what="kv_norm_rope")
         else:
             assert_quantized(got, ref, ol, rel=2e-6, what="kv_norm_rope")
+
+
+# ====================================================================== projections (bf16 GEMM)
+
+GEMM_CASES = [
+    # (M, N, K, batch, out dtype, rows checked (None: all))
+    (300, 200, 128, 1, "bf16", None),          # 128 x 128 tiles, ragged in M and N
+    (4096, 4096, 128, 1, "bf16", 96),          # 256 x 256 tiles, XCD tile order
+    (130, 96, 192, 3, "f32", None),            # batched, fp32 output
+    (8192, 32, 256, 1, "f32", 64),             # a skinny output (the indexer head weights)
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[str(i) for i in range(len(GEMM_CASES))])
+def test_gemm_bf16_nt(L, case):
+    import torch
+    M, N, Kd, nb, od, nrows = case
+    seed = 1000 + M + N
+    A = G.to_bf16(G.normal(seed, "extra", (nb, M, Kd)))
+    Bm = G.to_bf16(G.normal(seed + 1, "extra", (nb, N, Kd)))
+    C = torch.empty((nb, M, N), dtype=torch.float32 if od == "f32" else torch.bfloat16, device="cuda")
+    L.gemm_bf16_nt(dev(A), dev(Bm), C, batch=nb, stride_a=M * Kd, stride_b=N * Kd, stride_c=M * N, M=M, N=N, K=Kd)
+    got = host(C)
+    rows = np.arange(M) if nrows is None else np.unique(np.linspace(0, M - 1, nrows).astype(np.int64))
+    for b in range(nb):
+        ref = K.bf16_decode(A[b][rows]) @ K.bf16_decode(Bm[b]).T
+        g = got[b][rows]
+        if od == "f32":
+            assert_close(g, ref, fp32=True, tol=2e-6 * np.sqrt(Kd) * np.abs(ref).max(), what="gemm f32")
+        else:
+            assert_quantized(decode_act(g), ref, ROW_BF16, rel=2e-6, what="gemm bf16")
+
+
+def test_query_proj(L):
+    import torch
+    n, d, dc, nh, c, hI, cI = 200, 256, 128, 2, 128, 2, 64
+    r = lambda st, sh, sd: G.to_bf16(G.normal(1100 + len(sh), st, sh, sd))
+    h = r("H", (n, d), 1.0)
+    W_DQ, W_UQ, W_IUQ, W_w = (r("W_kv", (dc, d), d ** -0.5), r("W_ki", (nh * c, dc), dc ** -0.5),
+                              r("W_hca", (hI * cI, dc), dc ** -0.5), r("extra", (hI, d), d ** -0.5))
+    q = torch.empty((n, nh, c), dtype=torch.bfloat16, device="cuda")
+    qI = torch.empty((n, hI, cI), dtype=torch.bfloat16, device="cuda")
+    wI = torch.empty((n, hI), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.query_proj_workspace_size(n, dc), dtype=torch.uint8, device="cuda")
+    L.query_proj(dev(h), dev(W_DQ), dev(W_UQ), dev(W_IUQ), dev(W_w), nh=nh, c=c, hI=hI, cI=cI, q=q, qI=qI, wI=wI,
+                 ws=ws)
+    rq, rqI, rwI = O.query_proj(*[K.bf16_decode(x) for x in (h, W_DQ, W_UQ, W_IUQ, W_w)], nh=nh, c=c, hI=hI, cI=cI)
+    # the two sides round c^Q to bf16 from fp32 / fp64 sums: a rare one-ulp difference there moves q slightly
+    assert_close(decode_act(host(q)), rq, tol=1e-2, what="q")
+    assert_close(decode_act(host(qI)), rqI, tol=1e-2, what="qI")
+    assert_close(host(wI), rwI, fp32=True, tol=1e-4, what="wI")
+
+
+def test_output_proj(L):
+    import torch
+    n, nh, c, g, dg, d = 130, 8, 64, 4, 64, 192
+    r = lambda st, sh, sd: G.to_bf16(G.normal(1200 + len(sh), st, sh, sd))
+    o = r("o", (n, nh, c), 1.0)
+    W1 = r("W_kv", (g, dg, nh // g * c), (nh // g * c) ** -0.5)
+    W2 = r("W_ki", (d, g * dg), (g * dg) ** -0.5)
+    out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(L.output_proj_workspace_size(n, g, dg), dtype=torch.uint8, device="cuda")
+    L.output_proj(dev(o), dev(W1), dev(W2), out, g=g, ws=ws)
+    ref = O.output_proj(K.bf16_decode(o), K.bf16_decode(W1), K.bf16_decode(W2), g)
+    assert_close(decode_act(host(out)), ref, tol=1e-2, what="output_proj")
