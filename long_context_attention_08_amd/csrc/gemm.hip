@@ -19,7 +19,7 @@ namespace dsv4 {
 constexpr int GK = 64;           // K per tile: 128 bytes of bf16 per row
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int xcd_map) {
+__global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int xcd_map, int GM) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int ASZ = BM * GK * 2, BSZ = BN * GK * 2;      // bytes of one stage
   constexpr int CA = BM / 8 / 4, CB = BN / 8 / 4;           // 1 KB copies per wave and tile
@@ -29,10 +29,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int x
   const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
   const int wm = wv >> 1, wn = wv & 1;
   // tile order: with xcd_map, the 8 XCDs (blocks are dealt round-robin) each
-  // get a contiguous run of tiles, so the tiles sharing A rows share an L2
-  int64_t bid = blockIdx.x;
-  if (xcd_map) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-  const int64_t m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
+  // get a contiguous run of tile numbers; numbers run down groups of GM
+  // tile-rows before moving right.  GM = 8 makes the blocks an XCD runs at once
+  // a patch of about 8 x 4 tiles sharing both A and B tiles in L2 (long K);
+  // GM = 1 is plain row order, whose C writes spread over more HBM channels
+  // when K is short and the kernel is bound by writing C
+  int64_t t = blockIdx.x;
+  if (xcd_map) t = (t & 7) * (gridDim.x >> 3) + (t >> 3);
+  const int64_t tiles_m = gridDim.x / tiles_n;
+  const int64_t grp = t / (GM * tiles_n), first = grp * GM;
+  const int64_t gm = tiles_m - first < GM ? tiles_m - first : GM;
+  const int64_t in = t - grp * GM * tiles_n;
+  const int64_t m0 = (first + in % gm) * BM, n0 = (in / gm) * BN;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + (int64_t)blockIdx.z * a.sA;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + (int64_t)blockIdx.z * a.sB;
 
@@ -92,29 +100,46 @@ __global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int x
       for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(ta + (ra0 + 32 * i) * 128 + ch));
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + (rb0 + 32 * j) * 128 + ch));
+      // the B tile is the MFMA's row operand: each accumulator is a 32 x 32
+      // tile of C^T, so a lane ends up with 4 consecutive columns of C rows
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  // epilogue: lane holds column n = n0 + wn WN + 32 j + col, rows
-  // m0 + wm WM + 32 i + 8 (r/4) + 4 G + r % 4
+  // epilogue: lane holds row m = m0 + wm WM + 32 i + col and, in registers
+  // 4q .. 4q+3, columns n0 + wn WN + 32 j + 8 q + 4 G .. + 3: one 8-byte (bf16)
+  // or 16-byte (fp32) store each when the row is aligned and in range
   uint8_t* C = reinterpret_cast<uint8_t*>(a.C) + (int64_t)blockIdx.z * a.sC * (a.c_f32 ? 4 : 2);
+  const bool vec = (a.ldc & 3) == 0 && ((uintptr_t)C & 15) == 0;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t n = n0 + wn * WN + 32 * j + col;
-    if (n >= a.N) continue;
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm * WM + 32 * i + col;
+    if (m >= a.M) continue;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + 4 * G + (r & 3);
-        if (m >= a.M) continue;
-        if (a.c_f32) reinterpret_cast<float*>(C)[m * a.ldc + n] = acc[i][j][r];
-        else reinterpret_cast<uint16_t*>(C)[m * a.ldc + n] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * WN + 32 * j + 8 * q + 4 * G;
+        const f32x16& v = acc[i][j];
+        if (vec && n + 3 < a.N) {
+          if (a.c_f32)
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * a.ldc + n) =
+                (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          else
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(C) + m * a.ldc + n) =
+                (u32x2){pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3])};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= a.N) break;
+            if (a.c_f32) reinterpret_cast<float*>(C)[m * a.ldc + n + e] = v[4 * q + e];
+            else reinterpret_cast<uint16_t*>(C)[m * a.ldc + n + e] = (uint16_t)f32_to_bf16(v[4 * q + e]);
+          }
+        }
       }
   }
 }
@@ -126,12 +151,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int tn = (int)((a.N + 255) / 256);
     const int64_t tiles = ((a.M + 255) / 256) * tn;
     hipLaunchKernelGGL((gemm_nt<256, 256>), dim3((unsigned)tiles, 1, (unsigned)a.batch), dim3(256), 0, s, a, tn,
-                       tiles % 8 == 0 ? 1 : 0);
+                       tiles % 8 == 0 ? 1 : 0, a.K >= 4096 && tn >= 16 ? 8 : 1);
   } else {
     const int tn = (int)((a.N + 127) / 128);
     const int64_t tiles = ((a.M + 127) / 128) * tn;
     hipLaunchKernelGGL((gemm_nt<128, 128>), dim3((unsigned)tiles, 1, (unsigned)a.batch), dim3(256), 0, s, a, tn,
-                       tiles % 8 == 0 ? 1 : 0);
+                       tiles % 8 == 0 ? 1 : 0, a.K >= 4096 && tn >= 16 ? 8 : 1);
   }
   return hipGetLastError();
 }
