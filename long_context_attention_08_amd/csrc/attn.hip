@@ -851,12 +851,22 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     return win_base + (int64_t)(s - ncomp) * RB;
   };
   // copies of tile `it`: lane l serves stage slot l % 32, which holds key kperm(l % 32)
+  const int kp = kperm(l & 31);
   auto issue = [&](int it, uint8_t* stg) {
-    const int slot = slot_lo + it * TS + kperm(l & 31);
-    int pos;
-    bool win;
-    const uint8_t* rowp = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
-    const uint8_t* base = (rowp ? rowp : dummy) + 16 * G + 32 * wv;
+    const int s0 = slot_lo + it * TS;
+    const uint8_t* rowp;
+    if (s0 + TS <= ncomp && s0 + TS <= slot_hi && (!a.idx || idx_ok)) {
+      // a whole tile of compressed entries (indices already checked): no per-lane tests
+      const int e = a.idx ? s_sidx[s0 + kp - slot_lo] : s0 + kp;
+      rowp = comp_base + (int64_t)e * RB;
+    } else {
+      const int slot = s0 + kp;
+      int pos;
+      bool win;
+      rowp = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
+      rowp = rowp ? rowp : dummy;
+    }
+    const uint8_t* base = rowp + 16 * G + 32 * wv;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + wv * 1024));
     DmaCopies<0, (Cf::NDMA + Cf::NW - 1) / Cf::NW, Cf::NW, Cf::NDMA>::run(base, lds0, wv);

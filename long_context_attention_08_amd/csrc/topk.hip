@@ -162,7 +162,7 @@ struct TopkArgs {
   uint32_t* hoff;    // [rows, nparts, 2] write offsets (winners, bin candidates)
   HsMeta* hmeta;     // [rows]
   uint64_t* hwin;    // [rows, k] winners above the threshold bin
-  uint64_t* hcand;   // [rows, SK_CAP] keys of the threshold bin
+  uint64_t* hcand;   // [rows, HS_CAP] keys of the threshold bin
 };
 
 __device__ __forceinline__ int pow2_ceil(int x) {
@@ -266,14 +266,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_stage2(TopkArgs a, PosTable p
 // ------------------------------------------------------------------ streaming select (k <= 1024)
 
 constexpr int SK_NT = 256;                  // threads per block
-constexpr int SK_U = 4;                     // float4 loads per thread and step
+constexpr int SK_U = 2;                     // float4 loads per thread and step
 constexpr int SK_STEP = SK_NT * 4 * SK_U;   // scores per step
-constexpr int SK_CAP = 8192;                // candidate slots (>= SK_STEP + k)
+// candidate slots of the streaming kernel (>= SK_STEP + k): 28 KB, so that
+// four blocks share a CU; a block's loop is latency-bound (a barrier and a
+// ballot append per step), and more blocks per CU raise the HBM rate
+constexpr int SK_CAP = 3584;
+constexpr int HS_CAP = 8192;                // threshold-bin candidates of the histogram select
 constexpr int SK_BIN = 2048;                // 11-bit digits
 constexpr int SK_KMAX = 1024;
 
-struct SkShared {
-  uint64_t cand[SK_CAP];
+template <int CAP>
+struct SkSharedT {
+  uint64_t cand[CAP];
   union {                                   // the histogram is dead once the gather starts
     uint64_t out[SK_KMAX];
     uint32_t hist[SK_BIN];
@@ -283,6 +288,9 @@ struct SkShared {
   uint32_t cnt, cnt2;
   uint32_t sel_bin, sel_above, sel_cnt;
 };
+using SkShared = SkSharedT<SK_CAP>;     // streaming select
+using HsShared = SkSharedT<HS_CAP>;     // last step of the histogram select
+static_assert(SK_CAP >= SK_STEP + SK_KMAX, "a step must fit next to the k kept candidates");
 
 // Barrier for LDS traffic only (waits for this wave's LDS operations): unlike
 // __syncthreads() it carries no memory fence, so score loads in flight stay
@@ -379,7 +387,8 @@ __device__ __forceinline__ uint32_t sk_scan_excl(uint32_t v, uint32_t* wsum, uin
 }
 
 // the composite T with #{cand[i] >= T, i < n} == need (1 <= need <= n, unique, non-zero)
-__device__ uint64_t sk_select(SkShared& sh, int n, uint32_t need) {
+template <class Sh>
+__device__ uint64_t sk_select(Sh& sh, int n, uint32_t need) {
   uint64_t mn = ~0ull, mx = 0;
   for (int i = threadIdx.x; i < n; i += SK_NT) {
     const uint64_t x = sh.cand[i];
@@ -447,7 +456,8 @@ __device__ uint64_t sk_select(SkShared& sh, int n, uint32_t need) {
 }
 
 // keep the `need` candidates >= T in sh.out (any order); returns through sh.out
-__device__ void sk_gather(SkShared& sh, int n, uint64_t T) {
+template <class Sh>
+__device__ void sk_gather(Sh& sh, int n, uint64_t T) {
   if (threadIdx.x == 0) sh.cnt2 = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += SK_NT) {
@@ -736,7 +746,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_compact(TopkArgs a, PosTable pt,
   const int64_t s0 = (int64_t)p * a.part, s1 = s0 + a.part < nv ? s0 + a.part : nv;
   const float* src = a.scores + grow * a.S;
   uint64_t* win = a.hwin + row * a.k;
-  uint64_t* cand = a.hcand + row * SK_CAP;
+  uint64_t* cand = a.hcand + row * HS_CAP;
   for (int64_t base = s0; base < s1; base += 8 * SK_NT) {
     float x[8];
 #pragma unroll
@@ -754,7 +764,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_compact(TopkArgs a, PosTable pt,
         win[offa + atomicAdd(&na, 1u)] = composite(key, (uint32_t)s);
       } else if (bin == mt.bstar) {
         const uint32_t at = offb + atomicAdd(&nb, 1u);
-        if (at < (uint32_t)SK_CAP) cand[at] = composite(key, (uint32_t)s);
+        if (at < (uint32_t)HS_CAP) cand[at] = composite(key, (uint32_t)s);
       }
     }
   }
@@ -777,22 +787,22 @@ __device__ __forceinline__ void hs_copy(uint64_t* dst, const uint64_t* src, uint
   }
 }
 
-// dynamic LDS: sizeof(SkShared)
+// dynamic LDS: sizeof(HsShared)
 __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
   extern __shared__ __align__(16) uint8_t smem[];
-  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
+  HsShared& sh = *reinterpret_cast<HsShared*>(smem);
   const int64_t row = blockIdx.x;
   int64_t nv;
   const int64_t grow = hs_row(a, pt, b0, row, &nv);
   const HsMeta mt = a.hmeta[row];
   const uint32_t need = mt.need, nab = mt.above;
   const uint32_t needb = need - nab;                 // to take from bin b*
-  const bool spill = mt.inbin > (uint32_t)SK_CAP;
+  const bool spill = mt.inbin > (uint32_t)HS_CAP;
   const float* src = a.scores + grow * a.S;
   const uint64_t pre = (uint64_t)(uint32_t)mt.bstar << 53;   // composites of bin b* start with it
   uint64_t T = ~0ull;
   if (needb > 0 && !spill) {
-    hs_copy(sh.cand, a.hcand + row * SK_CAP, mt.inbin);
+    hs_copy(sh.cand, a.hcand + row * HS_CAP, mt.inbin);
     __syncthreads();
     T = sk_select(sh, (int)mt.inbin, needb);
   } else if (needb > 0) {
@@ -876,7 +886,7 @@ static size_t hs_bytes(int64_t rows, int nparts, int k, size_t* o_suf, size_t* o
   *o_off = o; o = al(o + (size_t)rows * nparts * 2 * 4);
   *o_meta = o; o = al(o + (size_t)rows * sizeof(HsMeta));
   *o_win = o; o = al(o + (size_t)rows * k * 8);
-  *o_cand = o; o = al(o + (size_t)rows * SK_CAP * 8);
+  *o_cand = o; o = al(o + (size_t)rows * HS_CAP * 8);
   return o;
 }
 
@@ -954,7 +964,7 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
     a.hwin = reinterpret_cast<uint64_t*>(w + o_win);
     a.hcand = reinterpret_cast<uint64_t*>(w + o_cand);
     hipError_t e = hipFuncSetAttribute((const void*)topk_h_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(SkShared));
+                                       (int)sizeof(HsShared));
     if (e != hipSuccess) return e;
     for (int64_t b0 = 0; b0 < B; b0 += MAXB) {
       const int nb = (int)(B - b0 < MAXB ? B - b0 : MAXB);
@@ -964,7 +974,7 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
       hipLaunchKernelGGL(topk_h_hist, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
       hipLaunchKernelGGL(topk_h_thresh, dim3(rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
       hipLaunchKernelGGL(topk_h_compact, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
-      hipLaunchKernelGGL(topk_h_finish, dim3(rows), dim3(SK_NT), sizeof(SkShared), s, a, pt, (int)b0);
+      hipLaunchKernelGGL(topk_h_finish, dim3(rows), dim3(SK_NT), sizeof(HsShared), s, a, pt, (int)b0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
