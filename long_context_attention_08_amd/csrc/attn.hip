@@ -953,24 +953,43 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     }
     return sacc;
   };
-  // PV over key half s: lane l's 8-byte transposed read of m-tile mo
+  // PV over key half s: lane l's 8-byte transposed read of m-tile mo.  The
+  // reads run three m-tiles ahead of the conversions and MFMAs (sched_barrier
+  // keeps that order), so an LDS read's latency overlaps three MFMAs instead of
+  // stalling each one; at occupancy 2 there is room for just these registers
   const int lam = l & 15, grp = (l >> 4) & 1;
   auto pv_half = [&](auto chc, const uint8_t* stg, int s, const bf16x8& pf) {
     constexpr int CHW = decltype(chc)::value;
     const int slot8 = 16 * s + 8 * G;              // first of the 8 stage slots of this lane half
     if constexpr (CHW == 0) {
-#pragma unroll
-      for (int mo = 0; mo < MO; ++mo) {            // E4M3 pieces 2 mo + grp
-        const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+      auto rd = [&](int mo) {                      // E4M3 pieces 2 mo + grp
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
             stg + ((2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+      };
+      v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
+#pragma unroll
+      for (int mo = 0; mo < MO; ++mo) {
+        const v2i w = w1;
+        w1 = w2;
+        w2 = w3;
+        if (mo + 3 < MO) w3 = rd(mo + 3);
         acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-#pragma unroll
-      for (int mo = 0; mo < 6; ++mo) {             // E4M3 pieces 16 + 2 mo + grp
-        const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+      auto rd = [&](int mo) {                      // E4M3 pieces 16 + 2 mo + grp
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
             stg + ((16 + 2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+      };
+      v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
+#pragma unroll
+      for (int mo = 0; mo < 6; ++mo) {
+        const v2i w = w1;
+        w1 = w2;
+        w2 = w3;
+        if (mo + 3 < 6) w3 = rd(mo + 3);
         acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int mo = 6; mo < MO; ++mo) {            // bf16 channels 448 + 32 (mo - 6) + 16 grp + lam
