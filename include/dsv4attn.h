@@ -275,6 +275,73 @@ size_t dsv4_output_proj_workspace_size(int64_t n, int g, int d_g);
 int dsv4_output_proj(const void* o, int64_t n, int nh, int c, int g, int d_g, const void* W_O1,
                      const void* W_O2, int d, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Streaming cache maintenance for decode (digest 模块 F: every compressed
+ * entry is persisted and a reused prefix computes only its incomplete
+ * trailing block again; the uncompressed window rows are cached, checkpointed
+ * or recomputed.  Pooling as dsv4_csa_compress / dsv4_hca_compress: 模块 B
+ * eq 9-12, 模块 C eq 20-23; blog 第一阶段 for the b-window).
+ *
+ * State: per sequence a caller-owned buffer of dsv4_stream_state_bytes()
+ * bytes (sequence b at state + b * that size), holding the projected rows of
+ * the tokens the next entries still need: R slots (R = 2m with overlap = 1,
+ * CSA: the current block and the previous one, whose b-rows the next entry
+ * pools; R = m with overlap = 0, HCA), slot x mod R holding position x.
+ * dsv4_stream_state_reset() marks every slot empty (a fill kernel, so it can
+ * sit in a captured graph).
+ */
+size_t dsv4_stream_state_bytes(int overlap, int m, int c);
+int dsv4_stream_state_reset(void* state, int64_t B, int overlap, int m, int c, void* stream);
+
+/* RMSNorm and partial RoPE applied to a row before it is packed (as in
+ * dsv4_kv_norm_rope).  norm 0 skips the RMSNorm; rope_dims 0 the rotation. */
+typedef struct {
+  int norm;             /* 1: x / sqrt(mean(x^2) + eps) * gamma */
+  const float* gamma;   /* [c] device, or NULL for 1 */
+  float eps;            /* >= 0 */
+  int rope_dims;        /* last dims rotated as pairs, multiple of 8, <= min(c, 512) */
+  float theta;          /* > 0 */
+} dsv4_norm_rope_t;
+
+/*
+ * Feed n_new tokens of each of B sequences: H [B, n_new, d] (act_dtype) holds
+ * the hidden states of positions pos0[b] + i (host array, >= 0).  W and bias
+ * as the batch compressors (CSA, overlap = 1: W [4c, d] = W^{aKV} | W^{bKV} |
+ * W^{aZ} | W^{bZ}, bias [2, m, c]; HCA, overlap = 0: W [2c, d], bias [m, c]).
+ * For every token, in order:
+ *   - its projected row goes to its state slot;
+ *   - its C^a (CSA) / C (HCA) row, normalised and rotated at its position
+ *     when nr != NULL, is packed into the window ring when ring != NULL:
+ *     ring [B, 2 ring_w, row] in ring_layout (F32, BF16, FP8_ROPE_BF16), rows
+ *     x mod ring_w and x mod ring_w + ring_w.  The attention calls read it as
+ *     kv_win with W = 2 ring_w and win_pos0[b] = dsv4_swa_ring_pos0(p, ring_w)
+ *     for a query at p, provided n_win <= ring_w;
+ *   - if it completes block s (position m (s + 1) - 1) and
+ *     emit_from[b] <= s < S (emit_from: host array, or NULL for 0), entry s
+ *     is pooled from the state, normalised and rotated at position
+ *     m (s + 1) - 1 when nr != NULL, and packed into cache[b, s] (cache
+ *     [B, S, row] in cache_layout; MXFP4 also cache_scales [B, S, c/32];
+ *     cache NULL: no entries).
+ * Resuming after P persisted tokens: reset the state, then feed positions
+ * from m floor(P/m) (HCA) or m max(floor(P/m) - 1, 0) (CSA: the b-window)
+ * with emit_from = floor(P/m).  An entry whose rows were not all fed is written as
+ * the layout's NaN (F32 / BF16 NaN, E4M3 0x7F, MXFP4 scale 0xFF).
+ * c even and <= 512 (FP8 rows: c >= 64, c % 16 == 0; MXFP4: c % 32 == 0);
+ * bf16 needs d % 8 == 0.  ws: dsv4_stream_workspace_size() bytes, 16-byte
+ * aligned.  Results for a sequence do not depend on B or on the other rows.
+ */
+size_t dsv4_stream_workspace_size(int64_t B, int64_t n_new, int64_t d, int overlap, int c);
+int dsv4_stream_compress(const void* H, int64_t B, int64_t n_new, int64_t d, int act_dtype,
+                         const void* W, const float* bias, int overlap, int m, int c,
+                         const int64_t* pos0, const int64_t* emit_from, void* state,
+                         void* cache, void* cache_scales, int cache_layout, int64_t S,
+                         void* ring, int64_t ring_w, int ring_layout, const dsv4_norm_rope_t* nr,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Position held by row 0 of a window ring whose newest position is p_last:
+ * floor((p_last - ring_w + 1) / ring_w) * ring_w (may be negative).  Host only. */
+int64_t dsv4_swa_ring_pos0(int64_t p_last, int64_t ring_w);
+
 /* Status text, and the last error message of the calling thread. */
 const char* dsv4_status_string(int status);
 const char* dsv4_last_error(void);

@@ -21,6 +21,8 @@ EXPORTS = [
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
+    "dsv4_stream_state_bytes", "dsv4_stream_state_reset", "dsv4_stream_workspace_size",
+    "dsv4_stream_compress", "dsv4_swa_ring_pos0",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -67,6 +69,20 @@ _sig("dsv4_sparse_mqa_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int,
 _sig("dsv4_hca_dense_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _int,
                                   _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
 
+
+
+class NormRope(ctypes.Structure):
+    """dsv4_norm_rope_t: RMSNorm and partial RoPE before a row is packed."""
+    _fields_ = [("norm", _int), ("gamma", _vp), ("eps", _f32), ("rope_dims", _int), ("theta", _f32)]
+
+
+_sig("dsv4_stream_state_bytes", _sz, [_int, _int, _int])
+_sig("dsv4_stream_state_reset", _int, [_vp, _i64, _int, _int, _int, _vp])
+_sig("dsv4_stream_workspace_size", _sz, [_i64, _i64, _i64, _int, _int])
+_sig("dsv4_stream_compress", _int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _int, _int, _int, _P64, _P64, _vp,
+                                    _vp, _vp, _int, _i64, _vp, _i64, _int, ctypes.POINTER(NormRope),
+                                    _vp, _sz, _vp])
+_sig("dsv4_swa_ring_pos0", _i64, [_i64, _i64])
 
 class Dsv4Error(RuntimeError):
     def __init__(self, status, msg):
@@ -271,3 +287,45 @@ def output_proj(o, W_O1, W_O2, out, *, g, ws=None, stream=None):
     d = W_O2.shape[0]
     _check(lib.dsv4_output_proj(_ptr(o), n, nh, c, g, d_g, _ptr(W_O1), _ptr(W_O2), d, _ptr(out), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+# --------------------------------------------------------------------- streaming cache maintenance (decode)
+
+def stream_state_bytes(overlap, m, c):
+    """Bytes of one sequence's streaming-compressor state."""
+    return int(lib.dsv4_stream_state_bytes(overlap, m, c))
+
+
+def stream_state_reset(state, B, overlap, m, c, *, stream=None):
+    """Mark every slot of B sequences' states empty."""
+    _check(lib.dsv4_stream_state_reset(_ptr(state), B, overlap, m, c, _stream(stream)))
+
+
+def stream_workspace_size(B, n_new, d, overlap, c):
+    return int(lib.dsv4_stream_workspace_size(B, n_new, d, overlap, c))
+
+
+def swa_ring_pos0(p_last, ring_w):
+    """Window-buffer position of row 0 of a mirrored ring whose newest row is p_last."""
+    return int(lib.dsv4_swa_ring_pos0(p_last, ring_w))
+
+
+def stream_compress(H, W, bias, overlap, m, c, pos0, state, *, emit_from=None, cache=None, cache_scales=None,
+                    cache_layout=ROW_F32, S=None, ring=None, ring_w=0, ring_layout=ROW_F32, norm=False,
+                    gamma=None, eps=1e-6, rope_dims=0, theta=10000.0, ws=None, stream=None):
+    """Feed H [B, n_new, d] (positions pos0[b] + i) to the streaming compressor
+    of B sequences: completed entries go to cache [B, S, row], every token's
+    C^a / C row to the mirrored ring [B, 2 ring_w, row]."""
+    B, n_new, d = H.shape
+    if S is None:
+        S = cache.shape[1] if cache is not None else 0
+    nr = None
+    if norm or rope_dims:
+        nr = ctypes.byref(NormRope(1 if norm else 0, _ptr(gamma), eps, rope_dims, theta))
+    if ws is None:
+        nbytes = stream_workspace_size(B, n_new, d, overlap, c)
+        ws = _torch().empty(max(16, nbytes), dtype=_torch().uint8, device=H.device)
+    _check(lib.dsv4_stream_compress(_ptr(H), B, n_new, d, _act(H), _ptr(W), _ptr(bias), overlap, m, c,
+                                    _host_i64(pos0), None if emit_from is None else _host_i64(emit_from),
+                                    _ptr(state), _ptr(cache), _ptr(cache_scales), cache_layout, S,
+                                    _ptr(ring), ring_w, ring_layout, nr, _ptr(ws), ws.numel(), _stream(stream)))

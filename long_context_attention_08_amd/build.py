@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libdsv4attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "normrope.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "normrope.hip", "gemm.hip",
+           "stream.hip"]
 ARCH = os.environ.get("DSV4_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -357,6 +357,81 @@ int dsv4_out_rope(void* o, int o_dtype, int64_t B, int64_t nq, int nh, int c, fl
   return hip_status(dsv4::launch_q_prep(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+// --------------------------------------------------------------------------- streaming cache maintenance
+
+size_t dsv4_stream_state_bytes(int overlap, int m, int c) {
+  if ((overlap != 0 && overlap != 1) || m < 1 || c < 1) return 0;
+  return dsv4::stream_state_bytes(overlap, m, c);
+}
+
+int dsv4_stream_state_reset(void* state, int64_t B, int overlap, int m, int c, void* stream) {
+  const char* fn = "dsv4_stream_state_reset";
+  if (B < 0 || m < 1 || m > 1024 || c < 1 || (overlap != 0 && overlap != 1))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (B == 0) return ok();
+  int r = check_ptrs16(fn, {{state, "state"}});
+  if (r) return r;
+  return hip_status(dsv4::launch_stream_reset(state, B, overlap, m, c, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t dsv4_stream_workspace_size(int64_t B, int64_t n_new, int64_t d, int overlap, int c) {
+  if (B <= 0 || n_new <= 0 || d <= 0 || c <= 0 || (overlap != 0 && overlap != 1)) return 0;
+  return dsv4::stream_ws_bytes(B * n_new, overlap, c, d);
+}
+
+int64_t dsv4_swa_ring_pos0(int64_t p_last, int64_t ring_w) {
+  if (ring_w <= 0) return 0;
+  const int64_t x = p_last - ring_w + 1;
+  const int64_t q = x >= 0 ? x / ring_w : -((-x + ring_w - 1) / ring_w);   // floor division
+  return q * ring_w;
+}
+
+int dsv4_stream_compress(const void* H, int64_t B, int64_t n_new, int64_t d, int act_dtype,
+                         const void* W, const float* bias, int overlap, int m, int c,
+                         const int64_t* pos0, const int64_t* emit_from, void* state,
+                         void* cache, void* cache_scales, int cache_layout, int64_t S,
+                         void* ring, int64_t ring_w, int ring_layout, const dsv4_norm_rope_t* nr,
+                         void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_stream_compress";
+  if (B < 0 || n_new < 0 || d < 1 || S < 0 || m < 1 || m > 1024 || (overlap != 0 && overlap != 1))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (c < 2 || c > 512 || c % 2) return fail(DSV4_ERR_UNSUPPORTED, "%s: c=%d (even, <= 512)", fn, c);
+  if (!act_ok(act_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: act_dtype %d", fn, act_dtype);
+  if (act_dtype == DSV4_BF16 && d % 8) return fail(DSV4_ERR_UNSUPPORTED, "%s: bf16 needs d %% 8 == 0", fn);
+  if (cache && !kv_layout_ok(cache_layout, c) && !(cache_layout == DSV4_ROW_MXFP4 && c % 32 == 0))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: cache_layout %d with c=%d", fn, cache_layout, c);
+  if (ring && !kv_layout_ok(ring_layout, c))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: ring_layout %d with c=%d", fn, ring_layout, c);
+  if (ring && ring_w < 1) return fail(DSV4_ERR_INVALID_ARG, "%s: ring_w < 1", fn);
+  if (nr) {
+    int r = rope_args_ok(fn, c, nr->eps, nr->theta, nr->rope_dims);
+    if (r) return r;
+  }
+  if (B == 0 || n_new == 0) return ok();
+  if (!pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: pos0 is NULL", fn);
+  for (int64_t b = 0; b < B; ++b)
+    if (pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: pos0[%lld] < 0", fn, (long long)b);
+  int r = check_ptrs16(fn, {{H, "H"}, {W, "W"}, {state, "state"}, {ws, "ws"}});
+  if (r) return r;
+  if (!bias) return fail(DSV4_ERR_INVALID_ARG, "%s: bias is NULL", fn);
+  if (cache && cache_layout == DSV4_ROW_MXFP4 && !cache_scales)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: cache_scales is NULL", fn);
+  const size_t need = dsv4::stream_ws_bytes(B * n_new, overlap, c, d);
+  if (ws_bytes < need)
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  dsv4::StreamArgs a{};
+  a.H = H; a.act = act_dtype; a.d = d; a.W = W; a.bias = bias;
+  a.nmat = overlap ? 4 : 2; a.c = c; a.m = m; a.overlap = overlap;
+  a.B = B; a.n_new = n_new; a.part = reinterpret_cast<float*>(ws); a.state = state;
+  a.cache = S > 0 ? cache : nullptr; a.cache_scales = reinterpret_cast<uint8_t*>(cache_scales);
+  a.cache_layout = cache_layout; a.S = S;
+  a.ring = ring; a.ring_w = ring_w; a.ring_layout = ring_layout;
+  if (nr) {
+    a.norm = nr->norm ? 1 : 0; a.gamma = nr->gamma; a.eps = nr->eps; a.theta = nr->theta; a.rope_dims = nr->rope_dims;
+  }
+  return hip_status(dsv4::launch_stream(a, pos0, emit_from, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 // --------------------------------------------------------------------------- projections (GEMM)
 
 static int gemm_check(const char* fn, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,

@@ -169,6 +169,19 @@ __device__ __forceinline__ void store_row_elem(uint8_t* row, int layout, int c, 
   else reinterpret_cast<uint16_t*>(row + nf8)[j - nf8] = (uint16_t)f32_to_bf16(v);
 }
 
+// cos / sin of pos * theta^(-2j/R)
+__device__ __forceinline__ void rope_cs(int64_t pos, int j, int R, float theta, float* c, float* s) {
+  const double inv = exp2(-2.0 * (double)j / (double)R * log2((double)theta));
+  double ang = (double)pos * inv;
+  // reduce to [-pi, pi] in fp64 before the fp64 sincos
+  const double twopi = 6.283185307179586476925286766559;
+  ang -= twopi * rint(ang / twopi);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
 // ------------------------------------------------------------------ wave helpers
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -104,6 +104,35 @@ struct KvPrepArgs {
 hipError_t launch_q_prep(const QPrepArgs& a, const int64_t* q_pos0, hipStream_t s);
 hipError_t launch_kv_prep(const KvPrepArgs& a, const int64_t* pos0, hipStream_t s);
 
+// streaming compressors and the window ring (stream.hip)
+struct StreamArgs {
+  const void* H;        // [B, n_new, d]
+  int act;
+  int64_t d;
+  const void* W;        // [nmat * c, d]
+  const float* bias;    // CSA [2, m, c]; HCA [m, c]
+  int nmat, c, m, overlap;
+  int64_t B, n_new;
+  float* part;          // workspace: [KS, B * n_new, nmat * c] projection partials
+  void* state;          // [B] x state_bytes
+  int64_t state_bytes;
+  void* cache;          // [B, S, row] or null
+  uint8_t* cache_scales;
+  int cache_layout;
+  int64_t S;
+  void* ring;           // [B, 2 ring_w, row] or null
+  int64_t ring_w;
+  int ring_layout;
+  int norm;             // RMSNorm (gamma, eps) before the rotation
+  const float* gamma;
+  float eps, theta;
+  int rope_dims;
+};
+size_t stream_state_bytes(int overlap, int m, int c);
+size_t stream_ws_bytes(int64_t rows, int overlap, int c, int64_t d);
+hipError_t launch_stream_reset(void* state, int64_t B, int overlap, int m, int c, hipStream_t s);
+hipError_t launch_stream(const StreamArgs& a, const int64_t* pos0, const int64_t* emit_from, hipStream_t s);
+
 // bf16 GEMM C = A B^T, fp32 accumulation (gemm.hip)
 struct GemmArgs {
   const void* A;        // [M, K] bf16, row stride lda elements

@@ -20,19 +20,6 @@ constexpr int NR_THREADS = 256;
 constexpr int NR_MAXC = 4096;          // widest row (8 passes of 512)
 constexpr int NR_MAXR = 512;           // widest rotated block (R/2 <= 256 pairs)
 
-// cos / sin of pos * theta^(-2j/R)
-__device__ __forceinline__ void rope_cs(int64_t pos, int j, int R, float theta, float* c, float* s) {
-  const double inv = exp2(-2.0 * (double)j / (double)R * log2((double)theta));
-  double ang = (double)pos * inv;
-  // reduce to [-pi, pi] in fp64 before the fp64 sincos
-  const double twopi = 6.283185307179586476925286766559;
-  ang -= twopi * rint(ang / twopi);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
-}
-
 __device__ __forceinline__ void load8(const void* p, int dtype, int64_t off, float (&x)[8]) {
   if (dtype == ACT_F32) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + off);

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 20
+    assert len(syms) == 25
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -166,3 +166,42 @@ def test_attention_validation(L):
     st = g(FAKE, 1, 2, 1, 64, 512, FAKE, 2, 8192, 128, FAKE, 128, pos((1 << 20) - 127, (1 << 20) - 127), 128,
            pos(1 << 20, 1 << 20), None, 1.0, FAKE, None, 0, None)
     assert st in (1, 4)
+
+
+def test_stream_validation(L):
+    f = L.lib.dsv4_stream_compress
+    NR = L._lib.NormRope
+    big = 1 << 30
+
+    def call(B=2, n_new=1, d=128, act=1, overlap=1, m=4, c=128, p0=(0, 0), state=FAKE, cache=FAKE, scales=None,
+             cl=2, S=8, ring=FAKE, ring_w=8, rl=2, nr=None, ws=FAKE, wsb=big):
+        return f(FAKE, B, n_new, d, act, FAKE, FAKE, overlap, m, c, pos(*p0), None, state, cache, scales, cl, S,
+                 ring, ring_w, rl, nr, ws, wsb, None)
+
+    assert call(c=127) == 2 and "c=127" in err(L)
+    assert call(c=1024) == 2
+    assert call(m=0) == 1
+    assert call(overlap=2) == 1
+    assert call(p0=(0, -1)) == 1 and "pos0[1]" in err(L)
+    assert call(wsb=64) == 4
+    assert call(cl=3, scales=None) == 1 and "cache_scales" in err(L)
+    assert call(c=32, cl=0, rl=2) == 2 and "ring_layout" in err(L)
+    assert call(ring_w=0) == 1
+    assert call(nr=ctypes.byref(NR(1, None, 1e-6, 12, 10000.0))) == 2
+    assert call(nr=ctypes.byref(NR(1, None, -1.0, 8, 10000.0))) == 1
+    assert call(state=None) == 1 and "state" in err(L)
+    assert call(act=1, d=12) == 2
+    assert call(B=0) == 0 and call(n_new=0) == 0             # nothing to do: no launch
+    assert L.lib.dsv4_stream_workspace_size(16, 1, 4096, 1, 512) == 8 * 16 * 2048 * 4
+    assert L.lib.dsv4_stream_state_bytes(1, 4, 512) == 256 + 8 * 2048 * 4
+    assert L.lib.dsv4_stream_state_bytes(2, 4, 512) == 0
+    assert L.lib.dsv4_stream_state_reset(FAKE, 2, 1, 0, 64, None) == 1
+    assert L.lib.dsv4_stream_state_reset(FAKE, 0, 1, 4, 64, None) == 0
+
+
+def test_swa_ring_pos0(L):
+    import oracle.stream as OS
+    for ring_w in (1, 3, 8, 128):
+        for p in range(0, 4 * ring_w + 5):
+            assert L.swa_ring_pos0(p, ring_w) == OS.ring_pos0(p, ring_w)
+    assert L.swa_ring_pos0(5, 0) == 0
