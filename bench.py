@@ -244,6 +244,72 @@ def projections_report(steps, stream, n=8192, d=4096, d_c=1024, nh=64, c=512, hI
     return rep
 
 
+def decode_cache_report(steps, stream, B=16, d=4096, c=512, cI=64, m=4, mp=128, ring_w=128):
+    """Time the decode-time cache maintenance of one token for each of B
+    sequences at position 2^20 + 127, which completes a CSA block and an HCA
+    block, so every compressor pools: the CSA KV compressor and the HCA
+    compressor (RMSNorm + partial RoPE, FP8 + bf16-RoPE rows, window rings of
+    2 x 128 rows) and the indexer-key compressor (MXFP4 rows).  The states are
+    first fed the earlier tokens of the blocks.  Algorithmic bytes: the weights
+    and hidden rows read once, the per-channel softmax accumulators of the
+    state read and written, the ring and cache rows written."""
+    import torch
+    from long_context_attention_08_amd import _lib as L
+    bf = torch.bfloat16
+    p = (1 << 20) + 127
+    r = lambda *sh: (torch.randn(sh, device="cuda") * sh[-1] ** -0.5).to(bf)
+    H = torch.randn((B, 1, d), device="cuda").to(bf)
+    g = torch.ones(c, dtype=torch.float32, device="cuda")
+    rb = c + 64
+    comps = {
+        # name: (overlap, m, width, layout, norm + rope, ring)
+        "csa_kv": (1, m, c, L.ROW_FP8_ROPE_BF16, True, True),
+        "indexer_keys": (1, m, cI, L.ROW_MXFP4, False, False),
+        "hca": (0, mp, c, L.ROW_FP8_ROPE_BF16, True, True),
+    }
+    rep = {}
+    total_ms, total_bytes = 0.0, 0
+    for name, (ov, mm, cw, lay, nr, use_ring) in comps.items():
+        nmat = 4 if ov else 2
+        W = r(nmat * cw, d)
+        bias = torch.randn((2, mm, cw) if ov else (mm, cw), device="cuda") * 0.5
+        st = torch.zeros(B * L.stream_state_bytes(ov, mm, cw), dtype=torch.uint8, device="cuda")
+        L.stream_state_reset(st, B, ov, mm, cw)
+        S = (p + 1) // mm
+        row = L.row_bytes(lay, cw)
+        cache = torch.empty((B, S, row), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((B, S, cw // 32), dtype=torch.uint8, device="cuda") if lay == L.ROW_MXFP4 else None
+        ring = torch.empty((B, 2 * ring_w, rb), dtype=torch.uint8, device="cuda") if use_ring else None
+        kw = dict(cache=cache, cache_scales=scales, cache_layout=lay, ring=ring, ring_w=ring_w if use_ring else 0,
+                  ring_layout=lay if use_ring else L.ROW_F32, norm=nr, gamma=g[:cw] if nr else None,
+                  rope_dims=64 if nr else 0)
+        first = p - (2 * mm - 1 if ov else mm - 1)      # the rows the entry pools
+        Hp = torch.randn((B, p - first, d), device="cuda").to(bf)
+        L.stream_compress(Hp, W, bias, ov, mm, cw, [first] * B, st, **kw)
+        ws = torch.empty(max(16, L.stream_workspace_size(B, 1, d, ov, cw)), dtype=torch.uint8, device="cuda")
+        f = lambda: L.stream_compress(H, W, bias, ov, mm, cw, [p] * B, st, ws=ws, **kw)
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = W.numel() * 2 + B * (d * 2 + 2 * L.stream_state_bytes(ov, mm, cw) + row +
+                                      (2 * row if use_ring else 0))
+        rep[name] = {"us": round(ms * 1e3, 2), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(nbytes)}
+        total_ms += ms
+        total_bytes += nbytes
+        del cache, scales, ring, st, W, Hp
+    rep["all_three"] = {"us": round(total_ms * 1e3, 2),
+                        "frac_hbm": round(total_bytes / (total_ms * 1e-3) / 1e9 / PEAK["hbm"], 4)}
+    rep["shape"] = {"sequences": B, "position": p, "d": d, "c": c, "c_I": cI, "m": m, "m_prime": mp}
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +389,7 @@ def main():
     line["fp4_indexer"] = fp4_indexer_report(layer, work["indexer"]["flop"], args.steps, stream)
     line["norm_rope"] = norm_rope_report(layer, args.steps, stream)
     line["projections"] = projections_report(args.steps, stream)
+    line["decode_cache"] = decode_cache_report(args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
     print(json.dumps(line), flush=True)

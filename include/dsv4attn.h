@@ -283,12 +283,13 @@ int dsv4_output_proj(const void* o, int64_t n, int nh, int c, int g, int d_g, co
  * eq 9-12, 模块 C eq 20-23; blog 第一阶段 for the b-window).
  *
  * State: per sequence a caller-owned buffer of dsv4_stream_state_bytes()
- * bytes (sequence b at state + b * that size), holding the projected rows of
- * the tokens the next entries still need: R slots (R = 2m with overlap = 1,
- * CSA: the current block and the previous one, whose b-rows the next entry
- * pools; R = m with overlap = 0, HCA), slot x mod R holding position x.
- * dsv4_stream_state_reset() marks every slot empty (a fill kernel, so it can
- * sit in a captured graph).
+ * bytes (sequence b at state + b * that size): per channel an online-softmax
+ * accumulator (running maximum, sum of weights, weighted sum) of the entry of
+ * the current block and, with overlap = 1 (CSA), one of the next entry's
+ * b-part (the current block's b-rows), each tagged with its entry and the
+ * number of rows it holds.  overlap = 0 is HCA (no b-window).
+ * dsv4_stream_state_reset() marks both accumulators empty (a fill kernel, so
+ * it can sit in a captured graph).
  */
 size_t dsv4_stream_state_bytes(int overlap, int m, int c);
 int dsv4_stream_state_reset(void* state, int64_t B, int overlap, int m, int c, void* stream);
@@ -309,7 +310,7 @@ typedef struct {
  * as the batch compressors (CSA, overlap = 1: W [4c, d] = W^{aKV} | W^{bKV} |
  * W^{aZ} | W^{bZ}, bias [2, m, c]; HCA, overlap = 0: W [2c, d], bias [m, c]).
  * For every token, in order:
- *   - its projected row goes to its state slot;
+ *   - its logits and values enter the accumulators;
  *   - its C^a (CSA) / C (HCA) row, normalised and rotated at its position
  *     when nr != NULL, is packed into the window ring when ring != NULL:
  *     ring [B, 2 ring_w, row] in ring_layout (F32, BF16, FP8_ROPE_BF16), rows
@@ -318,14 +319,16 @@ typedef struct {
  *     for a query at p, provided n_win <= ring_w;
  *   - if it completes block s (position m (s + 1) - 1) and
  *     emit_from[b] <= s < S (emit_from: host array, or NULL for 0), entry s
- *     is pooled from the state, normalised and rotated at position
+ *     (the accumulated weighted sum over the sum of weights, per channel),
+ *     normalised and rotated at position
  *     m (s + 1) - 1 when nr != NULL, and packed into cache[b, s] (cache
  *     [B, S, row] in cache_layout; MXFP4 also cache_scales [B, S, c/32];
  *     cache NULL: no entries).
  * Resuming after P persisted tokens: reset the state, then feed positions
  * from m floor(P/m) (HCA) or m max(floor(P/m) - 1, 0) (CSA: the b-window)
- * with emit_from = floor(P/m).  An entry whose rows were not all fed is written as
- * the layout's NaN (F32 / BF16 NaN, E4M3 0x7F, MXFP4 scale 0xFF).
+ * with emit_from = floor(P/m).  An entry whose rows were not all fed since
+ * the reset is written as the layout's NaN (F32 / BF16 NaN, E4M3 0x7F, MXFP4
+ * scale 0xFF).
  * c even and <= 512 (FP8 rows: c >= 64, c % 16 == 0; MXFP4: c % 32 == 0);
  * bf16 needs d % 8 == 0.  ws: dsv4_stream_workspace_size() bytes, 16-byte
  * aligned.  Results for a sequence do not depend on B or on the other rows.

@@ -4,21 +4,24 @@
 // uncompressed window rows are cached, checkpointed or recomputed; 模块 B eq 9-12
 // and 模块 C eq 20-23 for the pooling; jsqmd blog 第一阶段 for the b-window).
 //
-// State of one sequence: a ring of R slots (R = 2m for CSA: the current block
-// and the one before it, whose b-rows the next entry pools; R = m for HCA),
-// slot x mod R holding the projected fp32 row [C^a | C^b | Z^a | Z^b] (CSA) or
-// [C | Z] (HCA) of position x, tagged with x.
+// State of one sequence: per channel an online-softmax accumulator (running
+// maximum, sum of weights, weighted sum) of the entry of the current block
+// and, for CSA, one for the b-part of the next entry (the current block's
+// b-rows), each tagged with its entry and the number of rows it holds.  An
+// entry pools the same rows with the same weights as the batch compressor;
+// only the order of the exponentials differs.
 //
 // A call runs two kernels:
 //   1. the projection P = H W^T of the B * n_new new rows, split along d into
 //      KS slices whose fp32 partials go to the workspace (KS depends on the
 //      shapes only, so a row's sum does not depend on the batch);
-//   2. one block per sequence walks its new tokens in order: the partials are
-//      summed in slice order into the token's slot, its C^a / C row is
-//      normalised, rotated and packed into the window ring, and a token that
-//      completes block s pools entry s from the ring slots (tags checked: an
-//      entry whose rows were never fed is written as NaN) and stores it,
-//      normalised, rotated and packed, as cache row s.
+//   2. one block per sequence walks its new tokens in order, thread t owning
+//      channels 2t and 2t + 1 with the accumulators in registers: the
+//      partials are summed in slice order, the C^a / C row is normalised,
+//      rotated and packed into the window ring, the token's logits and values
+//      enter the accumulators, and a token that completes block s stores entry
+//      s (normalised, rotated, packed) as cache row s, or the layout's NaN if
+//      the accumulator did not see every row of the entry.
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
@@ -41,11 +44,19 @@ static void stream_split(int64_t NC, int64_t d, int* ks, int64_t* kslice) {
   *ks = (int)((d + sl - 1) / sl);
 }
 
+// state: [meta 256 B][mx | sum | wsum] x c of the current entry, and for CSA
+// the same for the next entry's b-part
+struct StreamMeta {
+  int64_t a_entry, b_entry;     // entry the accumulator belongs to (-1: none)
+  int32_t a_na, a_nb, b_cnt;    // a-rows and b-rows in it; b-rows in the next
+  int32_t pad;
+};
+constexpr int SMETA = 256;
+
 size_t stream_state_bytes(int overlap, int m, int c) {
-  const int64_t R = overlap ? 2 * (int64_t)m : m;
-  const int64_t nc = (overlap ? 4 : 2) * (int64_t)c;
-  const size_t tags = (size_t)((R * 8 + 255) / 256 * 256);
-  return ((tags + (size_t)(R * nc * 4)) + 255) / 256 * 256;
+  (void)m;
+  const size_t acc = (size_t)(overlap ? 6 : 3) * (size_t)c * 4;
+  return (SMETA + acc + 255) / 256 * 256;
 }
 
 size_t stream_ws_bytes(int64_t rows, int overlap, int c, int64_t d) {
@@ -178,108 +189,137 @@ __device__ void emit_pair(const StreamArgs& a, float v0, float v1, bool act, int
   }
 }
 
+// online softmax: fold logit L with value v into (mx, sum, wsum)
+__device__ __forceinline__ void acc_add(float& mx, float& sum, float& wsum, float L, float v) {
+  if (L > mx) {
+    const float sc = mx == -INFINITY ? 0.f : __expf(mx - L);
+    sum = fmaf(sum, sc, 1.f);
+    wsum = fmaf(wsum, sc, v);
+    mx = L;
+  } else {
+    const float w = __expf(L - mx);
+    sum += w;
+    wsum = fmaf(w, v, wsum);
+  }
+}
+
 __global__ __launch_bounds__(SU_THREADS) void stream_update(StreamArgs a, PosTable pt, int b0, int64_t M, int ks) {
   __shared__ float red[SU_THREADS / 64];
   const int bl = blockIdx.x;
   const int64_t b = b0 + bl;
   const int t = threadIdx.x, c = a.c, m = a.m;
   const int64_t NC = a.nmat * (int64_t)c;
-  const int R = a.overlap ? 2 * m : m;
   uint8_t* sbase = reinterpret_cast<uint8_t*>(a.state) + b * (int64_t)a.state_bytes;
-  int64_t* tags = reinterpret_cast<int64_t*>(sbase);
-  float* srows = reinterpret_cast<float*>(sbase + (R * 8 + 255) / 256 * 256);
+  StreamMeta* meta = reinterpret_cast<StreamMeta*>(sbase);
+  float* acc = reinterpret_cast<float*>(sbase + SMETA);       // [6 or 3][c]
   const bool act = t < c / 2;
   const int j0 = 2 * t;
   const int crb = row_bytes(a.cache_layout, c), rrb = row_bytes(a.ring_layout, c);
+  // accumulators of channels j0, j0 + 1 (A: current entry, N: next entry's b-part)
+  float amx[2], asum[2], aws[2], nmx[2], nsum[2], nws[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = act ? j0 + h : 0;
+    amx[h] = acc[0 * c + j]; asum[h] = acc[1 * c + j]; aws[h] = acc[2 * c + j];
+    nmx[h] = a.overlap ? acc[3 * c + j] : 0.f;
+    nsum[h] = a.overlap ? acc[4 * c + j] : 0.f;
+    nws[h] = a.overlap ? acc[5 * c + j] : 0.f;
+  }
+  StreamMeta md = *meta;                 // every thread keeps the same copy
+  const float* Ba = a.bias;
+  const float* Bb = a.bias + (int64_t)m * c;
   for (int64_t i = 0; i < a.n_new; ++i) {
-    // the previous token's pooling may still read the slot (and tag) this one overwrites
-    if (i > 0) __syncthreads();
     const int64_t x = pt.q_pos0[bl] + i;
-    const int slot = (int)(x % R);
+    const int64_t s = x / m;
+    const int r = (int)(x % m);
     const int64_t prow = b * a.n_new + i;                // row of the projection
-    // the token's projected row, partials summed in slice order, into its slot
-    float* dst = srows + (int64_t)slot * NC;
-    float raw0 = 0.f, raw1 = 0.f;
-    for (int64_t j = t; j < NC; j += SU_THREADS) {
-      float v = 0.f;
-      for (int k = 0; k < ks; ++k) v += a.part[((int64_t)k * M + prow) * NC + j];
-      dst[j] = v;
-    }
-    if (act) {                                           // C^a / C channels 2t, 2t + 1, recomputed the same way
+    // the token's projected values of this thread's channels, partials summed in slice order
+    float ca[2] = {0.f, 0.f}, cb[2] = {0.f, 0.f}, za[2] = {0.f, 0.f}, zb[2] = {0.f, 0.f};
+    if (act) {
+      const int64_t zoff = a.overlap ? 2 * c : c;
       for (int k = 0; k < ks; ++k) {
-        raw0 += a.part[((int64_t)k * M + prow) * NC + j0];
-        raw1 += a.part[((int64_t)k * M + prow) * NC + j0 + 1];
+        const float* pr = a.part + ((int64_t)k * M + prow) * NC;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ca[h] += pr[j0 + h];
+          za[h] += pr[zoff + j0 + h];
+          if (a.overlap) {
+            cb[h] += pr[c + j0 + h];
+            zb[h] += pr[3 * c + j0 + h];
+          }
+        }
       }
     }
-    if (t == 0) tags[slot] = x;
-    // the slot is read back below (pooling) by other threads of this block:
-    // one workgroup shares the CU's L1, so the barrier's fence suffices
-    __syncthreads();
     if (a.ring) {
       const int64_t rr = x % a.ring_w;
       uint8_t* ring_b = reinterpret_cast<uint8_t*>(a.ring) + b * 2 * a.ring_w * (int64_t)rrb;
-      emit_pair(a, raw0, raw1, act, x, false, ring_b + rr * rrb, nullptr, a.ring_layout, red);
-      emit_pair(a, raw0, raw1, act, x, false, ring_b + (rr + a.ring_w) * rrb, nullptr, a.ring_layout, red);
+      emit_pair(a, ca[0], ca[1], act, x, false, ring_b + rr * rrb, nullptr, a.ring_layout, red);
+      emit_pair(a, ca[0], ca[1], act, x, false, ring_b + (rr + a.ring_w) * rrb, nullptr, a.ring_layout, red);
     }
-    if ((x + 1) % m != 0) continue;
-    const int64_t s = (x + 1) / m - 1;                   // this token completes block s
-    if (s < pt.win_pos0[bl] || s >= a.S || !a.cache) continue;
-    // pool channels 2t, 2t + 1 (R1-R3 of the batch compressor)
-    bool ok = true;
-    for (int r = 0; r < m; ++r) {
-      ok = ok && tags[(m * s + r) % R] == m * s + r;
-      if (a.overlap && s >= 1) ok = ok && tags[(m * (s - 1) + r) % R] == m * (s - 1) + r;
-    }
-    float v[2] = {0.f, 0.f};
-    if (act && ok) {
+    // the current entry: a new block takes over the b-part gathered during the
+    // previous one (CSA); a stream that starts inside a block starts empty
+    if (r == 0 || md.a_entry != s) {
+      const bool carry = a.overlap && r == 0 && md.b_entry == s;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int j = j0 + h;
-        const int64_t zoff = a.overlap ? 2 * c : c;
-        float mx = -INFINITY;
-        for (int r = 0; r < m; ++r) {
-          const float* ra = srows + (int64_t)((m * s + r) % R) * NC;
-          mx = fmaxf(mx, ra[zoff + j] + a.bias[r * c + j]);
-          if (a.overlap && s >= 1) {
-            const float* rb = srows + (int64_t)((m * (s - 1) + r) % R) * NC;
-            mx = fmaxf(mx, rb[3 * c + j] + a.bias[(m + r) * c + j]);
-          }
-        }
-        float num = 0.f, den = 0.f;
-        for (int r = 0; r < m; ++r) {
-          const float* ra = srows + (int64_t)((m * s + r) % R) * NC;
-          const float w = __expf(ra[zoff + j] + a.bias[r * c + j] - mx);
-          num = fmaf(w, ra[j], num);
-          den += w;
-        }
-        if (a.overlap && s >= 1)
-          for (int r = 0; r < m; ++r) {
-            const float* rb = srows + (int64_t)((m * (s - 1) + r) % R) * NC;
-            const float w = __expf(rb[3 * c + j] + a.bias[(m + r) * c + j] - mx);
-            num = fmaf(w, rb[c + j], num);
-            den += w;
-          }
-        v[h] = num / den;
+        amx[h] = carry ? nmx[h] : -INFINITY;
+        asum[h] = carry ? nsum[h] : 0.f;
+        aws[h] = carry ? nws[h] : 0.f;
       }
+      md.a_nb = carry ? md.b_cnt : 0;
+      md.a_na = 0;
+      md.a_entry = s;
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (act) acc_add(amx[h], asum[h], aws[h], za[h] + Ba[r * c + j0 + h], ca[h]);
+    md.a_na += 1;
+    if (a.overlap) {                                     // b-rows of block s serve entry s + 1
+      if (r == 0 || md.b_entry != s + 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) { nmx[h] = -INFINITY; nsum[h] = 0.f; nws[h] = 0.f; }
+        md.b_entry = s + 1;
+        md.b_cnt = 0;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (act) acc_add(nmx[h], nsum[h], nws[h], zb[h] + Bb[r * c + j0 + h], cb[h]);
+      md.b_cnt += 1;
+    }
+    if (r != m - 1) continue;
+    // this token completes block s
+    if (s < pt.win_pos0[bl] || s >= a.S || !a.cache) continue;
+    const bool ok = md.a_na == m && (!a.overlap || s == 0 || md.a_nb == m);
+    const float v0 = ok ? aws[0] / asum[0] : 0.f, v1 = ok ? aws[1] / asum[1] : 0.f;
     uint8_t* crow = reinterpret_cast<uint8_t*>(a.cache) + (b * a.S + s) * (int64_t)crb;
     uint8_t* cscl = a.cache_scales ? a.cache_scales + (b * a.S + s) * (int64_t)(c / 32) : nullptr;
-    emit_pair(a, v[0], v[1], act, m * (s + 1) - 1, !ok, crow, cscl, a.cache_layout, red);
+    emit_pair(a, v0, v1, act, m * (s + 1) - 1, !ok, crow, cscl, a.cache_layout, red);
   }
+  // the accumulators and the bookkeeping back to the state
+  if (act) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = j0 + h;
+      acc[0 * c + j] = amx[h]; acc[1 * c + j] = asum[h]; acc[2 * c + j] = aws[h];
+      if (a.overlap) { acc[3 * c + j] = nmx[h]; acc[4 * c + j] = nsum[h]; acc[5 * c + j] = nws[h]; }
+    }
+  }
+  if (t == 0) *meta = md;
 }
 
-__global__ void stream_reset(uint8_t* state, int64_t B, int64_t state_bytes, int R) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= B * R) return;
-  reinterpret_cast<int64_t*>(state + (t / R) * state_bytes)[t % R] = -1;
+__global__ void stream_reset(uint8_t* state, int64_t B, int64_t state_bytes) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  StreamMeta md;
+  md.a_entry = -1; md.b_entry = -1;
+  md.a_na = 0; md.a_nb = 0; md.b_cnt = 0; md.pad = 0;
+  *reinterpret_cast<StreamMeta*>(state + b * state_bytes) = md;
 }
 
 hipError_t launch_stream_reset(void* state, int64_t B, int overlap, int m, int c, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  const int R = overlap ? 2 * m : m;
-  const int64_t n = B * R;
-  hipLaunchKernelGGL(stream_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<uint8_t*>(state), B, (int64_t)stream_state_bytes(overlap, m, c), R);
+  hipLaunchKernelGGL(stream_reset, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<uint8_t*>(state), B, (int64_t)stream_state_bytes(overlap, m, c));
   return hipGetLastError();
 }
 

@@ -193,7 +193,8 @@ def test_stream_validation(L):
     assert call(act=1, d=12) == 2
     assert call(B=0) == 0 and call(n_new=0) == 0             # nothing to do: no launch
     assert L.lib.dsv4_stream_workspace_size(16, 1, 4096, 1, 512) == 8 * 16 * 2048 * 4
-    assert L.lib.dsv4_stream_state_bytes(1, 4, 512) == 256 + 8 * 2048 * 4
+    assert L.lib.dsv4_stream_state_bytes(1, 4, 512) == 256 + 6 * 512 * 4
+    assert L.lib.dsv4_stream_state_bytes(0, 128, 512) == 256 + 3 * 512 * 4
     assert L.lib.dsv4_stream_state_bytes(2, 4, 512) == 0
     assert L.lib.dsv4_stream_state_reset(FAKE, 2, 1, 0, 64, None) == 1
     assert L.lib.dsv4_stream_state_reset(FAKE, 0, 1, 4, 64, None) == 0
