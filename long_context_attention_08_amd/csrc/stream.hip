@@ -142,13 +142,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Normalise, rotate (position pos) and store channels 2t, 2t + 1 of a row,
-// held by thread t (every thread of the block calls this; `act` marks the
-// threads with t < c / 2).  nan: store the NaN marker of the layout instead.
-__device__ void emit_pair(const StreamArgs& a, float v0, float v1, bool act, int64_t pos, bool nan,
-                          uint8_t* row, uint8_t* scale_row, int layout, float* red) {
-  const int t = threadIdx.x, c = a.c;
-  const int j0 = 2 * t;
+// Normalise and rotate channels 2t, 2t + 1 of a row, held by thread t (every
+// thread of the block calls this; `act` marks the threads with t < c / 2);
+// (cs, sn) is the rotation of this thread's pair at the row's position.
+__device__ void prep_pair(const StreamArgs& a, float& v0, float& v1, bool act, float cs, float sn, float* red) {
+  const int j0 = 2 * threadIdx.x, c = a.c;
   if (a.norm) {
     const float ss = block_sum(act ? fmaf(v0, v0, v1 * v1) : 0.f, red);
     const float inv = 1.0f / sqrtf(ss / (float)c + a.eps);
@@ -157,12 +155,18 @@ __device__ void emit_pair(const StreamArgs& a, float v0, float v1, bool act, int
     v1 *= inv * g1;
   }
   if (act && a.rope_dims > 0 && j0 >= c - a.rope_dims) {
-    float cs, sn;
-    rope_cs(pos, (j0 - (c - a.rope_dims)) >> 1, a.rope_dims, a.theta, &cs, &sn);
     const float u = v0, w = v1;
     v0 = u * cs - w * sn;
     v1 = u * sn + w * cs;
   }
+}
+
+// Store channels 2t, 2t + 1 into a row in `layout` (every thread calls this:
+// MXFP4 blocks reduce over 16 threads).  nan: the NaN marker of the layout.
+__device__ void store_pair(const StreamArgs& a, float v0, float v1, bool act, bool nan, uint8_t* row,
+                           uint8_t* scale_row, int layout) {
+  const int t = threadIdx.x, c = a.c;
+  const int j0 = 2 * t;
   if (layout == ROW_MXFP4) {
     // 16 threads (32 channels) per E8M0 block; every thread takes part in the shuffles
     float amax = act ? fmaxf(fabsf(v0), fabsf(v1)) : 0.f;
@@ -233,10 +237,16 @@ __global__ __launch_bounds__(SU_THREADS) void stream_update(StreamArgs a, PosTab
     const int64_t s = x / m;
     const int r = (int)(x % m);
     const int64_t prow = b * a.n_new + i;                // row of the projection
+    // the rotation of this thread's pair at position x: the window row's, and
+    // the entry's when x completes a block (its newest token is x)
+    float cs = 1.f, sn = 0.f;
+    if (act && a.rope_dims > 0 && j0 >= c - a.rope_dims)
+      rope_cs(x, (j0 - (c - a.rope_dims)) >> 1, a.rope_dims, a.theta, &cs, &sn);
     // the token's projected values of this thread's channels, partials summed in slice order
     float ca[2] = {0.f, 0.f}, cb[2] = {0.f, 0.f}, za[2] = {0.f, 0.f}, zb[2] = {0.f, 0.f};
     if (act) {
       const int64_t zoff = a.overlap ? 2 * c : c;
+#pragma unroll 8
       for (int k = 0; k < ks; ++k) {
         const float* pr = a.part + ((int64_t)k * M + prow) * NC;
 #pragma unroll
@@ -250,11 +260,13 @@ __global__ __launch_bounds__(SU_THREADS) void stream_update(StreamArgs a, PosTab
         }
       }
     }
-    if (a.ring) {
+    if (a.ring) {                                        // both mirrored rows, one preparation
       const int64_t rr = x % a.ring_w;
       uint8_t* ring_b = reinterpret_cast<uint8_t*>(a.ring) + b * 2 * a.ring_w * (int64_t)rrb;
-      emit_pair(a, ca[0], ca[1], act, x, false, ring_b + rr * rrb, nullptr, a.ring_layout, red);
-      emit_pair(a, ca[0], ca[1], act, x, false, ring_b + (rr + a.ring_w) * rrb, nullptr, a.ring_layout, red);
+      float w0 = ca[0], w1 = ca[1];
+      prep_pair(a, w0, w1, act, cs, sn, red);
+      store_pair(a, w0, w1, act, false, ring_b + rr * rrb, nullptr, a.ring_layout);
+      store_pair(a, w0, w1, act, false, ring_b + (rr + a.ring_w) * rrb, nullptr, a.ring_layout);
     }
     // the current entry: a new block takes over the b-part gathered during the
     // previous one (CSA); a stream that starts inside a block starts empty
@@ -290,10 +302,11 @@ __global__ __launch_bounds__(SU_THREADS) void stream_update(StreamArgs a, PosTab
     // this token completes block s
     if (s < pt.win_pos0[bl] || s >= a.S || !a.cache) continue;
     const bool ok = md.a_na == m && (!a.overlap || s == 0 || md.a_nb == m);
-    const float v0 = ok ? aws[0] / asum[0] : 0.f, v1 = ok ? aws[1] / asum[1] : 0.f;
+    float v0 = ok ? aws[0] / asum[0] : 0.f, v1 = ok ? aws[1] / asum[1] : 0.f;
     uint8_t* crow = reinterpret_cast<uint8_t*>(a.cache) + (b * a.S + s) * (int64_t)crb;
     uint8_t* cscl = a.cache_scales ? a.cache_scales + (b * a.S + s) * (int64_t)(c / 32) : nullptr;
-    emit_pair(a, v0, v1, act, m * (s + 1) - 1, !ok, crow, cscl, a.cache_layout, red);
+    prep_pair(a, v0, v1, act, cs, sn, red);             // position m (s + 1) - 1 == x
+    store_pair(a, v0, v1, act, !ok, crow, cscl, a.cache_layout);
   }
   // the accumulators and the bookkeeping back to the state
   if (act) {
