@@ -397,9 +397,204 @@ static bool mfma_ok(const CompressArgs& a, int want_m) {
   return a.act == ACT_BF16 && a.m == want_m && a.c % 32 == 0 && a.d % KSTEP == 0 && a.n > 0;
 }
 
+// the pipelined path: wide rows stored element by element (not MXFP4)
+static bool gemm_path_ok(const CompressArgs& a, int want_m) {
+  return mfma_ok(a, want_m) && a.c % 64 == 0 && a.c >= 256 && a.comp_layout != ROW_MXFP4 &&
+         (!a.raw || a.raw_layout != ROW_MXFP4);
+}
+
+// ------------------------------------------------------------------------
+// Pipelined MFMA path for wide rows (bf16, c % 64 == 0, c >= 256)
+// ------------------------------------------------------------------------
+// Block: 256 tokens x 64 channels, four waves in 2 x 2; wave (wm, wn) holds
+// tokens [128 wm, 128 wm + 128) of the block and channels j0 + 32 wn + [0, 32)
+// in 32x32 tiles of v_mfma_f32_32x32x16_bf16: NT column tiles, one per matrix
+// (CSA: C^a, C^b, Z^a, Z^b; HCA: C, Z), so a lane's column is one channel of
+// every matrix, and its registers 4q .. 4q+3 of a tile are 4 consecutive
+// tokens.  The b-matrices of CSA multiply the H rows 4 tokens earlier, so a
+// lane holds an entry's four a-tokens next to the b-tokens of the block
+// before and pools them in registers; an HCA entry is exactly one wave's 128
+// tokens, pooled within the lane (64 rows) and with its partner lane (the
+// other 64).  H rows T0 - 32 .. T0 + 255 and the block's W rows travel
+// global -> LDS by global_load_lds_dwordx4 into an XOR-swizzled layout (chunk
+// j of row r at j ^ (r & 7)), two stages, one barrier per 64-wide k tile.
+// Staged H rows outside the input are clamped copies that no entry uses.
+constexpr int CG_K = 64;
+constexpr int CG_AR = 288;          // staged H rows: 32 before the tile, 256 in it
+template <bool HCA>
+__global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
+  constexpr int NT = HCA ? 2 : 4;               // column tiles (matrices) per wave
+  constexpr int BN = 2 * 32 * NT;               // staged W rows
+  constexpr int ASZ = CG_AR * CG_K * 2, BSZ = BN * CG_K * 2;
+  constexpr int CA = CG_AR / 32, CB = BN / 32;  // 1 KB copies per wave and k tile
+  __shared__ __align__(16) uint8_t s_a[2 * ASZ];
+  __shared__ __align__(16) uint8_t s_b[2 * BSZ];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int c = a.c;
+  const int64_t T0 = (int64_t)blockIdx.x * 256;    // chunk-local token of tile row 0
+  const int j0 = blockIdx.y * 64;
+  const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
+  // copy k of a tile covers staged rows [8k, 8k + 8): lane L takes row 8k + L/8
+  // and writes LDS chunk L % 8, which holds source chunk (L % 8) ^ (row & 7)
+  const int crow = l >> 3, gch = (l & 7) ^ (crow & 7);
+  const int64_t hrows = a.n_left + a.n;
+  const uint16_t* pa[CA];
+  const uint16_t* pb[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    int64_t hr = a.n_left + T0 - 32 + 8 * (wv + 4 * i) + crow;
+    hr = hr < 0 ? 0 : (hr >= hrows ? hrows - 1 : hr);
+    pa[i] = H + hr * a.d + 8 * gch;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int nb = 8 * (wv + 4 * i) + crow;       // W row: matrix t, channel j0 + 32 wn' + jj
+    const int wnb = nb / (32 * NT), t = (nb / 32) % NT, jj = nb & 31;
+    pb[i] = W + ((int64_t)t * c + j0 + 32 * wnb + jj) * a.d + 8 * gch;
+  }
+  const uint32_t la = lds_addr(s_a), lb = lds_addr(s_b);
+  auto issue = [&](int kt, int st) {
+    const int64_t k0 = (int64_t)kt * CG_K;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) dma16<0>(pa[i] + k0, la + st * ASZ + 1024 * (wv + 4 * i));
+#pragma unroll
+    for (int i = 0; i < CB; ++i) dma16<0>(pb[i] + k0, lb + st * BSZ + 1024 * (wv + 4 * i));
+  };
+
+  f32x16 acc[4][NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
+
+  // fragment rows: a-tokens at staged row (tile row + 32), b-tokens at (tile row + 28)
+  const int ra = 128 * wm + 32 + col, rbr = 128 * wm + 28 + col;   // + 32 i
+  const int swa = ra & 7, swb = rbr & 7;
+  const int rw = 32 * NT * wn + col, sww = rw & 7;                  // + 32 t
+  const int nk = (int)(a.d / CG_K);
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): this wave's copies of tile kt
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();                 // every copy landed; stage st ^ 1 is free
+    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+    const uint8_t* ta = s_a + st * ASZ;
+    const uint8_t* tb = s_b + st * BSZ;
+#pragma unroll
+    for (int kk = 0; kk < CG_K / 16; ++kk) {
+      const int cq = 2 * kk + G;
+      bf16x8 fw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        fw[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + (rw + 32 * t) * 128 + ((cq ^ sww) << 4)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 fa = as_bf16x8(*reinterpret_cast<const u32x4*>(ta + (ra + 32 * i) * 128 + ((cq ^ swa) << 4)));
+        if constexpr (HCA) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fw[t], acc[i][t], 0, 0, 0);
+        } else {
+          const bf16x8 fb = as_bf16x8(*reinterpret_cast<const u32x4*>(ta + (rbr + 32 * i) * 128 + ((cq ^ swb) << 4)));
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((t & 1) ? fb : fa, fw[t], acc[i][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds channel j of every matrix; register 4q + e of M tile i
+  // is tile row 32 i + 8 q + 4 G + e of this wave's 128 tokens
+  const int j = j0 + 32 * wn + col;
+  const int rb = row_bytes(a.comp_layout, c), rrb = row_bytes(a.raw_layout, c);
+  uint8_t* comp = reinterpret_cast<uint8_t*>(a.comp);
+  uint8_t* raw = reinterpret_cast<uint8_t*>(a.raw);
+  const int64_t tw = T0 + 128 * wm;                  // first token of this wave
+  if (a.raw) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t tok = tw + 32 * i + 8 * (r >> 2) + 4 * G + (r & 3);
+        if (tok < a.n) store_row_elem(raw + tok * rrb, a.raw_layout, c, j, acc[i][0][r]);
+      }
+  }
+  if constexpr (HCA) {
+    const int64_t e = tw / 128;                      // this wave's entry
+    if (tw + 128 > a.n) return;                      // an incomplete block emits nothing
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * i + 8 * (r >> 2) + 4 * G + (r & 3);
+        acc[i][1][r] += a.bias[row * c + j];          // logit Z + B
+        mx = fmaxf(mx, acc[i][1][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float w = __expf(acc[i][1][r] - mx);
+        num = fmaf(w, acc[i][0][r], num);
+        den += w;
+      }
+    num += __shfl_xor(num, 32);
+    den += __shfl_xor(den, 32);
+    if (G == 0) store_row_elem(comp + e * rb, a.comp_layout, c, j, num / den);
+  } else {
+    const int64_t n_ent = a.n / 4;
+    float ba[4], bb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { ba[e] = a.bias[e * c + j]; bb[e] = a.bias[(4 + e) * c + j]; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t ent = (tw + 32 * i + 8 * q + 4 * G) / 4;
+        if (ent >= n_ent) continue;
+        const bool has_b = a.block0 + ent >= 1;
+        float La[4], Lb[4], mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          La[e] = acc[i][2][4 * q + e] + ba[e];
+          Lb[e] = acc[i][3][4 * q + e] + bb[e];
+          mx = fmaxf(mx, La[e]);
+          if (has_b) mx = fmaxf(mx, Lb[e]);
+        }
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w = __expf(La[e] - mx);
+          num = fmaf(w, acc[i][0][4 * q + e], num);
+          den += w;
+        }
+        if (has_b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = __expf(Lb[e] - mx);
+            num = fmaf(w, acc[i][1][4 * q + e], num);
+            den += w;
+          }
+        store_row_elem(comp + ent * rb, a.comp_layout, c, j, num / den);
+      }
+  }
+}
+
 hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  if (mfma_ok(a, 4)) {
+  if (gemm_path_ok(a, 4)) {
+    dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)(a.c / 64));
+    hipLaunchKernelGGL(compress_gemm<false>, grid, dim3(256), 0, s, a);
+  } else if (mfma_ok(a, 4)) {
     dim3 grid((unsigned)((a.n + 63) / 64), (unsigned)(a.c / 32));
     hipLaunchKernelGGL(csa_compress_mfma, grid, dim3(256), 0, s, a);
   } else {
@@ -412,7 +607,10 @@ hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
 
 hipError_t launch_hca_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  if (mfma_ok(a, 128)) {
+  if (gemm_path_ok(a, 128)) {
+    dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)(a.c / 64));
+    hipLaunchKernelGGL(compress_gemm<true>, grid, dim3(256), 0, s, a);
+  } else if (mfma_ok(a, 128)) {
     dim3 grid((unsigned)((a.n + 127) / 128), (unsigned)(a.c / 32));
     hipLaunchKernelGGL(hca_compress_mfma, grid, dim3(256), 0, s, a);
   } else {

@@ -42,6 +42,8 @@ CSA_CASES = [
     ("bf16", 96, 64, 64, 4, 5, 4, ROW_MXFP4, ROW_F32),            # MFMA, MXFP4 keys
     ("bf16", 64, 40, 32, 4, 0, 0, ROW_MXFP4, ROW_BF16),           # generic (d % 64 != 0), MXFP4
     ("bf16", 36, 64, 64, 1, 0, 0, ROW_F32, ROW_F32),              # generic, m = 1
+    ("bf16", 520, 256, 256, 4, 3, 4, ROW_FP8, ROW_FP8),           # pipelined 256-token tiles, ragged, left context
+    ("bf16", 300, 192, 512, 4, 0, 0, ROW_BF16, ROW_F32),          # pipelined, entry 0 without b-window
 ]
 
 
@@ -76,6 +78,7 @@ HCA_CASES = [
     ("bf16", 512, 64, 128, 128, ROW_BF16, ROW_BF16),  # MFMA
     ("bf16", 256, 128, 512, 128, ROW_FP8, ROW_FP8),   # MFMA, fp8 rows at c = 512
     ("bf16", 64, 64, 32, 16, ROW_MXFP4, ROW_F32),     # generic, MXFP4
+    ("bf16", 700, 128, 256, 128, ROW_F32, ROW_BF16),  # pipelined 256-token tiles, ragged tail
 ]
 
 
