@@ -397,33 +397,38 @@ static bool mfma_ok(const CompressArgs& a, int want_m) {
   return a.act == ACT_BF16 && a.m == want_m && a.c % 32 == 0 && a.d % KSTEP == 0 && a.n > 0;
 }
 
-// the pipelined path: wide rows stored element by element (not MXFP4)
+// the pipelined path: c a multiple of 64; MXFP4 entries for CSA only
 static bool gemm_path_ok(const CompressArgs& a, int want_m) {
-  return mfma_ok(a, want_m) && a.c % 64 == 0 && a.c >= 256 && a.comp_layout != ROW_MXFP4 &&
+  return mfma_ok(a, want_m) && a.c % 64 == 0 && (want_m == 4 || a.comp_layout != ROW_MXFP4) &&
          (!a.raw || a.raw_layout != ROW_MXFP4);
 }
 
 // ------------------------------------------------------------------------
-// Pipelined MFMA path for wide rows (bf16, c % 64 == 0, c >= 256)
+// Pipelined MFMA path (bf16, c % 64 == 0)
 // ------------------------------------------------------------------------
-// Block: 256 tokens x 64 channels, four waves in 2 x 2; wave (wm, wn) holds
-// tokens [128 wm, 128 wm + 128) of the block and channels j0 + 32 wn + [0, 32)
+// Block: 64 MT tokens x 64 channels, four waves in 2 x 2; wave (wm, wn) holds
+// tokens [32 MT wm, 32 MT (wm + 1)) of the block and channels j0 + 32 wn + [0, 32)
 // in 32x32 tiles of v_mfma_f32_32x32x16_bf16: NT column tiles, one per matrix
 // (CSA: C^a, C^b, Z^a, Z^b; HCA: C, Z), so a lane's column is one channel of
 // every matrix, and its registers 4q .. 4q+3 of a tile are 4 consecutive
 // tokens.  The b-matrices of CSA multiply the H rows 4 tokens earlier, so a
 // lane holds an entry's four a-tokens next to the b-tokens of the block
-// before and pools them in registers; an HCA entry is exactly one wave's 128
-// tokens, pooled within the lane (64 rows) and with its partner lane (the
-// other 64).  H rows T0 - 32 .. T0 + 255 and the block's W rows travel
+// before and pools them in registers (MXFP4 rows: the 32 lanes of a lane half
+// hold one entry's 32 channels, so the E8M0 block scale is a lane reduction);
+// an HCA entry (MT = 4) is exactly one wave's 128 tokens, pooled within the
+// lane (64 rows) and with its partner lane (the other 64).  MT = 4 for wide
+// rows, MT = 1 (64-token blocks, more of them) for narrow ones.  H rows
+// T0 - 32 .. T0 + 64 MT - 1 and the block's W rows travel
 // global -> LDS by global_load_lds_dwordx4 into an XOR-swizzled layout (chunk
 // j of row r at j ^ (r & 7)), two stages, one barrier per 64-wide k tile.
 // Staged H rows outside the input are clamped copies that no entry uses.
 constexpr int CG_K = 64;
-constexpr int CG_AR = 288;          // staged H rows: 32 before the tile, 256 in it
-template <bool HCA>
+template <bool HCA, int MT>
 __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
+  static_assert(!HCA || MT == 4, "an HCA entry is one wave's 128 tokens");
   constexpr int NT = HCA ? 2 : 4;               // column tiles (matrices) per wave
+  constexpr int BM = 64 * MT;                   // tokens per block
+  constexpr int CG_AR = BM + 32;                // staged H rows: 32 before the tile, BM in it
   constexpr int BN = 2 * 32 * NT;               // staged W rows
   constexpr int ASZ = CG_AR * CG_K * 2, BSZ = BN * CG_K * 2;
   constexpr int CA = CG_AR / 32, CB = BN / 32;  // 1 KB copies per wave and k tile
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
   const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
   const int wm = wv >> 1, wn = wv & 1;
   const int c = a.c;
-  const int64_t T0 = (int64_t)blockIdx.x * 256;    // chunk-local token of tile row 0
+  const int64_t T0 = (int64_t)blockIdx.x * BM;     // chunk-local token of tile row 0
   const int j0 = blockIdx.y * 64;
   const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
@@ -464,16 +469,16 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
     for (int i = 0; i < CB; ++i) dma16<0>(pb[i] + k0, lb + st * BSZ + 1024 * (wv + 4 * i));
   };
 
-  f32x16 acc[4][NT];
+  f32x16 acc[MT][NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
 
   // fragment rows: a-tokens at staged row (tile row + 32), b-tokens at (tile row + 28)
-  const int ra = 128 * wm + 32 + col, rbr = 128 * wm + 28 + col;   // + 32 i
+  const int ra = 32 * MT * wm + 32 + col, rbr = 32 * MT * wm + 28 + col;   // + 32 i
   const int swa = ra & 7, swb = rbr & 7;
   const int rw = 32 * NT * wn + col, sww = rw & 7;                  // + 32 t
   const int nk = (int)(a.d / CG_K);
@@ -494,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
       for (int t = 0; t < NT; ++t)
         fw[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(tb + (rw + 32 * t) * 128 + ((cq ^ sww) << 4)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MT; ++i) {
         const bf16x8 fa = as_bf16x8(*reinterpret_cast<const u32x4*>(ta + (ra + 32 * i) * 128 + ((cq ^ swa) << 4)));
         if constexpr (HCA) {
 #pragma unroll
@@ -515,10 +520,10 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
   const int rb = row_bytes(a.comp_layout, c), rrb = row_bytes(a.raw_layout, c);
   uint8_t* comp = reinterpret_cast<uint8_t*>(a.comp);
   uint8_t* raw = reinterpret_cast<uint8_t*>(a.raw);
-  const int64_t tw = T0 + 128 * wm;                  // first token of this wave
+  const int64_t tw = T0 + 32 * MT * wm;              // first token of this wave
   if (a.raw) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t tok = tw + 32 * i + 8 * (r >> 2) + 4 * G + (r & 3);
@@ -556,7 +561,7 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { ba[e] = a.bias[e * c + j]; bb[e] = a.bias[(4 + e) * c + j]; }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t ent = (tw + 32 * i + 8 * q + 4 * G) / 4;
@@ -584,16 +589,32 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
             num = fmaf(w, acc[i][1][4 * q + e], num);
             den += w;
           }
-        store_row_elem(comp + ent * rb, a.comp_layout, c, j, num / den);
+        const float v = num / den;
+        if (a.comp_layout == ROW_MXFP4) {
+          // E8M0 block of channels j0 + 32 wn + [0, 32): the 32 lanes of this lane half
+          float amax = fabsf(v);
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+          const uint32_t E = mx_scale_code(amax);
+          const uint32_t code = E ? f32_to_e2m1(v * ldexpf(1.0f, 127 - (int)E)) : 0u;
+          const uint32_t hi = __shfl_xor(code, 1);
+          if ((col & 1) == 0) comp[ent * rb + (j >> 1)] = (uint8_t)(code | (hi << 4));
+          if (col == 0) a.comp_scales[ent * (c / 32) + (j >> 5)] = (uint8_t)E;
+        } else {
+          store_row_elem(comp + ent * rb, a.comp_layout, c, j, v);
+        }
       }
   }
 }
 
 hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  if (gemm_path_ok(a, 4)) {
+  if (gemm_path_ok(a, 4) && a.c >= 256) {
     dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)(a.c / 64));
-    hipLaunchKernelGGL(compress_gemm<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((compress_gemm<false, 4>), grid, dim3(256), 0, s, a);
+  } else if (gemm_path_ok(a, 4)) {
+    dim3 grid((unsigned)((a.n + 63) / 64), (unsigned)(a.c / 64));
+    hipLaunchKernelGGL((compress_gemm<false, 1>), grid, dim3(256), 0, s, a);
   } else if (mfma_ok(a, 4)) {
     dim3 grid((unsigned)((a.n + 63) / 64), (unsigned)(a.c / 32));
     hipLaunchKernelGGL(csa_compress_mfma, grid, dim3(256), 0, s, a);
@@ -609,7 +630,7 @@ hipError_t launch_hca_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   if (gemm_path_ok(a, 128)) {
     dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)(a.c / 64));
-    hipLaunchKernelGGL(compress_gemm<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((compress_gemm<true, 4>), grid, dim3(256), 0, s, a);
   } else if (mfma_ok(a, 128)) {
     dim3 grid((unsigned)((a.n + 127) / 128), (unsigned)(a.c / 32));
     hipLaunchKernelGGL(hca_compress_mfma, grid, dim3(256), 0, s, a);
