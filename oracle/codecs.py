@@ -189,6 +189,32 @@ def mxfp4_decode(codes, scales):
     return v * np.repeat(X, 32, axis=-1)
 
 
+def mxfp8_encode(x):
+    """[..., c] float64 -> (E4M3 codes [..., c] uint8, E8M0 scales [..., c/32] uint8):
+    OCP MX blocks of 32 consecutive values sharing the scale
+    2^(floor(log2 amax) - 8) (8 = emax of E4M3), elements rounded to nearest
+    even and saturated at +-448; an all-zero block has scale code 0."""
+    x = np.asarray(x, dtype=np.float64)
+    c = x.shape[-1]
+    assert c % 32 == 0
+    blocks = x.reshape(x.shape[:-1] + (c // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1)
+    scale_codes = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    _, e = np.frexp(amax[nz])
+    shared = np.clip((e - 1) - 8, -127, 127)   # floor(log2 amax) - emax(E4M3)
+    scale_codes[nz] = shared + 127
+    X = np.where(nz, np.ldexp(1.0, scale_codes - 127), 1.0)
+    elems = e4m3_encode(blocks / X[..., None])
+    elems[~nz] = 0
+    return elems.reshape(x.shape).astype(np.uint8), scale_codes.astype(np.uint8)
+
+
+def mxfp8_decode(codes, scales):
+    X = e8m0_decode(scales)
+    return e4m3_decode(codes) * np.repeat(X, 32, axis=-1)
+
+
 # --------------------------------------------------------------------------
 # KV row layouts
 # --------------------------------------------------------------------------

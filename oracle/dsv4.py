@@ -40,6 +40,9 @@ reason, in the design notes of the repository):
   R19b the FP4 indexer rounds each query head q^I[t, h] to MXFP4 (blocks of
       32 consecutive c_I dims, the key encoder) before eq 16; the keys are the
       stored MXFP4 rows, decoded;
+  R19c the FP8-query indexer rounds each query head to MXFP8 instead: blocks
+      of 32 consecutive c_I dims share the E8M0 scale 2^(floor(log2 amax) - 8),
+      elements rounded to E4M3 (nearest even, saturating at 448);
   R32 RMSNorm (digest 模块 D, Q/KV normalisation) of a vector x of width c is
       x / sqrt(mean(x^2) + eps) * gamma, eps = 1e-6, gamma per channel; it is
       applied to every query head and to every KV row that core attention
@@ -194,6 +197,15 @@ def indexer_score_fp4q(qI, wI, KI, m, q_pos):
     qI = np.asarray(qI, dtype=np.float64)
     codes, scales = _codecs.mxfp4_encode(qI)
     return indexer_score(_codecs.mxfp4_decode(codes, scales), wI, KI, m, q_pos)
+
+
+def indexer_score_fp8q(qI, wI, KI, m, q_pos):
+    """Index scores with the queries in FP8 (NEXT-3's FP8 variant of the
+    digest 模块 F FP4 indexer): eq 16 over the query heads rounded to MXFP8
+    along c_I (R19c); KI [S, cI] are the decoded MXFP4 keys."""
+    qI = np.asarray(qI, dtype=np.float64)
+    codes, scales = _codecs.mxfp8_encode(qI)
+    return indexer_score(_codecs.mxfp8_decode(codes, scales), wI, KI, m, q_pos)
 
 
 def rmsnorm(x, gamma, eps=1e-6):

@@ -156,3 +156,46 @@ def test_row_layout_fp8_rope_bf16():
     y = K.decode_rows(enc, K.ROW_FP8_ROPE_BF16, 512)
     assert np.array_equal(y[:, :448], K.e4m3_round(x[:, :448]))
     assert np.array_equal(y[:, 448:], K.bf16_round(x[:, 448:]))
+
+
+def test_mxfp8_scale_rule_and_codes():
+    """OCP MX with E4M3 elements: the shared scale is 2^(floor(log2 amax) - 8),
+    so a block maximum of 1.0 is stored as 256 (code 0x78) at scale 2^-8 (code
+    119) and 1.75 as 448 (0x7E); values between 1.75 and 2 times a power of two
+    saturate to the 448 code; an all-zero block has scale code 0."""
+    x = np.zeros(32)
+    x[:4] = [1.0, 0.5, -0.25, 1.0 / 3.0]
+    codes, scales = K.mxfp8_encode(x)
+    assert scales[0] == 119 and codes[0] == 0x78 and codes[1] == 0x70 and codes[2] == 0xE8 and codes[3] == 0x6B
+    y = K.mxfp8_decode(codes, scales)
+    assert y[0] == 1.0 and y[1] == 0.5 and y[2] == -0.25
+    assert y[3] == 0.34375              # 85.33 rounds to 88 on the E4M3 grid (steps of 8 in [64, 128))
+    x[0] = 1.75
+    codes, scales = K.mxfp8_encode(x)
+    assert codes[0] == 0x7E and K.mxfp8_decode(codes, scales)[0] == 1.75
+    x[0] = 1.9
+    codes, scales = K.mxfp8_encode(x)
+    assert codes[0] == 0x7E and K.mxfp8_decode(codes, scales)[0] == 1.75
+    codes, scales = K.mxfp8_encode(np.zeros(64))
+    assert (scales == 0).all() and (codes == 0).all()
+
+
+def test_mxfp8_elements_match_torch_and_round_trip():
+    """Element codes equal torch's float8_e4m3fn cast of x / scale (the scale is
+    a power of two, so the division is exact); the error is at most half an
+    E4M3 step outside the saturation band; decoded values are fixed points."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 128)) * np.exp(rng.uniform(-6, 6, (6, 1)))
+    codes, scales = K.mxfp8_encode(x)
+    X = np.repeat(K.e8m0_decode(scales), 32, axis=-1)
+    ref = torch.from_numpy((x / X).astype(np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes, ref.view(torch.uint8).numpy())
+    y = K.mxfp8_decode(codes, scales)
+    blocks = np.abs(x).reshape(6, 4, 32)
+    band = np.repeat((blocks.max(-1) >= 1.75 * 2.0 ** np.floor(np.log2(blocks.max(-1)))), 32, axis=-1).reshape(6, 128)
+    small = np.abs(x) < 2.0**-6 * X
+    ok = band | small | (np.abs(y - x) <= 2.0**-4 * np.abs(x) * (1 + 1e-12))
+    assert ok.all()
+    c2, s2 = K.mxfp8_encode(y)
+    assert np.array_equal(K.mxfp8_decode(c2, s2), y)

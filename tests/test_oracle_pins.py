@@ -319,6 +319,59 @@ def test_indexer_fp4q_blocks_are_per_head():
                           base[np.isfinite(base)] * 2.0**-7)
 
 
+def test_indexer_fp8q_hand_example():
+    """FP8 queries (R19c) on basis keys.  Head 0, block 0: amax 3 gives scale
+    2^-7; 3 -> 384 (exact), 0.1 -> 12.8 -> 13 on the E4M3 grid, so 0.1015625.
+    Head 1: amax 0.3 gives scale 2^-10; 0.3 -> 307.2 -> 320, so 0.3125."""
+    q = np.zeros((1, 2, 64))
+    q[0, 0, [0, 1]] = [3.0, 0.1]
+    q[0, 1, 0] = 0.3
+    w = np.array([[1.0, 10.0]])
+    I = O.indexer_score_fp8q(q, w, np.eye(64), 1, [63])
+    want = np.zeros(64)
+    want[[0, 1]] = [3.0 + 10 * 0.3125, 0.1015625]
+    assert np.array_equal(I[0], want)
+    assert O.indexer_score(q, w, np.eye(64), 1, [63])[0, 0] == 6.0
+
+
+def test_indexer_fp8q_grid_query_equals_plain_scores():
+    """A query already on the MXFP8 grid (each block holds a +-448 element, so
+    its scale is its own) rounds to itself: the FP8 scores equal eq 16."""
+    rng = np.random.default_rng(96)
+    nq, hI, cI, S = 3, 4, 64, 40
+    codes = rng.integers(0, 0x7F, (nq, hI, cI)).astype(np.uint8)
+    codes = codes | (rng.integers(0, 2, codes.shape).astype(np.uint8) << 7)
+    codes[..., 0] = 0x7E                                   # +448 in block 0
+    codes[..., 32] = 0xFE                                  # -448 in block 1
+    scales = rng.integers(110, 130, (nq, hI, cI // 32)).astype(np.uint8)
+    q = O.codecs.mxfp8_decode(codes, scales)
+    K = rnd(97, S, cI)
+    w = rnd(98, nq, hI)
+    pos = [39, 20, 5]
+    assert np.array_equal(O.indexer_score_fp8q(q, w, K, 1, pos), O.indexer_score(q, w, K, 1, pos))
+
+
+def test_indexer_fp8q_blocks_are_per_head_and_closer_than_fp4():
+    """Power-of-two scaling of one head (and the inverse on its weight) leaves
+    the scores unchanged; on random data FP8 queries stay well closer to the
+    bf16 scores than FP4 queries (not by the full 4x of the finer grid: block
+    maxima between 1.75 and 2 times a power of two saturate at 448)."""
+    q = rnd(99, 2, 3, 64)
+    w = rnd(100, 2, 3)
+    K = rnd(101, 30, 64)
+    pos = [29, 12]
+    base = O.indexer_score_fp8q(q, w, K, 1, pos)
+    q2, w2 = q.copy(), w.copy()
+    q2[:, 1] *= 2.0**20
+    w2[:, 1] *= 2.0**-20
+    assert np.array_equal(O.indexer_score_fp8q(q2, w2, K, 1, pos), base)
+    ref = O.indexer_score(q, w, K, 1, pos)
+    f = np.isfinite(ref)
+    e8 = np.abs(base[f] - ref[f]).max()
+    e4 = np.abs(O.indexer_score_fp4q(q, w, K, 1, pos)[f] - ref[f]).max()
+    assert e8 < e4 / 2
+
+
 # ----------------------------------------------------------------------
 # Q/KV RMSNorm and partial RoPE (digest 模块 D; readings R32-R35)
 # ----------------------------------------------------------------------
