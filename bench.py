@@ -135,19 +135,21 @@ def cpu_baseline(inp, rows_n=16, seed=4):
                       "rows (%.1f s); host cores available %d" % (t_comp, rows_n, t_rows, cores)}
 
 
-def fp4_indexer_report(layer, flop, steps, stream, rows_n=256):
-    """Time the FP4-query indexer on the same chunk and measure the recall of
-    its top-k against the bf16-query top-k on rows_n evenly spaced rows."""
+def quantised_indexer_report(layer, fmt, flop, steps, stream, rows_n=256):
+    """Time the FP4- (fmt 4) or FP8-query (fmt 8) indexer on the same chunk and
+    measure the recall of its top-k against the bf16-query top-k on rows_n
+    evenly spaced rows."""
     import torch
+    call = layer.indexer_fp8q if fmt == 8 else layer.indexer_fp4q
     layer.indexer()
     layer.topk()
     torch.cuda.synchronize()
     ref = layer.idx[0].cpu().numpy()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    layer.indexer_fp4q()
+    call()
     e0.record(stream)
     for _ in range(steps):
-        layer.indexer_fp4q()
+        call()
     e1.record(stream)
     layer.topk()
     torch.cuda.synchronize()
@@ -386,7 +388,8 @@ def main():
                        "c": cfg["c"], "heads": cfg["nh"], "m": cfg["m"], "m_prime": cfg["mp"], "top_k": cfg["k"],
                        "window": cfg["n_win"], "kv": "fp8_e4m3+bf16_rope", "indexer_keys": "mxfp4"},
             "roofline": roof, "calls": calls}
-    line["fp4_indexer"] = fp4_indexer_report(layer, work["indexer"]["flop"], args.steps, stream)
+    line["fp4_indexer"] = quantised_indexer_report(layer, 4, work["indexer"]["flop"], args.steps, stream)
+    line["fp8_indexer"] = quantised_indexer_report(layer, 8, work["indexer"]["flop"], args.steps, stream)
     line["norm_rope"] = norm_rope_report(layer, args.steps, stream)
     line["projections"] = projections_report(args.steps, stream)
     line["decode_cache"] = decode_cache_report(args.steps, stream)

@@ -138,6 +138,19 @@ int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
                             const int64_t* q_pos0, float* scores, void* stream);
 
 /*
+ * Index scores with the queries in FP8: as dsv4_indexer_score_fp4q, but each
+ * query head's 32-value blocks along c_I are quantised to MXFP8 (OCP MX: E8M0
+ * scale 2^(floor(log2 amax) - 8), E4M3 elements rounded to nearest even and
+ * saturated at 448) and multiplied with the stored MXFP4 keys on the scaled
+ * MFMA (E4M3 x E2M1 products exact, sums in fp32).  The FP8 side of the
+ * pages' low-precision indexer (digest 模块 F); same arguments and limits.
+ */
+int dsv4_indexer_score_fp8q(const void* qI, int q_dtype, const float* wI,
+                            const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                            const int64_t* q_pos0, float* scores, void* stream);
+
+/*
  * Top-k selector (digest 模块 B eq 17; blog 第二阶段 Top-k稀疏选择).
  * For each row (b, t): the k visible entries with the largest score; ties go
  * to the lower index; order (score descending, index ascending); fewer than

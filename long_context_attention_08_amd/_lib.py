@@ -16,7 +16,7 @@ ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
     "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
-    "dsv4_indexer_score_fp4q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
+    "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
@@ -50,6 +50,8 @@ _sig("dsv4_hca_compress", _int, [_vp, _i64, _i64, _int, _vp, _vp, _int, _int, _v
 _sig("dsv4_indexer_score", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _i64, _int,
                                   _P64, _vp, _vp])
 _sig("dsv4_indexer_score_fp4q", _int, [_vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _int, _i64, _int,
+                                       _P64, _vp, _vp])
+_sig("dsv4_indexer_score_fp8q", _int, [_vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _int, _i64, _int,
                                        _P64, _vp, _vp])
 _sig("dsv4_q_norm_rope", _int, [_vp, _int, _vp, _i64, _i64, _int, _int, _vp, _f32, _f32, _int, _P64, _vp])
 _sig("dsv4_kv_norm_rope", _int, [_vp, _int, _i64, _i64, _int, _vp, _f32, _f32, _int, _P64, _i64, _vp, _int, _vp])
@@ -174,6 +176,16 @@ def indexer_score_fp4q(qI, wI, k_codes, k_scales, m, q_pos0, scores, *, S=None, 
                                        B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores),
                                        _stream(stream)))
 
+
+
+def indexer_score_fp8q(qI, wI, k_codes, k_scales, m, q_pos0, scores, *, S=None, stream=None):
+    """Index scores with FP8 queries: the query heads are rounded to MXFP8
+    (E4M3) and multiplied with the MXFP4 keys.  Shapes as indexer_score_fp4q."""
+    B, nq, hI, cI = qI.shape
+    S = scores.shape[2] if S is None else S
+    _check(lib.dsv4_indexer_score_fp8q(_ptr(qI), _act(qI), _ptr(wI), _ptr(k_codes), _ptr(k_scales),
+                                       B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores),
+                                       _stream(stream)))
 
 def topk_workspace_size(B, nq, S, k):
     return int(lib.dsv4_topk_workspace_size(B, nq, S, k))

@@ -167,11 +167,9 @@ int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
   return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
-int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
-                            const uint8_t* k_codes, const uint8_t* k_scales,
-                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
-                            const int64_t* q_pos0, float* scores, void* stream) {
-  const char* fn = "dsv4_indexer_score_fp4q";
+static int indexer_quantised(const char* fn, int qfmt, const void* qI, int q_dtype, const float* wI,
+                             const uint8_t* k_codes, const uint8_t* k_scales, int64_t B, int64_t nq, int hI,
+                             int cI, int64_t S, int m, const int64_t* q_pos0, float* scores, void* stream) {
   if (B < 0 || nq < 0 || S < 0 || hI <= 0 || cI <= 0 || m <= 0)
     return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
@@ -184,8 +182,24 @@ int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
   if (r) return r;
   if (!wI) return fail(DSV4_ERR_INVALID_ARG, "%s: wI is NULL", fn);
   if (!k_scales) return fail(DSV4_ERR_INVALID_ARG, "%s: k_scales is NULL", fn);
-  dsv4::IndexerArgs a{qI, q_dtype, wI, k_codes, k_scales, DSV4_ROW_MXFP4, B, nq, hI, cI, S, m, scores, 1};
+  dsv4::IndexerArgs a{qI, q_dtype, wI, k_codes, k_scales, DSV4_ROW_MXFP4, B, nq, hI, cI, S, m, scores, qfmt};
   return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_indexer_score_fp4q(const void* qI, int q_dtype, const float* wI,
+                            const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                            const int64_t* q_pos0, float* scores, void* stream) {
+  return indexer_quantised("dsv4_indexer_score_fp4q", 4, qI, q_dtype, wI, k_codes, k_scales, B, nq, hI, cI, S, m,
+                           q_pos0, scores, stream);
+}
+
+int dsv4_indexer_score_fp8q(const void* qI, int q_dtype, const float* wI,
+                            const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                            const int64_t* q_pos0, float* scores, void* stream) {
+  return indexer_quantised("dsv4_indexer_score_fp8q", 8, qI, q_dtype, wI, k_codes, k_scales, B, nq, hI, cI, S, m,
+                           q_pos0, scores, stream);
 }
 
 // --------------------------------------------------------------------------- top-k

@@ -112,6 +112,13 @@ __device__ __forceinline__ uint32_t mx_scale_code(float amax) {
   return (uint32_t)(E < 0 ? 0 : (E > 254 ? 254 : E));
 }
 
+// E8M0 code of the MXFP8 (E4M3) block scale 2^(floor(log2 amax) - 8)
+__device__ __forceinline__ uint32_t mx8_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 0u;
+  int E = (int)(__float_as_uint(amax) >> 23) - 8;
+  return (uint32_t)(E < 0 ? 0 : (E > 254 ? 254 : E));
+}
+
 // ------------------------------------------------------------------ global -> LDS copies
 
 // 16-byte global -> LDS copy of every lane: lane l's bytes from gsrc + OFF land

@@ -37,7 +37,7 @@ struct IndexerArgs {
   int64_t S;
   int m;
   float* scores;        // [B, nq, S]
-  int q4;               // 1: the queries are quantised to MXFP4 (keys MXFP4 too)
+  int qfmt;             // 0: bf16 / f32 queries; 4 or 8: quantised to MXFP4 or MXFP8 (keys MXFP4)
 };
 
 // Per-batch absolute positions travel to the kernels by value: a launch covers

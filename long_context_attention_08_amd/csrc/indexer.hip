@@ -51,19 +51,23 @@ __global__ void indexer_generic(IndexerArgs a, PosTable pt, int b0, int nb) {
   *out = score;
 }
 
-// value of element j of a query head quantised to MXFP4 (its 32-element block
-// scaled by 2^(floor(log2 amax) - 2), elements rounded to E2M1)
-__device__ __forceinline__ float q4_elem(const IndexerArgs& a, int64_t qbase, int j) {
+// value of element j of a query head quantised to MXFP4 (QF = 4: its
+// 32-element block scaled by 2^(floor(log2 amax) - 2), elements rounded to
+// E2M1) or MXFP8 (QF = 8: scale 2^(floor(log2 amax) - 8), E4M3 elements)
+template <int QF>
+__device__ __forceinline__ float qx_elem(const IndexerArgs& a, int64_t qbase, int j) {
   const int j0 = j & ~31;
   float amax = 0.f;
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_act(a.qI, a.q_dtype, qbase + j0 + i)));
-  const uint32_t E = mx_scale_code(amax);
+  const uint32_t E = QF == 8 ? mx8_scale_code(amax) : mx_scale_code(amax);
   const float inv = __uint_as_float((254u - E) << 23);            // 2^(127 - E)
-  return e2m1_to_f32(f32_to_e2m1(load_act(a.qI, a.q_dtype, qbase + j) * inv)) * e8m0_to_f32(E);
+  const float v = load_act(a.qI, a.q_dtype, qbase + j) * inv;
+  return (QF == 8 ? e4m3_to_f32(f32_to_e4m3(v)) : e2m1_to_f32(f32_to_e2m1(v))) * e8m0_to_f32(E);
 }
 
-// generic path of the FP4-query scores: one thread per (b, t, s)
-__global__ void indexer_generic_q4(IndexerArgs a, PosTable pt, int b0, int nb) {
+// generic path of the FP4- / FP8-query scores: one thread per (b, t, s)
+template <int QF>
+__global__ void indexer_generic_qx(IndexerArgs a, PosTable pt, int b0, int nb) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_b = a.nq * a.S;
   if (gid >= per_b * nb) return;
@@ -78,7 +82,7 @@ __global__ void indexer_generic_q4(IndexerArgs a, PosTable pt, int b0, int nb) {
   for (int h = 0; h < a.hI; ++h) {
     const int64_t qbase = ((b * a.nq + t) * a.hI + h) * a.cI;
     float dot = 0.0f;
-    for (int j = 0; j < a.cI; ++j) dot = fmaf(q4_elem(a, qbase, j), key_elem(a, b, s, j), dot);
+    for (int j = 0; j < a.cI; ++j) dot = fmaf(qx_elem<QF>(a, qbase, j), key_elem(a, b, s, j), dot);
     score = fmaf(a.wI[(b * a.nq + t) * a.hI + h], fmaxf(dot, 0.0f), score);
   }
   *out = score;
@@ -101,24 +105,46 @@ __device__ __forceinline__ void mxfp4_block(const float (&x)[32], u32x4& codes, 
   }
 }
 
+// 32 values -> one MXFP8 block: 32 E4M3 code bytes (element i in byte i; lo
+// holds elements 0..15, hi 16..31) and the E8M0 scale code
+__device__ __forceinline__ void mxfp8_block(const float (&x)[32], u32x4& lo, u32x4& hi, uint32_t& E) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  E = mx8_scale_code(amax);
+  const float inv = __uint_as_float((254u - E) << 23);            // 2^(127 - E)
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w |= f32_to_e4m3(x[4 * d + e] * inv) << (8 * e);
+    if (d < 4) lo[d] = w;
+    else hi[d - 4] = w;
+  }
+}
+
 // ------------------------------------------------------------------ MFMA path
 constexpr int KT = 256;   // keys per LDS tile
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // WQ waves split the queries, 4/WQ waves split the 8 n-tiles of a key tile;
-// each wave holds QPW queries.  Q4: the queries are quantised to MXFP4 in
-// registers and the MXFP4 key tile stays in its stored form in LDS; each
-// 64-channel k-step is one v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands
-// with their E8M0 block scales (lane l of either operand holds row/column
-// l % 32, channels 32 (l / 32) .. + 32, as 16 code bytes plus one scale).
-template <int CI, int KL, int WQ, int QPW, bool Q4>
+// each wave holds QPW queries.  QF = 4 or 8: the queries are quantised to
+// MXFP4 or MXFP8 in registers and the MXFP4 key tile stays in its stored form
+// in LDS; each 64-channel k-step is one v_mfma_scale_f32_32x32x64_f8f6f4 on
+// E2M1 or E4M3 queries against E2M1 keys with their E8M0 block scales.  Lane
+// l of either operand holds row/column l % 32 and the scale of 32-channel block
+// l / 32 of the k-step; an E2M1 lane holds that block's 32 codes in 16 bytes,
+// an E4M3 lane holds channels 16 (l / 32) .. + 15 of block 0 in bytes 0..15 and
+// the same channels of block 1 in bytes 16..31.
+template <int CI, int KL, int WQ, int QPW, int QF>
 __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable pt, int b0,
                                                         int qblocks, int tiles_per_split) {
   constexpr int WK = 4 / WQ;          // waves along the key tile
   constexpr int QB = WQ * QPW;        // queries per block
   constexpr int NTW = 8 / WK;         // 32-key n-tiles per wave
   constexpr int KS = CI / 16;         // bf16 MFMA k-steps
-  constexpr int K4 = CI / 64;         // scaled-MFMA k-steps (Q4)
+  constexpr bool Q4 = QF != 0;        // scaled path: quantised queries, stored MXFP4 key tile
+  constexpr int K4 = CI / 64;         // scaled-MFMA k-steps
   constexpr int LDK = CI + 8;
   constexpr int CB = CI / 2, NBS = CI / 32;              // MXFP4 code / scale bytes per key
   constexpr int LDC = CB + (CI >= 128 ? 16 : 0);         // LDS code row stride (bytes)
@@ -141,6 +167,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   // query fragments (B operand is the key; A operand is the 32 heads x cI)
   bf16x8 qf[QPW][Q4 ? 1 : KS];
   u32x4 q4c[QPW][Q4 ? K4 : 1];
+  u32x4 q8h[QPW][QF == 8 ? K4 : 1];    // E4M3 code bytes 16..31 (MXFP8 queries)
   uint32_t q4s[QPW][Q4 ? K4 : 1];
   float wh[QPW][16];
   int64_t nvis[QPW];
@@ -173,7 +200,21 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
             x[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
           }
         }
-        mxfp4_block(x, q4c[qi][k4], q4s[qi][k4]);
+        if constexpr (QF == 8) {
+          // lane half G quantises block G of the k-step (its scale is the one
+          // the MFMA applies to block G), but the 8-bit operand wants channels
+          // 16 G .. 16 G + 15 of both blocks: trade halves with lane l ^ 32
+          u32x4 lo, hi;
+          mxfp8_block(x, lo, hi, q4s[qi][k4]);
+          const u32x4 send = (l >> 5) ? lo : hi;
+          u32x4 recv;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) recv[d] = (uint32_t)__shfl_xor((int)send[d], 32);
+          q4c[qi][k4] = (l >> 5) ? recv : lo;
+          q8h[qi][QF == 8 ? k4 : 0] = (l >> 5) ? hi : recv;
+        } else {
+          mxfp4_block(x, q4c[qi][k4], q4s[qi][k4]);
+        }
       }
     } else {
 #pragma unroll
@@ -309,9 +350,16 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
 #pragma unroll
           for (int k4 = 0; k4 < K4; ++k4) {
             const u32x4 qc = q4c[qi][k4];
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                (i32x8){(int)qc[0], (int)qc[1], (int)qc[2], (int)qc[3], 0, 0, 0, 0}, k4c[k4], acc,
-                4, 4, 0, (int)q4s[qi][k4], 0, k4s[k4]);
+            if constexpr (QF == 8) {                  // E4M3 queries: format 0, 32 bytes per lane
+              const u32x4 qh = q8h[qi][k4];
+              acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  (i32x8){(int)qc[0], (int)qc[1], (int)qc[2], (int)qc[3], (int)qh[0], (int)qh[1], (int)qh[2], (int)qh[3]},
+                  k4c[k4], acc, 0, 4, 0, (int)q4s[qi][k4], 0, k4s[k4]);
+            } else {                                  // E2M1 queries: format 4, 16 bytes per lane
+              acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  (i32x8){(int)qc[0], (int)qc[1], (int)qc[2], (int)qc[3], 0, 0, 0, 0}, k4c[k4], acc,
+                  4, 4, 0, (int)q4s[qi][k4], 0, k4s[k4]);
+            }
           }
         } else {
 #pragma unroll
@@ -343,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   }
 }
 
-template <int CI, int KL, bool Q4 = false>
+template <int CI, int KL, int QF = 0>
 static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
   const int64_t ntiles = (a.S + KT - 1) / KT;
   if (a.nq >= 16) {
@@ -355,7 +403,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
     if (splits < 1) splits = 1;
     const int tps = (int)((ntiles + splits - 1) / splits);
     splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, Q4>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, QF>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
                        a, pt, b0, qblocks, tps);
   } else {
     constexpr int WQ = 1, QPW = 1;
@@ -366,7 +414,7 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
     if (splits < 1) splits = 1;
     const int tps = (int)((ntiles + splits - 1) / splits);
     splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, Q4>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
+    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, QF>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
                        a, pt, b0, qblocks, tps);
   }
 }
@@ -383,13 +431,17 @@ hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream
     const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
-    if (a.q4) {
+    if (a.qfmt != 0) {
+      const bool q8 = a.qfmt == 8;
       if (a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 64 || a.cI == 128) && a.S < ((int64_t)1 << 25)) {
-        if (a.cI == 64) launch_mfma_variant<64, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
-        else launch_mfma_variant<128, ROW_MXFP4, true>(a, pt, (int)b0, nb, s);
+        if (a.cI == 64) q8 ? launch_mfma_variant<64, ROW_MXFP4, 8>(a, pt, (int)b0, nb, s)
+                           : launch_mfma_variant<64, ROW_MXFP4, 4>(a, pt, (int)b0, nb, s);
+        else q8 ? launch_mfma_variant<128, ROW_MXFP4, 8>(a, pt, (int)b0, nb, s)
+                : launch_mfma_variant<128, ROW_MXFP4, 4>(a, pt, (int)b0, nb, s);
       } else {
         const int64_t total = a.nq * a.S * nb;
-        hipLaunchKernelGGL(indexer_generic_q4, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pt, (int)b0, nb);
+        if (q8) hipLaunchKernelGGL(indexer_generic_qx<8>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pt, (int)b0, nb);
+        else hipLaunchKernelGGL(indexer_generic_qx<4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pt, (int)b0, nb);
       }
     } else if (indexer_mfma_ok(a)) {
       const bool mx = a.k_layout == ROW_MXFP4;

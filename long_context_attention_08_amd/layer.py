@@ -68,6 +68,12 @@ class PairLayer:
                              self.ki_codes[:self.S].view(1, self.S, -1), self.ki_scales[:self.S].view(1, self.S, -1),
                              self.m, self.q_pos0, self.scores, stream=stream)
 
+    def indexer_fp8q(self, stream=None):
+        """The same scores with the query heads rounded to MXFP8."""
+        L.indexer_score_fp8q(self.qI.view(1, self.n, self.hI, self.cI), self.wI.view(1, self.n, self.hI),
+                             self.ki_codes[:self.S].view(1, self.S, -1), self.ki_scales[:self.S].view(1, self.S, -1),
+                             self.m, self.q_pos0, self.scores, stream=stream)
+
     def topk(self, stream=None):
         L.topk_select(self.scores, self.m, self.q_pos0, self.k, self.idx, self.ws_topk, stream=stream)
 

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 25
+    assert len(syms) == 26
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -87,8 +87,9 @@ def test_indexer_validation(L):
     assert f(FAKE, 1, FAKE, FAKE, None, 1, 0, 4, 32, 64, 100, 4, None, FAKE, None) == 0      # B = 0 no-op
 
 
-def test_indexer_fp4q_validation(L):
-    f = L.lib.dsv4_indexer_score_fp4q
+@pytest.mark.parametrize("name", ["dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q"])
+def test_indexer_quantised_query_validation(L, name):
+    f = getattr(L.lib, name)
     assert f(FAKE, 1, FAKE, FAKE, FAKE, 1, 4, 32, 48, 100, 4, pos(0), FAKE, None) == 2       # cI % 32
     assert f(FAKE, 1, FAKE, FAKE, None, 1, 4, 32, 64, 100, 4, pos(0), FAKE, None) == 1       # no scales
     assert f(FAKE, 1, FAKE, FAKE, FAKE, 1, 4, 32, 64, 100, 4, pos(-1), FAKE, None) == 1      # negative pos

@@ -187,25 +187,28 @@ IDX4_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", [4, 8])
 @pytest.mark.parametrize("case", IDX4_CASES, ids=[str(i) for i in range(len(IDX4_CASES))])
-def test_indexer_score_fp4q(L, case):
-    """FP4 indexer: the library rounds the query to MXFP4 itself; the oracle
-    rounds the same stored query; the rounding decisions are exact on both
-    sides (power-of-two scaling of the same bf16/f32 values), so only the
-    summation order differs."""
+def test_indexer_score_quantised_queries(L, case, fmt):
+    """FP4 / FP8 indexer: the library rounds the query to MXFP4 or MXFP8
+    itself; the oracle rounds the same stored query; the rounding decisions are
+    exact on both sides (power-of-two scaling of the same bf16/f32 values), so
+    only the summation order differs."""
     import torch
     qd, B, nq, hI, cI, S, m, pos = case
+    call = L.indexer_score_fp8q if fmt == 8 else L.indexer_score_fp4q
+    oracle_fn = O.indexer_score_fp8q if fmt == 8 else O.indexer_score_fp4q
     seed = 700 + S + nq
     qI = act_arr(seed, "qI", (B, nq, hI, cI), 0.5, qd)
     wI = G.normal(seed, "wI", (B, nq, hI))
     kx = G.normal(seed, "cache_ki", (B, S, cI))
     codes, ksc = G.store(kx, ROW_MXFP4)
     scores = torch.full((B, nq, S), float("nan"), dtype=torch.float32, device="cuda")
-    L.indexer_score_fp4q(dev(qI), dev(wI), dev(codes), dev(ksc), m, pos, scores)
+    call(dev(qI), dev(wI), dev(codes), dev(ksc), m, pos, scores)
     got = host(scores)
     for b in range(B):
         kf = stored_rows_f64(codes[b], ROW_MXFP4, cI, ksc[b])
-        ref = O.indexer_score_fp4q(decode_act(qI[b]), wI[b].astype(np.float64), kf, m, pos[b] + np.arange(nq))
+        ref = oracle_fn(decode_act(qI[b]), wI[b].astype(np.float64), kf, m, pos[b] + np.arange(nq))
         vis = np.isfinite(ref)
         assert np.array_equal(np.isneginf(got[b]), ~vis), "visibility mask"
         if vis.any():
@@ -230,6 +233,27 @@ def test_indexer_fp4q_small_integers_bit_exact(L):
     scores = torch.empty((B, nq, S), dtype=torch.float32, device="cuda")
     L.indexer_score_fp4q(dev(G.to_bf16(q)), dev(w), dev(codes), dev(ksc), m, [2000], scores)
     ref = O.indexer_score_fp4q(q[0].astype(np.float64), w[0].astype(np.float64), kf, m, 2000 + np.arange(nq))
+    assert np.array_equal(host(scores)[0], ref.astype(np.float32))
+
+
+def test_indexer_fp8q_small_integers_bit_exact(L):
+    """Integer queries with |q| <= 14 and a block maximum of 8 or more (scale
+    2^-5) sit on the E4M3 grid, E2M1 keys are multiples of 1/2, so every
+    product and partial sum is a multiple of 1/2 below 2^24: any accumulation
+    order gives the oracle's value bit for bit."""
+    import torch
+    rng = np.random.default_rng(9)
+    B, nq, hI, cI, S, m = 1, 40, 32, 128, 650, 4
+    q = rng.integers(-14, 15, (B, nq, hI, cI)).astype(np.float32)
+    q[..., 0::32] = rng.choice(np.array([8, 9, 13, -9, -14], dtype=np.float32), q[..., 0::32].shape)
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6], dtype=np.float32)
+    kx = vals[rng.integers(0, len(vals), (B, S, cI))]
+    w = rng.choice(np.array([-2, -1, 1, 2], dtype=np.float32), (B, nq, hI))
+    codes, ksc = G.store(kx, ROW_MXFP4)
+    kf = stored_rows_f64(codes[0], ROW_MXFP4, cI, ksc[0])
+    scores = torch.empty((B, nq, S), dtype=torch.float32, device="cuda")
+    L.indexer_score_fp8q(dev(G.to_bf16(q)), dev(w), dev(codes), dev(ksc), m, [1900], scores)
+    ref = O.indexer_score_fp8q(q[0].astype(np.float64), w[0].astype(np.float64), kf, m, 1900 + np.arange(nq))
     assert np.array_equal(host(scores)[0], ref.astype(np.float32))
 
 
