@@ -372,13 +372,16 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         part[qi] = sc;
       }
       // queries in pairs: the lower half finishes query 2 p, the upper half
-      // 2 p + 1, each taking the other half's partial; one 64-lane store per pair
+      // 2 p + 1; one v_permlane32_swap of the two partials leaves each lane
+      // with its own partial of that query and its partner's (lanes l ^ 32),
+      // without a trip through LDS; one 64-lane store per pair
       const int s32 = (int)s;
       auto finish_pair = [&](auto ppc) {
         constexpr int pp = decltype(ppc)::value;
         constexpr int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
-        const float keep = hi ? part[qb] : part[qa];
-        const float total = keep + __shfl_xor(hi ? part[qa] : part[qb], 32);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qa]), __float_as_uint(part[qb]),
+                                                         false, false);
+        const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const uint32_t off = pok[pp] && s32 < S32 ? prow[pp] + 4u * (uint32_t)s32 : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32 < pvis[pp] ? total : -INFINITY), srsrc,
                                               (int)off, 0, 0);
@@ -395,7 +398,9 @@ template <int CI, int KL, int QF = 0>
 static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
   const int64_t ntiles = (a.S + KT - 1) / KT;
   if (a.nq >= 16) {
-    constexpr int WQ = 4, QPW = 4;
+    // four queries per wave; two for bf16 queries at cI = 128, whose query
+    // fragments alone would take 128 registers at four
+    constexpr int WQ = 4, QPW = QF == 0 && CI == 128 ? 2 : 4;
     const int qblocks = (int)((a.nq + WQ * QPW - 1) / (WQ * QPW));
     int64_t units = (int64_t)qblocks * nb;
     int64_t splits = (4096 + units - 1) / units;

@@ -360,6 +360,9 @@ DENSE_CASES = [
     ("f32", ROW_F32, 1, 30, 4, 64, 20, 8, 16, [120], True),                  # generic
     ("bf16", ROW_BF16, 1, 70, 16, 128, 40, 128, 128, [4000], True),          # MFMA, 4 queries per block
     ("bf16", ROW_FP8, 1, 40, 64, 512, 200, 128, 128, [20000], True),         # MFMA, c = 512
+    ("bf16", ROW_FP8, 1, 33, 64, 512, 600, 128, 128, [64100], True),         # c = 512, visible count steps mid-chunk
+    ("bf16", ROW_FP8, 1, 10, 32, 512, 300, 128, 128, [40000], False),        # c = 512, 2 queries per block, odd tail
+    ("bf16", ROW_FP8, 1, 13, 16, 512, 150, 128, 64, [19000], True),          # c = 512, 4 queries per block, ragged
     ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 128, [1 << 16, 30000], True), # decode: split + combine
     ("bf16", ROW_BF16, 1, 37, 32, 128, 10, 16, 0, [100], False),             # 2 queries per block, no window
 ]
