@@ -527,7 +527,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < HK; ++i) mx = fmaxf(mx, hn[i]);
-    return fmaxf(mx, __shfl_xor(mx, 32));
+    return max_halves(mx);
   };
 
   // PV of the tile in key tile KB: O^T[c][row] += V^T[c][keys] P^T[keys][row].
@@ -697,7 +697,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     }
   }
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_halves(l_run);
   if constexpr (CS > 1) {            // each wave of a pair summed P over its own key half
     s_xm[wv * 64 + l] = l_run;
     lds_barrier();
@@ -1045,7 +1045,7 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+    mx = max_halves(mx) * sl;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
       float alpha = 1.f;
       if (mx > m_run + 8.0f) {
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   if (ch == 0) tile_loop(std::integral_constant<int, 0>());
   else tile_loop(std::integral_constant<int, 1>());
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_halves(l_run);
   if (!qvalid) return;
   if (pl.max_splits == 1) {
     float f = m_run == -INFINITY ? 0.f : 1.f, den = l_run;

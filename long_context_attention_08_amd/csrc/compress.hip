@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void hca_compress_mfma(CompressArgs a) {
                          acc[t][0][h][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     if (g == 0) red[wv][16 * h + col] = mx;
   }
   __syncthreads();
@@ -370,9 +370,9 @@ __global__ __launch_bounds__(256) void hca_compress_mfma(CompressArgs a) {
         den += w;
       }
     num += __shfl_xor(num, 16);
-    num += __shfl_xor(num, 32);
+    num = sum_halves(num);
     den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
+    den = sum_halves(den);
     __syncthreads();   // red is reused below
     if (g == 0) { red[wv][cc] = num; red2[wv][cc] = den; }
     __syncthreads();
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
         acc[i][1][r] += a.bias[row * c + j];          // logit Z + B
         mx = fmaxf(mx, acc[i][1][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -552,8 +552,8 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
         num = fmaf(w, acc[i][0][r], num);
         den += w;
       }
-    num += __shfl_xor(num, 32);
-    den += __shfl_xor(den, 32);
+    num = sum_halves(num);
+    den = sum_halves(den);
     if (G == 0) store_row_elem(comp + e * rb, a.comp_layout, c, j, num / den);
   } else {
     const int64_t n_ent = a.n / 4;

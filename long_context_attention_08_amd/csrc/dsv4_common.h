@@ -200,6 +200,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// v combined with the value of lane l ^ 32, for every lane, by one
+// v_permlane32_swap (a VALU exchange of the wave's halves, no LDS round trip).
+// The swap leaves {v[l], v[l ^ 32]} in its two results, in an order that
+// depends on the half; max and sum do not care, so the results equal those of
+// an exchange through LDS bit for bit.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // position of the first entry NOT visible at position p for ratio m: entries
