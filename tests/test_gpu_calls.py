@@ -364,6 +364,7 @@ DENSE_CASES = [
     ("bf16", ROW_FP8, 1, 10, 32, 512, 300, 128, 128, [40000], False),        # c = 512, 2 queries per block, odd tail
     ("bf16", ROW_FP8, 1, 13, 16, 512, 150, 128, 64, [19000], True),          # c = 512, 4 queries per block, ragged
     ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 128, [1 << 16, 30000], True), # decode: split + combine
+    ("bf16", ROW_FP8, 1, 8, 64, 512, 10, 128, 128, [50], True),              # no entry visible yet: window only
     ("bf16", ROW_BF16, 1, 37, 32, 128, 10, 16, 0, [100], False),             # 2 queries per block, no window
 ]
 
@@ -410,6 +411,26 @@ def test_attention_decodes_every_fp8_code(L):
     want = K.decode_rows(row[0, 0], ROW_FP8, c)
     # the output is stored as bf16: every E4M3 value and every bf16 value is exact in bf16
     assert np.array_equal(got, np.broadcast_to(want, (nh, c)))
+
+
+@pytest.mark.parametrize("use_sink", [False, True])
+def test_sparse_all_padding_gives_zero(L, use_sink):
+    """Every index slot is padding and there is no window: no key is visible,
+    so the output is exactly zero (the sink, if any, carries a zero value)."""
+    import torch
+    c, nh, nq, S, k = 512, 64, 3, 100, 64
+    q = torch.from_numpy(G.to_bf16(G.normal(5, "q", (1, nq, nh, c))).view(np.int16)).cuda().view(torch.bfloat16)
+    kv = make_rows(5, "cache_kv", (1, S, c), ROW_FP8)
+    idx = torch.full((1, nq, k), -1, dtype=torch.int32, device="cuda")
+    sink = torch.from_numpy(G.normal(5, "sink", (nh,), 0.5)).cuda() if use_sink else None
+    out = torch.full_like(q, 7.0)
+    ws = torch.empty(max(1, L.attn_workspace_size(False, 1, nq, nh, c, k)), dtype=torch.uint8, device="cuda")
+    L.sparse_mqa_fwd(q, dev(kv), ROW_FP8, idx, None, [0], 0, [400], sink, 0.05, out, ws)
+    ref = O.sparse_mqa(np.zeros((nq, nh, c)), K.decode_rows(kv[0], ROW_FP8, c), np.full((nq, k), -1), np.zeros((0, c)), 0, 0,
+                       400 + np.arange(nq), G.normal(5, "sink", (nh,), 0.5).astype(np.float64) if use_sink else None,
+                       0.05)
+    assert not ref.any()
+    assert not host(out.float()).any()
 
 
 def test_attention_window_must_be_covered(L):
