@@ -1135,6 +1135,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   const float* owb = mlb + (int64_t)gridDim.x * pl.max_splits * rows * 2;
   const float* ml = mlb + (unit * pl.max_splits * rows + r) * 2;          // split s at + 2 s rows
   float M = -INFINITY;
+#pragma unroll 4
   for (int64_t sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[sp * rows * 2]);
   const float z = a.sink ? a.sink[h] * LOG2E : -INFINITY;
   const float Mt = fmaxf(M, z);
@@ -1143,10 +1144,13 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
 #pragma unroll
   for (int j = 0; j < CPT; ++j) o[j] = 0.f;
   const float* ow = owb + (unit * pl.max_splits * rows + r) * (int64_t)c + lane * CPT;   // split s at + s rows c
+  // splits in increasing order; a split that saw no visible key (m = -inf,
+  // zero partial) gets weight 0.  No branch in the loop, so that the partial
+  // loads of several splits are in flight together
+#pragma unroll 4
   for (int64_t sp = 0; sp < nsplit; ++sp) {
     const float ms = ml[sp * rows * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - Mt);
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - Mt);
     den = fmaf(ml[sp * rows * 2 + 1], w, den);
     const float* src = ow + sp * rows * (int64_t)c;
     if constexpr (CPT % 4 == 0) {
