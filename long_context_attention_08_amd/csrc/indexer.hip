@@ -172,12 +172,13 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   float wh[QPW][16];
   int64_t nvis[QPW];
   bool qvalid[QPW];
-  int64_t nvis_max = 0;
-  for (int qi = 0; qi < QB; ++qi) {           // block-wide maximum (uniform)
+  int64_t nvis_max = 0, nvis_min = S;
+  for (int qi = 0; qi < QB; ++qi) {           // block-wide maximum and minimum (uniform)
     const int64_t t = t0 + qi;
     if (t < a.nq) {
       const int64_t v = visible_count(pt.q_pos0[bl] + t, a.m, S);
       nvis_max = v > nvis_max ? v : nvis_max;
+      nvis_min = v < nvis_min ? v : nvis_min;
     }
   }
 #pragma unroll
@@ -251,6 +252,12 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     pvis[pp] = (int)(hi ? nvis[qb] : nvis[qa]);
     pok[pp] = (hi ? qvalid[qb] : qvalid[qa]) && (QPW > 1 || !hi);
   }
+  // full-tile stores: the same row offsets; a lane that finishes no query
+  // points past the range (which is below 2^31: nrows <= 16, S < 2^25), and
+  // a query past nq has its row at or beyond nrows, also past the range
+  uint32_t prow_f[NPAIR];
+#pragma unroll
+  for (int pp = 0; pp < NPAIR; ++pp) prow_f[pp] = (QPW > 1 || !hi) ? prow[pp] : 0x80000000u;
   const int S32 = (int)S;
 
   for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
@@ -319,7 +326,11 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
       }
     }
     __syncthreads();
-    // ---- scores
+    // ---- scores.  FULL: every key of the tile is visible to every query of
+    // the block, so a store needs no per-lane test (rows of queries past nq,
+    // and lanes that finish no query, lie beyond the buffer's range)
+    auto ntile_loop = [&](auto fullc) {
+    constexpr bool FULL = decltype(fullc)::value;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int ntile = wk * NTW + nt;
@@ -382,14 +393,22 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qa]), __float_as_uint(part[qb]),
                                                          false, false);
         const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const uint32_t off = pok[pp] && s32 < S32 ? prow[pp] + 4u * (uint32_t)s32 : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32 < pvis[pp] ? total : -INFINITY), srsrc,
-                                              (int)off, 0, 0);
+        if constexpr (FULL) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), srsrc, (int)(prow_f[pp] + 4u * (uint32_t)s32),
+                                                0, 0);
+        } else {
+          const uint32_t off = pok[pp] && s32 < S32 ? prow[pp] + 4u * (uint32_t)s32 : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32 < pvis[pp] ? total : -INFINITY), srsrc,
+                                                (int)off, 0, 0);
+        }
       };
       finish_pair(std::integral_constant<int, 0>());
       if constexpr (NPAIR > 1) finish_pair(std::integral_constant<int, 1>());
       static_assert(NPAIR <= 2, "pairs");
     }
+    };
+    if (s0 + KT <= nvis_min) ntile_loop(std::true_type());
+    else ntile_loop(std::false_type());
     __syncthreads();
   }
 }
