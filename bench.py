@@ -91,7 +91,7 @@ def calibrate_copy(gib=1):
     print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
 
 
-def cpu_baseline(inp, rows_n=16, seed=4):
+def cpu_baseline(inp, rows_n=256, seed=4):
     """The float64 oracle on a bounded sample: the three compressors in full,
     then the per-query steps (index scores, top-k, sparse MQA, dense MQA) for
     `rows_n` seeded query rows.  Returns query tokens/s with the compress cost
@@ -318,7 +318,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-rows", type=int, default=256)   # about 10 s of oracle work on 16 cores
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
