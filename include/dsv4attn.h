@@ -106,6 +106,35 @@ int dsv4_hca_compress(const void* H, int64_t n, int64_t d, int act_dtype,
                       void* raw_out, int raw_layout, void* stream);
 
 /*
+ * The compressors of one chunk together (digest 核心思路: CSA and HCA layers
+ * alternate, and both, with the indexer keys, compress the same hidden states
+ * H of the chunk): the results are those of
+ *   dsv4_csa_compress(H, n_left, n, ..., csa_kv ...),
+ *   dsv4_csa_compress(H, n_left, n, ..., csa_keys ...) and
+ *   dsv4_hca_compress(H + n_left rows, n, ..., hca ...),
+ * bit for bit.  Any of the three may be NULL (skipped).  Each is validated as
+ * its own call would be, all before anything is launched.  When every given
+ * compressor takes the pipelined MFMA path (bf16 H, d % 64 == 0, c % 64 == 0,
+ * m = 4, m' = 128, no MXFP4 window rows, MXFP4 entries for CSA only) they run
+ * in one launch over the same 256-token tiles of H; otherwise one after the
+ * other.
+ */
+typedef struct {
+  const void* W;         /* CSA: [4c, d] = W_aKV | W_bKV | W_aZ | W_bZ; HCA: [2c, d] = W_KV | W_Z */
+  const float* bias;     /* CSA: [2, m, c] = B^a, B^b; HCA: [m', c] */
+  int c;
+  void* comp_out;        /* entries in comp_layout; comp_scales for MXFP4 (else may be NULL) */
+  void* comp_scales;
+  int comp_layout;
+  void* raw_out;         /* window rows in raw_layout, or NULL */
+  int raw_layout;
+} dsv4_compressor_t;
+
+int dsv4_compress_chunk(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                        int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                        int m_prime, const dsv4_compressor_t* hca, void* stream);
+
+/*
  * Lightning-indexer scores (digest 模块 B eq 16; blog 第二阶段):
  *   I[b, t, s] = sum_h wI[b, t, h] * ReLU(qI[b, t, h, :] . K[b, s, :])
  * for entries visible to the query (m*(s+1) <= p+1), -inf otherwise.  No scale.

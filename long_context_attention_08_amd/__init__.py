@@ -11,13 +11,13 @@ kernels behind the C ABI
 of include/dsv4attn.h; this package is a thin ctypes binding over it.
 """
 from ._lib import (BF16, EXPORTS, F32, ROW_BF16, ROW_F32, ROW_FP8_ROPE_BF16, ROW_MXFP4, Dsv4Error,
-                   LIB_PATH, attn_workspace_size, csa_compress, hca_compress, hca_dense_fwd,
+                   LIB_PATH, attn_workspace_size, compress_chunk, compressor, csa_compress, hca_compress, hca_dense_fwd,
                    indexer_score, indexer_score_fp4q, indexer_score_fp8q, kv_norm_rope, lib, out_rope, q_norm_rope,
                    gemm_bf16_nt, query_proj, query_proj_workspace_size, output_proj, output_proj_workspace_size, row_bytes, sparse_mqa_fwd, topk_select, topk_workspace_size,
                    stream_compress, stream_state_bytes, stream_state_reset, stream_workspace_size, swa_ring_pos0)
 
 __all__ = ["BF16", "F32", "ROW_BF16", "ROW_F32", "ROW_FP8_ROPE_BF16", "ROW_MXFP4", "Dsv4Error", "EXPORTS",
-           "LIB_PATH", "attn_workspace_size", "csa_compress", "hca_compress", "hca_dense_fwd",
+           "LIB_PATH", "attn_workspace_size", "compress_chunk", "compressor", "csa_compress", "hca_compress", "hca_dense_fwd",
            "indexer_score", "indexer_score_fp4q", "indexer_score_fp8q", "kv_norm_rope", "lib", "out_rope", "q_norm_rope",
            "gemm_bf16_nt", "query_proj", "query_proj_workspace_size", "output_proj", "output_proj_workspace_size", "row_bytes", "sparse_mqa_fwd", "topk_select", "topk_workspace_size",
            "stream_compress", "stream_state_bytes", "stream_state_reset", "stream_workspace_size", "swa_ring_pos0"]

@@ -15,7 +15,7 @@ F32, BF16 = 0, 1
 ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
-    "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_indexer_score",
+    "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_compress_chunk", "dsv4_indexer_score",
     "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
@@ -46,6 +46,14 @@ _sig("dsv4_status_string", ctypes.c_char_p, [_int])
 _sig("dsv4_last_error", ctypes.c_char_p, [])
 _sig("dsv4_csa_compress", _int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _int, _int, _i64,
                                  _vp, _vp, _int, _vp, _int, _vp])
+class Compressor(ctypes.Structure):
+    """dsv4_compressor_t: one compressor's weights and outputs for dsv4_compress_chunk."""
+    _fields_ = [("W", _vp), ("bias", _vp), ("c", _int), ("comp_out", _vp), ("comp_scales", _vp),
+                ("comp_layout", _int), ("raw_out", _vp), ("raw_layout", _int)]
+
+
+_sig("dsv4_compress_chunk", _int, [_vp, _i64, _i64, _i64, _int, _int, _i64, ctypes.POINTER(Compressor),
+                                   ctypes.POINTER(Compressor), _int, ctypes.POINTER(Compressor), _vp])
 _sig("dsv4_hca_compress", _int, [_vp, _i64, _i64, _int, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _int, _vp])
 _sig("dsv4_indexer_score", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _i64, _int,
                                   _P64, _vp, _vp])
@@ -156,6 +164,22 @@ def hca_compress(H, W, bias, m_prime, c, comp_out, comp_layout, *, comp_scales=N
     _check(lib.dsv4_hca_compress(_ptr(H), H.shape[0], H.shape[1], _act(H), _ptr(W), _ptr(bias), m_prime, c,
                                  _ptr(comp_out), _ptr(comp_scales), comp_layout, _ptr(raw_out), raw_layout,
                                  _stream(stream)))
+
+
+def compressor(W, bias, c, comp_out, comp_layout, *, comp_scales=None, raw_out=None, raw_layout=ROW_F32):
+    """One compressor's weights and outputs for compress_chunk."""
+    return Compressor(_ptr(W), _ptr(bias), c, _ptr(comp_out), _ptr(comp_scales), comp_layout, _ptr(raw_out),
+                      raw_layout)
+
+
+def compress_chunk(H, m, *, n_left=0, block0=0, csa_kv=None, csa_keys=None, m_prime=128, hca=None, stream=None):
+    """The CSA KV, CSA indexer-key and HCA compressors of one chunk in one call
+    (each a `compressor(...)` or None).  H [n_left + n, d]; the HCA compressor
+    takes rows n_left.. of H."""
+    n = H.shape[0] - n_left
+    ref = lambda j: ctypes.byref(j) if j is not None else None
+    _check(lib.dsv4_compress_chunk(_ptr(H), n_left, n, H.shape[1], _act(H), m, block0, ref(csa_kv), ref(csa_keys),
+                                   m_prime, ref(hca), _stream(stream)))
 
 
 def indexer_score(qI, wI, keys, k_layout, m, q_pos0, scores, *, k_scales=None, S=None, stream=None):

@@ -82,6 +82,7 @@ const char* dsv4_last_error(void) { return g_err; }
 
 // --------------------------------------------------------------------------- compressors
 
+static int check_csa_extra(const char* fn, int64_t n_left, int64_t n, int m, int64_t block0);
 static int check_compress(const char* fn, const void* H, int64_t n_left, int64_t n, int64_t d, int act,
                           const void* W, const float* bias, int m, int c, void* comp, void* scales,
                           int comp_layout, void* raw, int raw_layout) {
@@ -117,11 +118,8 @@ int dsv4_csa_compress(const void* H, int64_t n_left, int64_t n, int64_t d, int a
   int r = check_compress(fn, H, n_left, n, d, act_dtype, W, bias_ab, m, c, comp_out, comp_scales,
                          comp_layout, raw_out, raw_layout);
   if (r) return r;
-  if (m > 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: m=%d > 64", fn, m);
-  if (block0 < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: block0 < 0", fn);
-  if (block0 >= 1 && n >= m && n_left < m)
-    return fail(DSV4_ERR_INVALID_ARG, "%s: entry %lld needs %d rows of left context, got n_left=%lld", fn,
-                (long long)block0, m, (long long)n_left);
+  r = check_csa_extra(fn, n_left, n, m, block0);
+  if (r) return r;
   if (n == 0) return ok();
   dsv4::CompressArgs a{H, n_left, n, d, act_dtype, W, bias_ab, m, c, block0, comp_out,
                        reinterpret_cast<uint8_t*>(comp_scales), comp_layout, raw_out, raw_layout};
@@ -140,6 +138,57 @@ int dsv4_hca_compress(const void* H, int64_t n, int64_t d, int act_dtype,
   dsv4::CompressArgs a{H, 0, n, d, act_dtype, W, bias, m_prime, c, 0, comp_out,
                        reinterpret_cast<uint8_t*>(comp_scales), comp_layout, raw_out, raw_layout};
   return hip_status(dsv4::launch_hca_compress(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+static int check_csa_extra(const char* fn, int64_t n_left, int64_t n, int m, int64_t block0) {
+  if (m > 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: m=%d > 64", fn, m);
+  if (block0 < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: block0 < 0", fn);
+  if (block0 >= 1 && n >= m && n_left < m)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: entry %lld needs %d rows of left context, got n_left=%lld", fn,
+                (long long)block0, m, (long long)n_left);
+  return 0;
+}
+
+int dsv4_compress_chunk(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                        int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                        int m_prime, const dsv4_compressor_t* hca, void* stream) {
+  const char* fn = "dsv4_compress_chunk";
+  for (const dsv4_compressor_t* j : {csa_kv, csa_keys}) {
+    if (!j) continue;
+    int r = check_compress(fn, H, n_left, n, d, act_dtype, j->W, j->bias, m, j->c, j->comp_out, j->comp_scales,
+                           j->comp_layout, j->raw_out, j->raw_layout);
+    if (!r) r = check_csa_extra(fn, n_left, n, m, block0);
+    if (r) return r;
+  }
+  if (hca) {
+    int r = check_compress(fn, H, 0, n, d, act_dtype, hca->W, hca->bias, m_prime, hca->c, hca->comp_out,
+                           hca->comp_scales, hca->comp_layout, hca->raw_out, hca->raw_layout);
+    if (r) return r;
+  }
+  if (n == 0 || (!csa_kv && !csa_keys && !hca)) return ok();
+  const size_t esz = act_dtype == DSV4_F32 ? 4 : 2;
+  const void* Hh = reinterpret_cast<const uint8_t*>(H) + (size_t)n_left * (size_t)d * esz;
+  auto csa = [&](const dsv4_compressor_t* j) {
+    return dsv4::CompressArgs{H, n_left, n, d, act_dtype, j->W, j->bias, m, j->c, block0, j->comp_out,
+                              reinterpret_cast<uint8_t*>(j->comp_scales), j->comp_layout, j->raw_out, j->raw_layout};
+  };
+  dsv4::CompressArgs akv{}, aki{}, ahc{};
+  if (csa_kv) akv = csa(csa_kv);
+  if (csa_keys) aki = csa(csa_keys);
+  if (hca)
+    ahc = dsv4::CompressArgs{Hh, 0, n, d, act_dtype, hca->W, hca->bias, m_prime, hca->c, 0, hca->comp_out,
+                             reinterpret_cast<uint8_t*>(hca->comp_scales), hca->comp_layout, hca->raw_out,
+                             hca->raw_layout};
+  const dsv4::CompressArgs *pkv = csa_kv ? &akv : nullptr, *pki = csa_keys ? &aki : nullptr,
+                           *phc = hca ? &ahc : nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dsv4::compress_fused_ok(pkv, pki, phc)) return hip_status(dsv4::launch_compress_fused(pkv, pki, phc, s), fn);
+  for (const dsv4::CompressArgs* a : {pkv, pki}) {
+    if (!a) continue;
+    int r = hip_status(dsv4::launch_csa_compress(*a, s), fn);
+    if (r) return r;
+  }
+  return phc ? hip_status(dsv4::launch_hca_compress(*phc, s), fn) : ok();
 }
 
 // --------------------------------------------------------------------------- indexer

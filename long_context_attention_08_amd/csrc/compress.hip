@@ -424,22 +424,29 @@ static bool gemm_path_ok(const CompressArgs& a, int want_m) {
 // Staged H rows outside the input are clamped copies that no entry uses.
 constexpr int CG_K = 64;
 template <bool HCA, int MT>
-__global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
+struct CgShape {
+  static constexpr int NT = HCA ? 2 : 4;               // column tiles (matrices) per wave
+  static constexpr int BM = 64 * MT;                   // tokens per block
+  static constexpr int CG_AR = BM + 32;                // staged H rows: 32 before the tile, BM in it
+  static constexpr int BN = 2 * 32 * NT;               // staged W rows
+  static constexpr int ASZ = CG_AR * CG_K * 2, BSZ = BN * CG_K * 2;   // bytes of one stage
+};
+
+// One block's tile: tokens [bx BM, bx BM + BM) of the chunk, channels
+// [64 by, 64 by + 64) of every matrix; s_a / s_b hold two stages each.
+template <bool HCA, int MT>
+__device__ __forceinline__ void compress_tile(const CompressArgs& a, int64_t bx, int by, uint8_t* s_a,
+                                              uint8_t* s_b) {
   static_assert(!HCA || MT == 4, "an HCA entry is one wave's 128 tokens");
-  constexpr int NT = HCA ? 2 : 4;               // column tiles (matrices) per wave
-  constexpr int BM = 64 * MT;                   // tokens per block
-  constexpr int CG_AR = BM + 32;                // staged H rows: 32 before the tile, BM in it
-  constexpr int BN = 2 * 32 * NT;               // staged W rows
-  constexpr int ASZ = CG_AR * CG_K * 2, BSZ = BN * CG_K * 2;
+  using Sh = CgShape<HCA, MT>;
+  constexpr int NT = Sh::NT, BM = Sh::BM, CG_AR = Sh::CG_AR, BN = Sh::BN, ASZ = Sh::ASZ, BSZ = Sh::BSZ;
   constexpr int CA = CG_AR / 32, CB = BN / 32;  // 1 KB copies per wave and k tile
-  __shared__ __align__(16) uint8_t s_a[2 * ASZ];
-  __shared__ __align__(16) uint8_t s_b[2 * BSZ];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
   const int wm = wv >> 1, wn = wv & 1;
   const int c = a.c;
-  const int64_t T0 = (int64_t)blockIdx.x * BM;     // chunk-local token of tile row 0
-  const int j0 = blockIdx.y * 64;
+  const int64_t T0 = bx * BM;                      // chunk-local token of tile row 0
+  const int j0 = by * 64;
   const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
   // copy k of a tile covers staged rows [8k, 8k + 8): lane L takes row 8k + L/8
@@ -607,6 +614,29 @@ __global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
   }
 }
 
+template <bool HCA, int MT>
+__global__ __launch_bounds__(256, 1) void compress_gemm(CompressArgs a) {
+  using Sh = CgShape<HCA, MT>;
+  __shared__ __align__(16) uint8_t s_a[2 * Sh::ASZ];
+  __shared__ __align__(16) uint8_t s_b[2 * Sh::BSZ];
+  compress_tile<HCA, MT>(a, blockIdx.x, blockIdx.y, s_a, s_b);
+}
+
+// The three compressors of a chunk in one launch, all over the same 256-token
+// tiles of H: grid.y runs the 64-channel tiles of the CSA KV compressor
+// (ny0), then of the indexer-key compressor (ny1), then of the HCA compressor.
+__global__ __launch_bounds__(256, 1) void compress_fused(CompressArgs kv, CompressArgs ki, CompressArgs hca,
+                                                         int ny0, int ny1) {
+  using S4 = CgShape<false, 4>;
+  static_assert(CgShape<true, 4>::ASZ <= S4::ASZ && CgShape<true, 4>::BSZ <= S4::BSZ, "stage sizes");
+  __shared__ __align__(16) uint8_t s_a[2 * S4::ASZ];
+  __shared__ __align__(16) uint8_t s_b[2 * S4::BSZ];
+  const int y = blockIdx.y;
+  if (y < ny0) compress_tile<false, 4>(kv, blockIdx.x, y, s_a, s_b);
+  else if (y < ny0 + ny1) compress_tile<false, 4>(ki, blockIdx.x, y - ny0, s_a, s_b);
+  else compress_tile<true, 4>(hca, blockIdx.x, y - ny0 - ny1, s_a, s_b);
+}
+
 hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   if (gemm_path_ok(a, 4) && a.c >= 256) {
@@ -623,6 +653,30 @@ hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s) {
     const int64_t threads = slots * a.c;
     hipLaunchKernelGGL(csa_compress_generic, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+// the fused path serves a chunk when every given compressor takes the
+// pipelined MFMA path at 256-token tiles and all share n
+bool compress_fused_ok(const CompressArgs* kv, const CompressArgs* ki, const CompressArgs* hca) {
+  int64_t n = -1;
+  for (const CompressArgs* a : {kv, ki, hca}) {
+    if (!a) continue;
+    if (!gemm_path_ok(*a, a == hca ? 128 : 4)) return false;
+    if (n >= 0 && a->n != n) return false;
+    n = a->n;
+  }
+  return n > 0;
+}
+
+hipError_t launch_compress_fused(const CompressArgs* kv, const CompressArgs* ki, const CompressArgs* hca,
+                                 hipStream_t s) {
+  const int ny0 = kv ? kv->c / 64 : 0, ny1 = ki ? ki->c / 64 : 0, ny2 = hca ? hca->c / 64 : 0;
+  const int64_t n = kv ? kv->n : ki ? ki->n : hca->n;
+  const CompressArgs none{};
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)(ny0 + ny1 + ny2));
+  hipLaunchKernelGGL(compress_fused, grid, dim3(256), 0, s, kv ? *kv : none, ki ? *ki : none, hca ? *hca : none,
+                     ny0, ny1);
   return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@ struct CompressArgs {
 
 hipError_t launch_csa_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_hca_compress(const CompressArgs& a, hipStream_t s);
+// the compressors of one chunk in one launch (any pointer may be null)
+bool compress_fused_ok(const CompressArgs* kv, const CompressArgs* ki, const CompressArgs* hca);
+hipError_t launch_compress_fused(const CompressArgs* kv, const CompressArgs* ki, const CompressArgs* hca,
+                                 hipStream_t s);
 
 struct IndexerArgs {
   const void* qI;       // [B, nq, hI, cI]

@@ -5,11 +5,13 @@ Efficient Million-Token Context Intelligence"): CSA and HCA layers alternate
 layer by layer (核心思路); the compressed entries of a prefix are cached and
 reused, and only complete blocks produce entries (模块 F).
 
-One `step()` enqueues, on one stream, the seven calls of the pair:
-  CSA: compress KV (appended to the KV cache, window rows to the CSA window
-       buffer), compress indexer keys (appended), index scores, top-k,
-       sparse MQA;
-  HCA: compress (appended, window rows to the HCA window buffer), dense MQA.
+One `step()` enqueues, on one stream, the calls of the pair:
+  the three compressors of the chunk in one launch over the same tiles of H
+       (CSA KV appended to the KV cache with its window rows to the CSA window
+       buffer, CSA indexer keys appended, HCA entries appended with their
+       window rows to the HCA window buffer);
+  CSA: index scores, top-k, sparse MQA;
+  HCA: dense MQA.
 Buffers are torch tensors owned by the caller; nothing is allocated in step().
 """
 import math
@@ -57,6 +59,16 @@ class PairLayer:
         L.csa_compress(self.H, self.W_ki, self.B_ki, self.m, self.cI, self.ki_new, self.key_layout,
                        n_left=self.n_left, block0=self.S0, comp_scales=self.ki_sc_new, stream=stream)
 
+    def compress(self, stream=None):
+        """All three compressors of the chunk in one call (dsv4_compress_chunk)."""
+        kv = L.compressor(self.W_kv, self.B_kv, self.c, self.kv_new, self.kv_layout, raw_out=self.kv_win_new,
+                          raw_layout=self.kv_layout)
+        ki = L.compressor(self.W_ki, self.B_ki, self.cI, self.ki_new, self.key_layout, comp_scales=self.ki_sc_new)
+        hc = L.compressor(self.W_hca, self.B_hca, self.c, self.hca_new, self.kv_layout, raw_out=self.hca_win_new,
+                          raw_layout=self.kv_layout)
+        L.compress_chunk(self.H, self.m, n_left=self.n_left, block0=self.S0, csa_kv=kv, csa_keys=ki,
+                         m_prime=self.mp, hca=hc, stream=stream)
+
     def indexer(self, stream=None):
         L.indexer_score(self.qI.view(1, self.n, self.hI, self.cI), self.wI.view(1, self.n, self.hI),
                         self.ki_codes[:self.S].view(1, self.S, -1), self.key_layout, self.m, self.q_pos0,
@@ -94,11 +106,10 @@ class PairLayer:
                         self.out_hca.view(1, self.n, self.nh, self.c), self.ws_attn, stream=stream)
 
     def step(self, stream=None):
-        self.csa_compress(stream)
+        self.compress(stream)
         self.indexer(stream)
         self.topk(stream)
         self.sparse(stream)
-        self.hca_compress(stream)
         self.hca_dense(stream)
 
 

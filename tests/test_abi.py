@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 26
+    assert len(syms) == 27
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -57,6 +57,25 @@ def pos(*v):
 
 def err(L):
     return L.lib.dsv4_last_error().decode()
+
+
+def test_compress_chunk_validation(L):
+    f = L.lib.dsv4_compress_chunk
+    C = L._lib.Compressor
+    good = C(FAKE, FAKE, 64, FAKE, None, 0, None, 0)
+    mx = C(FAKE, FAKE, 64, FAKE, None, 3, None, 0)                       # MXFP4 entries without scales
+    bad_raw = C(FAKE, FAKE, 64, FAKE, None, 0, FAKE, 3)                 # MXFP4 window rows
+    r = ctypes.byref
+    assert f(FAKE, 4, 16, 64, 1, 4, 1, r(good), r(mx), 128, None, None) == 1
+    assert "scales" in err(L)
+    assert f(FAKE, 4, 16, 64, 1, 4, 1, r(good), None, 128, r(bad_raw), None) == 2
+    assert f(FAKE, 0, 16, 64, 1, 4, 3, r(good), None, 128, None, None) == 1          # no left context
+    assert "left context" in err(L)
+    assert f(FAKE, 4, 16, 64, 1, 4, -1, None, r(good), 128, None, None) == 1         # block0 < 0
+    assert f(FAKE, 4, 16, 64, 1, 4, 0, None, None, 0, r(good), None) == 1            # m' = 0
+    assert f(None, 4, 16, 64, 1, 4, 0, r(good), None, 128, None, None) == 1          # null H
+    assert f(FAKE, 4, 0, 64, 1, 4, 1, r(good), r(good), 128, r(good), None) == 0     # n = 0 no-op
+    assert f(FAKE, 4, 16, 64, 1, 4, 1, None, None, 128, None, None) == 0             # nothing to do
 
 
 def test_compress_validation(L):

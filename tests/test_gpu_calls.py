@@ -120,6 +120,65 @@ def test_compress_validation_errors(L):
     assert e.value.status == 2
 
 
+CHUNK_CASES = [
+    # (n, d, n_left, block0, (c, layout, raw layout) of CSA KV / keys / HCA or None)
+    (520, 256, 4, 5, (256, ROW_FP8, ROW_FP8), (64, ROW_MXFP4, None), (256, ROW_FP8, ROW_FP8)),   # fused, ragged
+    (512, 192, 4, 0, (128, ROW_BF16, None), None, (64, ROW_F32, ROW_BF16)),                     # fused, no keys
+    (300, 128, 4, 2, (64, ROW_F32, ROW_F32), (32, ROW_MXFP4, None), None),                      # keys c = 32: one by one
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[str(i) for i in range(len(CHUNK_CASES))])
+def test_compress_chunk_equals_separate_calls(L, case):
+    """The compressors of a chunk in one call give the separate calls' rows
+    bit for bit (those calls are checked against the oracle above)."""
+    import torch
+    n, d, n_left, block0, kv, ki, hc = case
+    seed = 900 + n + d
+    H = dev(act_arr(seed, "H", (n_left + n, d), 1.0, "bf16"))
+
+    def job(name, spec, mult, ratio):
+        if spec is None:
+            return None
+        c, cl, rl = spec
+        W = dev(act_arr(seed, "W_" + name, (mult * c, d), 2.0 / math.sqrt(d), "bf16"))
+        B = dev(G.normal(seed, "B_" + name, (2, ratio, c) if mult == 4 else (ratio, c), 0.5))
+        S = n // ratio
+
+        def outs():
+            comp = empty_rows(max(S, 1), cl, c)
+            sc = torch.zeros((max(S, 1), c // 32), dtype=torch.uint8, device="cuda") if cl == ROW_MXFP4 else None
+            raw = empty_rows(n, rl, c) if rl is not None else None
+            return comp, sc, raw
+        return dict(W=W, B=B, c=c, cl=cl, rl=rl if rl is not None else ROW_F32, fused=outs(), sep=outs())
+
+    jobs = {"kv": job("kv", kv, 4, 4), "ki": job("ki", ki, 4, 4), "hca": job("hca", hc, 2, 128)}
+    mk = lambda j: None if j is None else L.compressor(j["W"], j["B"], j["c"], j["fused"][0], j["cl"],
+                                                      comp_scales=j["fused"][1], raw_out=j["fused"][2],
+                                                      raw_layout=j["rl"])
+    L.compress_chunk(H, 4, n_left=n_left, block0=block0, csa_kv=mk(jobs["kv"]), csa_keys=mk(jobs["ki"]),
+                     m_prime=128, hca=mk(jobs["hca"]))
+    for name in ("kv", "ki"):
+        j = jobs[name]
+        if j is not None:
+            comp, sc, raw = j["sep"]
+            L.csa_compress(H, j["W"], j["B"], 4, j["c"], comp, j["cl"], n_left=n_left, block0=block0,
+                           comp_scales=sc, raw_out=raw, raw_layout=j["rl"])
+    j = jobs["hca"]
+    if j is not None:
+        comp, sc, raw = j["sep"]
+        L.hca_compress(H[n_left:], j["W"], j["B"], 128, j["c"], comp, j["cl"], comp_scales=sc, raw_out=raw,
+                       raw_layout=j["rl"])
+    torch.cuda.synchronize()
+    for name, j in jobs.items():
+        if j is None:
+            continue
+        for a, b in zip(j["fused"], j["sep"]):
+            if a is not None:
+                assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                                   b.view(torch.uint8) if b.dtype != torch.uint8 else b), name
+
+
 # ====================================================================== indexer
 
 IDX_CASES = [
