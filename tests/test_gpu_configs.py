@@ -228,3 +228,23 @@ def test_cfg5_layer_pair(L):
     ref_h = O.hca_dense(decode_act(inp["q_hca"])[rows], hc_all, mp, win_h, P - nw, nw, pos,
                         inp["sink_hca"].astype(np.float64), scale)
     assert_close(decode_act(host(layer.out_hca[rows])), ref_h, what="hca output")
+
+
+def test_cfg5_step_is_bitwise_repeatable(L):
+    """Every reduction order in the step is fixed (no floating-point atomics,
+    split-K merged in split order, exact integer top-k), so two steps over the
+    same chunk give the same bytes in every output: caches, scores, indices
+    and both attention outputs."""
+    import torch
+    from long_context_attention_08_amd.layer import pair_from_arrays
+    layer = pair_from_arrays(G.make(5))
+    outs = lambda: [t.clone() for t in (layer.kv_new, layer.kv_win_new, layer.ki_new, layer.ki_sc_new, layer.hca_new,
+                                        layer.hca_win_new, layer.scores, layer.idx, layer.out, layer.out_hca)]
+    layer.step()
+    torch.cuda.synchronize()
+    first = outs()
+    layer.step()
+    torch.cuda.synchronize()
+    for a, b in zip(first, outs()):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b)
