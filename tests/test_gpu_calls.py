@@ -121,10 +121,11 @@ def test_compress_validation_errors(L):
 
 
 CHUNK_CASES = [
-    # (n, d, n_left, block0, (c, layout, raw layout) of CSA KV / keys / HCA or None)
-    (520, 256, 4, 5, (256, ROW_FP8, ROW_FP8), (64, ROW_MXFP4, None), (256, ROW_FP8, ROW_FP8)),   # fused, ragged
-    (512, 192, 4, 0, (128, ROW_BF16, None), None, (64, ROW_F32, ROW_BF16)),                     # fused, no keys
-    (300, 128, 4, 2, (64, ROW_F32, ROW_F32), (32, ROW_MXFP4, None), None),                      # keys c = 32: one by one
+    # (H dtype, n, d, n_left, block0, (c, layout, raw layout) of CSA KV / keys / HCA or None)
+    ("bf16", 520, 256, 4, 5, (256, ROW_FP8, ROW_FP8), (64, ROW_MXFP4, None), (256, ROW_FP8, ROW_FP8)),  # fused, ragged
+    ("bf16", 512, 192, 4, 0, (128, ROW_BF16, None), None, (64, ROW_F32, ROW_BF16)),                    # fused, no keys
+    ("bf16", 300, 128, 4, 2, (64, ROW_F32, ROW_F32), (32, ROW_MXFP4, None), None),     # keys c = 32: one by one
+    ("f32", 260, 64, 4, 3, (64, ROW_F32, ROW_F32), None, (32, ROW_BF16, ROW_F32)),     # f32 H: HCA rows start n_left in
 ]
 
 
@@ -133,15 +134,15 @@ def test_compress_chunk_equals_separate_calls(L, case):
     """The compressors of a chunk in one call give the separate calls' rows
     bit for bit (those calls are checked against the oracle above)."""
     import torch
-    n, d, n_left, block0, kv, ki, hc = case
+    dt, n, d, n_left, block0, kv, ki, hc = case
     seed = 900 + n + d
-    H = dev(act_arr(seed, "H", (n_left + n, d), 1.0, "bf16"))
+    H = dev(act_arr(seed, "H", (n_left + n, d), 1.0, dt))
 
     def job(name, spec, mult, ratio):
         if spec is None:
             return None
         c, cl, rl = spec
-        W = dev(act_arr(seed, "W_" + name, (mult * c, d), 2.0 / math.sqrt(d), "bf16"))
+        W = dev(act_arr(seed, "W_" + name, (mult * c, d), 2.0 / math.sqrt(d), dt))
         B = dev(G.normal(seed, "B_" + name, (2, ratio, c) if mult == 4 else (ratio, c), 0.5))
         S = n // ratio
 
