@@ -212,9 +212,31 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
  * covered, else DSV4_ERR_INVALID_ARG.  idx [B, nq, k] int32.
  * ws: workspace of dsv4_attn_workspace_size() bytes, where dense is 0 for this
  * call and 1 for dsv4_hca_dense_fwd, and max_keys bounds the compressed
- * entries plus window rows of any query (k + n_win here; S + n_win for HCA).
+ * entries plus window rows of any query (k + n_win here; S + n_win for HCA);
+ * the exact need of a call is dsv4_attn_plan()'s workspace_bytes.  A smaller
+ * workspace fails with DSV4_ERR_WORKSPACE before anything is launched.
  */
 size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c, int64_t max_keys);
+
+/*
+ * Launch plan of an attention call (host only, no HIP call): the kernel that
+ * runs, how many queries share a block, and how a block's key slots are split
+ * across blocks (splits > 1: fp32 partials in the workspace, merged in split
+ * order).  workspace_bytes is exactly what the call with these arguments
+ * needs; dsv4_attn_workspace_size() bounds it from above.  Arguments as for
+ * the calls themselves: dense 0 is dsv4_sparse_mqa_fwd (k used), dense 1 is
+ * dsv4_hca_dense_fwd (m_prime used); q_pos0 is a host array [B].  Returns
+ * DSV4_OK, DSV4_ERR_INVALID_ARG or DSV4_ERR_UNSUPPORTED (as the call would).
+ */
+typedef struct {
+  int path;                /* 0 generic fp32-math kernel, 1 bf16-row MFMA (c = 128), 2 FP8-row MFMA (c = 512) */
+  int queries_per_block;
+  int splits;              /* key-slot splits of a query group (blocks per group) */
+  int split_slots;         /* key slots per split (splits > 1) */
+  size_t workspace_bytes;
+} dsv4_attn_plan_t;
+int dsv4_attn_plan(int dense, int q_dtype, int kv_layout, int64_t B, int64_t nq, int nh, int c, int64_t S,
+                   int k, int m_prime, int n_win, const int64_t* q_pos0, dsv4_attn_plan_t* plan);
 int dsv4_sparse_mqa_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
                         const void* kv_comp, int kv_layout, int64_t S,
                         const int32_t* idx, int k,

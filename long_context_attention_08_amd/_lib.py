@@ -19,7 +19,7 @@ EXPORTS = [
     "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
-    "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size",
+    "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size", "dsv4_attn_plan",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
     "dsv4_stream_state_bytes", "dsv4_stream_state_reset", "dsv4_stream_workspace_size",
     "dsv4_stream_compress", "dsv4_swa_ring_pos0",
@@ -74,6 +74,16 @@ _sig("dsv4_output_proj", _int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _in
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
+
+
+class AttnPlan(ctypes.Structure):
+    """dsv4_attn_plan_t"""
+    _fields_ = [("path", ctypes.c_int), ("queries_per_block", ctypes.c_int), ("splits", ctypes.c_int),
+                ("split_slots", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_sig("dsv4_attn_plan", _int, [_int, _int, _int, _i64, _i64, _int, _int, _i64, _int, _int, _int, _P64,
+                              ctypes.POINTER(AttnPlan)])
 _sig("dsv4_sparse_mqa_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _vp, _int,
                                    _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
 _sig("dsv4_hca_dense_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _int,
@@ -225,6 +235,14 @@ def topk_select(scores, m, q_pos0, k, idx_out, ws=None, *, stream=None):
 
 def attn_workspace_size(dense, B, nq, nh, c, max_keys):
     return int(lib.dsv4_attn_workspace_size(1 if dense else 0, B, nq, nh, c, max_keys))
+
+
+def attn_plan(dense, q_dtype, kv_layout, B, nq, nh, c, S, k, m_prime, n_win, q_pos0):
+    """The launch plan of an attention call (host only): an AttnPlan."""
+    p = AttnPlan()
+    _check(lib.dsv4_attn_plan(1 if dense else 0, q_dtype, kv_layout, B, nq, nh, c, S, k, m_prime, n_win,
+                              _host_i64(q_pos0), ctypes.byref(p)))
+    return p
 
 
 def sparse_mqa_fwd(q, kv_comp, kv_layout, idx, kv_win, win_pos0, n_win, q_pos0, sink, scale, out,

@@ -255,7 +255,7 @@ int dsv4_indexer_score_fp8q(const void* qI, int q_dtype, const float* wI,
 
 size_t dsv4_topk_workspace_size(int64_t B, int64_t nq, int64_t S, int k) {
   if (B <= 0 || nq <= 0 || S <= 0 || k <= 0) return 0;
-  return dsv4::topk_workspace_bytes(B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq, S, k);
+  return dsv4::topk_make_plan(B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq, S, k).bytes;
 }
 
 int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
@@ -272,11 +272,11 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
   if (S > 0 && !scores) return fail(DSV4_ERR_INVALID_ARG, "%s: scores is NULL", fn);
   if (S >= (int64_t)1 << 31) return fail(DSV4_ERR_UNSUPPORTED, "%s: S >= 2^31", fn);
   const int64_t rows = B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq;
-  if (!dsv4::topk_supported(rows, S > 0 ? S : 1, k)) return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
-  const size_t need = dsv4::topk_workspace_bytes(rows, S > 0 ? S : 1, k);
-  if (ws_bytes < need || (need && !ws))
-    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
-  return hip_status(dsv4::launch_topk(scores, B, nq, S, m, q_pos0, k, idx_out, ws,
+  const dsv4::TopkPlan plan = dsv4::topk_make_plan(rows, S > 0 ? S : 1, k);
+  if (!plan.supported) return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
+  if (ws_bytes < plan.bytes || (plan.bytes && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.bytes);
+  return hip_status(dsv4::launch_topk(scores, B, nq, S, m, q_pos0, k, idx_out, ws, plan,
                                       reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
@@ -284,7 +284,31 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
 
 size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c, int64_t max_keys) {
   if (B <= 0 || nq <= 0 || nh <= 0 || c <= 0) return 0;
-  return dsv4::attn_workspace_bytes(B, nq, nh, c, max_keys + 64, dense != 0);
+  return dsv4::attn_workspace_bound(B, nq, nh, c, max_keys, dense != 0);
+}
+
+int dsv4_attn_plan(int dense, int q_dtype, int kv_layout, int64_t B, int64_t nq, int nh, int c, int64_t S,
+                   int k, int m_prime, int n_win, const int64_t* q_pos0, dsv4_attn_plan_t* plan) {
+  const char* fn = "dsv4_attn_plan";
+  if (!plan) return fail(DSV4_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+  if (B < 0 || nq < 0 || nh <= 0 || c <= 0 || S < 0 || n_win < 0 || k < 0 || (dense && m_prime <= 0))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (c > 1024 || !act_ok(q_dtype) || !kv_layout_ok(kv_layout, c))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: dtype, layout or c", fn);
+  if (B > 0 && nq > 0 && !q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  for (int64_t b = 0; b < B && nq > 0; ++b)
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+  dsv4::AttnArgs a{};
+  a.q_dtype = q_dtype; a.B = B; a.nq = nq; a.nh = nh; a.c = c; a.kv_layout = kv_layout; a.S = S;
+  a.k = dense ? 0 : k; a.ratio = dense ? m_prime : 1; a.n_win = n_win; a.scale = 1.f;
+  const dsv4::AttnLaunchPlan lp =
+      dsv4::attn_make_plan(a, dense != 0, B > 0 && nq > 0 ? dsv4::attn_group_slots(a, q_pos0, dense != 0) : 0);
+  plan->path = lp.path;
+  plan->queries_per_block = lp.pl.qpw;
+  plan->splits = lp.pl.max_splits;
+  plan->split_slots = lp.pl.max_splits > 1 ? lp.pl.chunk : 0;
+  plan->workspace_bytes = B > 0 && nq > 0 ? lp.ws_bytes : 0;
+  return ok();
 }
 
 static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, int64_t B, int64_t nq, int nh,
@@ -322,18 +346,13 @@ static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, i
                     (long long)(win_pos0[b] + W));
     }
   }
-  int64_t max_keys = 0;
-  for (int64_t b = 0; b < B; ++b) {
-    const int64_t nc = dense ? dsv4::visible_count(q_pos0[b] + nq - 1, ratio, S) : k;
-    const int64_t kk = nc + (n_win > 0 ? n_win + 7 : 0);
-    max_keys = kk > max_keys ? kk : max_keys;
-  }
-  const size_t need = dsv4::attn_workspace_bytes(B, nq, nh, c, max_keys, dense);
-  if (ws_bytes < need || (need && !ws))
-    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   dsv4::AttnArgs a{q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, dense ? nullptr : idx, dense ? 0 : k,
                    dense ? ratio : 1, kv_win, W, n_win, sink, scale, out, ws, ws_bytes};
-  return hip_status(dsv4::launch_attn(a, q_pos0, win_pos0, dense, reinterpret_cast<hipStream_t>(stream)), fn);
+  // one plan serves the check and the launch
+  const dsv4::AttnLaunchPlan plan = dsv4::attn_make_plan(a, dense, dsv4::attn_group_slots(a, q_pos0, dense));
+  if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.ws_bytes);
+  return hip_status(dsv4::launch_attn(a, q_pos0, win_pos0, plan, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 int dsv4_sparse_mqa_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,

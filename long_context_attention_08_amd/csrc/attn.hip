@@ -21,15 +21,6 @@
 
 namespace dsv4 {
 
-struct AttnPlan {
-  int64_t units_per_b;   // query groups per batch entry
-  int qpw;               // queries per group
-  int chunk;             // key slots per split (multiple of 32)
-  int max_splits;        // grid.y
-  int dense;
-  float scale_log2;
-};
-
 struct UnitInfo {
   int64_t t0, tl;        // first and last query of the group
   int64_t ncomp;         // compressed-entry slots
@@ -182,7 +173,7 @@ constexpr int TS = 32;           // key slots per tile
 // zero (their logits are masked; a zero value keeps P = 0 from meeting a
 // non-finite byte pattern in PV).  Read-only; zero-initialised at load.
 __device__ __align__(16) uint8_t g_zero_row[1024];
-constexpr int SIDX_CAP = 2048;   // index-list slots a sparse block caches in LDS
+constexpr int SIDX_CAP = ATTN_SIDX_CAP;   // index-list slots a sparse block caches in LDS
 
 // The copies of one wave for one tile: copy q = wv + NW i (q < NDMA) takes
 // bytes 32 q + 16 G of each lane's row (offset 32 NW i from `base`, which
@@ -1179,63 +1170,9 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   }
 }
 
-// ------------------------------------------------------------------ planning and launch
-static bool attn_mfma_ok(const AttnArgs& a, bool dense) {
-  if (a.q_dtype != ACT_BF16 || (a.kv_layout != ROW_BF16 && a.kv_layout != ROW_FP8)) return false;
-  if (!dense && a.k > SIDX_CAP) return false;
-  // c = 512 with bf16 rows: two 32 KB stages and three key tiles exceed the
-  // 160 KB of LDS, so that layout takes the generic kernel
-  if (a.c == 512) {
-    if (a.kv_layout != ROW_FP8) return false;
-    return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
-  }
-  if (a.c == 128) return dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64 || a.nh == 128)
-                               : (a.nh == 32 || a.nh == 64 || a.nh == 128);
-  return false;
-}
-
-// rows per block: one query (sparse) or 128 rows of queries sharing their keys
-// (dense); c = 512 keeps 64 rows per block: Q^T and O^T of 32 rows x 256
-// channels already take 192 registers per wave (all 512 channels of 32 rows
-// in one wave would need 384 and spill)
-static int rows_per_block(const AttnArgs& a, bool dense) {
-  if (!dense) return a.nh;
-  if (a.c >= 512) return a.nh < 64 ? 64 : a.nh;
-  return a.nh > 128 ? a.nh : 128;
-}
-
-static AttnPlan make_plan(const AttnArgs& a, bool dense, int64_t max_keys) {
-  AttnPlan pl;
-  pl.dense = dense ? 1 : 0;
-  pl.scale_log2 = a.scale * LOG2E;
-  pl.qpw = rows_per_block(a, dense) / a.nh;
-  if (pl.qpw < 1) pl.qpw = 1;
-  pl.units_per_b = (a.nq + pl.qpw - 1) / pl.qpw;
-  // split the keys only when a sequence has few query groups.  The split size
-  // depends on the key bound alone (never on the batch), so a sequence's
-  // results do not depend on the batch: about 16 splits of at least 256 slots,
-  // so that a split's fp32 partial (rows x c) stays small next to the rows it reads
-  if (pl.units_per_b >= 32) {
-    pl.chunk = 1 << 30;
-    pl.max_splits = 1;
-  } else {
-    int64_t ch = (max_keys + 15) / 16;
-    ch = ch < 256 ? 256 : ch;
-    pl.chunk = (int)((ch + 31) / 32 * 32);
-    int64_t ms = (max_keys + pl.chunk - 1) / pl.chunk;
-    pl.max_splits = (int)(ms < 1 ? 1 : ms);
-  }
-  return pl;
-}
-
-size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense) {
-  AttnArgs a = {};
-  a.nq = nq; a.nh = nh; a.c = c; a.scale = 1.f;
-  AttnPlan pl = make_plan(a, dense, max_keys);
-  if (pl.max_splits == 1) return 0;
-  const int64_t units = (B < MAXB ? B : MAXB) * pl.units_per_b;
-  return (size_t)units * pl.max_splits * pl.qpw * nh * (c + 2) * sizeof(float);
-}
+// ------------------------------------------------------------------ launch
+// The plan (path, rows per block, split) comes from attn_make_plan, the same
+// function the argument checks sized the workspace with.
 
 template <int C, int KVL, int CS, int NRG_MAX>
 static void launch_mfma_c(const AttnArgs& a, dim3 grid, int nrg, const PosTable& pt, int b0, const AttnPlan& pl,
@@ -1249,32 +1186,24 @@ static void launch_mfma_c(const AttnArgs& a, dim3 grid, int nrg, const PosTable&
   }
 }
 
-hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0, bool dense, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0, const AttnLaunchPlan& lp,
+                       hipStream_t s) {
   if (a.B <= 0 || a.nq <= 0) return hipSuccess;
-  const bool mf = attn_mfma_ok(a, dense);
-  const int qpw = mf ? rows_per_block(a, dense) / a.nh : 1;
-  // most key slots any group can have
-  int64_t max_keys = 0;
-  for (int64_t b = 0; b < a.B; ++b) {
-    const int64_t pl_ = q_pos0[b] + a.nq - 1;
-    const int64_t ncomp = dense ? visible_count(pl_, a.ratio, a.S) : a.k;
-    const int64_t wl = a.n_win > 0 ? a.n_win + (qpw < a.nq ? qpw : a.nq) - 1 : 0;
-    max_keys = ncomp + wl > max_keys ? ncomp + wl : max_keys;
-  }
+  // the partials of a split launch must fit the workspace the checks accepted
+  if (lp.ws_bytes > 0 && (a.ws == nullptr || a.ws_bytes < lp.ws_bytes)) return hipErrorInvalidValue;
+  const AttnPlan& pl = lp.pl;
   for (int64_t b0 = 0; b0 < a.B; b0 += MAXB) {
     const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = win_pos0 ? win_pos0[b0 + i] : 0; }
-    if (mf) {
-      AttnPlan pl = make_plan(a, dense, max_keys);
+    if (lp.path != ATTN_GENERIC) {
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
-      const int nrg = rows_per_block(a, dense) / 32;
-      if (a.c == 512) {
-        if (nrg == 1) hipLaunchKernelGGL(attn_f8<1>, grid, dim3(128), 0, s, a, pt, (int)b0, pl);
+      if (lp.path == ATTN_F8) {
+        if (lp.nrg == 1) hipLaunchKernelGGL(attn_f8<1>, grid, dim3(128), 0, s, a, pt, (int)b0, pl);
         else hipLaunchKernelGGL(attn_f8<2>, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
       } else {
-        if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
-        else launch_mfma_c<128, ROW_BF16, 1, 4>(a, grid, nrg, pt, (int)b0, pl, s);
+        if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1, 4>(a, grid, lp.nrg, pt, (int)b0, pl, s);
+        else launch_mfma_c<128, ROW_BF16, 1, 4>(a, grid, lp.nrg, pt, (int)b0, pl, s);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1285,13 +1214,6 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
         else hipLaunchKernelGGL(attn_combine<2>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
       }
     } else {
-      AttnPlan pl = {};
-      pl.dense = dense ? 1 : 0;
-      pl.qpw = 1;
-      pl.units_per_b = a.nq;
-      pl.chunk = 1 << 30;
-      pl.max_splits = 1;
-      pl.scale_log2 = a.scale * LOG2E;
       hipLaunchKernelGGL(attn_generic, dim3((unsigned)(nb * a.nq * a.nh)), dim3(256), 0, s, a, pt, (int)b0, pl);
     }
     hipError_t e = hipGetLastError();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dsv4_internal.h"
+
 namespace dsv4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -13,10 +15,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-enum { ACT_F32 = 0, ACT_BF16 = 1 };
-enum { ROW_F32 = 0, ROW_BF16 = 1, ROW_FP8 = 2, ROW_MXFP4 = 3 };
-constexpr int ROPE_DIMS = 64;   // the last 64 dims of a KV row stay bf16
 
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -215,13 +213,5 @@ __device__ __forceinline__ float sum_halves(float v) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// position of the first entry NOT visible at position p for ratio m: entries
-// s < floor((p+1)/m) satisfy m*(s+1) <= p+1
-__host__ __device__ __forceinline__ int64_t visible_count(int64_t p, int64_t m, int64_t S) {
-  int64_t v = (p + 1) / m;
-  if (v < 0) v = 0;
-  return v < S ? v : S;
-}
 
 }  // namespace dsv4

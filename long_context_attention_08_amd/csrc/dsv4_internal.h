@@ -5,7 +5,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__HIPCC__)
+#define DSV4_HD __host__ __device__
+#else
+#define DSV4_HD
+#endif
+
 namespace dsv4 {
+
+enum { ACT_F32 = 0, ACT_BF16 = 1 };
+enum { ROW_F32 = 0, ROW_BF16 = 1, ROW_FP8 = 2, ROW_MXFP4 = 3 };
+constexpr int ROPE_DIMS = 64;   // the last 64 dims of a KV row stay bf16
+
+// number of entries visible at position p for ratio m: entries s < floor((p+1)/m)
+// satisfy m*(s+1) <= p+1
+DSV4_HD inline int64_t visible_count(int64_t p, int64_t m, int64_t S) {
+  int64_t v = (p + 1) / m;
+  if (v < 0) v = 0;
+  return v < S ? v : S;
+}
 
 struct CompressArgs {
   const void* H;        // [n_left + n, d]
@@ -55,10 +73,33 @@ struct PosTable {
 // q_pos0: host array [B]
 hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s);
 
-size_t topk_workspace_bytes(int64_t rows, int64_t S, int k);
-bool topk_supported(int64_t rows, int64_t S, int k);
+// ---- top-k planning (plan.cpp; host only)
+constexpr int SK_KMAX = 1024;     // largest k of the streaming and histogram selects
+constexpr int HS_BIN = 2048;      // histogram bins of the histogram select (11-bit digits)
+constexpr int HS_CAP = 8192;      // threshold-bin candidates of the histogram select
+constexpr int TK_MAX_CAND = 16384;   // part winners a stage-2 merge holds in LDS
+
+struct HsMeta {
+  int bstar;         // threshold bin (-1: every visible score is taken)
+  uint32_t above;    // visible keys in bins above bstar (all winners)
+  uint32_t inbin;    // visible keys in bin bstar
+  uint32_t need;     // min(k, visible)
+};
+
+enum { TOPK_STREAM = 0, TOPK_STAGE = 1, TOPK_HIST = 2 };
+struct TopkPlan {
+  int kind;          // TOPK_*
+  int part, nparts;  // scores per part, parts per row
+  bool supported;
+  size_t bytes;      // workspace the launch uses
+  // histogram select: byte offsets of its workspace arrays
+  size_t o_suf, o_off, o_meta, o_win, o_cand;
+};
+// plan for `rows` rows (of one launch: at most MAXB batch entries) of S scores
+TopkPlan topk_make_plan(int64_t rows, int64_t S, int k);
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
-                       const int64_t* q_pos0, int k, int32_t* idx, void* ws, hipStream_t s);
+                       const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan,
+                       hipStream_t s);
 
 struct AttnArgs {
   const void* q;        // [B, nq, nh, c]
@@ -150,8 +191,35 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
-size_t attn_workspace_bytes(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense);
+// ---- attention planning (plan.cpp; host only)
+// Kernel-visible part of a plan: how queries form blocks and how key slots split.
+struct AttnPlan {
+  int64_t units_per_b;   // query groups per batch entry
+  int qpw;               // queries per group
+  int chunk;             // key slots per split (multiple of 32)
+  int max_splits;        // grid.y
+  int dense;
+  float scale_log2;
+};
+enum { ATTN_GENERIC = 0, ATTN_MFMA = 1, ATTN_F8 = 2 };
+constexpr int ATTN_SIDX_CAP = 2048;   // index-list slots a sparse MFMA block caches in LDS
+constexpr int ATTN_QPW_MAX = 8;       // most queries one MFMA block serves
+struct AttnLaunchPlan {
+  int path;              // ATTN_*
+  int nrg;               // row groups of 32 rows per block (MFMA paths)
+  AttnPlan pl;
+  size_t ws_bytes;       // workspace bytes the launch writes (split partials)
+};
+// Key slots of the largest query group of a call: compressed entries of its
+// last query (dense) or k (sparse), plus the window positions its queries span.
+int64_t attn_group_slots(const AttnArgs& a, const int64_t* q_pos0, bool dense);
+// The plan of a call whose groups have at most `slots` key slots.  ws_bytes is
+// non-decreasing in `slots`, so a bound on the slots bounds the workspace.
+AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots);
+// Workspace bound for any call with these sizes whose queries see at most
+// max_keys compressed entries plus window rows each (every path and layout).
+size_t attn_workspace_bound(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense);
 hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* win_pos0,
-                       bool dense, hipStream_t s);
+                       const AttnLaunchPlan& plan, hipStream_t s);
 
 }  // namespace dsv4

@@ -1,0 +1,200 @@
+// Host-side planning of the top-k and attention launches: which kernel runs,
+// how a row or a query group is split into parts, and how many workspace
+// bytes the launch writes.  The C ABI's size queries, its argument checks and
+// the launchers all call these functions, so a workspace the checks accept is
+// exactly the one the kernels use.  No HIP calls (plain host code).
+#include "dsv4_internal.h"
+
+namespace dsv4 {
+
+// ------------------------------------------------------------------ top-k
+
+// histogram select for few long rows: parts of at least 8192 scores, at most 64
+static bool hs_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
+  if (k > SK_KMAX || rows >= 512 || S <= 16384) return false;
+  int64_t np = (512 + rows - 1) / rows;
+  const int64_t by_len = S / 8192;
+  if (np > by_len) np = by_len;
+  if (np > 64) np = 64;
+  if (np < 2) np = 2;
+  const int64_t p = (S + np - 1) / np;
+  *part = (int)p;
+  *nparts = (int)((S + p - 1) / p);
+  return true;
+}
+
+static void topk_parts(int64_t rows, int64_t S, int k, int* part, int* nparts) {
+  if (k <= SK_KMAX) {
+    // streaming: whole rows when there are enough of them, else up to 16
+    // parts of at least 16384 scores so that some 512 blocks run
+    int np = 1;
+    if (rows < 512 && S > 16384) {
+      np = (int)((512 + rows - 1) / rows);
+      const int64_t by_len = S / 16384;
+      if (np > by_len) np = (int)by_len;
+      if (np > 16) np = 16;
+      if (np < 1) np = 1;
+    }
+    int64_t p = (S + np - 1) / np;
+    p = (p + 3) / 4 * 4;                       // parts start 16-byte aligned in aligned rows
+    *part = (int)p;
+    *nparts = (int)((S + p - 1) / p);
+    return;
+  }
+  int p = k <= 1024 ? 32768 : 16384;
+  if (rows < 256 && S > 16384 && k <= 1024) p = 16384;   // more blocks for few rows
+  int fit = 4096;                                         // short rows: a smaller LDS stage
+  while (fit < S && fit < p) fit <<= 1;
+  p = fit < p ? fit : p;
+  *part = p;
+  *nparts = (int)((S + p - 1) / p);
+}
+
+TopkPlan topk_make_plan(int64_t rows, int64_t S, int k) {
+  TopkPlan t = {};
+  if (rows <= 0 || S <= 0 || k <= 0) {
+    t.kind = TOPK_STREAM;
+    t.part = 1;
+    t.nparts = 1;
+    t.supported = k >= 1 && k <= 4096;
+    return t;
+  }
+  if (hs_plan(rows, S, k, &t.part, &t.nparts)) {
+    t.kind = TOPK_HIST;
+    t.supported = true;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o = 0;
+    t.o_suf = o; o = al(o + (size_t)rows * t.nparts * HS_BIN * 4);
+    t.o_off = o; o = al(o + (size_t)rows * t.nparts * 2 * 4);
+    t.o_meta = o; o = al(o + (size_t)rows * sizeof(HsMeta));
+    t.o_win = o; o = al(o + (size_t)rows * k * 8);
+    t.o_cand = o; o = al(o + (size_t)rows * HS_CAP * 8);
+    t.bytes = o;
+    return t;
+  }
+  topk_parts(rows, S, k, &t.part, &t.nparts);
+  t.kind = k <= SK_KMAX ? TOPK_STREAM : TOPK_STAGE;
+  t.supported = k <= 4096 && (t.nparts == 1 || (int64_t)t.nparts * k <= TK_MAX_CAND);
+  t.bytes = t.nparts > 1 ? (size_t)rows * t.nparts * k * sizeof(uint64_t) : 0;
+  return t;
+}
+
+// ------------------------------------------------------------------ attention
+
+static int attn_path(const AttnArgs& a, bool dense) {
+  if (a.q_dtype != ACT_BF16 || (a.kv_layout != ROW_BF16 && a.kv_layout != ROW_FP8)) return ATTN_GENERIC;
+  if (!dense && a.k > ATTN_SIDX_CAP) return ATTN_GENERIC;
+  // c = 512 with bf16 rows: two 32 KB stages and three key tiles exceed the
+  // 160 KB of LDS, so that layout takes the generic kernel
+  if (a.c == 512) {
+    if (a.kv_layout != ROW_FP8) return ATTN_GENERIC;
+    const bool ok = dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
+    return ok ? ATTN_F8 : ATTN_GENERIC;
+  }
+  if (a.c == 128) {
+    const bool ok = dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64 || a.nh == 128)
+                          : (a.nh == 32 || a.nh == 64 || a.nh == 128);
+    return ok ? ATTN_MFMA : ATTN_GENERIC;
+  }
+  return ATTN_GENERIC;
+}
+
+// rows per block: one query (sparse) or 128 rows of queries sharing their keys
+// (dense); c = 512 keeps 64 rows per block: Q^T and O^T of 32 rows x 256
+// channels already take 192 registers per wave (all 512 channels of 32 rows
+// in one wave would need 384 and spill)
+static int rows_per_block(const AttnArgs& a, bool dense) {
+  if (!dense) return a.nh;
+  if (a.c >= 512) return a.nh < 64 ? 64 : a.nh;
+  return a.nh > 128 ? a.nh : 128;
+}
+
+static int queries_per_group(const AttnArgs& a, bool dense) {
+  if (attn_path(a, dense) == ATTN_GENERIC) return 1;
+  const int q = rows_per_block(a, dense) / a.nh;
+  return q < 1 ? 1 : q;
+}
+
+int64_t attn_group_slots(const AttnArgs& a, const int64_t* q_pos0, bool dense) {
+  const int64_t qpw = queries_per_group(a, dense);
+  int64_t best = 0;
+  for (int64_t b = 0; b < a.B; ++b) {
+    for (int64_t t0 = 0; t0 < a.nq; t0 += qpw) {
+      const int64_t tl = (t0 + qpw < a.nq ? t0 + qpw : a.nq) - 1;
+      const int64_t pf = q_pos0[b] + t0, pl = q_pos0[b] + tl;
+      const int64_t ncomp = dense ? visible_count(pl, a.ratio, a.S) : a.k;
+      int64_t wlen = 0;
+      if (a.n_win > 0) {
+        const int64_t wlo = pf - a.n_win + 1 > 0 ? pf - a.n_win + 1 : 0;
+        wlen = pl - wlo + 1;
+      }
+      best = ncomp + wlen > best ? ncomp + wlen : best;
+    }
+  }
+  return best;
+}
+
+AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
+  AttnLaunchPlan lp = {};
+  lp.path = attn_path(a, dense);
+  AttnPlan& pl = lp.pl;
+  pl.dense = dense ? 1 : 0;
+  pl.scale_log2 = a.scale * 1.4426950408889634f;
+  if (lp.path == ATTN_GENERIC) {
+    pl.qpw = 1;
+    pl.units_per_b = a.nq;
+    pl.chunk = 1 << 30;
+    pl.max_splits = 1;
+    lp.nrg = 0;
+    lp.ws_bytes = 0;
+    return lp;
+  }
+  const int rows = rows_per_block(a, dense);
+  lp.nrg = rows / 32;
+  pl.qpw = queries_per_group(a, dense);
+  pl.units_per_b = (a.nq + pl.qpw - 1) / pl.qpw;
+  // split the keys only when a sequence has few query groups.  The split size
+  // depends on the key bound alone (never on the batch), so a sequence's
+  // results do not depend on the batch.  The split count comes first and is
+  // non-decreasing in the bound: up to 16 splits of at least 256 slots, each
+  // split's fp32 partial (rows x c) small next to the rows it reads
+  if (pl.units_per_b >= 32 || slots <= 0) {
+    pl.chunk = 1 << 30;
+    pl.max_splits = 1;
+  } else {
+    int64_t ms = (slots + 255) / 256;
+    ms = ms < 1 ? 1 : (ms > 16 ? 16 : ms);
+    const int64_t per = (slots + ms - 1) / ms;
+    pl.chunk = (int)((per + 31) / 32 * 32);
+    pl.max_splits = (int)ms;
+  }
+  if (pl.max_splits > 1) {
+    const int64_t units = (a.B < MAXB ? a.B : MAXB) * pl.units_per_b;
+    lp.ws_bytes = (size_t)units * pl.max_splits * pl.qpw * a.nh * (size_t)(a.c + 2) * sizeof(float);
+  }
+  return lp;
+}
+
+size_t attn_workspace_bound(int64_t B, int64_t nq, int nh, int c, int64_t max_keys, bool dense) {
+  if (B <= 0 || nq <= 0 || nh <= 0 || c <= 0) return 0;
+  size_t best = 0;
+  const int layouts[3] = {ROW_F32, ROW_BF16, ROW_FP8};
+  for (int dt = ACT_F32; dt <= ACT_BF16; ++dt) {
+    for (int li = 0; li < 3; ++li) {
+      AttnArgs a = {};
+      a.B = B; a.nq = nq; a.nh = nh; a.c = c; a.q_dtype = dt; a.kv_layout = layouts[li];
+      a.k = dense ? 0 : (int)(max_keys < ATTN_SIDX_CAP ? max_keys : ATTN_SIDX_CAP);
+      a.scale = 1.f;
+      // a group's slots: one query's compressed entries and window rows, plus
+      // the extra window positions its other queries reach back to
+      const int64_t qpw = queries_per_group(a, dense);
+      const int64_t span = qpw < nq ? qpw : nq;
+      const int64_t slots = (max_keys > 0 ? max_keys : 0) + span - 1;
+      const AttnLaunchPlan lp = attn_make_plan(a, dense, slots);
+      best = lp.ws_bytes > best ? lp.ws_bytes : best;
+    }
+  }
+  return best;
+}
+
+}  // namespace dsv4

@@ -5,8 +5,9 @@
 // so "score descending, ties to the lower index" is plain descending order of
 // the composite, and the selected set is exactly { x >= T } for the k-th
 // largest composite T.  T is found by an MSD radix select in LDS (12-bit
-// digits, stopping as soon as a whole bin is taken), the winners are gathered
-// and bitonic-sorted in LDS.
+// digits in the k > 1024 stages, 11-bit digits in the streaming and histogram
+// selects; each stops as soon as a whole bin is taken), the winners are
+// gathered and bitonic-sorted in LDS.
 //
 // k <= 1024, streaming: one block per (row, part) reads its scores once from
 //          HBM.  A running threshold tau (a composite no larger than the k-th
@@ -29,7 +30,6 @@ namespace dsv4 {
 
 constexpr int TK_THREADS = 1024;
 constexpr int NBIN = 4096;
-constexpr int MAX_CAND = 16384;
 
 __device__ __forceinline__ uint32_t score_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -141,13 +141,6 @@ __device__ void bitonic_desc(uint64_t* buf, int n) {
     }
   }
 }
-
-struct HsMeta {
-  int bstar;         // threshold bin (-1: every visible score is taken)
-  uint32_t above;    // visible keys in bins above bstar (all winners)
-  uint32_t inbin;    // visible keys in bin bstar
-  uint32_t need;     // min(k, visible)
-};
 
 struct TopkArgs {
   const float* scores;
@@ -272,9 +265,7 @@ constexpr int SK_STEP = SK_NT * 4 * SK_U;   // scores per step
 // four blocks share a CU; a block's loop is latency-bound (a barrier and a
 // ballot append per step), and more blocks per CU raise the HBM rate
 constexpr int SK_CAP = 3584;
-constexpr int HS_CAP = 8192;                // threshold-bin candidates of the histogram select
 constexpr int SK_BIN = 2048;                // 11-bit digits
-constexpr int SK_KMAX = 1024;
 
 template <int CAP>
 struct SkSharedT {
@@ -629,7 +620,6 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
 //      keys than the candidate list (heavy ties), the select runs over the row
 //      in global memory instead.
 // The selected set is the same exact set as on every other path.
-constexpr int HS_BIN = 2048;
 constexpr int HS_PER = HS_BIN / SK_NT;     // bins per thread
 
 __device__ __forceinline__ int64_t hs_row(const TopkArgs& a, const PosTable& pt, int b0, int64_t row,
@@ -877,92 +867,20 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
     a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
 }
 
-// bytes of the histogram-select workspace for `rows` rows of `nparts` parts
-static size_t hs_bytes(int64_t rows, int nparts, int k, size_t* o_suf, size_t* o_off, size_t* o_meta,
-                       size_t* o_win, size_t* o_cand) {
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  size_t o = 0;
-  *o_suf = o; o = al(o + (size_t)rows * nparts * HS_BIN * 4);
-  *o_off = o; o = al(o + (size_t)rows * nparts * 2 * 4);
-  *o_meta = o; o = al(o + (size_t)rows * sizeof(HsMeta));
-  *o_win = o; o = al(o + (size_t)rows * k * 8);
-  *o_cand = o; o = al(o + (size_t)rows * HS_CAP * 8);
-  return o;
-}
-
-// histogram select for few long rows: parts of at least 8192 scores, at most 64
-static bool hs_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
-  if (k > SK_KMAX || rows >= 512 || S <= 16384) return false;
-  int64_t np = (512 + rows - 1) / rows;
-  const int64_t by_len = S / 8192;
-  if (np > by_len) np = by_len;
-  if (np > 64) np = 64;
-  if (np < 2) np = 2;
-  const int64_t p = (S + np - 1) / np;
-  *part = (int)p;
-  *nparts = (int)((S + p - 1) / p);
-  return true;
-}
-
-static void topk_plan(int64_t rows, int64_t S, int k, int* part, int* nparts) {
-  if (k <= SK_KMAX) {
-    // streaming: whole rows when there are enough of them, else up to 16
-    // parts of at least 16384 scores so that some 512 blocks run
-    int np = 1;
-    if (rows < 512 && S > 16384) {
-      np = (int)((512 + rows - 1) / rows);
-      const int64_t by_len = S / 16384;
-      if (np > by_len) np = (int)by_len;
-      if (np > 16) np = 16;
-      if (np < 1) np = 1;
-    }
-    int64_t p = (S + np - 1) / np;
-    p = (p + 3) / 4 * 4;                       // parts start 16-byte aligned in aligned rows
-    *part = (int)p;
-    *nparts = (int)((S + p - 1) / p);
-    return;
-  }
-  int p = k <= 1024 ? 32768 : 16384;
-  if (rows < 256 && S > 16384 && k <= 1024) p = 16384;   // more blocks for few rows
-  int fit = 4096;                                         // short rows: a smaller LDS stage
-  while (fit < S && fit < p) fit <<= 1;
-  p = fit < p ? fit : p;
-  *part = p;
-  *nparts = (int)((S + p - 1) / p);
-}
-
-size_t topk_workspace_bytes(int64_t rows, int64_t S, int k) {
-  int part, nparts;
-  if (hs_plan(rows, S, k, &part, &nparts)) {
-    size_t o1, o2, o3, o4, o5;
-    return hs_bytes(rows, nparts, k, &o1, &o2, &o3, &o4, &o5);
-  }
-  topk_plan(rows, S, k, &part, &nparts);
-  return nparts > 1 ? (size_t)rows * nparts * k * sizeof(uint64_t) : 0;
-}
-
-bool topk_supported(int64_t rows, int64_t S, int k) {
-  int part, nparts;
-  if (k >= 1 && hs_plan(rows, S, k, &part, &nparts)) return true;
-  topk_plan(rows, S, k, &part, &nparts);
-  return k >= 1 && k <= 4096 && (nparts == 1 || (int64_t)nparts * k <= MAX_CAND);
-}
-
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
-                       const int64_t* q_pos0, int k, int32_t* idx, void* ws, hipStream_t s) {
+                       const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan, hipStream_t s) {
   if (B <= 0 || nq <= 0) return hipSuccess;
   TopkArgs a = {};
   a.scores = scores; a.nq = nq; a.S = S; a.m = m; a.k = k; a.idx = idx;
-  const int64_t rows_l = (B < MAXB ? B : MAXB) * nq;
-  if (hs_plan(rows_l, S, k, &a.part, &a.nparts)) {
-    size_t o_suf, o_off, o_meta, o_win, o_cand;
-    hs_bytes(rows_l, a.nparts, k, &o_suf, &o_off, &o_meta, &o_win, &o_cand);
+  a.part = plan.part;
+  a.nparts = plan.nparts;
+  if (plan.kind == TOPK_HIST) {
     uint8_t* w = reinterpret_cast<uint8_t*>(ws);
-    a.hsuf = reinterpret_cast<uint32_t*>(w + o_suf);
-    a.hoff = reinterpret_cast<uint32_t*>(w + o_off);
-    a.hmeta = reinterpret_cast<HsMeta*>(w + o_meta);
-    a.hwin = reinterpret_cast<uint64_t*>(w + o_win);
-    a.hcand = reinterpret_cast<uint64_t*>(w + o_cand);
+    a.hsuf = reinterpret_cast<uint32_t*>(w + plan.o_suf);
+    a.hoff = reinterpret_cast<uint32_t*>(w + plan.o_off);
+    a.hmeta = reinterpret_cast<HsMeta*>(w + plan.o_meta);
+    a.hwin = reinterpret_cast<uint64_t*>(w + plan.o_win);
+    a.hcand = reinterpret_cast<uint64_t*>(w + plan.o_cand);
     hipError_t e = hipFuncSetAttribute((const void*)topk_h_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(HsShared));
     if (e != hipSuccess) return e;
@@ -980,10 +898,9 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
     }
     return hipSuccess;
   }
-  topk_plan(rows_l, S, k, &a.part, &a.nparts);
   a.cand = reinterpret_cast<uint64_t*>(ws);
   const int n2 = [&] { int p = 1; while (p < k) p <<= 1; return p; }();
-  const bool stream = k <= SK_KMAX;
+  const bool stream = plan.kind == TOPK_STREAM;
   const size_t lds1 = stream ? sizeof(SkShared) : (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
   const size_t lds2 = (size_t)a.nparts * k * 8 + NBIN * 4 + (size_t)n2 * 8;
   const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && S % 4 == 0 && a.part % 4 == 0;

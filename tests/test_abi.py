@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 27
+    assert len(syms) == 28
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -186,6 +186,78 @@ def test_attention_validation(L):
     st = g(FAKE, 1, 2, 1, 64, 512, FAKE, 2, 8192, 128, FAKE, 128, pos((1 << 20) - 127, (1 << 20) - 127), 128,
            pos(1 << 20, 1 << 20), None, 1.0, FAKE, None, 0, None)
     assert st in (1, 4)
+
+
+def _groups(nq, qpw):
+    return [(t0, min(t0 + qpw, nq) - 1) for t0 in range(0, nq, qpw)]
+
+
+def _group_slots(dense, k, m_prime, n_win, S, p0, t0, tl):
+    """Key slots of one query group, from the calls' definition: the compressed
+    entries of its last query (dense: m'(s+1) <= p+1, s < S; sparse: k) plus
+    the window positions [max(0, p - n_win + 1), p] of its queries."""
+    pf, pl = p0 + t0, p0 + tl
+    ncomp = min(S, (pl + 1) // m_prime) if dense else k
+    wlen = pl - max(0, pf - n_win + 1) + 1 if n_win > 0 else 0
+    return ncomp + wlen
+
+
+@pytest.mark.parametrize("dense", [True, False])
+def test_attention_workspace_plan_sweep(L, dense):
+    """The size query bounds the exact need of every call, and the plan covers
+    every key slot: for each query group, ceil(slots / split_slots) <= splits,
+    and the partials the kernels write (units x splits x rows x (c + 2) fp32,
+    units = groups of at most 64 sequences) fit the workspace the call needs.
+    Visible counts sweep 0 .. 300k with the neighbourhoods of the split-count
+    steps (multiples of 256 and 4096) in full."""
+    BF16, FP8, BF16ROW = L.BF16, L.ROW_FP8_ROPE_BF16, L.ROW_BF16
+    mp = 4
+    vis = set(range(0, 300001, 997)) | set(range(3800, 4400)) | set(range(250, 262))
+    vis |= {v + d for v in range(256, 300001, 4096) for d in (-33, -1, 0, 1, 31)}
+    shapes = [(512, 64, FP8), (512, 16, FP8), (128, 16, BF16ROW), (128, 64, BF16ROW)] if dense else \
+             [(512, 64, FP8), (128, 32, BF16ROW)]
+    checked = 0
+    for c, nh, lay in shapes:
+        for nq in (1, 4, 8):
+            for n_win in (0, 64, 128):
+                for B in (1, 3):
+                    for V in sorted(vis):
+                        if dense:
+                            S, k = 300000, 0
+                            p0 = [max(0, V * mp - nq) + b for b in range(B)]   # last query sees about V entries
+                        else:
+                            S, k = 1 << 20, max(1, min(2048, V))
+                            p0 = [V + 1000 * b for b in range(B)]
+                        pl = L.attn_plan(dense, BF16, lay, B, nq, nh, c, S, k, mp, n_win, p0)
+                        slots = [_group_slots(dense, k, mp, n_win, S, p, t0, tl)
+                                 for p in p0 for (t0, tl) in _groups(nq, pl.queries_per_block)]
+                        max_keys = max(min(S, (p + nq) // mp) if dense else k for p in p0) + n_win
+                        query = L.attn_workspace_size(dense, B, nq, nh, c, max_keys)
+                        assert query >= pl.workspace_bytes, (c, nh, nq, n_win, B, V)
+                        if pl.splits > 1:
+                            assert max(-(-x // pl.split_slots) for x in slots) <= pl.splits
+                            units = min(B, 64) * -(-nq // pl.queries_per_block)
+                            rows = pl.queries_per_block * nh
+                            assert units * pl.splits * rows * (c + 2) * 4 <= pl.workspace_bytes
+                        else:
+                            assert pl.workspace_bytes == 0
+                        checked += 1
+    assert checked > 1000
+
+
+def test_attention_workspace_regression_hca_decode(L):
+    """An HCA decode at the visible counts where the split count once differed
+    between the size query, the argument check and the launch: a workspace of
+    the documented size passes the check, and one byte less than the exact
+    need fails with DSV4_ERR_WORKSPACE before any launch."""
+    g = L.lib.dsv4_hca_dense_fwd
+    for V in (3962, 3965, 3968, 4096, 4097):
+        p = V * 128 + 5
+        need = L.attn_plan(True, L.BF16, L.ROW_FP8_ROPE_BF16, 1, 1, 64, 512, 8192, 0, 128, 128, [p]).workspace_bytes
+        assert 0 < need <= L.attn_workspace_size(True, 1, 1, 64, 512, 8192 + 128)
+        st = g(FAKE, 1, 1, 1, 64, 512, FAKE, 2, 8192, 128, FAKE, 128, pos(p - 127), 128, pos(p), None, 1.0, FAKE,
+               FAKE, need - 1, None)
+        assert st == 4, err(L)
 
 
 def test_stream_validation(L):
