@@ -70,11 +70,15 @@ def to_fp8_rope_rows(x):
 
 
 _E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+# a value exactly at a midpoint goes to the neighbour with the even code
+# (round to nearest even): down at 0.25, 1.25, 2.5, 5.0; up at 0.75, 1.75, 3.5
+_E2M1_TIE_UP = np.array([False, True, False, True, False, True, False])
 
 
 def to_mxfp4(x):
     """[..., c] float32 -> (codes [..., c/2], scales [..., c/32]) by nearest-grid
-    rounding after dividing by 2**(floor(log2 amax) - 2)."""
+    rounding (ties to the even code, saturating at 6) after dividing by
+    2**(floor(log2 amax) - 2)."""
     c = x.shape[-1]
     blk = x.reshape(x.shape[:-1] + (c // 32, 32)).astype(np.float32)
     amax = np.abs(blk).max(axis=-1)
@@ -82,9 +86,10 @@ def to_mxfp4(x):
     E = np.where(amax > 0, np.clip(e - 3 + 127, 0, 254), 0)
     X = np.where(amax > 0, np.ldexp(np.float32(1.0), (E - 127).astype(np.int32)), 1.0).astype(np.float32)
     y = np.abs(blk) / X[..., None]
-    mag = np.searchsorted(_E2M1_MIDS, y.ravel(), side="left").reshape(y.shape).astype(np.uint8)
+    mag = np.zeros(y.shape, dtype=np.uint8)
+    for mid, up in zip(_E2M1_MIDS, _E2M1_TIE_UP):
+        mag += (y >= mid) if up else (y > mid)
     el = mag | (np.signbit(blk).astype(np.uint8) << 3)
-    el[mag == 0] = 0
     el = el.reshape(x.shape[:-1] + (c,))
     codes = (el[..., 0::2] & 0xF) | (el[..., 1::2] << 4)
     return codes.astype(np.uint8), E.astype(np.uint8)

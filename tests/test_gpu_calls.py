@@ -333,32 +333,59 @@ TOPK_CASES = [
     (1, 8, 100000, 1024, 1, [200000], "int"),  # long rows, heavy ties at the threshold
     (1, 2, 70000, 512, 4, [300000], "zeros"),  # long rows: the threshold bin holds 10000 equal keys
     (1, 3, 40000, 1024, 4, [1000], "normal"),  # long rows with fewer visible scores than k
+    # the layer-pair chunk's routing: 512 or more rows of 264192 scores (2^18 + 2048 entries) at
+    # positions 2^20 + 7000 + t, each row read whole by one streaming block (float4 loads)
+    (1, 512, 264192, 1024, 4, [(1 << 20) + 7000], "asc"),
+    (1, 512, 264192, 1024, 4, [(1 << 20) + 7000], "desc"),
+    (1, 512, 264192, 1024, 4, [(1 << 20) + 7000], "int"),
+    (1, 512, 264192, 1024, 4, [(1 << 20) + 7000], "zeros"),
+    (2, 300, 264192, 1024, 4, [(1 << 20) + 1, (1 << 20) + 8000], "normal"),   # 600 rows over two sequences
+    # S % 4 != 0: the same streaming kernel with scalar loads
+    (1, 512, 264193, 1024, 4, [(1 << 20) + 7000], "normal"),
+    (1, 512, 264193, 1024, 4, [(1 << 20) + 7000], "int"),
 ]
+
+
+def topk_scores(B, nq, S, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "int":
+        return rng.integers(-20, 20, (B, nq, S)).astype(np.float32)
+    if kind == "zeros":
+        sc = np.where(rng.random((B, nq, S)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        sc[..., ::7] = 1.0
+        return sc
+    if kind in ("asc", "desc"):
+        ramp = np.linspace(-3.0, 5.0, S, dtype=np.float32)
+        return np.broadcast_to(ramp if kind == "asc" else ramp[::-1], (B, nq, S)).copy()
+    return G.normal(S, "extra", (B, nq, S), 10.0)
+
+
+def topk_check_rows(B, nq, seed):
+    """Every row of small cases; 64 seeded rows plus the first and last of each
+    sequence when there are many (the oracle sorts whole rows)."""
+    if B * nq <= 128:
+        return [(b, t) for b in range(B) for t in range(nq)]
+    rng = np.random.default_rng(seed)
+    rows = {(b, 0) for b in range(B)} | {(b, nq - 1) for b in range(B)}
+    for r in rng.choice(B * nq, size=64, replace=False):
+        rows.add((int(r) // nq, int(r) % nq))
+    return sorted(rows)
 
 
 @pytest.mark.parametrize("case", TOPK_CASES, ids=[str(i) for i in range(len(TOPK_CASES))])
 def test_topk_select_bit_exact(L, case):
     import torch
     B, nq, S, k, m, pos, kind = case
-    rng = np.random.default_rng(S + k)
-    if kind == "int":
-        sc = rng.integers(-20, 20, (B, nq, S)).astype(np.float32)
-    elif kind == "zeros":
-        sc = np.where(rng.random((B, nq, S)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
-        sc[..., ::7] = 1.0
-    elif kind in ("asc", "desc"):
-        ramp = np.linspace(-3.0, 5.0, S, dtype=np.float32)
-        sc = np.broadcast_to(ramp if kind == "asc" else ramp[::-1], (B, nq, S)).copy()
-    else:
-        sc = G.normal(S, "extra", (B, nq, S), 10.0)
+    sc = topk_scores(B, nq, S, kind, S + k)
     scores = dev(sc)
     idx = torch.empty((B, nq, k), dtype=torch.int32, device="cuda")
     ws = torch.empty(max(1, L.topk_workspace_size(B, nq, S, k)), dtype=torch.uint8, device="cuda")
     L.topk_select(scores, m, pos, k, idx, ws)
     got = host(idx)
-    for b in range(B):
-        ref = O.topk_select(sc[b].astype(np.float64), m, pos[b] + np.arange(nq), k)
-        assert np.array_equal(got[b], ref)
+    del scores
+    for b, t in topk_check_rows(B, nq, S + nq):
+        ref = O.topk_select(sc[b, t:t + 1].astype(np.float64), m, [pos[b] + t], k)
+        assert np.array_equal(got[b, t], ref[0]), (b, t)
 
 
 # ====================================================================== attention cores
@@ -426,6 +453,9 @@ DENSE_CASES = [
     ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 128, [1 << 16, 30000], True), # decode: split + combine
     ("bf16", ROW_FP8, 1, 8, 64, 512, 10, 128, 128, [50], True),              # no entry visible yet: window only
     ("bf16", ROW_BF16, 1, 37, 32, 128, 10, 16, 0, [100], False),             # 2 queries per block, no window
+    # HCA decode with 3965 visible entries, in the workspace the call needs exactly (the visible counts where
+    # the split plan of the size query, the argument check and the launch once disagreed)
+    ("bf16", ROW_FP8, 1, 1, 64, 512, 8192, 128, 128, [3965 * 128 + 5], True),
 ]
 
 
@@ -443,7 +473,9 @@ def test_hca_dense(L, case):
     scale = 1 / math.sqrt(c)
     qt = dev(q)
     out = torch.empty_like(qt)
-    ws = torch.empty(max(1, L.attn_workspace_size(True, B, nq, nh, c, S + nw)), dtype=torch.uint8, device="cuda")
+    need = L.attn_plan(True, L.BF16 if qd == "bf16" else L.F32, lay, B, nq, nh, c, S, 0, mp, nw, pos).workspace_bytes
+    assert need <= L.attn_workspace_size(True, B, nq, nh, c, S + nw)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
     L.hca_dense_fwd(qt, dev(kv), lay, mp, dev(win), wpos, nw, pos, dev(sink) if use_sink else None, scale, out, ws)
     got = decode_act(host(out))
     for b in range(B):

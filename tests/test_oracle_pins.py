@@ -444,6 +444,61 @@ def test_rope_chain_depends_only_on_relative_positions():
     assert np.allclose(o0, o1, rtol=0, atol=1e-9)
 
 
+def test_q_norm_rope_hand_example_order_and_positions():
+    """Query preparation normalises first, then rotates (digest 模块 D: RMSNorm of
+    each head before core attention; partial RoPE of the last dims), and every
+    head of query t turns by that query's own position.  With c = 8, 4 rotated
+    dims and gamma = (1 .. 8): the row (2, 0, 2, 0, 2, 0, 2, 0) has
+    rms = sqrt(2), so the normalised row is sqrt(2) * (1, 0, 3, 0, 5, 0, 7, 0);
+    its pairs (4, 5) and (6, 7) then turn by p and by p / 100 (theta = 10000,
+    angle p * theta^(-2j/4)).  Rotating before normalising would scale the
+    rotated components by gamma 6 and 8 instead of 5 and 7, and broadcasting
+    the positions over heads instead of queries would turn head h by q_pos[h]."""
+    c, R = 8, 4
+    g = np.arange(1.0, 9.0)
+    row = np.array([2.0, 0, 2.0, 0, 2.0, 0, 2.0, 0])
+    q = np.zeros((2, 3, c))
+    q[0, 0] = q[0, 1] = q[1, 0] = q[1, 2] = row
+    q[0, 2] = q[1, 1] = 3.0 * row            # RMSNorm is scale invariant (eps = 0)
+    pos = [1.0, 3.0]
+    y = O.q_norm_rope(q, g, pos, eps=0.0, theta=10000.0, rope_dims=R)
+    r2 = np.sqrt(2.0)
+
+    def want(p):
+        a, b = p, p / 100.0
+        return np.array([r2 * 1, 0, r2 * 3, 0, r2 * 5 * np.cos(a), r2 * 5 * np.sin(a),
+                         r2 * 7 * np.cos(b), r2 * 7 * np.sin(b)])
+
+    for h in range(3):
+        assert np.allclose(y[0, h], want(1.0), rtol=0, atol=1e-14), h
+        assert np.allclose(y[1, h], want(3.0), rtol=0, atol=1e-14), h
+    # the composition in the other order is a different function on this input
+    wrong = O.rmsnorm(O.rope_last(q[0, 0][None], [1.0], 10000.0, R), g, 0.0)[0]
+    assert not np.allclose(wrong, want(1.0), atol=1e-3)
+
+
+def test_kv_norm_rope_hand_example_rows_use_their_own_positions():
+    """KV row preparation (R32-R34): each row is normalised with the per-channel
+    gamma and then turned by its own position; entries at m(s+1) - 1.  Row 0 =
+    (0, 0, 0, 4) has rms 2, so the normalised row is (0, 0, 0, 2 gamma_3) =
+    (0, 0, 0, 8); its only rotated pair (2, 3) with R = 2 turns by p: (0, 8)
+    becomes (-8 sin p, 8 cos p).  Row 1 = (1, 1, 1, 1) normalises to gamma and
+    turns by its own position q: (3 cos q - 4 sin q, 3 sin q + 4 cos q)."""
+    g = np.array([1.0, 2.0, 3.0, 4.0])
+    rows = np.array([[0.0, 0, 0, 4.0], [1.0, 1, 1, 1]])
+    m, s0 = 4, 5
+    pos = O.entry_positions(m, s0, 2)              # 23, 27
+    assert list(pos) == [23, 27]
+    y = O.kv_norm_rope(rows, g, pos, eps=0.0, theta=10000.0, rope_dims=2)
+    p, q = 23.0, 27.0
+    assert np.allclose(y[0], [0, 0, -8 * np.sin(p), 8 * np.cos(p)], rtol=0, atol=1e-13)
+    assert np.allclose(y[1], [1, 2, 3 * np.cos(q) - 4 * np.sin(q), 3 * np.sin(q) + 4 * np.cos(q)], rtol=0,
+                       atol=1e-13)
+    # eps enters under the root: (0, 0, 0, 4) with eps = 12 has rms sqrt(4 + 12) = 4
+    y2 = O.kv_norm_rope(rows[:1], g, [0], eps=12.0, theta=10000.0, rope_dims=2)
+    assert np.allclose(y2[0], [0, 0, 0, 4.0], rtol=0, atol=1e-15)
+
+
 def test_entry_positions_match_visibility():
     """Entry s sits at the newest token it pools, m (s + 1) - 1, so it is visible
     at position p exactly when its position is <= p (R5, R34)."""
