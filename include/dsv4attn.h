@@ -195,6 +195,22 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsv4_topk_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and results as
+ * dsv4_topk_select.  Its workspace is a static device array of
+ * DSV4_TOPK_SCRATCH_BYTES per GPU, held until the process ends; a shape whose
+ * dsv4_topk_workspace_size() exceeds it fails with DSV4_ERR_UNSUPPORTED
+ * before anything runs.  The call allocates nothing (no hipMalloc, no
+ * hipFree).  Every call on one GPU shares that array: calls that overlap on
+ * one GPU (concurrent streams, other threads) race and must be serialised by
+ * the caller.
+ */
+#define DSV4_TOPK_SCRATCH_BYTES ((size_t)16 << 20)
+int dsv4_topk_select_noalloc(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                             const int64_t* q_pos0, int k, int32_t* idx_out, void* stream);
+
+/*
  * CSA core: shared-KV multi-query attention over the selected compressed
  * entries plus the sliding window, with an attention sink (digest 模块 B
  * eq 18-19, 模块 D; blog 第三阶段).  For query (b, t) at position p and head h:

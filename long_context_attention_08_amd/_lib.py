@@ -19,7 +19,7 @@ EXPORTS = [
     "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
-    "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_attn_workspace_size", "dsv4_attn_plan",
+    "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_topk_select_noalloc", "dsv4_attn_workspace_size", "dsv4_attn_plan",
     "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
     "dsv4_stream_state_bytes", "dsv4_stream_state_reset", "dsv4_stream_workspace_size",
     "dsv4_stream_compress", "dsv4_swa_ring_pos0",
@@ -73,6 +73,7 @@ _sig("dsv4_output_proj_workspace_size", _sz, [_i64, _int, _int])
 _sig("dsv4_output_proj", _int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
+_sig("dsv4_topk_select_noalloc", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp])
 _sig("dsv4_attn_workspace_size", _sz, [_int, _i64, _i64, _int, _int, _i64])
 
 
@@ -231,6 +232,13 @@ def topk_select(scores, m, q_pos0, k, idx_out, ws=None, *, stream=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.dsv4_topk_select(_ptr(scores), B, nq, S, m, _host_i64(q_pos0), k, _ptr(idx_out),
                                 _ptr(ws), wsb, _stream(stream)))
+
+
+def topk_select_noalloc(scores, m, q_pos0, k, idx_out, *, stream=None):
+    """Top-k without a workspace argument (the library's static per-GPU array)."""
+    B, nq, S = scores.shape
+    _check(lib.dsv4_topk_select_noalloc(_ptr(scores), B, nq, S, m, _host_i64(q_pos0), k, _ptr(idx_out),
+                                        _stream(stream)))
 
 
 def attn_workspace_size(dense, B, nq, nh, c, max_keys):

@@ -258,13 +258,11 @@ size_t dsv4_topk_workspace_size(int64_t B, int64_t nq, int64_t S, int k) {
   return dsv4::topk_make_plan(B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq, S, k).bytes;
 }
 
-int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
-                     const int64_t* q_pos0, int k, int32_t* idx_out,
-                     void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "dsv4_topk_select";
+static int topk_check(const char* fn, const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                      const int64_t* q_pos0, int k, int32_t* idx_out, dsv4::TopkPlan* plan) {
   if (B < 0 || nq < 0 || S < 0 || m <= 0 || k <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "%s: k=%d > 4096", fn, k);
-  if (B == 0 || nq == 0) return ok();
+  if (B == 0 || nq == 0) return DSV4_OK;
   if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
   for (int64_t b = 0; b < B; ++b)
     if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
@@ -272,10 +270,41 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
   if (S > 0 && !scores) return fail(DSV4_ERR_INVALID_ARG, "%s: scores is NULL", fn);
   if (S >= (int64_t)1 << 31) return fail(DSV4_ERR_UNSUPPORTED, "%s: S >= 2^31", fn);
   const int64_t rows = B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq;
-  const dsv4::TopkPlan plan = dsv4::topk_make_plan(rows, S > 0 ? S : 1, k);
-  if (!plan.supported) return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
+  *plan = dsv4::topk_make_plan(rows, S > 0 ? S : 1, k);
+  if (!plan->supported) return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
+  return DSV4_OK;
+}
+
+int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                     const int64_t* q_pos0, int k, int32_t* idx_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_topk_select";
+  dsv4::TopkPlan plan{};
+  int r = topk_check(fn, scores, B, nq, S, m, q_pos0, k, idx_out, &plan);
+  if (r) return r;
+  if (B == 0 || nq == 0) return ok();
   if (ws_bytes < plan.bytes || (plan.bytes && !ws))
     return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.bytes);
+  return hip_status(dsv4::launch_topk(scores, B, nq, S, m, q_pos0, k, idx_out, ws, plan,
+                                      reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int dsv4_topk_select_noalloc(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                             const int64_t* q_pos0, int k, int32_t* idx_out, void* stream) {
+  const char* fn = "dsv4_topk_select_noalloc";
+  dsv4::TopkPlan plan{};
+  int r = topk_check(fn, scores, B, nq, S, m, q_pos0, k, idx_out, &plan);
+  if (r) return r;
+  if (B == 0 || nq == 0) return ok();
+  if (plan.bytes > dsv4::TOPK_SCRATCH_BYTES)
+    return fail(DSV4_ERR_UNSUPPORTED,
+                "%s: this shape needs %zu bytes of workspace, more than the %zu the allocation-free call holds "
+                "(use dsv4_topk_select with a workspace)", fn, plan.bytes, dsv4::TOPK_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (plan.bytes > 0) {
+    r = hip_status(dsv4::topk_scratch_ptr(&ws), fn);
+    if (r) return r;
+  }
   return hip_status(dsv4::launch_topk(scores, B, nq, S, m, q_pos0, k, idx_out, ws, plan,
                                       reinterpret_cast<hipStream_t>(stream)), fn);
 }

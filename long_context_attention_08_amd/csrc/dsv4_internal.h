@@ -100,6 +100,10 @@ TopkPlan topk_make_plan(int64_t rows, int64_t S, int k);
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
                        const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan,
                        hipStream_t s);
+// the allocation-free top-k call's workspace: a static device array per GPU
+constexpr size_t TOPK_SCRATCH_BYTES = (size_t)16 << 20;
+// its device address on the current GPU (looked up once per device)
+hipError_t topk_scratch_ptr(void** ptr);
 
 struct AttnArgs {
   const void* q;        // [B, nq, nh, c]

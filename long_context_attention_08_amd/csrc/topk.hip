@@ -23,10 +23,40 @@
 // otherwise its k best composites go to the workspace and stage 2 (one block
 // per row) merges the parts' candidates (at most 16384).  Everything is exact
 // integer work, so the result is bit-identical for any decomposition.
+#include <mutex>
+
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
 
 namespace dsv4 {
+
+// Workspace of the allocation-free top-k call: one array per GPU, zero at
+// load and holding the last call's contents afterwards.  Nothing in it needs
+// to start at zero: every top-k kernel writes each workspace word before any
+// kernel reads it (the counting atomics are in LDS).  Calls that overlap on
+// one GPU share it and race.
+static __device__ __align__(256) uint8_t scratch[TOPK_SCRATCH_BYTES];
+
+hipError_t topk_scratch_ptr(void** ptr) {
+  static std::mutex mu;
+  static void* per_dev[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_dev[dev]) {
+    // the device address of this GPU's copy of the array (its name in host
+    // code is only a stand-in)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_dev[dev] = p;
+  }
+  *ptr = per_dev[dev];
+  return hipSuccess;
+}
 
 constexpr int TK_THREADS = 1024;
 constexpr int NBIN = 4096;

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 28
+    assert len(syms) == 29
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -163,6 +163,19 @@ def test_topk_validation(L):
     assert need > 0
     assert f(FAKE, 16, 1, 262144, 4, pos(*[0] * 16), 1024, FAKE, None, 0, None) == 4         # workspace
     assert f(FAKE, 16, 1, 262144, 4, pos(*[0] * 16), 1024, FAKE, FAKE, need - 8, None) == 4
+
+
+def test_topk_noalloc_validation(L):
+    """The allocation-free top-k call checks its arguments like the workspace
+    call and refuses a shape whose workspace exceeds its static array, before
+    any HIP call."""
+    f = L.lib.dsv4_topk_select_noalloc
+    assert f(FAKE, 1, 4, 100, 4, pos(0), 5000, FAKE, None) == 2                          # k > 4096
+    assert f(FAKE, 1, 4, 100, 4, pos(0), 0, FAKE, None) == 1                             # k = 0
+    assert f(FAKE, 1, 4, 100, 4, None, 16, FAKE, None) == 1                              # q_pos0 NULL
+    assert L.lib.dsv4_topk_workspace_size(1, 300, 262144, 1024) > 16 << 20
+    assert f(FAKE, 1, 300, 262144, 4, pos(1 << 20), 1024, FAKE, None) == 2
+    assert "allocation-free" in err(L)
 
 
 def test_attention_validation(L):
