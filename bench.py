@@ -314,6 +314,191 @@ def decode_cache_report(steps, stream, B=16, d=4096, c=512, cI=64, m=4, mp=128, 
     return rep
 
 
+def _time_calls(calls, steps, stream):
+    """Average ms of each callable over `steps` back-to-back launches (HIP
+    events on the library's stream), after one untimed call each."""
+    import torch
+    out = {}
+    for name, f in calls:
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / steps
+    return out
+
+
+def _dev(x):
+    """numpy array -> device tensor; uint16 arrays hold bf16 bit patterns"""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t.view(torch.bfloat16) if x.dtype == np.uint16 else t
+
+
+def decode_report(steps, stream):
+    """One decode step of configuration 4 (16 sequences, one query each at
+    position 2^20, caches of 2^20 tokens): the indexer over 262144 MXFP4 keys,
+    top-k 1024, sparse MQA over 1024 FP8 + bf16-RoPE entries plus the 128-row
+    window, and HCA dense attention over 8192 entries plus the window, each
+    timed alone, then the four back to back.  Algorithmic bytes: inputs read
+    once, outputs written once (the gathered rows of the selected entries for
+    sparse MQA)."""
+    from long_context_attention_08_amd import _lib as L
+    from synth import gen as G
+    import torch
+    inp = G.make(4)
+    cfg = inp["cfg"]
+    B, c, nh, hI, cI, k, nw, m, mp = (cfg[x] for x in ("B", "c", "nh", "hI", "cI", "k", "n_win", "m", "mp"))
+    S, Sh = inp["kv_cache"].shape[1], inp["hca_cache"].shape[1]
+    qp, wp = [int(x) for x in inp["q_pos0"]], [int(x) for x in inp["win_pos0"]]
+    d = {key: _dev(inp[key]) for key in ("q", "qI", "wI", "q_hca", "sink", "sink_hca", "kv_cache", "ki_codes",
+                                         "ki_scales", "hca_cache", "kv_win", "hca_win")}
+    del inp
+    scores = torch.empty((B, 1, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    tws = torch.empty(max(1, L.topk_workspace_size(B, 1, S, k)), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    out_h = torch.empty_like(d["q_hca"])
+    need_s = L.attn_plan(False, L.BF16, L.ROW_FP8_ROPE_BF16, B, 1, nh, c, S, k, 1, nw, qp)
+    need_h = L.attn_plan(True, L.BF16, L.ROW_FP8_ROPE_BF16, B, 1, nh, c, Sh, 0, mp, nw, qp)
+    aws = torch.empty(max(1, need_s.workspace_bytes, need_h.workspace_bytes), dtype=torch.uint8, device="cuda")
+    scale = 1 / math.sqrt(c)
+    f_idx = lambda: L.indexer_score(d["qI"], d["wI"], d["ki_codes"], L.ROW_MXFP4, m, qp, scores, k_scales=d["ki_scales"])
+    f_topk = lambda: L.topk_select(scores, m, qp, k, idx, tws)
+    f_sparse = lambda: L.sparse_mqa_fwd(d["q"], d["kv_cache"], L.ROW_FP8_ROPE_BF16, idx, d["kv_win"], wp, nw, qp,
+                                        d["sink"], scale, out, aws)
+    f_hca = lambda: L.hca_dense_fwd(d["q_hca"], d["hca_cache"], L.ROW_FP8_ROPE_BF16, mp, d["hca_win"], wp, nw, qp,
+                                    d["sink_hca"], scale, out_h, aws)
+    f_idx()
+    f_topk()
+    torch.cuda.synchronize()
+    row = c + 64
+    qb = B * nh * c * 2
+    work = {
+        "indexer": B * S * (cI // 2 + cI // 32) + B * hI * (cI * 2 + 4) + B * S * 4,
+        "topk": B * S * 4 + B * k * 4,
+        "sparse": B * (k + nw) * row + 2 * qb + B * k * 4,
+        "hca_dense": B * (Sh + nw) * row + 2 * qb,
+    }
+    ms = _time_calls([("indexer", f_idx), ("topk", f_topk), ("sparse", f_sparse), ("hca_dense", f_hca)], steps, stream)
+    step = lambda: (f_idx(), f_topk(), f_sparse(), f_hca())
+    ms["step"] = _time_calls([("step", step)], steps, stream)["step"]
+    rep = {}
+    for name in ("indexer", "topk", "sparse", "hca_dense"):
+        gbps = work[name] / (ms[name] * 1e-3) / 1e9
+        rep[name] = {"us": round(ms[name] * 1e3, 2), "gbps": round(gbps, 1), "frac_hbm": round(gbps / PEAK["hbm"], 4),
+                     "bytes": int(work[name])}
+    rep["sparse"]["plan"] = {"splits": need_s.splits, "split_slots": need_s.split_slots}
+    rep["hca_dense"]["plan"] = {"splits": need_h.splits, "split_slots": need_h.split_slots}
+    tot = sum(work.values())
+    rep["step"] = {"us": round(ms["step"] * 1e3, 2), "query_tokens_per_s": round(B / (ms["step"] * 1e-3), 1),
+                   "frac_hbm": round(tot / (ms["step"] * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(tot)}
+    rep["shape"] = {"sequences": B, "position": qp[0], "csa_entries": S, "hca_entries": Sh, "top_k": k,
+                    "window": nw, "heads": nh, "c": c}
+    return rep
+
+
+def prefill_configs_report(steps, stream):
+    """Configurations 2 (HCA layer, bf16, n = 32768, c = 128, 16 heads) and 3
+    (CSA prefill, bf16, n = 65536, c = 128, 64 heads, top-k 512): each call
+    timed alone on the configuration's own seeded inputs, with its binding
+    roofline (HBM for configuration 2 and the top-k, MFMA for the indexer,
+    the compressors and the sparse core of configuration 3)."""
+    from long_context_attention_08_amd import _lib as L
+    from synth import gen as G
+    import torch
+    rep = {}
+    # ---- configuration 2
+    inp = G.make(2)
+    cfg = inp["cfg"]
+    n, d, c, nh, mp, nw = (cfg[x] for x in ("n", "d", "c", "nh", "mp", "n_win"))
+    S = n // mp
+    H, W, Bb, q, sink = (_dev(inp[x]) for x in ("H", "W_hca", "B_hca", "q", "sink"))
+    del inp
+    rb = c * 2
+    comp = torch.empty((S, rb), dtype=torch.uint8, device="cuda")
+    raw = torch.empty((n, rb), dtype=torch.uint8, device="cuda")
+    qv = q.view(1, n, nh, c)
+    out = torch.empty_like(qv)
+    need = L.attn_plan(True, L.BF16, L.ROW_BF16, 1, n, nh, c, S, 0, mp, nw, [0]).workspace_bytes
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    f_c = lambda: L.hca_compress(H, W, Bb, mp, c, comp, L.ROW_BF16, raw_out=raw, raw_layout=L.ROW_BF16)
+    f_a = lambda: L.hca_dense_fwd(qv, comp.view(1, S, -1), L.ROW_BF16, mp, raw.view(1, n, -1), [0], nw, [0], sink,
+                                  1 / math.sqrt(c), out, ws)
+    f_c()
+    torch.cuda.synchronize()
+    ms = _time_calls([("hca_compress", f_c), ("hca_dense", f_a)], steps, stream)
+    t = np.arange(n)
+    keys = float((np.minimum(S, (t + 1) // mp) + np.minimum(nw, t + 1)).sum())
+    work = {"hca_compress": (n * d * 2 + 2 * c * d * 2 + S * rb + n * rb, 2.0 * n * d * 2 * c),
+            "hca_dense": (2 * n * nh * c * 2 + (S + n) * rb, 4.0 * keys * nh * c)}
+    r2 = {}
+    for name, (nbytes, flop) in work.items():
+        t_s = ms[name] * 1e-3
+        r2[name] = {"us": round(ms[name] * 1e3, 2), "gbps": round(nbytes / t_s / 1e9, 1),
+                    "tflops": round(flop / t_s / 1e12, 2), "frac_hbm": round(nbytes / t_s / 1e9 / PEAK["hbm"], 4)}
+    tot_ms = ms["hca_compress"] + ms["hca_dense"]
+    r2["layer"] = {"us": round(tot_ms * 1e3, 2), "query_tokens_per_s": round(n / (tot_ms * 1e-3), 1),
+                   "frac_hbm": round(sum(v[0] for v in work.values()) / (tot_ms * 1e-3) / 1e9 / PEAK["hbm"], 4)}
+    rep["hca_bf16_n32768"] = r2
+    del H, W, Bb, q, sink, comp, raw, out, ws
+    # ---- configuration 3
+    inp = G.make(3)
+    cfg = inp["cfg"]
+    n, d, c, nh, m, cI, hI, k, nw = (cfg[x] for x in ("n", "d", "c", "nh", "m", "cI", "hI", "k", "n_win"))
+    S = n // m
+    H, Wkv, Bkv, Wki, Bki, q, qI, wI, sink = (_dev(inp[x]) for x in ("H", "W_kv", "B_kv", "W_ki", "B_ki", "q", "qI",
+                                                                    "wI", "sink"))
+    del inp
+    rb = c * 2
+    comp = torch.empty((S, rb), dtype=torch.uint8, device="cuda")
+    raw = torch.empty((n, rb), dtype=torch.uint8, device="cuda")
+    ki = torch.empty((S, cI * 2), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((1, n, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, n, k), dtype=torch.int32, device="cuda")
+    tws = torch.empty(max(1, L.topk_workspace_size(1, n, S, k)), dtype=torch.uint8, device="cuda")
+    qv = q.view(1, n, nh, c)
+    out = torch.empty_like(qv)
+    need = L.attn_plan(False, L.BF16, L.ROW_BF16, 1, n, nh, c, S, k, 1, nw, [0]).workspace_bytes
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    kvc = L.compressor(Wkv, Bkv, c, comp, L.ROW_BF16, raw_out=raw, raw_layout=L.ROW_BF16)
+    kic = L.compressor(Wki, Bki, cI, ki, L.ROW_BF16)
+    f_c = lambda: L.compress_chunk(H, m, csa_kv=kvc, csa_keys=kic)
+    f_i = lambda: L.indexer_score(qI.view(1, n, hI, cI), wI.view(1, n, hI), ki.view(1, S, -1), L.ROW_BF16, m, [0],
+                                  scores)
+    f_t = lambda: L.topk_select(scores, m, [0], k, idx, tws)
+    f_s = lambda: L.sparse_mqa_fwd(qv, comp.view(1, S, -1), L.ROW_BF16, idx, raw.view(1, n, -1), [0], nw, [0], sink,
+                                   1 / math.sqrt(c), out, ws)
+    f_c()
+    f_i()
+    f_t()
+    torch.cuda.synchronize()
+    ms = _time_calls([("compress", f_c), ("indexer", f_i), ("topk", f_t), ("sparse", f_s)], steps, stream)
+    t = np.arange(n)
+    nvis = np.minimum(S, (t + 1) // m)
+    work = {"compress": (n * d * 2, 2.0 * n * d * (4 * c + 4 * cI), "mfma"),
+            "indexer": (float(n) * S * 4 + S * cI * 2, 2.0 * float(nvis.sum()) * hI * cI, "mfma"),
+            "topk": (float(nvis.sum()) * 4 + n * k * 4, 0.0, "hbm"),
+            "sparse": (2.0 * n * nh * c * 2 + (S + n) * rb + n * k * 4,
+                       4.0 * float((np.minimum(k, nvis) + np.minimum(nw, t + 1)).sum()) * nh * c, "mfma")}
+    r3 = {}
+    for name, (nbytes, flop, bound) in work.items():
+        t_s = ms[name] * 1e-3
+        e = {"us": round(ms[name] * 1e3, 2), "gbps": round(nbytes / t_s / 1e9, 1)}
+        if flop:
+            e["tflops"] = round(flop / t_s / 1e12, 2)
+        e["frac_" + bound] = round((flop / t_s / 1e12 / PEAK["mfma"]) if bound == "mfma" else
+                                   (nbytes / t_s / 1e9 / PEAK["hbm"]), 4)
+        r3[name] = e
+    tot_ms = sum(ms.values())
+    r3["layer"] = {"us": round(tot_ms * 1e3, 2), "query_tokens_per_s": round(n / (tot_ms * 1e-3), 1)}
+    rep["csa_prefill_bf16_n65536"] = r3
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +506,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)   # about 10 s of oracle work on 16 cores
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the layer-pair step only (no side reports, no CPU baseline): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -390,11 +577,19 @@ def main():
                        "c": cfg["c"], "heads": cfg["nh"], "m": cfg["m"], "m_prime": cfg["mp"], "top_k": cfg["k"],
                        "window": cfg["n_win"], "kv": "fp8_e4m3+bf16_rope", "indexer_keys": "mxfp4"},
             "roofline": roof, "calls": calls}
+    if args.step_only:
+        print(json.dumps(line), flush=True)
+        return
     line["fp4_indexer"] = quantised_indexer_report(layer, 4, work["indexer"]["flop"], args.steps, stream)
     line["fp8_indexer"] = quantised_indexer_report(layer, 8, work["indexer"]["flop"], args.steps, stream)
     line["norm_rope"] = norm_rope_report(layer, args.steps, stream)
     line["projections"] = projections_report(args.steps, stream)
     line["decode_cache"] = decode_cache_report(args.steps, stream)
+    del layer
+    torch.cuda.empty_cache()
+    line["decode"] = decode_report(args.steps, stream)
+    torch.cuda.empty_cache()
+    line["prefill_configs"] = prefill_configs_report(args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, rows_n=args.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -484,6 +484,50 @@ def test_hca_dense(L, case):
         assert_close(got[b], ref, fp32=(qd == "f32"), what="dense b=%d" % b)
 
 
+@pytest.mark.parametrize("dense,late", [(True, True), (True, False), (False, True), (False, False)])
+def test_attention_late_key_far_above_first_tiles(L, dense, late):
+    """A key whose logits exceed those of the first key tile by far more than
+    2^32 (log2 units): the softmax of a row is taken against the maximum of
+    its first visible tile, so a key this large in a later tile makes the
+    block run its keys a second time against the exact maximum.  The output
+    must match the oracle either way (late = False puts the key first)."""
+    import torch
+    B, nq, nh, c, S, mp, nw = 1, 3, 64, 512, 300, 4, 128
+    pos = [1500]
+    seed = 700 + int(dense) + 2 * int(late)
+    q = np.abs(G.normal(seed, "q", (B, nq, nh, c), 1.0)).astype(np.float32)
+    x = G.normal(seed, "cache_hca", (B, S, c), 1.0)
+    big = 250 if late else 3                       # a visible entry in a late / the first key tile
+    x[0, big, :c - 64] = 400.0
+    x[0, big, c - 64:] = 2.0
+    kv, _ = G.store(x, ROW_FP8)
+    win, _ = G.store(G.normal(seed, "win_hca", (B, nq + nw, c), 1.0), ROW_FP8)
+    wpos = [pos[0] - nw + 1]
+    sink = G.normal(seed, "sink", (nh,), 0.5)
+    scale = 1 / math.sqrt(c)
+    qt = dev(G.to_bf16(q))
+    out = torch.empty_like(qt)
+    qd = decode_act(G.to_bf16(q))
+    kvf, winf = stored_rows_f64(kv[0], ROW_FP8, c), stored_rows_f64(win[0], ROW_FP8, c)
+    pq = pos[0] + np.arange(nq)
+    if dense:
+        need = L.attn_plan(True, L.BF16, ROW_FP8, B, nq, nh, c, S, 0, mp, nw, pos).workspace_bytes
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+        L.hca_dense_fwd(qt, dev(kv), ROW_FP8, mp, dev(win), wpos, nw, pos, dev(sink), scale, out, ws)
+        ref = O.hca_dense(qd[0], kvf, mp, winf, wpos[0], nw, pq, sink.astype(np.float64), scale)
+    else:
+        k = 256
+        others = np.array([e for e in range(S) if e != big])
+        rows = [np.random.default_rng(seed + t).permutation(others)[:k - 1] for t in range(nq)]
+        # the big key last (a late tile) or first
+        idx = np.stack([np.append(r, big) if late else np.insert(r, 0, big) for r in rows])[None].astype(np.int32)
+        need = L.attn_plan(False, L.BF16, ROW_FP8, B, nq, nh, c, S, k, 1, nw, pos).workspace_bytes
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+        L.sparse_mqa_fwd(qt, dev(kv), ROW_FP8, dev(idx), dev(win), wpos, nw, pos, dev(sink), scale, out, ws)
+        ref = O.sparse_mqa(qd[0], kvf, idx[0], winf, wpos[0], nw, pq, sink.astype(np.float64), scale)
+    assert_close(decode_act(host(out))[0], ref, what="late large key")
+
+
 def test_attention_decodes_every_fp8_code(L):
     """q = 0 and a single key: the output is that key, so each stored E4M3 code
     (all 254 finite ones) and the bf16 RoPE dims come back exactly."""
