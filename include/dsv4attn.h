@@ -245,8 +245,7 @@ size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c,
  * DSV4_OK, DSV4_ERR_INVALID_ARG or DSV4_ERR_UNSUPPORTED (as the call would).
  */
 typedef struct {
-  int path;                /* 0 generic fp32-math kernel, 1 bf16-row MFMA (c = 128), 2 FP8-row MFMA (c = 512),
-                              3 FP8-row MFMA with whole rows per wave (c = 512, 64 heads) */
+  int path;                /* 0 generic fp32-math kernel, 1 bf16-row MFMA (c = 128), 2 FP8-row MFMA (c = 512) */
   int queries_per_block;
   int splits;              /* key-slot splits of a query group (blocks per group) */
   int split_slots;         /* key slots per split (splits > 1) */

@@ -1103,341 +1103,6 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   }
 }
 
-// ------------------------------------------------------------------ FP8 rows at c = 512, 64 heads: score and PV waves
-// One query (64 head rows) per block, one block of four waves per CU, one
-// wave per SIMD (so a wave may hold 512 registers).  The waves specialise:
-//   waves 0, 1 (score waves, rows 32 r .. 32 r + 31 for r = 0, 1) hold Q^T of
-//     their rows over all 512 channels (128 registers) and compute the full
-//     scores S^T of each key tile (32 MFMAs), the softmax, and P (bf16), which
-//     they hand to the PV wave of the same rows through LDS;
-//   waves 2, 3 (PV waves) hold O^T of the same rows over all 512 channels (256
-//     accumulation registers), issue the tile copies, and accumulate
-//     O^T += V^T P^T (32 MFMAs) one tile behind the score waves.
-// Each role runs a loop of its own (the same barriers in the same order), so
-// that the compiler keeps O^T in the accumulation registers: a branch around
-// the accumulating MFMAs inside one shared loop makes it shadow them in VGPRs.
-// Softmax reference: the exponentials of a row are taken against a fixed
-// reference m_ref, the maximum of the first tile in which the row sees a key
-// (O^T and l are still zero then); O^T is never rescaled.  A later tile whose
-// maximum passes m_ref by more than 32 (log2 units; P stays below 2^32
-// otherwise) marks the pass, and the block then runs its keys a second time
-// with the row's exact maximum, seen in the first pass, as the reference.
-// The raw FP8 + bf16 rows are staged in a ring of five tiles and read
-// straight into the MFMA operands, as in attn_f8 (same key-slot permutation,
-// same transposed reads).  One block barrier per tile.
-constexpr int S8_NSTG = 5;
-
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_f8s(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
-  constexpr int C = 512, RB = C + ROPE_DIMS, NF8 = (C - ROPE_DIMS) / 16, STAGE = TS * RB;
-  constexpr int NDMA = STAGE / 1024;          // 18 wave copies per tile, 9 per PV wave
-  static_assert(NF8 == 28 && NDMA == 18, "c = 512, FP8 + 64 bf16 RoPE dims");
-  __shared__ __align__(16) uint8_t s_stage[S8_NSTG * STAGE];
-  __shared__ __align__(16) u32x4 s_p[2][2][2][64];   // [buffer][row group][key half][lane]: P^T fragments
-  __shared__ float s_ml[2][64][2];                    // per row group and lane: m, l of the score wave
-  __shared__ uint32_t s_vmask[S8_NSTG];
-  __shared__ int s_sidx[SIDX_CAP];
-  __shared__ int s_bad;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
-  const int rg = wv & 1;                              // row group: heads 32 rg .. 32 rg + 31
-  const int64_t bl = blockIdx.x / pl.units_per_b, t = blockIdx.x % pl.units_per_b;
-  const int64_t b = b0 + bl;
-  const int64_t p0 = pt.q_pos0[bl], wpos0 = pt.win_pos0[bl];
-  const UnitInfo ui = unit_info(a, pl, p0, t);        // one query per unit
-  const int64_t nsplit = pl.max_splits == 1 ? 1 : (ui.total + pl.chunk - 1) / pl.chunk;
-  const int split = blockIdx.y;
-  if (split > 0 && split >= nsplit) return;
-  const int slot_lo = split * pl.chunk;
-  const int slot_hi = (int)(pl.max_splits == 1 ? ui.total : (slot_lo + pl.chunk < ui.total ? slot_lo + pl.chunk : ui.total));
-  const int ncomp = (int)ui.ncomp;
-  const int p = (int)(p0 + t);
-  const int wlo = (int)ui.wlo;
-  const int nit = slot_hi > slot_lo ? (slot_hi - slot_lo + TS - 1) / TS : 0;
-  const int nvis = pl.dense ? (int)visible_count(p, a.ratio, a.S) : (int)a.S;
-  const uint8_t* comp_base = reinterpret_cast<const uint8_t*>(a.kv_comp) + b * a.S * (int64_t)RB;
-  const uint8_t* win_base = reinterpret_cast<const uint8_t*>(a.kv_win) + (b * a.W + (ui.wlo - wpos0)) * (int64_t)RB;
-  static_assert(RB <= (int)sizeof(g_zero_row), "zero row shorter than a stored row");
-  const int h = 32 * rg + col;
-
-  // the index list of the block's compressed slots, cached in LDS
-  if (threadIdx.x == 0) s_bad = 0;
-  __syncthreads();
-  if (a.idx) {
-    const int32_t* irow = a.idx + (b * a.nq + t) * a.k;
-    const int n_i = (ncomp < slot_hi ? ncomp : slot_hi) - slot_lo;
-    int bad = 0;
-    for (int i = threadIdx.x; i < n_i; i += 256) {
-      const int e = irow[slot_lo + i];
-      s_sidx[i] = e;
-      bad |= (e < 0 || e >= a.S) ? 1 : 0;
-    }
-    if (bad) s_bad = 1;
-  }
-  __syncthreads();
-  const bool idx_ok = s_bad == 0;
-
-  auto tile_full = [&](int it) -> bool {
-    const int s0 = slot_lo + it * TS, s1 = s0 + TS;
-    if (s1 > slot_hi) return false;
-    if (s0 < ncomp && (a.idx ? !idx_ok : (s1 < ncomp ? s1 : ncomp) > nvis)) return false;
-    if (s1 > ncomp) {
-      const int lo = wlo + ((s0 > ncomp ? s0 : ncomp) - ncomp), hi = wlo + (s1 - 1 - ncomp);
-      if (hi > p || lo < p - a.n_win + 1) return false;
-    }
-    return true;
-  };
-  auto e4m3x8 = [](u32x2 w) -> bf16x8 {
-    return as_bf16x8((u32x4){e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
-                             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)});
-  };
-  auto stage_of = [&](int it) -> const uint8_t* { return s_stage + (it % S8_NSTG) * STAGE; };
-
-  if (wv < 2) {
-    // ================================================================ score waves
-    // Q^T in the contraction order of S^T: k-step kk < 28 of lane half G
-    // takes channels 16 (2 (kk / 2) + G) + 8 (kk % 2) .. + 8 (E4M3 part), then
-    // 448 + 16 (kk - 28) + 8 G .. + 8 (bf16 part)
-    bf16x8 qf[32];
-    {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + t) * a.nh + h) * C;
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const int c8 = kk < NF8 ? 16 * (2 * (kk >> 1) + G) + 8 * (kk & 1) : 448 + 16 * (kk - NF8) + 8 * G;
-        qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + c8));
-      }
-    }
-    // S^T of the tile in stage stg: key col at slot kperm(col); one 16-byte
-    // unit of 16 E4M3 channels per lane feeds two k-steps; two chains
-    const int kslot = kperm(col) * 16;
-    auto score = [&](const uint8_t* stg) -> f32x16 {
-      f32x16 s0 = {}, s1 = {};
-#pragma unroll
-      for (int j = 0; j < NF8 / 2; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (2 * j + G) * (TS * 16) + kslot);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], s1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(stg + (NF8 + 2 * kk + G) * (TS * 16) + kslot);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(stg + (NF8 + 2 * kk + 2 + G) * (TS * 16) + kslot);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w0), qf[NF8 + kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w1), qf[NF8 + kk + 1], s1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s0[i] += s1[i];
-      return s0;
-    };
-    const float sl = pl.scale_log2;
-    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
-    bool over = false;
-    for (int pass = 0;; ++pass) {
-      f32x16 sc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = -INFINITY;
-      lds_barrier();                                   // tile 0 has landed
-      if (nit > 0) sc = score(stage_of(0));
-      // iteration it: the softmax of tile it (P to LDS), then S^T of tile it+1
-      for (int it = 0; it <= nit; ++it) {
-        lds_barrier();                                 // tile it+1 landed; P buffer it % 2 is free
-        if (it < nit) {
-          if (!tile_full(it)) {
-            const uint32_t mk = s_vmask[it % S8_NSTG] >> (4 * G);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[r] = ((mk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sc[r] : -INFINITY;
-          }
-          float mx = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-          mx = max_halves(mx) * sl;
-          m_seen = fmaxf(m_seen, mx);
-          if (m_ref == -INFINITY) m_ref = mx;
-          else over |= mx > m_ref + 32.0f;
-          const float mneg = m_ref == -INFINITY ? 0.f : -m_ref;
-          uint32_t pk[8];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            // v_exp_f32 directly: results below 2^-126 flush to zero, which
-            // leaves the normalised output unchanged at fp32 resolution
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[r], sl, mneg));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], sl, mneg));
-            l_run += e0 + e1;
-            pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
-          }
-          s_p[it & 1][rg][0][l] = (u32x4){pk[0], pk[1], pk[2], pk[3]};
-          s_p[it & 1][rg][1][l] = (u32x4){pk[4], pk[5], pk[6], pk[7]};
-          // S^T of tile it+1 (past the end: a stale stage, result unused)
-          sc = score(stage_of(it + 1));
-        }
-      }
-      // the whole block agrees (every copy has landed, every stage is read)
-      if (pass > 0 || !__syncthreads_or(over ? 1 : 0)) break;
-      l_run = 0.f;
-      m_ref = m_seen;
-      over = false;
-    }
-    // hand (m, l) of each row to the PV wave of the same rows
-    const float lt = sum_halves(l_run);
-    s_ml[rg][l][0] = m_ref;
-    s_ml[rg][l][1] = lt;
-    __syncthreads();
-    return;
-  }
-
-  // ================================================================== PV waves
-  const int wc = wv - 2;                              // copy index
-  const uint8_t* dummy = g_zero_row;
-  auto slot_src = [&](int s, int* pos, bool* win) -> const uint8_t* {
-    if (s < ncomp) {
-      *win = false;
-      const int e = a.idx ? s_sidx[s - slot_lo] : s;
-      *pos = e;
-      if (e < 0 || e >= a.S) return nullptr;
-      return comp_base + (int64_t)e * RB;
-    }
-    *win = true;
-    *pos = wlo + (s - ncomp);
-    return win_base + (int64_t)(s - ncomp) * RB;
-  };
-  // copies of tile it into ring stage it % S8_NSTG: lane l serves stage slot
-  // l % 32, which holds key kperm(l % 32)
-  const int kp = kperm(l & 31);
-  auto issue = [&](int it) {
-    const int s0 = slot_lo + it * TS;
-    const uint8_t* rowp;
-    if (s0 + TS <= ncomp && s0 + TS <= slot_hi && (!a.idx || idx_ok)) {
-      const int e = a.idx ? s_sidx[s0 + kp - slot_lo] : s0 + kp;
-      rowp = comp_base + (int64_t)e * RB;
-    } else {
-      const int slot = s0 + kp;
-      int pos;
-      bool win;
-      rowp = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
-      rowp = rowp ? rowp : dummy;
-    }
-    const uint8_t* base = rowp + 16 * G + 32 * wc;
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(s_stage + (it % S8_NSTG) * STAGE + wc * 1024));
-    DmaCopies<0, NDMA / 2, 2, NDMA>::run(base, lds0, wc);
-  };
-  // visible key bits of a tile that is not whole (first PV wave)
-  auto masks = [&](int it) {
-    if (wc != 0 || tile_full(it)) return;
-    const int slot = slot_lo + it * TS + l;
-    bool ok = false;
-    if (l < TS && slot < slot_hi) {
-      int pos;
-      bool win;
-      if (slot_src(slot, &pos, &win)) ok = win ? (pos <= p && pos >= p - a.n_win + 1) : pos < nvis;
-    }
-    const uint32_t bal = (uint32_t)__ballot(ok);
-    if (l == 0) s_vmask[it % S8_NSTG] = bal;
-  };
-  // wait until at most n of this wave's tile copies are in flight
-  auto wait_copies = [&](int n) {
-    if (n >= 18) __builtin_amdgcn_s_waitcnt(0x4F72);        // vmcnt(18): high bits 15:14
-    else if (n >= 9) __builtin_amdgcn_s_waitcnt(0x0F79);    // vmcnt(9)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
-  };
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef int v2i __attribute__((ext_vector_type(2)));
-  f32x16 acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  // O^T += V^T P^T over key half s of the tile in stage stg (see attn_f8)
-  const int lam = l & 15, grp = (l >> 4) & 1;
-  auto pv_half = [&](const uint8_t* stg, int s, const bf16x8& pf) {
-    const int slot8 = 16 * s + 8 * G;
-    auto rd = [&](int mo) {
-      return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
-          stg + ((2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
-    };
-    v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
-#pragma unroll
-    for (int mo = 0; mo < NF8 / 2; ++mo) {
-      const v2i w = w1;
-      w1 = w2;
-      w2 = w3;
-      if (mo + 3 < NF8 / 2) w3 = rd(mo + 3);
-      acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
-    }
-#pragma unroll
-    for (int mo = NF8 / 2; mo < 16; ++mo) {        // bf16 channels 448 + 32 (mo - 14) + 16 grp + lam
-      const int piece = NF8 + 4 * (mo - NF8 / 2) + 2 * grp + ((lam & 3) >> 1);
-      const uint8_t* pp = stg + (piece * TS + slot8 + (lam >> 2)) * 16 + 8 * (lam & 1);
-      const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(pp));
-      const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(pp + 4 * 16));
-      const u32x2 x0 = __builtin_bit_cast(u32x2, t0), x1 = __builtin_bit_cast(u32x2, t1);
-      acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){x0[0], x0[1], x1[0], x1[1]}), pf,
-                                                        acc[mo], 0, 0, 0);
-    }
-  };
-  for (int pass = 0;; ++pass) {
-    // prologue: copies of tiles 0, 1, 2 in flight, tile 0 landed
-    for (int it = 0; it < 3 && it < nit; ++it) {
-      issue(it);
-      masks(it);
-    }
-    if (nit > 0) wait_copies((nit - 1 < 2 ? nit - 1 : 2) * (NDMA / 2));
-    lds_barrier();
-    for (int it = 0; it <= nit; ++it) {
-      wait_copies(it + 2 < nit ? NDMA / 2 : 0);     // this wave's copies of tile it+1 have landed
-      lds_barrier();                                // ... for every wave; P of tile it-1 is in LDS; stage (it+3) % 5 is free
-      if (it + 3 < nit) {
-        issue(it + 3);
-        masks(it + 3);
-      }
-      if (it >= 1) {
-        const uint8_t* cur = stage_of(it - 1);
-        pv_half(cur, 0, as_bf16x8(s_p[(it - 1) & 1][rg][0][l]));
-        pv_half(cur, 1, as_bf16x8(s_p[(it - 1) & 1][rg][1][l]));
-      }
-    }
-    if (pass > 0 || !__syncthreads_or(0)) break;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  }
-  __syncthreads();                                   // (m, l) of the score waves
-  const float m_run = s_ml[rg][l][0], l_tot = s_ml[rg][l][1];
-  if (pl.max_splits == 1) {
-    float f = m_run == -INFINITY ? 0.f : 1.f, den = l_tot;
-    if (a.sink) {
-      const float z = a.sink[h] * LOG2E;
-      const float M = fmaxf(m_run, z);
-      f = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-      den = l_tot * f + exp2f(z - M);
-    }
-    const float inv = den > 0.f ? f / den : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C;
-#pragma unroll
-    for (int mo = 0; mo < 16; ++mo)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j] * inv), (__bf16)(acc[mo][4 * j + 1] * inv)}),
-                         __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j + 2] * inv), (__bf16)(acc[mo][4 * j + 3] * inv)})};
-        *reinterpret_cast<u32x2*>(orow + 32 * mo + 8 * j + 4 * G) = w;
-      }
-  } else {
-    // partials: [unit][split][64 rows] {m, l} and [unit][split][64 rows][C]
-    const int64_t unit = blockIdx.x;
-    const int64_t rows = 64;
-    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + h) * 2;
-    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + h) * C;
-    if (G == 0) { ml[0] = m_run; ml[1] = l_tot; }
-#pragma unroll
-    for (int mo = 0; mo < 16; ++mo)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
-            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
-  }
-}
-
 // Merge of the split partials, splits in increasing order (deterministic).
 // A block takes 4 rows of one unit; each row's 64 threads own CPT = c / 64
 // consecutive channels and read every split's partial for them with vector
@@ -1533,9 +1198,7 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = win_pos0 ? win_pos0[b0 + i] : 0; }
     if (lp.path != ATTN_GENERIC) {
       dim3 grid((unsigned)(nb * pl.units_per_b), (unsigned)pl.max_splits);
-      if (lp.path == ATTN_F8W) {
-        hipLaunchKernelGGL(attn_f8s, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
-      } else if (lp.path == ATTN_F8) {
+      if (lp.path == ATTN_F8) {
         if (lp.nrg == 1) hipLaunchKernelGGL(attn_f8<1>, grid, dim3(128), 0, s, a, pt, (int)b0, pl);
         else hipLaunchKernelGGL(attn_f8<2>, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
       } else {

@@ -205,7 +205,7 @@ struct AttnPlan {
   int dense;
   float scale_log2;
 };
-enum { ATTN_GENERIC = 0, ATTN_MFMA = 1, ATTN_F8 = 2, ATTN_F8W = 3 };
+enum { ATTN_GENERIC = 0, ATTN_MFMA = 1, ATTN_F8 = 2 };
 constexpr int ATTN_SIDX_CAP = 2048;   // index-list slots a sparse MFMA block caches in LDS
 constexpr int ATTN_QPW_MAX = 8;       // most queries one MFMA block serves
 struct AttnLaunchPlan {

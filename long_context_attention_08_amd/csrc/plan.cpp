@@ -88,8 +88,6 @@ static int attn_path(const AttnArgs& a, bool dense) {
   // 160 KB of LDS, so that layout takes the generic kernel
   if (a.c == 512) {
     if (a.kv_layout != ROW_FP8) return ATTN_GENERIC;
-    // 64 heads: one query per block, score and PV waves
-    if (a.nh == 64) return ATTN_F8W;
     const bool ok = dense ? (a.nh == 16 || a.nh == 32 || a.nh == 64) : (a.nh == 32 || a.nh == 64);
     return ok ? ATTN_F8 : ATTN_GENERIC;
   }
@@ -106,8 +104,6 @@ static int attn_path(const AttnArgs& a, bool dense) {
 // channels already take 192 registers per wave (all 512 channels of 32 rows
 // in one wave would need 384 and spill)
 static int rows_per_block(const AttnArgs& a, bool dense) {
-  // score/PV kernel: one query per block
-  if (attn_path(a, dense) == ATTN_F8W) return a.nh;
   if (!dense) return a.nh;
   if (a.c >= 512) return a.nh < 64 ? 64 : a.nh;
   return a.nh > 128 ? a.nh : 128;
