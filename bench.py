@@ -1,6 +1,8 @@
 """Benchmark: query tokens/s of the interleaved CSA + HCA layer pair at 1M context.
 
-Workload (one step = every call of the hot path once): an 8192-token chunk
+Workload (one step = every call of the hot path once: the chunk's three
+compressors in one launch, index scores + top-k in one call, sparse MQA, HCA
+dense MQA): an 8192-token chunk
 at positions [2^20, 2^20 + 8192) against caches prefilled with 2^20 tokens
 (262144 CSA entries, 8192 HCA entries, 128-row SWA tails); bf16 activations,
 fp8 + bf16-RoPE KV rows, MXFP4 indexer keys, d = 4096, c = 512, 64 heads,
@@ -28,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "query tokens/s for CSA+HCA layer at 1M ctx; % of HBM/MFMA roofline"
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}    # MI355X: dense bf16 TFLOP/s, HBM GB/s
-CALLS = ["compress", "indexer", "topk", "sparse", "hca_dense"]
+CALLS = ["compress", "indexer_topk", "sparse", "hca_dense"]
 
 
 def algorithmic_work(cfg, P, S0, Sh0):
@@ -45,6 +47,10 @@ def algorithmic_work(cfg, P, S0, Sh0):
     w["indexer"] = dict(flop=2.0 * float(nvis.sum()) * hI * cI, bound="mfma",
                         bytes=float(n) * S * 4 + S * (cI // 2 + cI // 32) + n * hI * (2 * cI + 4))
     w["topk"] = dict(bytes=float(nvis.sum()) * 4 + n * k * 4, bound="hbm")
+    # index scores + top-k in one call: the index-score contraction (the score
+    # rows never reach HBM; the strided sample pass is overhead, not counted)
+    w["indexer_topk"] = dict(flop=w["indexer"]["flop"], bound="mfma",
+                             bytes=S * (cI // 2 + cI // 32) + n * hI * (2 * cI + 4) + n * k * 4)
     keys_sparse = float(n) * (k + nw)
     w["sparse"] = dict(flop=4.0 * keys_sparse * nh * c, bound="mfma",
                        bytes=2.0 * n * nh * c * 2 + S * row + n * k * 4)
@@ -167,6 +173,29 @@ def quantised_indexer_report(layer, fmt, flop, steps, stream, rows_n=256):
     torch.cuda.synchronize()
     return {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "recall_at_k_vs_bf16_query": round(float(np.mean(rec)), 4), "recall_rows": len(rec)}
+
+
+def two_call_report(layer, work, steps, stream):
+    """The same selection as two calls through the stored [n, S] score rows
+    (indexer_score, then topk_select), timed alone, against the one-call
+    index scores + top-k of the step; checks that both give the same indices."""
+    import torch
+    layer.indexer_topk()
+    torch.cuda.synchronize()
+    one = layer.idx.clone()
+    ms = _time_calls([("indexer", layer.indexer), ("topk", layer.topk), ("indexer_topk", layer.indexer_topk)],
+                     steps, stream)
+    layer.indexer()
+    layer.topk()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(one, layer.idx))
+    fi = work["indexer"]["flop"]
+    return {"indexer_ms": round(ms["indexer"], 4), "topk_ms": round(ms["topk"], 4),
+            "two_calls_ms": round(ms["indexer"] + ms["topk"], 4), "one_call_ms": round(ms["indexer_topk"], 4),
+            "saved_ms": round(ms["indexer"] + ms["topk"] - ms["indexer_topk"], 4),
+            "indexer_tflops": round(fi / (ms["indexer"] * 1e-3) / 1e12, 2),
+            "topk_gbps": round(work["topk"]["bytes"] / (ms["topk"] * 1e-3) / 1e9, 1),
+            "identical_indices": same}
 
 
 def norm_rope_report(layer, steps, stream):
@@ -343,9 +372,10 @@ def decode_report(steps, stream):
     position 2^20, caches of 2^20 tokens): the indexer over 262144 MXFP4 keys,
     top-k 1024, sparse MQA over 1024 FP8 + bf16-RoPE entries plus the 128-row
     window, and HCA dense attention over 8192 entries plus the window, each
-    timed alone, then the four back to back.  Algorithmic bytes: inputs read
-    once, outputs written once (the gathered rows of the selected entries for
-    sparse MQA)."""
+    timed alone, and index scores + top-k as one call; then the step back to
+    back with the faster of the two selection paths.  Algorithmic bytes:
+    inputs read once, outputs written once (the gathered rows of the selected
+    entries for sparse MQA; no score rows for the one-call path)."""
     from long_context_attention_08_amd import _lib as L
     from synth import gen as G
     import torch
@@ -368,6 +398,10 @@ def decode_report(steps, stream):
     scale = 1 / math.sqrt(c)
     f_idx = lambda: L.indexer_score(d["qI"], d["wI"], d["ki_codes"], L.ROW_MXFP4, m, qp, scores, k_scales=d["ki_scales"])
     f_topk = lambda: L.topk_select(scores, m, qp, k, idx, tws)
+    itws = torch.empty(max(1, L.indexer_topk_workspace_size(L.BF16, L.ROW_MXFP4, B, 1, hI, cI, S, k)),
+                       dtype=torch.uint8, device="cuda")
+    f_it = lambda: L.indexer_topk(d["qI"], d["wI"], d["ki_codes"], L.ROW_MXFP4, m, qp, k, idx, itws,
+                                  k_scales=d["ki_scales"])
     f_sparse = lambda: L.sparse_mqa_fwd(d["q"], d["kv_cache"], L.ROW_FP8_ROPE_BF16, idx, d["kv_win"], wp, nw, qp,
                                         d["sink"], scale, out, aws)
     f_hca = lambda: L.hca_dense_fwd(d["q_hca"], d["hca_cache"], L.ROW_FP8_ROPE_BF16, mp, d["hca_win"], wp, nw, qp,
@@ -383,19 +417,25 @@ def decode_report(steps, stream):
         "sparse": B * (k + nw) * row + 2 * qb + B * k * 4,
         "hca_dense": B * (Sh + nw) * row + 2 * qb,
     }
-    ms = _time_calls([("indexer", f_idx), ("topk", f_topk), ("sparse", f_sparse), ("hca_dense", f_hca)], steps, stream)
-    step = lambda: (f_idx(), f_topk(), f_sparse(), f_hca())
+    work["indexer_topk"] = work["indexer"] - B * S * 4 + B * k * 4
+    ms = _time_calls([("indexer", f_idx), ("topk", f_topk), ("indexer_topk", f_it), ("sparse", f_sparse),
+                      ("hca_dense", f_hca)], steps, stream)
+    # the step takes whichever selection path is faster at this shape (the two give the same indices)
+    one_call = ms["indexer_topk"] < ms["indexer"] + ms["topk"]
+    step = (lambda: (f_it(), f_sparse(), f_hca())) if one_call else (lambda: (f_idx(), f_topk(), f_sparse(), f_hca()))
     ms["step"] = _time_calls([("step", step)], steps, stream)["step"]
     rep = {}
-    for name in ("indexer", "topk", "sparse", "hca_dense"):
+    for name in ("indexer", "topk", "indexer_topk", "sparse", "hca_dense"):
         gbps = work[name] / (ms[name] * 1e-3) / 1e9
         rep[name] = {"us": round(ms[name] * 1e3, 2), "gbps": round(gbps, 1), "frac_hbm": round(gbps / PEAK["hbm"], 4),
                      "bytes": int(work[name])}
     rep["sparse"]["plan"] = {"splits": need_s.splits, "split_slots": need_s.split_slots}
     rep["hca_dense"]["plan"] = {"splits": need_h.splits, "split_slots": need_h.split_slots}
-    tot = sum(work.values())
+    sel = ["indexer_topk"] if one_call else ["indexer", "topk"]
+    tot = sum(work[x] for x in sel + ["sparse", "hca_dense"])
     rep["step"] = {"us": round(ms["step"] * 1e3, 2), "query_tokens_per_s": round(B / (ms["step"] * 1e-3), 1),
-                   "frac_hbm": round(tot / (ms["step"] * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(tot)}
+                   "frac_hbm": round(tot / (ms["step"] * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(tot),
+                   "calls": sel + ["sparse", "hca_dense"]}
     rep["shape"] = {"sequences": B, "position": qp[0], "csa_entries": S, "hca_entries": Sh, "top_k": k,
                     "window": nw, "heads": nh, "c": c}
     return rep
@@ -470,18 +510,24 @@ def prefill_configs_report(steps, stream):
     f_i = lambda: L.indexer_score(qI.view(1, n, hI, cI), wI.view(1, n, hI), ki.view(1, S, -1), L.ROW_BF16, m, [0],
                                   scores)
     f_t = lambda: L.topk_select(scores, m, [0], k, idx, tws)
+    itws = torch.empty(max(1, L.indexer_topk_workspace_size(L.BF16, L.ROW_BF16, 1, n, hI, cI, S, k)),
+                       dtype=torch.uint8, device="cuda")
+    f_it = lambda: L.indexer_topk(qI.view(1, n, hI, cI), wI.view(1, n, hI), ki.view(1, S, -1), L.ROW_BF16, m, [0], k,
+                                  idx, itws)
     f_s = lambda: L.sparse_mqa_fwd(qv, comp.view(1, S, -1), L.ROW_BF16, idx, raw.view(1, n, -1), [0], nw, [0], sink,
                                    1 / math.sqrt(c), out, ws)
     f_c()
     f_i()
     f_t()
     torch.cuda.synchronize()
-    ms = _time_calls([("compress", f_c), ("indexer", f_i), ("topk", f_t), ("sparse", f_s)], steps, stream)
+    ms = _time_calls([("compress", f_c), ("indexer", f_i), ("topk", f_t), ("indexer_topk", f_it), ("sparse", f_s)],
+                     steps, stream)
     t = np.arange(n)
     nvis = np.minimum(S, (t + 1) // m)
     work = {"compress": (n * d * 2, 2.0 * n * d * (4 * c + 4 * cI), "mfma"),
             "indexer": (float(n) * S * 4 + S * cI * 2, 2.0 * float(nvis.sum()) * hI * cI, "mfma"),
             "topk": (float(nvis.sum()) * 4 + n * k * 4, 0.0, "hbm"),
+            "indexer_topk": (float(S) * cI * 2 + n * k * 4, 2.0 * float(nvis.sum()) * hI * cI, "mfma"),
             "sparse": (2.0 * n * nh * c * 2 + (S + n) * rb + n * k * 4,
                        4.0 * float((np.minimum(k, nvis) + np.minimum(nw, t + 1)).sum()) * nh * c, "mfma")}
     r3 = {}
@@ -493,8 +539,12 @@ def prefill_configs_report(steps, stream):
         e["frac_" + bound] = round((flop / t_s / 1e12 / PEAK["mfma"]) if bound == "mfma" else
                                    (nbytes / t_s / 1e9 / PEAK["hbm"]), 4)
         r3[name] = e
-    tot_ms = sum(ms.values())
-    r3["layer"] = {"us": round(tot_ms * 1e3, 2), "query_tokens_per_s": round(n / (tot_ms * 1e-3), 1)}
+    # the layer: compress, the faster selection path, sparse
+    sel = min(ms["indexer_topk"], ms["indexer"] + ms["topk"])
+    tot_ms = ms["compress"] + sel + ms["sparse"]
+    r3["layer"] = {"us": round(tot_ms * 1e3, 2), "query_tokens_per_s": round(n / (tot_ms * 1e-3), 1),
+                   "selection": "indexer_topk" if ms["indexer_topk"] <= ms["indexer"] + ms["topk"] else
+                                "indexer + topk"}
     rep["csa_prefill_bf16_n65536"] = r3
     return rep
 
@@ -528,7 +578,7 @@ def main():
     cfg = inp["cfg"]
     layer = pair_from_arrays(inp)
     stream = torch.cuda.current_stream()
-    fns = [layer.compress, layer.indexer, layer.topk, layer.sparse, layer.hca_dense]
+    fns = [layer.compress, layer.indexer_topk, layer.sparse, layer.hca_dense]
     for _ in range(args.warmup):
         layer.step()
     torch.cuda.synchronize()
@@ -580,6 +630,7 @@ def main():
     if args.step_only:
         print(json.dumps(line), flush=True)
         return
+    line["indexer_then_topk"] = two_call_report(layer, work, args.steps, stream)
     line["fp4_indexer"] = quantised_indexer_report(layer, 4, work["indexer"]["flop"], args.steps, stream)
     line["fp8_indexer"] = quantised_indexer_report(layer, 8, work["indexer"]["flop"], args.steps, stream)
     line["norm_rope"] = norm_rope_report(layer, args.steps, stream)

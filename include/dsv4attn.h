@@ -195,6 +195,33 @@ int dsv4_topk_select(const float* scores, int64_t B, int64_t nq, int64_t S, int 
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Index scores and top-k in one call (digest 模块 B eq 16 then eq 17): idx_out
+ * is bit for bit what dsv4_indexer_score into a [B, nq, S] buffer followed by
+ * dsv4_topk_select with the same k would give (same arguments, same limits as
+ * those two calls; k <= 4096), without the caller holding the score rows.
+ * For bf16 queries with 32 heads, cI in {32, 64, 128}, BF16 or MXFP4 keys and
+ * k <= 1024 the scores are not stored: every 32nd key is scored first, each
+ * row's threshold is a value at or below its ks-th best sample score (ks
+ * about k/32 plus six standard deviations), the full pass keeps only the
+ * visible scores at or above it, and a per-row select takes the k best of
+ * those.  A row that kept fewer than min(k, visible) scores, or more than its
+ * lists hold, has its scores recomputed in full and selected by the top-k
+ * pass, so the result never depends on the sample.  Other shapes run the two
+ * calls in sequence through the workspace.
+ * ws: workspace of dsv4_indexer_topk_workspace_size() bytes (the same
+ * arguments); it holds a full score row for each query of up to 64 sequences,
+ * written only for rows the threshold does not settle.  A smaller workspace
+ * fails with DSV4_ERR_WORKSPACE before anything is launched.
+ */
+size_t dsv4_indexer_topk_workspace_size(int q_dtype, int k_layout, int64_t B, int64_t nq, int hI, int cI,
+                                        int64_t S, int k);
+int dsv4_indexer_topk(const void* qI, int q_dtype, const float* wI,
+                      const void* keys, const uint8_t* k_scales, int k_layout,
+                      int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                      const int64_t* q_pos0, int k, int32_t* idx_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * dsv4_topk_select without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, semantics and results as

@@ -16,7 +16,7 @@ ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
     "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_compress_chunk", "dsv4_indexer_score",
-    "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
+    "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_indexer_topk_workspace_size", "dsv4_indexer_topk", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_topk_select_noalloc", "dsv4_attn_workspace_size", "dsv4_attn_plan",
@@ -71,6 +71,9 @@ _sig("dsv4_query_proj", _int, [_vp, _i64, _int, _vp, _int, _vp, _int, _int, _vp,
                                _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("dsv4_output_proj_workspace_size", _sz, [_i64, _int, _int])
 _sig("dsv4_output_proj", _int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp])
+_sig("dsv4_indexer_topk_workspace_size", _sz, [_int, _int, _i64, _i64, _int, _int, _i64, _int])
+_sig("dsv4_indexer_topk", _int, [_vp, _int, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _i64, _int, _P64, _int,
+                                 _vp, _vp, _sz, _vp])
 _sig("dsv4_topk_workspace_size", _sz, [_i64, _i64, _i64, _int])
 _sig("dsv4_topk_select", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp, _sz, _vp])
 _sig("dsv4_topk_select_noalloc", _int, [_vp, _i64, _i64, _i64, _int, _P64, _int, _vp, _vp])
@@ -221,6 +224,22 @@ def indexer_score_fp8q(qI, wI, k_codes, k_scales, m, q_pos0, scores, *, S=None, 
     _check(lib.dsv4_indexer_score_fp8q(_ptr(qI), _act(qI), _ptr(wI), _ptr(k_codes), _ptr(k_scales),
                                        B, nq, hI, cI, S, m, _host_i64(q_pos0), _ptr(scores),
                                        _stream(stream)))
+
+def indexer_topk_workspace_size(q_dtype, k_layout, B, nq, hI, cI, S, k):
+    return int(lib.dsv4_indexer_topk_workspace_size(q_dtype, k_layout, B, nq, hI, cI, S, k))
+
+
+def indexer_topk(qI, wI, keys, k_layout, m, q_pos0, k, idx_out, ws=None, *, k_scales=None, S=None, stream=None):
+    """Index scores and top-k in one call.  qI [B, nq, hI, cI]; wI [B, nq, hI];
+    keys [B, S, ...]; idx_out [B, nq, k] int32 (what indexer_score followed by
+    topk_select would give)."""
+    B, nq, hI, cI = qI.shape
+    S = keys.shape[1] if S is None else S
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv4_indexer_topk(_ptr(qI), _act(qI), _ptr(wI), _ptr(keys), _ptr(k_scales), k_layout,
+                                 B, nq, hI, cI, S, m, _host_i64(q_pos0), k, _ptr(idx_out), _ptr(ws), wsb,
+                                 _stream(stream)))
+
 
 def topk_workspace_size(B, nq, S, k):
     return int(lib.dsv4_topk_workspace_size(B, nq, S, k))

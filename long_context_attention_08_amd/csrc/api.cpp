@@ -216,6 +216,62 @@ int dsv4_indexer_score(const void* qI, int q_dtype, const float* wI,
   return hip_status(dsv4::launch_indexer(a, q_pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+static dsv4::IndexerArgs it_args(int q_dtype, int k_layout, int64_t B, int64_t nq, int hI, int cI, int64_t S, int m) {
+  dsv4::IndexerArgs a{};
+  a.q_dtype = q_dtype; a.k_layout = k_layout; a.B = B; a.nq = nq; a.hI = hI; a.cI = cI; a.S = S; a.m = m;
+  return a;
+}
+
+size_t dsv4_indexer_topk_workspace_size(int q_dtype, int k_layout, int64_t B, int64_t nq, int hI, int cI,
+                                        int64_t S, int k) {
+  if (B <= 0 || nq <= 0 || S <= 0 || hI <= 0 || cI <= 0 || k <= 0) return 0;
+  return dsv4::idxtopk_workspace(it_args(q_dtype, k_layout, B, nq, hI, cI, S, 1), k);
+}
+
+int dsv4_indexer_topk(const void* qI, int q_dtype, const float* wI,
+                      const void* keys, const uint8_t* k_scales, int k_layout,
+                      int64_t B, int64_t nq, int hI, int cI, int64_t S, int m,
+                      const int64_t* q_pos0, int k, int32_t* idx_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_indexer_topk";
+  if (B < 0 || nq < 0 || S < 0 || hI <= 0 || cI <= 0 || m <= 0 || k <= 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "%s: k=%d > 4096", fn, k);
+  if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
+  if (k_layout != DSV4_ROW_F32 && k_layout != DSV4_ROW_BF16 && k_layout != DSV4_ROW_MXFP4)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: k_layout %d", fn, k_layout);
+  if (k_layout == DSV4_ROW_MXFP4 && cI % 32) return fail(DSV4_ERR_UNSUPPORTED, "%s: MXFP4 keys need cI %% 32 == 0", fn);
+  if (S >= (int64_t)1 << 31) return fail(DSV4_ERR_UNSUPPORTED, "%s: S >= 2^31", fn);
+  if (B == 0 || nq == 0) return ok();
+  if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
+  for (int64_t b = 0; b < B; ++b)
+    if (q_pos0[b] < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0[%lld] < 0", fn, (long long)b);
+  if (!idx_out) return fail(DSV4_ERR_INVALID_ARG, "%s: idx_out is NULL", fn);
+  const dsv4::IndexerArgs sz = it_args(q_dtype, k_layout, B, nq, hI, cI, S > 0 ? S : 1, m);
+  const int64_t rows = B * nq < dsv4::MAXB * nq ? B * nq : dsv4::MAXB * nq;
+  if (!dsv4::topk_make_plan(rows, S > 0 ? S : 1, k).supported)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: S=%lld with k=%d", fn, (long long)S, k);
+  if (S > 0) {
+    int r = check_ptrs16(fn, {{qI, "qI"}, {keys, "keys"}});
+    if (r) return r;
+    if (!wI) return fail(DSV4_ERR_INVALID_ARG, "%s: wI is NULL", fn);
+    if (k_layout == DSV4_ROW_MXFP4 && !k_scales) return fail(DSV4_ERR_INVALID_ARG, "%s: k_scales is NULL", fn);
+  }
+  const size_t need = S > 0 ? dsv4::idxtopk_workspace(sz, k) : 0;
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  if (need && !aligned16(ws)) return fail(DSV4_ERR_INVALID_ARG, "%s: ws is not 16-byte aligned", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (S == 0) {
+    // nothing is visible: the top-k pass writes padding rows without reading scores
+    const dsv4::TopkPlan tp = dsv4::topk_make_plan(rows, 1, k);
+    return hip_status(dsv4::launch_topk(nullptr, B, nq, 0, m, q_pos0, k, idx_out, nullptr, tp, s), fn);
+  }
+  dsv4::IndexerArgs a = it_args(q_dtype, k_layout, B, nq, hI, cI, S, m);
+  a.qI = qI; a.wI = wI; a.keys = keys; a.k_scales = k_scales;
+  return hip_status(dsv4::launch_indexer_topk(a, q_pos0, k, idx_out, ws, s), fn);
+}
+
 static int indexer_quantised(const char* fn, int qfmt, const void* qI, int q_dtype, const float* wI,
                              const uint8_t* k_codes, const uint8_t* k_scales, int64_t B, int64_t nq, int hI,
                              int cI, int64_t S, int m, const int64_t* q_pos0, float* scores, void* stream) {

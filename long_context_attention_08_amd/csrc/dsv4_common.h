@@ -214,4 +214,17 @@ __device__ __forceinline__ float sum_halves(float v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ------------------------------------------------------------------ top-k order keys
+// Order-preserving uint32 key of an fp32 score (-0.0 ties with +0.0), and the
+// unique composite (key << 32 | ~index): "score descending, ties to the lower
+// index" is plain descending order of the composite.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(~idx);
+}
+
 }  // namespace dsv4

@@ -60,6 +60,18 @@ struct IndexerArgs {
   int m;
   float* scores;        // [B, nq, S]
   int qfmt;             // 0: bf16 / f32 queries; 4 or 8: quantised to MXFP4 or MXFP8 (keys MXFP4)
+  // candidate mode (cand != null; bf16 queries, MFMA path): no scores are
+  // stored; a visible score >= lval[row] (a finite float or -inf) is kept as
+  // its composite in cand[(row * splits + split) * cap + i] and the count of
+  // each (row, split) goes to ccount[row * splits + split] (row = b nq + t,
+  // split = the key range of one block, splits from indexer_grid)
+  uint64_t* cand;
+  uint32_t* ccount;
+  const float* lval;
+  int cap;
+  // restricted mode (row_flags != null): a block computes (and stores scores)
+  // only if one of its rows has a non-zero flag
+  const int* row_flags;
 };
 
 // Per-batch absolute positions travel to the kernels by value: a launch covers
@@ -72,6 +84,23 @@ struct PosTable {
 
 // q_pos0: host array [B]
 hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s);
+
+// keys 32 j + 31 (j < Ss) of every batch entry into a compact [B, Ss] key array
+hipError_t launch_indexer_sample_keys(const IndexerArgs& a, int64_t Ss, void* keys_out, uint8_t* scales_out,
+                                      hipStream_t s);
+
+// ---- indexer planning (plan.cpp; host only)
+constexpr int IDX_KT = 256;       // keys per LDS tile of the MFMA indexer
+// the MFMA path applies (bf16 queries, 32 heads, cI 32/64/128, BF16 or MXFP4 keys)
+bool indexer_mfma_ok(const IndexerArgs& a);
+// grid of one MFMA-indexer launch over nb batch entries: query blocks of qb
+// queries, each split into `splits` key ranges of tps tiles
+struct IndexerGrid {
+  int qb;
+  int64_t qblocks;
+  int splits, tps;
+};
+IndexerGrid indexer_grid(const IndexerArgs& a, int nb);
 
 // ---- top-k planning (plan.cpp; host only)
 constexpr int SK_KMAX = 1024;     // largest k of the streaming and histogram selects
@@ -100,6 +129,38 @@ TopkPlan topk_make_plan(int64_t rows, int64_t S, int k);
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
                        const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan,
                        hipStream_t s);
+// row_flags (optional, [launch rows]): rows with a zero flag are skipped
+hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                            const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan,
+                            const int* row_flags, hipStream_t s);
+
+// ---- index scores and top-k in one call (plan.cpp plans, topk.hip launches).
+// Sampled-threshold path: every 32nd key (keys 32 j + 31) is scored first;
+// a value at or below each row's ks-th best sample score is its threshold,
+// the full pass keeps only scores at or above it as composites, and a per-row
+// select takes the top k of those.  A row whose kept count is below
+// min(k, visible) or whose lists overflowed is flagged, and its scores are
+// recomputed in full and selected by the plain top-k, so the result is always
+// the top-k of the full score row.
+constexpr int IT_STRIDE = 32;     // one sample key per 32 keys
+constexpr int IT_SELCAP = 3584;   // candidates one select block holds in LDS
+struct IdxTopkPlan {
+  bool fused;        // sampled-threshold path (else: full scores, then top-k)
+  int ks;            // sample rank of the threshold
+  int cap;           // candidate slots per (row, key split)
+  IndexerGrid grid;  // of the full pass
+  int64_t Ss;        // sample keys per batch entry
+  TopkPlan tk_sample, tk_full;
+  size_t o_skeys, o_sscl, o_sscore, o_sidx, o_stk, o_lkey, o_cand, o_cnt, o_flags, o_scores, o_ftk;
+  size_t bytes;
+};
+// plan of one launch slice (a.B <= MAXB batch entries)
+IdxTopkPlan idxtopk_make_plan(const IndexerArgs& a, int k);
+// workspace of a whole call (the largest slice plan)
+size_t idxtopk_workspace(const IndexerArgs& a, int k);
+hipError_t launch_indexer_topk(const IndexerArgs& a, const int64_t* q_pos0, int k, int32_t* idx, void* ws,
+                               hipStream_t s);
+
 // the allocation-free top-k call's workspace: a static device array per GPU
 constexpr size_t TOPK_SCRATCH_BYTES = (size_t)16 << 20;
 // its device address on the current GPU (looked up once per device)

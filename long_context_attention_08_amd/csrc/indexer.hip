@@ -9,6 +9,11 @@
 // gfx950 scaled fp4->bf16 conversion, which is exact) and shared by the four
 // waves.  The head reduction sum_h w_h ReLU(acc) runs on the accumulator
 // registers: 16 heads per lane plus one cross-lane add.
+//
+// Candidate mode (EM): the same scores, but instead of the score row a block
+// keeps, per query, the composites (order key << 32 | ~index) of the visible
+// keys whose order key reaches the query's threshold key, appended to the
+// query's list for the block's key range; nothing else is stored.
 #include <type_traits>
 
 #include "dsv4_common.h"
@@ -38,6 +43,7 @@ __global__ void indexer_generic(IndexerArgs a, PosTable pt, int b0, int nb) {
   const int64_t b = b0 + bl;
   const int64_t t = (gid % per_b) / a.S;
   const int64_t s = gid % a.S;
+  if (a.row_flags && !a.row_flags[b * a.nq + t]) return;
   const int64_t p = pt.q_pos0[bl] + t;
   float* out = a.scores + (b * a.nq + t) * a.S + s;
   if (s >= visible_count(p, a.m, a.S)) { *out = -INFINITY; return; }
@@ -124,7 +130,7 @@ __device__ __forceinline__ void mxfp8_block(const float (&x)[32], u32x4& lo, u32
 }
 
 // ------------------------------------------------------------------ MFMA path
-constexpr int KT = 256;   // keys per LDS tile
+constexpr int KT = IDX_KT;   // keys per LDS tile
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // WQ waves split the queries, 4/WQ waves split the 8 n-tiles of a key tile;
@@ -136,7 +142,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // l / 32 of the k-step; an E2M1 lane holds that block's 32 codes in 16 bytes,
 // an E4M3 lane holds channels 16 (l / 32) .. + 15 of block 0 in bytes 0..15 and
 // the same channels of block 1 in bytes 16..31.
-template <int CI, int KL, int WQ, int QPW, int QF>
+template <int CI, int KL, int WQ, int QPW, int QF, bool EM>
 __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable pt, int b0,
                                                         int qblocks, int tiles_per_split) {
   constexpr int WK = 4 / WQ;          // waves along the key tile
@@ -162,7 +168,14 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   const int64_t ntiles = (S + KT - 1) / KT;
   const int64_t tile_lo = (int64_t)blockIdx.y * tiles_per_split;
   const int64_t tile_hi = tile_lo + tiles_per_split < ntiles ? tile_lo + tiles_per_split : ntiles;
-  if (tile_lo >= tile_hi) return;
+  static_assert(!EM || QF == 0, "candidate mode: bf16 queries");
+  if (!EM && tile_lo >= tile_hi) return;
+  if (a.row_flags) {                          // restricted: only blocks holding a flagged row
+    bool any = false;
+    for (int qi = 0; qi < QB; ++qi)
+      if (t0 + qi < a.nq && a.row_flags[b * a.nq + t0 + qi]) any = true;
+    if (!any) return;
+  }
 
   // query fragments (B operand is the key; A operand is the 32 heads x cI)
   bf16x8 qf[QPW][Q4 ? 1 : KS];
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
   // offset beyond the range and the hardware drops its store, so the store
   // needs no branch and the unrolled n-tile loop stays one scheduling region.
   const int64_t nrows = a.nq - t0 < QB ? a.nq - t0 : QB;
-  const uint64_t sbase = reinterpret_cast<uint64_t>(a.scores + (b * a.nq + t0) * S);
+  const uint64_t sbase = EM ? 0ull : reinterpret_cast<uint64_t>(a.scores + (b * a.nq + t0) * S);
   const uint32_t sb_lo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   const uint32_t sb_hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -259,10 +272,33 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
 #pragma unroll
   for (int pp = 0; pp < NPAIR; ++pp) prow_f[pp] = (QPW > 1 || !hi) ? prow[pp] : 0x80000000u;
   const int S32 = (int)S;
+  // candidate mode: per lane, the threshold of the query it finishes, the
+  // start of that query's list for this key range, and (one wave per query
+  // set) the list length so far; blocks whose waves share queries count in LDS
+  __shared__ uint32_t s_ccnt[EM && WK > 1 ? QB : 1];
+  float plk[NPAIR];
+  uint32_t ccnt[NPAIR];
+  uint64_t crow[NPAIR];
+  if constexpr (EM) {
+#pragma unroll
+    for (int pp = 0; pp < NPAIR; ++pp) {
+      const int qa = QPW > 1 ? 2 * pp : 0, qb = QPW > 1 ? 2 * pp + 1 : 0;
+      const int64_t tq = t0 + wq * QPW + (hi ? qb : qa);
+      const int64_t grow = b * a.nq + (tq < a.nq ? tq : a.nq - 1);
+      plk[pp] = a.lval[grow];
+      crow[pp] = ((uint64_t)grow * gridDim.y + blockIdx.y) * (uint64_t)a.cap;
+      ccnt[pp] = 0;
+    }
+    if constexpr (WK > 1) {
+      if (threadIdx.x < QB) s_ccnt[threadIdx.x] = 0;
+      __syncthreads();
+    }
+  }
 
   for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
     const int64_t s0 = tile * KT;
     if (s0 >= nvis_max) {
+      if constexpr (EM) continue;
       // nothing visible to any query of the block: -inf only
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
@@ -393,7 +429,30 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qa]), __float_as_uint(part[qb]),
                                                          false, false);
         const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        if constexpr (FULL) {
+        if constexpr (EM) {
+          // (scores are finite: the float order is the order of their keys)
+          const bool keep = (FULL ? pok[pp] : (pok[pp] && s32 < pvis[pp])) && total >= plk[pp];
+          const uint64_t bal = __ballot(keep);
+          if (bal != 0) {
+            const uint32_t lo32 = (uint32_t)bal, hi32 = (uint32_t)(bal >> 32);
+            // rank among the kept lanes of the same half (the same query)
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(hi32, __builtin_amdgcn_mbcnt_lo(lo32, 0u)) -
+                                   (hi ? (uint32_t)__popc(lo32) : 0u);
+            const uint32_t n = (uint32_t)__popc(hi ? hi32 : lo32);
+            uint32_t base;
+            if constexpr (WK == 1) {
+              base = ccnt[pp];
+              ccnt[pp] += n;
+            } else {
+              const int qrow = wq * QPW + (hi ? qb : qa);
+              uint32_t got = 0;
+              if ((l & 31) == 0 && n != 0) got = atomicAdd(&s_ccnt[qrow], n);
+              base = (uint32_t)__shfl((int)got, l & 32);
+            }
+            const uint32_t pos = base + below;
+            if (keep && pos < (uint32_t)a.cap) a.cand[crow[pp] + pos] = composite(score_key(total), (uint32_t)s32);
+          }
+        } else if constexpr (FULL) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), srsrc, (int)(prow_f[pp] + 4u * (uint32_t)s32),
                                                 0, 0);
         } else {
@@ -411,46 +470,70 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     else ntile_loop(std::false_type());
     __syncthreads();
   }
+  if constexpr (EM) {
+    // list lengths (the true count, also when it exceeds cap)
+    if constexpr (WK == 1) {
+#pragma unroll
+      for (int pp = 0; pp < NPAIR; ++pp)
+        if (pok[pp] && (l & 31) == 0) a.ccount[crow[pp] / (uint64_t)a.cap] = ccnt[pp];
+    } else {
+      if (threadIdx.x < QB && t0 + threadIdx.x < a.nq)
+        a.ccount[((uint64_t)(b * a.nq + t0 + threadIdx.x)) * gridDim.y + blockIdx.y] = s_ccnt[threadIdx.x];
+    }
+  }
+}
+
+template <int CI, int KL, int QF, int WQ, int QPW>
+static void launch_mfma_grid(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
+  const IndexerGrid g = indexer_grid(a, nb);
+  const dim3 grid((unsigned)(g.qblocks * nb), (unsigned)g.splits);
+  if constexpr (QF == 0) {
+    if (a.cand) {
+      hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, 0, true>), grid, dim3(256), 0, s, a, pt, b0, (int)g.qblocks,
+                         g.tps);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, QF, false>), grid, dim3(256), 0, s, a, pt, b0, (int)g.qblocks,
+                     g.tps);
 }
 
 template <int CI, int KL, int QF = 0>
 static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0, int nb, hipStream_t s) {
-  const int64_t ntiles = (a.S + KT - 1) / KT;
-  if (a.nq >= 16) {
-    // four queries per wave; two for bf16 queries at cI = 128, whose query
-    // fragments alone would take 128 registers at four
-    constexpr int WQ = 4, QPW = QF == 0 && CI == 128 ? 2 : 4;
-    const int qblocks = (int)((a.nq + WQ * QPW - 1) / (WQ * QPW));
-    int64_t units = (int64_t)qblocks * nb;
-    int64_t splits = (4096 + units - 1) / units;
-    if (splits > ntiles) splits = ntiles;
-    if (splits < 1) splits = 1;
-    const int tps = (int)((ntiles + splits - 1) / splits);
-    splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, QF>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
-                       a, pt, b0, qblocks, tps);
-  } else {
-    constexpr int WQ = 1, QPW = 1;
-    const int qblocks = (int)a.nq;
-    int64_t units = (int64_t)qblocks * nb;
-    int64_t splits = (2048 + units - 1) / units;
-    if (splits > ntiles) splits = ntiles;
-    if (splits < 1) splits = 1;
-    const int tps = (int)((ntiles + splits - 1) / splits);
-    splits = (ntiles + tps - 1) / tps;
-    hipLaunchKernelGGL((indexer_mfma<CI, KL, WQ, QPW, QF>), dim3((unsigned)units, (unsigned)splits), dim3(256), 0, s,
-                       a, pt, b0, qblocks, tps);
-  }
+  // four queries per wave (16 per block); two for bf16 queries at cI = 128,
+  // whose query fragments alone would take 128 registers at four; single
+  // queries when a sequence has fewer than 16 (indexer_grid matches these)
+  if (a.nq >= 16) launch_mfma_grid<CI, KL, QF, 4, QF == 0 && CI == 128 ? 2 : 4>(a, pt, b0, nb, s);
+  else launch_mfma_grid<CI, KL, QF, 1, 1>(a, pt, b0, nb, s);
 }
 
-static bool indexer_mfma_ok(const IndexerArgs& a) {
-  return a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 32 || a.cI == 64 || a.cI == 128) &&
-         a.S < ((int64_t)1 << 25) &&                 // 16 score rows fit a buffer range below 2^31 bytes
-         (a.k_layout == ROW_BF16 || a.k_layout == ROW_MXFP4);
+// keys 32 j + 31 of every batch entry, copied to a compact [nb, Ss] array
+__global__ void indexer_sample_keys(const uint8_t* keys, const uint8_t* scl, int64_t S, int64_t Ss, int krow,
+                                    int nbs, int64_t n, uint8_t* okeys, uint8_t* oscl) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t b = i / Ss, j = i % Ss;
+  const int64_t src = b * S + (int64_t)IT_STRIDE * j + (IT_STRIDE - 1);
+  const u32x4* sp = reinterpret_cast<const u32x4*>(keys + src * krow);
+  u32x4* dp = reinterpret_cast<u32x4*>(okeys + i * krow);
+  for (int c = 0; c < krow / 16; ++c) dp[c] = sp[c];
+  for (int c = 0; c < nbs; ++c) oscl[i * nbs + c] = scl[src * nbs + c];
+}
+
+hipError_t launch_indexer_sample_keys(const IndexerArgs& a, int64_t Ss, void* okeys, uint8_t* oscl, hipStream_t s) {
+  const int64_t n = a.B * Ss;
+  if (n <= 0) return hipSuccess;
+  const bool mx = a.k_layout == ROW_MXFP4;
+  const int krow = mx ? a.cI / 2 : row_bytes(a.k_layout, a.cI);
+  hipLaunchKernelGGL(indexer_sample_keys, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(a.keys), a.k_scales, a.S, Ss, krow, mx ? a.cI / 32 : 0, n,
+                     reinterpret_cast<uint8_t*>(okeys), oscl);
+  return hipGetLastError();
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s) {
   if (a.nq <= 0 || a.S <= 0 || a.B <= 0) return hipSuccess;
+  if (a.cand && (a.qfmt != 0 || !indexer_mfma_ok(a) || a.B > MAXB)) return hipErrorInvalidValue;
   for (int64_t b0 = 0; b0 < a.B; b0 += MAXB) {
     const int nb = (int)(a.B - b0 < MAXB ? a.B - b0 : MAXB);
     PosTable pt;

@@ -79,6 +79,99 @@ TopkPlan topk_make_plan(int64_t rows, int64_t S, int k) {
   return t;
 }
 
+// ------------------------------------------------------------------ indexer
+
+bool indexer_mfma_ok(const IndexerArgs& a) {
+  return a.q_dtype == ACT_BF16 && a.hI == 32 && (a.cI == 32 || a.cI == 64 || a.cI == 128) &&
+         a.S < ((int64_t)1 << 25) &&                 // 16 score rows fit a buffer range below 2^31 bytes
+         (a.k_layout == ROW_BF16 || a.k_layout == ROW_MXFP4);
+}
+
+// Query blocks of 16 queries (8 for bf16 queries at cI = 128), or single
+// queries below 16 per sequence; the key range of a block is split so that
+// about 4096 (2048 for single queries) blocks run.
+IndexerGrid indexer_grid(const IndexerArgs& a, int nb) {
+  IndexerGrid g = {};
+  const int64_t ntiles = (a.S + IDX_KT - 1) / IDX_KT;
+  int64_t target;
+  if (a.nq >= 16) {
+    g.qb = 4 * (a.qfmt == 0 && a.cI == 128 ? 2 : 4);
+    target = 4096;
+  } else {
+    g.qb = 1;
+    target = 2048;
+  }
+  g.qblocks = (a.nq + g.qb - 1) / g.qb;
+  const int64_t units = g.qblocks * nb;
+  int64_t splits = units > 0 ? (target + units - 1) / units : 1;
+  if (splits > ntiles) splits = ntiles;
+  if (splits < 1) splits = 1;
+  const int64_t tps = ntiles > 0 ? (ntiles + splits - 1) / splits : 1;
+  g.tps = (int)tps;
+  g.splits = (int)(ntiles > 0 ? (ntiles + tps - 1) / tps : 1);
+  return g;
+}
+
+// ------------------------------------------------------------------ index scores + top-k
+
+// Sample rank of the threshold: with one sample per 32 keys, the number of a
+// row's top-k scores that land in the sample has mean k / 32; ks sits six
+// standard deviations above it, so the threshold almost never cuts into the
+// top k, and about 32 ks scores pass it.
+static int it_sample_rank(int k) {
+  const double mu = (double)k / IT_STRIDE;
+  int ks = (int)(mu + 6.0 * __builtin_sqrt(mu)) + 2;
+  return ks < 1 ? 1 : ks;
+}
+
+IdxTopkPlan idxtopk_make_plan(const IndexerArgs& a, int k) {
+  IdxTopkPlan p = {};
+  const int64_t rows = a.B * a.nq;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t o = 0;
+  p.ks = it_sample_rank(k);
+  p.Ss = a.S / IT_STRIDE;
+  p.fused = a.qfmt == 0 && indexer_mfma_ok(a) && k <= SK_KMAX &&
+            (int64_t)IT_STRIDE * p.ks * 8 / 5 <= IT_SELCAP &&   // expected candidates well inside a select block
+            p.Ss >= 4 * (int64_t)p.ks && rows > 0;
+  if (p.fused) {
+    p.grid = indexer_grid(a, (int)a.B);
+    // slots per (row, split): four times the select block's share, at least 256
+    int64_t cap = (int64_t)4 * IT_SELCAP / p.grid.splits;
+    cap = cap < 256 ? 256 : (cap > IT_SELCAP ? IT_SELCAP : cap);
+    p.cap = (int)((cap + 63) / 64 * 64);
+    const size_t krow = a.k_layout == ROW_MXFP4 ? (size_t)a.cI / 2 : (size_t)a.cI * 2;
+    p.tk_sample = topk_make_plan(rows, p.Ss, p.ks);
+    p.o_skeys = o; o = al(o + (size_t)a.B * p.Ss * krow);
+    p.o_sscl = o; o = al(o + (a.k_layout == ROW_MXFP4 ? (size_t)a.B * p.Ss * (a.cI / 32) : 0));
+    p.o_sscore = o; o = al(o + (size_t)rows * p.Ss * 4);
+    p.o_sidx = o; o = al(o + (size_t)rows * p.ks * 4);
+    p.o_stk = o; o = al(o + p.tk_sample.bytes);
+    p.o_lkey = o; o = al(o + (size_t)rows * 4);
+    p.o_cand = o; o = al(o + (size_t)rows * p.grid.splits * p.cap * 8);
+    p.o_cnt = o; o = al(o + (size_t)rows * p.grid.splits * 4);
+    p.o_flags = o; o = al(o + (size_t)rows * 4);
+  }
+  p.tk_full = topk_make_plan(rows, a.S, k);
+  p.o_scores = o; o = al(o + (size_t)rows * a.S * 4);
+  p.o_ftk = o; o = al(o + p.tk_full.bytes);
+  p.bytes = o;
+  return p;
+}
+
+size_t idxtopk_workspace(const IndexerArgs& a, int k) {
+  if (a.B <= 0 || a.nq <= 0 || a.S <= 0) return 0;
+  IndexerArgs s = a;
+  s.B = a.B < MAXB ? a.B : MAXB;
+  size_t best = idxtopk_make_plan(s, k).bytes;
+  if (a.B > MAXB && a.B % MAXB) {
+    s.B = a.B % MAXB;
+    const size_t t = idxtopk_make_plan(s, k).bytes;
+    best = t > best ? t : best;
+  }
+  return best;
+}
+
 // ------------------------------------------------------------------ attention
 
 static int attn_path(const AttnArgs& a, bool dense) {

@@ -61,16 +61,6 @@ hipError_t topk_scratch_ptr(void** ptr) {
 constexpr int TK_THREADS = 1024;
 constexpr int NBIN = 4096;
 
-__device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;                    // -0.0 ties with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
-  return ((uint64_t)key << 32) | (uint64_t)(~idx);
-}
-
 // inclusive block scan of one value per thread (1024 threads)
 __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,7 +176,13 @@ struct TopkArgs {
   HsMeta* hmeta;     // [rows]
   uint64_t* hwin;    // [rows, k] winners above the threshold bin
   uint64_t* hcand;   // [rows, HS_CAP] keys of the threshold bin
+  const int* flags;  // [rows] or null: rows with a zero flag are skipped
 };
+
+// launch-local row `row` is skipped (block-uniform)
+__device__ __forceinline__ bool row_skipped(const TopkArgs& a, int64_t row) {
+  return a.flags && a.flags[row] == 0;
+}
 
 __device__ __forceinline__ int pow2_ceil(int x) {
   int p = 1;
@@ -205,6 +201,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_stage1(TopkArgs a, PosTable p
   uint64_t* out = reinterpret_cast<uint64_t*>(hist + NBIN);
 
   const int64_t row = (int64_t)blockIdx.x;         // row within this launch's batch slice
+  if (row_skipped(a, row)) return;
   const int pidx = blockIdx.y;
   const int64_t bl = row / a.nq, t = row % a.nq;
   const int64_t grow = (b0 + bl) * a.nq + t;       // global row
@@ -254,6 +251,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_stage2(TopkArgs a, PosTable p
   uint64_t* out = reinterpret_cast<uint64_t*>(hist + NBIN);
 
   const int64_t row = (int64_t)blockIdx.x;
+  if (row_skipped(a, row)) return;
   const int64_t bl = row / a.nq, t = row % a.nq;
   const int64_t grow = (b0 + bl) * a.nq + t;
   const int64_t nv = visible_count(pt.q_pos0[bl] + t, a.m, a.S);
@@ -499,6 +497,7 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
   extern __shared__ __align__(16) uint8_t smem[];
   SkShared& sh = *reinterpret_cast<SkShared*>(smem);
   const int64_t row = (int64_t)blockIdx.x;         // row within this launch's batch slice
+  if (row_skipped(a, row)) return;
   const int pidx = blockIdx.y;
   const int64_t bl = row / a.nq, t = row % a.nq;
   const int64_t grow = (b0 + bl) * a.nq + t;       // global row
@@ -663,6 +662,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_hist(TopkArgs a, PosTable pt, in
   __shared__ uint32_t h[HS_BIN];
   __shared__ uint32_t wsum[SK_NT / 64];
   const int64_t row = blockIdx.y;
+  if (row_skipped(a, row)) return;
   const int p = blockIdx.x;
   int64_t nv;
   const int64_t grow = hs_row(a, pt, b0, row, &nv);
@@ -704,6 +704,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_thresh(TopkArgs a, PosTable pt, 
   __shared__ uint32_t s_t0[SK_NT + 1];
   static_assert(HS_PER == 8, "two 16-byte loads per part and thread");
   const int64_t row = blockIdx.x;
+  if (row_skipped(a, row)) return;
   int64_t nv;
   hs_row(a, pt, b0, row, &nv);
   const uint32_t need = (uint32_t)(nv < a.k ? nv : a.k);
@@ -755,6 +756,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_thresh(TopkArgs a, PosTable pt, 
 __global__ __launch_bounds__(SK_NT) void topk_h_compact(TopkArgs a, PosTable pt, int b0) {
   __shared__ uint32_t na, nb;
   const int64_t row = blockIdx.y;
+  if (row_skipped(a, row)) return;
   const int p = blockIdx.x;
   int64_t nv;
   const int64_t grow = hs_row(a, pt, b0, row, &nv);
@@ -812,6 +814,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
   extern __shared__ __align__(16) uint8_t smem[];
   HsShared& sh = *reinterpret_cast<HsShared*>(smem);
   const int64_t row = blockIdx.x;
+  if (row_skipped(a, row)) return;
   int64_t nv;
   const int64_t grow = hs_row(a, pt, b0, row, &nv);
   const HsMeta mt = a.hmeta[row];
@@ -899,9 +902,17 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
 
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
                        const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan, hipStream_t s) {
+  return launch_topk_rows(scores, B, nq, S, m, q_pos0, k, idx, ws, plan, nullptr, s);
+}
+
+hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
+                            const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan,
+                            const int* row_flags, hipStream_t s) {
   if (B <= 0 || nq <= 0) return hipSuccess;
+  if (row_flags && B > MAXB) return hipErrorInvalidValue;     // flags index the rows of one launch slice
   TopkArgs a = {};
   a.scores = scores; a.nq = nq; a.S = S; a.m = m; a.k = k; a.idx = idx;
+  a.flags = row_flags;
   a.part = plan.part;
   a.nparts = plan.nparts;
   if (plan.kind == TOPK_HIST) {
@@ -963,6 +974,275 @@ hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, in
       if (e != hipSuccess) return e;
     }
   }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------------ index scores and top-k in one call
+
+// the float whose order key is `key` (finite or -inf for every key a
+// finite score or a prefix of one can have)
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Row thresholds from the sample top-k (long sample rows): the ks-th best
+// sample score, or -inf (every visible score passes) when the row sees fewer
+// than ks sample keys
+__global__ void it_lkey(const float* sscore, const int32_t* sidx, int64_t rows, int64_t Ss, int ks, float* lval) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int32_t j = sidx[r * ks + ks - 1];
+  lval[r] = j >= 0 ? key_to_float(score_key(sscore[r * Ss + j])) : -INFINITY;
+}
+
+constexpr int IT_THRESH_MAX = 16384;   // sample scores a threshold block holds in LDS
+
+// Row thresholds straight from the sample scores (rows of at most
+// IT_THRESH_MAX): one block per row stages the visible sample keys in LDS and
+// runs an MSD radix select (11, 11, 10 bits) for the ks-th largest key.  It
+// stops early when a whole digit bin is taken; the threshold is then the bin's
+// lowest key, with exactly ks sample keys at or above it.  Either way at
+// least ks sample scores reach the threshold.  dynamic LDS: Ss * 4 bytes
+__global__ __launch_bounds__(SK_NT) void it_thresh(const float* sscore, int64_t nq, int64_t Ss, int m, int ks,
+                                                    PosTable pt, float* lval) {
+  extern __shared__ __align__(16) uint32_t keys[];
+  __shared__ uint32_t hist[SK_BIN];
+  __shared__ uint32_t wsum[SK_NT / 64];
+  __shared__ uint32_t sel_bin, sel_above, sel_cnt;
+  const int64_t row = blockIdx.x;
+  const int64_t bl = row / nq, t = row % nq;
+  const int nv = (int)visible_count(pt.q_pos0[bl] + t, m, Ss);
+  if (nv < ks) {
+    if (threadIdx.x == 0) lval[row] = -INFINITY;
+    return;
+  }
+  const float* src = sscore + row * Ss;
+  for (int base = 0; base < nv; base += 8 * SK_NT) {      // eight loads in flight per thread
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * SK_NT + (int)threadIdx.x;
+      x[u] = src[i < nv ? i : nv - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * SK_NT + (int)threadIdx.x;
+      if (i < nv) keys[i] = score_key(x[u]);
+    }
+  }
+  uint32_t prefix = 0, remaining = (uint32_t)ks;
+  int shift = 32;
+  for (int level = 0; level < 3; ++level) {
+    const int width = level < 2 ? 11 : 10;
+    shift -= width;
+    const int top = shift + width;
+    for (int i = threadIdx.x; i < SK_BIN; i += SK_NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nv; i += SK_NT) {
+      const uint32_t k = keys[i];
+      if (top >= 32 || (k >> top) == (prefix >> top)) atomicAdd(&hist[(k >> shift) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    constexpr int PER = SK_BIN / SK_NT;
+    uint32_t c[PER];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) { c[q] = hist[SK_BIN - 1 - (PER * threadIdx.x + q)]; loc += c[q]; }
+    uint32_t total;
+    uint32_t above = sk_scan_excl(loc, wsum, &total);
+    if (above < remaining && remaining <= above + loc) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        if (above < remaining && remaining <= above + c[q]) {
+          sel_bin = SK_BIN - 1 - (PER * threadIdx.x + q);
+          sel_above = above;
+          sel_cnt = c[q];
+        }
+        above += c[q];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sel_bin, ab = sel_above, cb = sel_cnt;
+    __syncthreads();
+    prefix |= bin << shift;
+    remaining -= ab;
+    if (cb == remaining) break;          // the whole bin is taken
+  }
+  if (threadIdx.x == 0) lval[row] = key_to_float(prefix);
+}
+
+struct ItSelArgs {
+  const uint64_t* cand;     // [rows, splits, cap] composites
+  const uint32_t* ccount;   // [rows, splits] list lengths (may exceed cap)
+  int splits, cap;
+  int64_t nq, S;
+  int m, k;
+  int32_t* idx;             // [rows, k]
+  int* flags;               // [rows] out: 1 = left to the full-score path
+};
+
+static_assert(IT_SELCAP == SK_CAP, "a select block holds the candidates of one row");
+
+// One block per row: the k best of the row's lists, sorted.  Every visible
+// score at or above the row's threshold is in the lists unless one
+// overflowed; when there are at least min(k, visible) of them, the k best
+// of the row are among them.  A row where either fails, or whose lists
+// exceed one block's buffer, is flagged and left to the full-score path.
+__global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
+  __shared__ uint32_t s_cnt[SK_NT], s_off[SK_NT];
+  const int64_t row = blockIdx.x;
+  const int64_t bl = row / a.nq, t = row % a.nq;
+  const int64_t nv = visible_count(pt.q_pos0[bl] + t, a.m, a.S);
+  const uint32_t need = (uint32_t)(nv < a.k ? nv : a.k);
+  const uint32_t* cnt = a.ccount + row * a.splits;
+  uint32_t tot = 0;
+  int over = 0;
+  for (int i = threadIdx.x; i < a.splits; i += SK_NT) {
+    const uint32_t c = cnt[i];
+    tot += c;
+    over |= c > (uint32_t)a.cap ? 1 : 0;
+  }
+  uint32_t total;
+  sk_scan_excl(tot, sh.wsum, &total);
+  const bool flag = __syncthreads_or(over) || total < need || total > (uint32_t)SK_CAP;
+  if (threadIdx.x == 0) a.flags[row] = flag ? 1 : 0;
+  if (flag) return;
+  int32_t* out = a.idx + row * a.k;
+  if (need == 0) {
+    for (int i = threadIdx.x; i < a.k; i += SK_NT) out[i] = -1;
+    return;
+  }
+  // the lists into LDS, SK_NT lists at a time: offsets from a block scan of
+  // their lengths, then one wave copies each list
+  uint32_t base = 0;
+  for (int c0 = 0; c0 < a.splits; c0 += SK_NT) {
+    const int i = c0 + (int)threadIdx.x;
+    const uint32_t c = i < a.splits ? cnt[i] : 0u;
+    uint32_t sum;
+    const uint32_t ex = sk_scan_excl(c, sh.wsum, &sum);
+    s_cnt[threadIdx.x] = c;
+    s_off[threadIdx.x] = base + ex;
+    __syncthreads();
+    const int nsp = a.splits - c0 < SK_NT ? a.splits - c0 : SK_NT;
+    // flat positions [base, base + sum): list j holds [s_off[j], s_off[j] + s_cnt[j]);
+    // four loads in flight per thread
+    const uint64_t* lists = a.cand + ((uint64_t)row * a.splits + c0) * (uint64_t)a.cap;
+    for (uint32_t p0 = base; p0 < base + sum; p0 += 4 * SK_NT) {
+      uint64_t v[4];
+      uint32_t at[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t p = p0 + u * SK_NT + threadIdx.x;
+        at[u] = p;
+        int lo = 0, hi = nsp - 1;                  // last list starting at or before p
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_off[mid] <= p) lo = mid;
+          else hi = mid - 1;
+        }
+        v[u] = p < base + sum ? lists[(uint64_t)lo * a.cap + (p - s_off[lo])] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (at[u] < base + sum) sh.cand[at[u]] = v[u];
+    }
+    __syncthreads();
+    base += sum;
+  }
+  const int n = (int)total;
+  const uint64_t T = sk_select(sh, n, need);
+  sk_gather(sh, n, T);
+  const int n2 = pow2_ceil(a.k) > 256 ? SK_KMAX : pow2_ceil(a.k);
+  for (int i = need + threadIdx.x; i < n2; i += SK_NT) sh.out[i] = 0;
+  __syncthreads();
+  if (n2 == SK_KMAX) bitonic1024_desc(sh.out);
+  else bitonic_desc<SK_NT>(sh.out, n2);
+  for (int i = threadIdx.x; i < a.k; i += SK_NT) out[i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs& a0, const int64_t* q_pos0, int k, int32_t* idx, void* ws,
+                               hipStream_t s) {
+  if (a0.B <= 0 || a0.nq <= 0) return hipSuccess;
+  const size_t qes = a0.q_dtype == ACT_F32 ? 4 : 2;
+  const bool mx = a0.k_layout == ROW_MXFP4;
+  const size_t krow = mx ? (size_t)a0.cI / 2 : (size_t)row_bytes(a0.k_layout, a0.cI);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  hipError_t e = hipFuncSetAttribute((const void*)it_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)sizeof(SkShared));
+  if (e != hipSuccess) return e;
+#define IT_CHECK(x)            \
+  do {                         \
+    hipError_t e_ = (x);       \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+  for (int64_t b0 = 0; b0 < a0.B; b0 += MAXB) {
+    const int nb = (int)(a0.B - b0 < MAXB ? a0.B - b0 : MAXB);
+    IndexerArgs a = a0;
+    a.qI = reinterpret_cast<const uint8_t*>(a0.qI) + (size_t)b0 * a0.nq * a0.hI * a0.cI * qes;
+    a.wI = a0.wI + b0 * a0.nq * a0.hI;
+    a.keys = reinterpret_cast<const uint8_t*>(a0.keys) + (size_t)b0 * a0.S * krow;
+    a.k_scales = mx ? a0.k_scales + (size_t)b0 * a0.S * (a0.cI / 32) : nullptr;
+    a.B = nb;
+    a.scores = nullptr;
+    a.cand = nullptr; a.ccount = nullptr; a.lval = nullptr; a.cap = 0; a.row_flags = nullptr;
+    const int64_t* qp = q_pos0 + b0;
+    int32_t* oidx = idx + b0 * a0.nq * k;
+    const int64_t rows = (int64_t)nb * a.nq;
+    const IdxTopkPlan p = idxtopk_make_plan(a, k);
+    float* scores = reinterpret_cast<float*>(w + p.o_scores);
+    if (!p.fused) {
+      IndexerArgs af = a;
+      af.scores = scores;
+      IT_CHECK(launch_indexer(af, qp, s));
+      IT_CHECK(launch_topk(scores, nb, a.nq, a.S, a.m, qp, k, oidx, w + p.o_ftk, p.tk_full, s));
+      continue;
+    }
+    // sample scores and their ks-th best per row
+    uint8_t* sscl = mx ? w + p.o_sscl : nullptr;
+    IT_CHECK(launch_indexer_sample_keys(a, p.Ss, w + p.o_skeys, sscl, s));
+    IndexerArgs as = a;
+    as.keys = w + p.o_skeys;
+    as.k_scales = sscl;
+    as.S = p.Ss;
+    as.m = a.m * IT_STRIDE;
+    as.scores = reinterpret_cast<float*>(w + p.o_sscore);
+    IT_CHECK(launch_indexer(as, qp, s));
+    float* lval = reinterpret_cast<float*>(w + p.o_lkey);
+    PosTable pt;
+    for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = qp[i]; pt.win_pos0[i] = 0; }
+    if (p.Ss <= IT_THRESH_MAX) {
+      const size_t lds = (size_t)p.Ss * 4;
+      IT_CHECK(hipFuncSetAttribute((const void*)it_thresh, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(it_thresh, dim3((unsigned)rows), dim3(SK_NT), lds, s, as.scores, a.nq, p.Ss, as.m, p.ks, pt,
+                         lval);
+    } else {
+      int32_t* sidx = reinterpret_cast<int32_t*>(w + p.o_sidx);
+      IT_CHECK(launch_topk(as.scores, nb, a.nq, p.Ss, as.m, qp, p.ks, sidx, w + p.o_stk, p.tk_sample, s));
+      hipLaunchKernelGGL(it_lkey, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, as.scores, sidx, rows,
+                         p.Ss, p.ks, lval);
+    }
+    IT_CHECK(hipGetLastError());
+    // full pass: candidate lists
+    IndexerArgs ae = a;
+    ae.cand = reinterpret_cast<uint64_t*>(w + p.o_cand);
+    ae.ccount = reinterpret_cast<uint32_t*>(w + p.o_cnt);
+    ae.lval = lval;
+    ae.cap = p.cap;
+    IT_CHECK(launch_indexer(ae, qp, s));
+    // per-row select; flagged rows take the full-score path
+    int* flags = reinterpret_cast<int*>(w + p.o_flags);
+    ItSelArgs sa{ae.cand, ae.ccount, p.grid.splits, p.cap, a.nq, a.S, a.m, k, oidx, flags};
+    hipLaunchKernelGGL(it_select, dim3((unsigned)rows), dim3(SK_NT), sizeof(SkShared), s, sa, pt);
+    IT_CHECK(hipGetLastError());
+    IndexerArgs af = a;
+    af.scores = scores;
+    af.row_flags = flags;
+    IT_CHECK(launch_indexer(af, qp, s));
+    IT_CHECK(launch_topk_rows(scores, nb, a.nq, a.S, a.m, qp, k, oidx, w + p.o_ftk, p.tk_full, flags, s));
+  }
+#undef IT_CHECK
   return hipSuccess;
 }
 

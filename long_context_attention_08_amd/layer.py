@@ -10,8 +10,11 @@ One `step()` enqueues, on one stream, the calls of the pair:
        (CSA KV appended to the KV cache with its window rows to the CSA window
        buffer, CSA indexer keys appended, HCA entries appended with their
        window rows to the HCA window buffer);
-  CSA: index scores, top-k, sparse MQA;
+  CSA: index scores and top-k in one call (the score rows are not stored),
+       sparse MQA;
   HCA: dense MQA.
+indexer() and topk() are the same selection as two calls through a stored
+score buffer.
 Buffers are torch tensors owned by the caller; nothing is allocated in step().
 """
 import math
@@ -39,6 +42,9 @@ class PairLayer:
         self.out_hca = torch.empty_like(q_hca)
         nb = L.topk_workspace_size(1, n, self.S, k)
         self.ws_topk = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        nb = L.indexer_topk_workspace_size(L.BF16 if qI.dtype != torch.float32 else L.F32, key_layout, 1, n, hI, cI,
+                                           self.S, k)
+        self.ws_it = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         nb = max(L.attn_workspace_size(False, 1, n, nh, c, k + n_win),
                  L.attn_workspace_size(True, 1, n, nh, c, self.Sh + n_win))
         self.ws_attn = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
@@ -89,6 +95,12 @@ class PairLayer:
     def topk(self, stream=None):
         L.topk_select(self.scores, self.m, self.q_pos0, self.k, self.idx, self.ws_topk, stream=stream)
 
+    def indexer_topk(self, stream=None):
+        """idx as indexer() then topk() give it, in one call (dsv4_indexer_topk)."""
+        L.indexer_topk(self.qI.view(1, self.n, self.hI, self.cI), self.wI.view(1, self.n, self.hI),
+                       self.ki_codes[:self.S].view(1, self.S, -1), self.key_layout, self.m, self.q_pos0, self.k,
+                       self.idx, self.ws_it, k_scales=self.ki_scales[:self.S].view(1, self.S, -1), stream=stream)
+
     def sparse(self, stream=None):
         L.sparse_mqa_fwd(self.q.view(1, self.n, self.nh, self.c), self.kv_cache[:self.S].view(1, self.S, -1),
                          self.kv_layout, self.idx, self.kv_win.view(1, -1, self.kv_win.shape[1]), self.win_pos0,
@@ -107,8 +119,7 @@ class PairLayer:
 
     def step(self, stream=None):
         self.compress(stream)
-        self.indexer(stream)
-        self.topk(stream)
+        self.indexer_topk(stream)
         self.sparse(stream)
         self.hca_dense(stream)
 

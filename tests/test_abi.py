@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 29
+    assert len(syms) == 31
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -163,6 +163,56 @@ def test_topk_validation(L):
     assert need > 0
     assert f(FAKE, 16, 1, 262144, 4, pos(*[0] * 16), 1024, FAKE, None, 0, None) == 4         # workspace
     assert f(FAKE, 16, 1, 262144, 4, pos(*[0] * 16), 1024, FAKE, FAKE, need - 8, None) == 4
+
+
+def test_indexer_topk_validation(L):
+    """The one-call index scores + top-k checks its arguments and its
+    workspace before any HIP call."""
+    f = L.lib.dsv4_indexer_topk
+    mx = 3
+    args = lambda k, ws, wsb, q=pos(1 << 20): (FAKE, 1, FAKE, FAKE, FAKE, mx, 1, 64, 32, 64, 262144, 4, q, k,
+                                               FAKE, ws, wsb, None)
+    assert f(*args(5000, None, 0)) == 2                                   # k > 4096
+    assert f(*args(0, None, 0)) == 1                                      # k = 0
+    assert f(*args(64, None, 0, None)) == 1                               # q_pos0 NULL
+    need = L.lib.dsv4_indexer_topk_workspace_size(1, mx, 1, 64, 32, 64, 262144, 1024)
+    assert need >= 64 * 262144 * 4                                        # holds a full score row per query
+    assert f(*args(1024, None, 0)) == 4 and "workspace" in err(L)
+    assert f(*args(1024, FAKE, need - 256)) == 4
+    # MXFP4 keys with cI not a multiple of 32, and an unknown key layout
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, mx, 1, 64, 32, 48, 4096, 4, pos(0), 16, FAKE, FAKE, 1 << 30, None) == 2
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 7, 1, 64, 32, 64, 4096, 4, pos(0), 16, FAKE, FAKE, 1 << 30, None) == 2
+    # no scales for MXFP4 keys
+    assert f(FAKE, 1, FAKE, FAKE, None, mx, 1, 64, 32, 64, 4096, 4, pos(0), 16, FAKE, FAKE, 1 << 30, None) == 1
+
+
+def test_indexer_topk_workspace_sizes(L):
+    """Workspace of the one-call index scores + top-k: zero for empty calls; at
+    least the score rows of one 64-sequence slice; the largest slice decides
+    for batches beyond 64 sequences."""
+    ws = L.lib.dsv4_indexer_topk_workspace_size
+    assert ws(1, 3, 0, 64, 32, 64, 4096, 16) == 0
+    assert ws(1, 3, 1, 0, 32, 64, 4096, 16) == 0
+    for B in (1, 16, 64, 65, 130):
+        for nq in (1, 16, 64):
+            for k, S in ((16, 4096), (512, 16384), (1024, 262144)):
+                got = ws(1, 3, B, nq, 32, 64, S, k)
+                assert got >= min(B, 64) * nq * S * 4, (B, nq, k, S)
+                assert got % 256 == 0
+    # the fp32-query path (no sampled threshold) needs the score rows and the top-k workspace
+    base = ws(0, 0, 16, 4, 4, 32, 1 << 18, 1024)
+    assert base >= 16 * 4 * (1 << 18) * 4 + L.lib.dsv4_topk_workspace_size(16, 4, 1 << 18, 1024)
+
+
+def test_indexer_topk_sampled_path_workspace(L):
+    """The bf16 / 32-head shapes take the sampled-threshold path: its
+    workspace holds candidate lists on top of the score rows and the top-k
+    workspace that the plain sequence needs; fp32 queries do not."""
+    for B, nq, S, k in ((1, 512, 264192, 1024), (16, 1, 262144, 1024), (2, 40, 20011, 512)):
+        plain = B * nq * S * 4 + L.topk_workspace_size(B, nq, S, k)
+        assert L.indexer_topk_workspace_size(L.BF16, L.ROW_MXFP4, B, nq, 32, 64, S, k) > plain + B * nq * 8 * 256
+    plain = 2 * 10 * 5000 * 4 + L.topk_workspace_size(2, 10, 5000, 64)
+    assert L.indexer_topk_workspace_size(L.F32, L.ROW_F32, 2, 10, 4, 32, 5000, 64) < plain + 1024
 
 
 def test_topk_noalloc_validation(L):

@@ -218,7 +218,12 @@ def test_cfg5_layer_pair(L):
     P, S0, Sh0 = int(inp["q_pos0"][0]), inp["S0"], inp["Sh0"]
     layer = pair_from_arrays(inp)
     layer.step()
+    # the step's one-call index scores + top-k against the two calls through the stored scores, on all 8192 rows
+    idx_step = layer.idx.clone()
+    layer.indexer()
+    layer.topk()
     torch.cuda.synchronize()
+    assert torch.equal(idx_step, layer.idx), "indexer_topk differs from indexer_score + topk_select"
     H = decode_act(inp["H"])
     # ---- compressors (in full)
     comp, raw = O.csa_compress(H, decode_act(inp["W_kv"]), inp["B_kv"], m, block0=S0, n_left=nl)
@@ -267,13 +272,13 @@ def test_cfg5_layer_pair(L):
 def test_cfg5_step_is_bitwise_repeatable(L):
     """Every reduction order in the step is fixed (no floating-point atomics,
     split-K merged in split order, exact integer top-k), so two steps over the
-    same chunk give the same bytes in every output: caches, scores, indices
-    and both attention outputs."""
+    same chunk give the same bytes in every output: caches, indices and both
+    attention outputs."""
     import torch
     from long_context_attention_08_amd.layer import pair_from_arrays
     layer = pair_from_arrays(G.make(5))
     outs = lambda: [t.clone() for t in (layer.kv_new, layer.kv_win_new, layer.ki_new, layer.ki_sc_new, layer.hca_new,
-                                        layer.hca_win_new, layer.scores, layer.idx, layer.out, layer.out_hca)]
+                                        layer.hca_win_new, layer.idx, layer.out, layer.out_hca)]
     layer.step()
     torch.cuda.synchronize()
     first = outs()
