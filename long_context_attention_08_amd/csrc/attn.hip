@@ -748,6 +748,10 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 //     tile at slot kperm(j) (bits 2 and 3 of j swapped), so those 8 slots are
 //     the keys 16 s + 4 G + {0..3}, 16 s + 8 + 4 G + {0..3} that the P^T
 //     fragment of lane half G holds (registers 8 s .. 8 s + 7 of S^T);
+//   * a piece (16 bytes of a row) of the 32 keys is a 512-byte run of slots,
+//     and in odd pieces slot j sits at position j ^ 8: the transposed reads
+//     take the same 8 slots of pieces 2 i and 2 i + 1 together, which would
+//     otherwise lie 512 bytes apart, in the same LDS banks;
 //   * per tile: [copies of tile it landed] barrier, copies of tile it+2, S^T,
 //     partial out, barrier, softmax, PV.
 constexpr int F8_NSTG = 3;
@@ -841,8 +845,9 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     *pos = (int)ui.wlo + (s - ncomp);
     return win_base + (int64_t)(s - ncomp) * RB;
   };
-  // copies of tile `it`: lane l serves stage slot l % 32, which holds key kperm(l % 32)
-  const int kp = kperm(l & 31);
+  // copies of tile `it`: lane l fills position l % 32 of a piece of parity G,
+  // which holds slot (l % 32) ^ 8 G, that is key kperm((l % 32) ^ 8 G)
+  const int kp = kperm((l & 31) ^ (8 * G));
   auto issue = [&](int it, uint8_t* stg) {
     const int s0 = slot_lo + it * TS;
     const uint8_t* rowp;
@@ -915,7 +920,8 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   typedef int v2i __attribute__((ext_vector_type(2)));
   // S^T operand: key m = l % 32 at stage slot kperm(m); channel half ch: E4M3
   // pieces 16 ch + kk (kk < 16 - 4 ch), then bf16 pieces 28 + 2 (kk - 12) + G
-  const int kslot = kperm(col) * 16;
+  // (every piece a lane half reads has parity G)
+  const int kslot = (kperm(col) ^ (8 * G)) * 16;
   auto score_tile = [&](auto chc, const uint8_t* stg) -> f32x16 {
     constexpr int CHW = decltype(chc)::value;
     f32x16 sacc;
@@ -952,10 +958,11 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   auto pv_half = [&](auto chc, const uint8_t* stg, int s, const bf16x8& pf) {
     constexpr int CHW = decltype(chc)::value;
     const int slot8 = 16 * s + 8 * G;              // first of the 8 stage slots of this lane half
+    const int pos8 = slot8 ^ (8 * grp);            // their positions in a piece of parity grp
     if constexpr (CHW == 0) {
       auto rd = [&](int mo) {                      // E4M3 pieces 2 mo + grp
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
-            stg + ((2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+            stg + ((2 * mo + grp) * TS + pos8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
       };
       v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
 #pragma unroll
@@ -970,7 +977,7 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     } else {
       auto rd = [&](int mo) {                      // E4M3 pieces 16 + 2 mo + grp
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
-            stg + ((16 + 2 * mo + grp) * TS + slot8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+            stg + ((16 + 2 * mo + grp) * TS + pos8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
       };
       v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
 #pragma unroll
@@ -984,8 +991,9 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
       }
 #pragma unroll
       for (int mo = 6; mo < MO; ++mo) {            // bf16 channels 448 + 32 (mo - 6) + 16 grp + lam
-        const int piece = NF8 + 4 * (mo - 6) + 2 * grp + ((lam & 3) >> 1);
-        const uint8_t* p0 = stg + (piece * TS + slot8 + (lam >> 2)) * 16 + 8 * (lam & 1);
+        const int par = (lam >> 1) & 1;            // parity of the piece
+        const int piece = NF8 + 4 * (mo - 6) + 2 * grp + par;
+        const uint8_t* p0 = stg + (piece * TS + (slot8 ^ (8 * par)) + (lam >> 2)) * 16 + 8 * (lam & 1);
         const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0));
         const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * 16));
         const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
