@@ -1,8 +1,8 @@
 """Benchmark: query tokens/s of the interleaved CSA + HCA layer pair at 1M context.
 
 Workload (one step = every call of the hot path once: the chunk's three
-compressors in one launch, index scores + top-k in one call, sparse MQA, HCA
-dense MQA): an 8192-token chunk
+compressors in one launch, index scores + top-k in one call, sparse MQA and
+HCA dense MQA, each with the output rotation in its store): an 8192-token chunk
 at positions [2^20, 2^20 + 8192) against caches prefilled with 2^20 tokens
 (262144 CSA entries, 8192 HCA entries, 128-row SWA tails); bf16 activations,
 fp8 + bf16-RoPE KV rows, MXFP4 indexer keys, d = 4096, c = 512, 64 heads,

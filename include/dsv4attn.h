@@ -299,6 +299,31 @@ int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The two attention cores with the output rotation (dsv4_out_rope; digest
+ * 模块 D: each entry is key and value, so the output's RoPE dims are rotated
+ * back by the query's position) done in the same launch: out is bit for bit
+ * what the call without _rope followed by dsv4_out_rope(out, ..., theta,
+ * rope_dims, q_pos0) leaves, without the second pass over out.  rope_dims and
+ * c multiples of 8, rope_dims <= min(c, 512), theta > 0 (else
+ * DSV4_ERR_UNSUPPORTED / DSV4_ERR_INVALID_ARG before anything is launched);
+ * rope_dims 0 is the plain call.  Other arguments, the workspace and the
+ * limits as for dsv4_sparse_mqa_fwd / dsv4_hca_dense_fwd.
+ */
+int dsv4_sparse_mqa_fwd_rope(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                             const void* kv_comp, int kv_layout, int64_t S,
+                             const int32_t* idx, int k,
+                             const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                             const int64_t* q_pos0, const float* sink, float scale,
+                             float theta, int rope_dims,
+                             void* out, void* ws, size_t ws_bytes, void* stream);
+int dsv4_hca_dense_fwd_rope(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                            const void* kv_comp, int kv_layout, int64_t S, int m_prime,
+                            const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                            const int64_t* q_pos0, const float* sink, float scale,
+                            float theta, int rope_dims,
+                            void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Query-side RMSNorm and partial RoPE (digest 模块 D: each query head is
  * RMS-normalised before core attention; RoPE acts on the last dims only).
  * For every row x = q[b, t, h, :] of width c, at position p = q_pos0[b] + t:

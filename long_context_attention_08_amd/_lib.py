@@ -20,7 +20,8 @@ EXPORTS = [
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
     "dsv4_topk_workspace_size", "dsv4_topk_select", "dsv4_topk_select_noalloc", "dsv4_attn_workspace_size", "dsv4_attn_plan",
-    "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_status_string", "dsv4_last_error",
+    "dsv4_sparse_mqa_fwd", "dsv4_hca_dense_fwd", "dsv4_sparse_mqa_fwd_rope", "dsv4_hca_dense_fwd_rope",
+    "dsv4_status_string", "dsv4_last_error",
     "dsv4_stream_state_bytes", "dsv4_stream_state_reset", "dsv4_stream_workspace_size",
     "dsv4_stream_compress", "dsv4_swa_ring_pos0",
 ]
@@ -92,6 +93,10 @@ _sig("dsv4_sparse_mqa_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int,
                                    _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
 _sig("dsv4_hca_dense_fwd", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _int,
                                   _vp, _i64, _P64, _int, _P64, _vp, _f32, _vp, _vp, _sz, _vp])
+_sig("dsv4_sparse_mqa_fwd_rope", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _vp, _int,
+                                        _vp, _i64, _P64, _int, _P64, _vp, _f32, _f32, _int, _vp, _vp, _sz, _vp])
+_sig("dsv4_hca_dense_fwd_rope", _int, [_vp, _int, _i64, _i64, _int, _int, _vp, _int, _i64, _int,
+                                       _vp, _i64, _P64, _int, _P64, _vp, _f32, _f32, _int, _vp, _vp, _sz, _vp])
 
 
 
@@ -273,28 +278,40 @@ def attn_plan(dense, q_dtype, kv_layout, B, nq, nh, c, S, k, m_prime, n_win, q_p
 
 
 def sparse_mqa_fwd(q, kv_comp, kv_layout, idx, kv_win, win_pos0, n_win, q_pos0, sink, scale, out,
-                   ws=None, *, S=None, W=None, stream=None):
-    """CSA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; idx [B, nq, k]; kv_win [B, W, row]."""
+                   ws=None, *, S=None, W=None, out_rope=None, stream=None):
+    """CSA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; idx [B, nq, k]; kv_win [B, W, row].
+    out_rope=(theta, rope_dims): the output rotation in the same launch
+    (dsv4_sparse_mqa_fwd_rope)."""
     B, nq, nh, c = q.shape
     S = kv_comp.shape[1] if S is None else S
     W = kv_win.shape[1] if (W is None and kv_win is not None) else (W or 0)
     k = idx.shape[2] if idx is not None else 0
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.dsv4_sparse_mqa_fwd(_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, _ptr(idx), k,
-                                   _ptr(kv_win), W, _host_i64(win_pos0), n_win, _host_i64(q_pos0),
-                                   _ptr(sink), float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    head = (_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, _ptr(idx), k, _ptr(kv_win), W,
+            _host_i64(win_pos0), n_win, _host_i64(q_pos0), _ptr(sink), float(scale))
+    tail = (_ptr(out), _ptr(ws), wsb, _stream(stream))
+    if out_rope is None:
+        _check(lib.dsv4_sparse_mqa_fwd(*head, *tail))
+    else:
+        _check(lib.dsv4_sparse_mqa_fwd_rope(*head, float(out_rope[0]), int(out_rope[1]), *tail))
 
 
 def hca_dense_fwd(q, kv_comp, kv_layout, m_prime, kv_win, win_pos0, n_win, q_pos0, sink, scale, out,
-                  ws=None, *, S=None, W=None, stream=None):
-    """HCA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; kv_win [B, W, row]."""
+                  ws=None, *, S=None, W=None, out_rope=None, stream=None):
+    """HCA core.  q [B, nq, nh, c]; kv_comp [B, S, row]; kv_win [B, W, row].
+    out_rope=(theta, rope_dims): the output rotation in the same launch
+    (dsv4_hca_dense_fwd_rope)."""
     B, nq, nh, c = q.shape
     S = kv_comp.shape[1] if S is None else S
     W = kv_win.shape[1] if (W is None and kv_win is not None) else (W or 0)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.dsv4_hca_dense_fwd(_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, m_prime,
-                                  _ptr(kv_win), W, _host_i64(win_pos0), n_win, _host_i64(q_pos0),
-                                  _ptr(sink), float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    head = (_ptr(q), _act(q), B, nq, nh, c, _ptr(kv_comp), kv_layout, S, m_prime, _ptr(kv_win), W,
+            _host_i64(win_pos0), n_win, _host_i64(q_pos0), _ptr(sink), float(scale))
+    tail = (_ptr(out), _ptr(ws), wsb, _stream(stream))
+    if out_rope is None:
+        _check(lib.dsv4_hca_dense_fwd(*head, *tail))
+    else:
+        _check(lib.dsv4_hca_dense_fwd_rope(*head, float(out_rope[0]), int(out_rope[1]), *tail))
 
 
 # --------------------------------------------------------------------- Q/KV norm and RoPE

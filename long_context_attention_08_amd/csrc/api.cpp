@@ -396,11 +396,13 @@ int dsv4_attn_plan(int dense, int q_dtype, int kv_layout, int64_t B, int64_t nq,
   return ok();
 }
 
+static int rope_args_ok(const char* fn, int c, float eps, float theta, int rope_dims);
+
 static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, int64_t B, int64_t nq, int nh,
                        int c, const void* kv_comp, int kv_layout, int64_t S, const int32_t* idx, int k,
                        int ratio, const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
                        const int64_t* q_pos0, const float* sink, float scale, void* out, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, float rot_theta = 0.f, int rot_dims = 0) {
   if (B < 0 || nq < 0 || nh <= 0 || c <= 0 || S < 0 || W < 0 || n_win < 0 || k < 0)
     return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (dense && ratio <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: m_prime <= 0", fn);
@@ -408,6 +410,10 @@ static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, i
   if (!act_ok(q_dtype)) return fail(DSV4_ERR_UNSUPPORTED, "%s: q_dtype %d", fn, q_dtype);
   if (!kv_layout_ok(kv_layout, c)) return fail(DSV4_ERR_UNSUPPORTED, "%s: kv_layout %d with c=%d", fn, kv_layout, c);
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(DSV4_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (rot_dims != 0) {
+    int r = rope_args_ok(fn, c, 0.f, rot_theta, rot_dims);
+    if (r) return r;
+  }
   if (B == 0 || nq == 0) return ok();
   if (!q_pos0) return fail(DSV4_ERR_INVALID_ARG, "%s: q_pos0 is NULL", fn);
   int r = check_ptrs16(fn, {{q, "q"}, {out, "out"}});
@@ -432,7 +438,7 @@ static int attn_common(const char* fn, bool dense, const void* q, int q_dtype, i
     }
   }
   dsv4::AttnArgs a{q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, dense ? nullptr : idx, dense ? 0 : k,
-                   dense ? ratio : 1, kv_win, W, n_win, sink, scale, out, ws, ws_bytes};
+                   dense ? ratio : 1, kv_win, W, n_win, sink, scale, out, ws, ws_bytes, rot_theta, rot_dims};
   // one plan serves the check and the launch
   const dsv4::AttnLaunchPlan plan = dsv4::attn_make_plan(a, dense, dsv4::attn_group_slots(a, q_pos0, dense));
   if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
@@ -457,6 +463,28 @@ int dsv4_hca_dense_fwd(const void* q, int q_dtype, int64_t B, int64_t nq, int nh
                        void* out, void* ws, size_t ws_bytes, void* stream) {
   return attn_common("dsv4_hca_dense_fwd", true, q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, nullptr, 0,
                      m_prime, kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream);
+}
+
+int dsv4_sparse_mqa_fwd_rope(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                             const void* kv_comp, int kv_layout, int64_t S,
+                             const int32_t* idx, int k,
+                             const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                             const int64_t* q_pos0, const float* sink, float scale,
+                             float theta, int rope_dims,
+                             void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common("dsv4_sparse_mqa_fwd_rope", false, q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, idx, k, 1,
+                     kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream, theta, rope_dims);
+}
+
+int dsv4_hca_dense_fwd_rope(const void* q, int q_dtype, int64_t B, int64_t nq, int nh, int c,
+                            const void* kv_comp, int kv_layout, int64_t S, int m_prime,
+                            const void* kv_win, int64_t W, const int64_t* win_pos0, int n_win,
+                            const int64_t* q_pos0, const float* sink, float scale,
+                            float theta, int rope_dims,
+                            void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common("dsv4_hca_dense_fwd_rope", true, q, q_dtype, B, nq, nh, c, kv_comp, kv_layout, S, nullptr, 0,
+                     m_prime, kv_win, W, win_pos0, n_win, q_pos0, sink, scale, out, ws, ws_bytes, stream, theta,
+                     rope_dims);
 }
 
 // --------------------------------------------------------------------------- Q/KV norm and RoPE

@@ -68,6 +68,41 @@ __device__ __forceinline__ bool slot_visible(bool win, int64_t pos, int64_t p, i
   return pos >= 0 && pos < nvis;
 }
 
+// ------------------------------------------------------------------ output rotation in the store
+// (DeepSeek-V4 digest, 模块 D: the output's RoPE dims are rotated back by the
+// query's position.)  The result is what storing the output and then rotating
+// the stored row gives: a bf16 output is rounded to bf16 first, the pair is
+// rotated in fp32 by rope_pair and rounded again.  Pairs are whole within
+// any 4 aligned channels (c and the rotated width are multiples of 8).
+
+// cos / sin of the rotation of nqb queries from position pfirst on: pair j of
+// query q at tcs / tsn[q * R / 2 + j] (block-wide)
+__device__ __forceinline__ void out_rot_table(float* tcs, float* tsn, int nqb, int64_t pfirst, int R, float theta) {
+  const int np = R >> 1;
+  for (int i = threadIdx.x; i < nqb * np; i += blockDim.x)
+    rope_cs(-(pfirst + i / np), i % np, R, theta, &tcs[i], &tsn[i]);
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+  return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) << 16);
+}
+
+// bf16 store of channels e0 .. e0 + 3 (e0 % 4 == 0) of a row; rotated when
+// they lie in the last R channels (cs / sn: the row's query's table)
+__device__ __forceinline__ void store4_bf16_rot(uint16_t* dst, float v0, float v1, float v2, float v3, int e0, int c,
+                                                int R, const float* cs, const float* sn) {
+  if (R > 0 && e0 >= c - R) {
+    float x0 = bf16_round(v0), x1 = bf16_round(v1), x2 = bf16_round(v2), x3 = bf16_round(v3);
+    const int j = (e0 - (c - R)) >> 1;
+    rope_pair(x0, x1, cs[j], sn[j]);
+    rope_pair(x2, x3, cs[j + 1], sn[j + 1]);
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+  } else {
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)v0, (__bf16)v1}),
+                                             __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)v2, (__bf16)v3})};
+  }
+}
+
 // ------------------------------------------------------------------ generic (fp32 math)
 // one block of 256 threads per (b, t, h); keys in chunks of 256 with an online softmax
 __global__ __launch_bounds__(256) void attn_generic(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
@@ -143,9 +178,22 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a, PosTable pt, int
     den = l_run * f + __expf(z - M);
   }
   const float inv = den > 0.f ? f / den : 0.f;
+  const int R = a.rot_dims;
   for (int jj = 0; jj < 4; ++jj) {
     const int j = threadIdx.x + 256 * jj;
-    if (j < c) store_act(a.out, a.q_dtype, qbase + j, o[jj] * inv);
+    float v = j < c ? o[jj] * inv : 0.f;
+    if (R > 0) {                          // pairs (j, j ^ 1): neighbouring lanes of one wave
+      if (a.q_dtype == ACT_BF16) v = bf16_round(v);
+      const float pv = __shfl_xor(v, 1);
+      if (j < c && j >= c - R) {
+        float cs, sn;
+        rope_cs(-(pt.q_pos0[bl] + t), (j - (c - R)) >> 1, R, a.rot_theta, &cs, &sn);
+        float x0 = (j & 1) ? pv : v, x1 = (j & 1) ? v : pv;
+        rope_pair(x0, x1, cs, sn);
+        v = (j & 1) ? x1 : x0;
+      }
+    }
+    if (j < c) store_act(a.out, a.q_dtype, qbase + j, v);
   }
 }
 
@@ -694,6 +742,15 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     lds_barrier();
     l_run += s_xm[partner * 64 + l];
   }
+  // output rotation table in the stage (every wave is done with it)
+  const int R = pl.max_splits == 1 ? a.rot_dims : 0;
+  float* tcs = reinterpret_cast<float*>(s_stage);
+  float* tsn = tcs + nq_blk * (R >> 1);
+  if (R > 0) {
+    lds_barrier();
+    out_rot_table(tcs, tsn, nq_blk, pfirst, R, a.rot_theta);
+    lds_barrier();
+  }
   if (!qvalid) return;
   // register r of m-tile mo holds channel ch*CH + 32 mo + 8 (r/4) + 4 G + r%4 of this lane's row
   if (pl.max_splits == 1) {
@@ -706,14 +763,15 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
     }
     const float inv = den > 0.f ? f / den : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + ch * CH;
+    const float* qcs = tcs + qloc * (R >> 1);
+    const float* qsn = tsn + qloc * (R >> 1);
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j] * inv), (__bf16)(acc[mo][4 * j + 1] * inv)}),
-                         __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j + 2] * inv), (__bf16)(acc[mo][4 * j + 3] * inv)})};
-        *reinterpret_cast<u32x2*>(orow + 32 * mo + 8 * j + 4 * G) = w;
-      }
+      for (int j = 0; j < 4; ++j)
+        store4_bf16_rot(orow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv,
+                        acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, ch * CH + 32 * mo + 8 * j + 4 * G, C, R,
+                        qcs, qsn);
   } else {
     // partials: [unit][split][R rows] {m, l} and [unit][split][R rows][C]
     const int64_t unit = blockIdx.x;
@@ -1076,6 +1134,15 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   else tile_loop(std::integral_constant<int, 1>());
 
   l_run = sum_halves(l_run);
+  // output rotation table in the stage (after a barrier: every wave is done with it)
+  const int R = pl.max_splits == 1 ? a.rot_dims : 0;
+  float* tcs = reinterpret_cast<float*>(s_stage);
+  float* tsn = tcs + nq_blk * (R >> 1);
+  if (R > 0) {
+    lds_barrier();
+    out_rot_table(tcs, tsn, nq_blk, pfirst, R, a.rot_theta);
+    lds_barrier();
+  }
   if (!qvalid) return;
   if (pl.max_splits == 1) {
     float f = m_run == -INFINITY ? 0.f : 1.f, den = l_run;
@@ -1087,14 +1154,15 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
     }
     const float inv = den > 0.f ? f / den : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + ch * 256;
+    const float* qcs = tcs + qloc * (R >> 1);
+    const float* qsn = tsn + qloc * (R >> 1);
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j] * inv), (__bf16)(acc[mo][4 * j + 1] * inv)}),
-                         __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(acc[mo][4 * j + 2] * inv), (__bf16)(acc[mo][4 * j + 3] * inv)})};
-        *reinterpret_cast<u32x2*>(orow + 32 * mo + 8 * j + 4 * G) = w;
-      }
+      for (int j = 0; j < 4; ++j)
+        store4_bf16_rot(orow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv,
+                        acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, ch * 256 + 32 * mo + 8 * j + 4 * G, C, R,
+                        qcs, qsn);
   } else {
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
@@ -1171,9 +1239,19 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t obase = ((b * a.nq + t) * a.nh + h) * c + lane * CPT;
+  const int R = a.rot_dims;
 #pragma unroll
   for (int j = 0; j < CPT; j += 2) {
-    const uint32_t w2 = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(o[j] * inv), (__bf16)(o[j + 1] * inv)});
+    const int e = lane * CPT + j;
+    uint32_t w2;
+    if (R > 0 && e >= c - R) {
+      float x0 = bf16_round(o[j] * inv), x1 = bf16_round(o[j + 1] * inv), cs, sn;
+      rope_cs(-(pt.q_pos0[bl] + t), (e - (c - R)) >> 1, R, a.rot_theta, &cs, &sn);
+      rope_pair(x0, x1, cs, sn);
+      w2 = pack_bf16x2(x0, x1);
+    } else {
+      w2 = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(o[j] * inv), (__bf16)(o[j + 1] * inv)});
+    }
     *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + obase + j) = w2;
   }
 }

@@ -174,6 +174,16 @@ __device__ __forceinline__ void store_row_elem(uint8_t* row, int layout, int c, 
   else reinterpret_cast<uint16_t*>(row + nf8)[j - nf8] = (uint16_t)f32_to_bf16(v);
 }
 
+// RoPE rotation of one pair by the angle with cosine c and sine s, in one
+// fixed rounding order (every rotation that must agree bit for bit with
+// another, such as the output rotation fused into an attention store and the
+// separate output-rotation call, goes through here)
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, float c, float s) {
+  const float a = x0, b = x1;
+  x0 = fmaf(a, c, -(b * s));
+  x1 = fmaf(a, s, b * c);
+}
+
 // cos / sin of pos * theta^(-2j/R)
 __device__ __forceinline__ void rope_cs(int64_t pos, int j, int R, float theta, float* c, float* s) {
   const double inv = exp2(-2.0 * (double)j / (double)R * log2((double)theta));

@@ -185,6 +185,11 @@ struct AttnArgs {
   void* out;            // [B, nq, nh, c]
   void* ws;
   size_t ws_bytes;
+  // output rotation in the store (rot_dims 0: none): the last rot_dims
+  // channels of each output row, as pairs, rotated by -(query position),
+  // exactly as the separate output-rotation call does to the stored row
+  float rot_theta;
+  int rot_dims;
 };
 
 // Q/KV RMSNorm + partial RoPE, and the output rotation (normrope.hip)

@@ -72,9 +72,7 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[NP][8], int c, int l, f
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         const int j = (e0 + i - (c - R)) >> 1;
-        const float a = x[p][i], b = x[p][i + 1];
-        x[p][i] = a * cs[j] - b * sn[j];
-        x[p][i + 1] = a * sn[j] + b * cs[j];
+        rope_pair(x[p][i], x[p][i + 1], cs[j], sn[j]);
       }
     }
   }

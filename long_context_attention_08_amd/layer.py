@@ -12,7 +12,9 @@ One `step()` enqueues, on one stream, the calls of the pair:
        window rows to the HCA window buffer);
   CSA: index scores and top-k in one call (the score rows are not stored),
        sparse MQA;
-  HCA: dense MQA.
+  HCA: dense MQA;
+  both attention calls rotate the output's RoPE dims back by the query
+  position in their store (out_rope=(theta, rope_dims); None: not rotated).
 indexer() and topk() are the same selection as two calls through a stored
 score buffer.
 Buffers are torch tensors owned by the caller; nothing is allocated in step().
@@ -26,7 +28,7 @@ class PairLayer:
     def __init__(self, *, H, n_left, m, mp, c, cI, hI, nh, k, n_win,
                  W_kv, B_kv, W_ki, B_ki, W_hca, B_hca,
                  kv_cache, S0, ki_codes, ki_scales, hca_cache, Sh0, kv_win, hca_win, win_pos0,
-                 q, qI, wI, q_hca, sink, sink_hca, q_pos0, kv_layout, key_layout):
+                 q, qI, wI, q_hca, sink, sink_hca, q_pos0, kv_layout, key_layout, out_rope=(10000.0, 64)):
         import torch
         self.__dict__.update(locals())
         del self.__dict__["self"]
@@ -105,7 +107,7 @@ class PairLayer:
         L.sparse_mqa_fwd(self.q.view(1, self.n, self.nh, self.c), self.kv_cache[:self.S].view(1, self.S, -1),
                          self.kv_layout, self.idx, self.kv_win.view(1, -1, self.kv_win.shape[1]), self.win_pos0,
                          self.n_win, self.q_pos0, self.sink, self.scale, self.out.view(1, self.n, self.nh, self.c),
-                         self.ws_attn, stream=stream)
+                         self.ws_attn, out_rope=self.out_rope, stream=stream)
 
     def hca_compress(self, stream=None):
         L.hca_compress(self.H[self.n_left:], self.W_hca, self.B_hca, self.mp, self.c, self.hca_new,
@@ -115,7 +117,8 @@ class PairLayer:
         L.hca_dense_fwd(self.q_hca.view(1, self.n, self.nh, self.c), self.hca_cache[:self.Sh].view(1, self.Sh, -1),
                         self.kv_layout, self.mp, self.hca_win.view(1, -1, self.hca_win.shape[1]), self.win_pos0,
                         self.n_win, self.q_pos0, self.sink_hca, self.scale,
-                        self.out_hca.view(1, self.n, self.nh, self.c), self.ws_attn, stream=stream)
+                        self.out_hca.view(1, self.n, self.nh, self.c), self.ws_attn, out_rope=self.out_rope,
+                        stream=stream)
 
     def step(self, stream=None):
         self.compress(stream)

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 31
+    assert len(syms) == 33
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -213,6 +213,22 @@ def test_indexer_topk_sampled_path_workspace(L):
         assert L.indexer_topk_workspace_size(L.BF16, L.ROW_MXFP4, B, nq, 32, 64, S, k) > plain + B * nq * 8 * 256
     plain = 2 * 10 * 5000 * 4 + L.topk_workspace_size(2, 10, 5000, 64)
     assert L.indexer_topk_workspace_size(L.F32, L.ROW_F32, 2, 10, 4, 32, 5000, 64) < plain + 1024
+
+
+def test_attention_rope_validation(L):
+    """The attention calls with the fused output rotation check the rotation
+    arguments like dsv4_out_rope, before any HIP call."""
+    fs = L.lib.dsv4_sparse_mqa_fwd_rope
+    fd = L.lib.dsv4_hca_dense_fwd_rope
+    sp = lambda th, R: fs(FAKE, 1, 1, 4, 64, 128, FAKE, 1, 8, FAKE, 2, FAKE, 10, pos(90), 8, pos(95), None, 1.0, th, R,
+                          FAKE, None, 0, None)
+    dn = lambda th, R: fd(FAKE, 1, 1, 4, 64, 128, FAKE, 1, 8, 128, FAKE, 10, pos(90), 8, pos(95), None, 1.0, th, R,
+                          FAKE, None, 0, None)
+    for f in (sp, dn):
+        assert f(10000.0, 60) == 2 and "rope_dims" in err(L)       # not a multiple of 8
+        assert f(10000.0, 136) == 2                                  # wider than c
+        assert f(0.0, 64) == 1                                       # theta <= 0
+        assert f(-1.0, 64) == 1
 
 
 def test_topk_noalloc_validation(L):

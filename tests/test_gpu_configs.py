@@ -258,14 +258,17 @@ def test_cfg5_layer_pair(L):
     g_idx = host(layer.idx[0, rows])
     assert_topk_exact_on_gpu_scores(g_idx, g_sc, m, pos, k, "cfg5")
     scale = 1 / math.sqrt(c)
-    ref = O.sparse_mqa(decode_act(inp["q"])[rows], kv_all, ref_idx, win_kv, P - nw, nw, pos,
-                       inp["sink"].astype(np.float64), scale)
+    # the step rotates both outputs' RoPE dims back by the query position in the attention store
+    theta, R = layer.out_rope
+    rot = lambda o, p: O.out_rope(o, p, theta, R)
+    ref = rot(O.sparse_mqa(decode_act(inp["q"])[rows], kv_all, ref_idx, win_kv, P - nw, nw, pos,
+                           inp["sink"].astype(np.float64), scale), pos)
     out = decode_act(host(layer.out[rows]))
-    ref_fn = lambda sel, ix: O.sparse_mqa(decode_act(inp["q"])[rows[sel]], kv_all, ix, win_kv, P - nw, nw, pos[sel],
-                                          inp["sink"].astype(np.float64), scale)
+    ref_fn = lambda sel, ix: rot(O.sparse_mqa(decode_act(inp["q"])[rows[sel]], kv_all, ix, win_kv, P - nw, nw,
+                                              pos[sel], inp["sink"].astype(np.float64), scale), pos[sel])
     check_attention_rows(out, ref, rows, g_idx, ref_idx, I, k, fp32=False, ref_with_idx=ref_fn)
-    ref_h = O.hca_dense(decode_act(inp["q_hca"])[rows], hc_all, mp, win_h, P - nw, nw, pos,
-                        inp["sink_hca"].astype(np.float64), scale)
+    ref_h = rot(O.hca_dense(decode_act(inp["q_hca"])[rows], hc_all, mp, win_h, P - nw, nw, pos,
+                            inp["sink_hca"].astype(np.float64), scale), pos)
     assert_close(decode_act(host(layer.out_hca[rows])), ref_h, what="hca output")
 
 
