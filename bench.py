@@ -1,8 +1,9 @@
 """Benchmark: query tokens/s of the interleaved CSA + HCA layer pair at 1M context.
 
 Workload (one step = every call of the hot path once: the chunk's three
-compressors in one launch, index scores + top-k in one call, sparse MQA and
-HCA dense MQA, each with the output rotation in its store): an 8192-token chunk
+compressors with the KV RMSNorm + RoPE in one call, index scores + top-k in
+one call, sparse MQA and HCA dense MQA, each with the output rotation in its
+store): an 8192-token chunk
 at positions [2^20, 2^20 + 8192) against caches prefilled with 2^20 tokens
 (262144 CSA entries, 8192 HCA entries, 128-row SWA tails); bf16 activations,
 fp8 + bf16-RoPE KV rows, MXFP4 indexer keys, d = 4096, c = 512, 64 heads,
@@ -100,10 +101,11 @@ def calibrate_copy(gib=1):
 
 
 def cpu_baseline(inp, rows_n=256, seed=4):
-    """The float64 oracle on a bounded sample: the three compressors in full,
-    then the per-query steps (index scores, top-k, sparse MQA, dense MQA) for
-    `rows_n` seeded query rows.  Returns query tokens/s with the compress cost
-    amortised over the chunk."""
+    """The float64 oracle on a bounded sample: the three compressors with the
+    KV norm + RoPE in full, then the per-query steps (index scores, top-k,
+    sparse MQA, dense MQA, each output rotated back) for `rows_n` seeded query
+    rows.  Returns query tokens/s with the compress cost amortised over the
+    chunk."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
@@ -120,6 +122,9 @@ def cpu_baseline(inp, rows_n=256, seed=4):
         comp, raw = O.csa_compress(H, dec(inp["W_kv"]), inp["B_kv"], m, block0=S0, n_left=nl)
         ki, _ = O.csa_compress(H, dec(inp["W_ki"]), inp["B_ki"], m, block0=S0, n_left=nl)
         hca, hraw = O.hca_compress(H[nl:], dec(inp["W_hca"]), inp["B_hca"], mp)
+        prep = lambda x, p: O.kv_norm_rope(x, np.ones(c), p, 1e-6, 10000.0, 64)
+        comp, raw = prep(comp, O.entry_positions(m, S0, comp.shape[0])), prep(raw, P + np.arange(n))
+        hca, hraw = prep(hca, P + mp * (np.arange(hca.shape[0]) + 1) - 1), prep(hraw, P + np.arange(n))
         t_comp = time.perf_counter() - t0
         kv_all = np.concatenate([K.decode_rows(inp["kv_cache"][:S0], 2, c), K.round_rows(comp, 2)])
         ki_all = np.concatenate([K.mxfp4_decode(inp["ki_codes"][:S0], inp["ki_scales"][:S0]), K.round_rows(ki, 3)])
@@ -133,8 +138,10 @@ def cpu_baseline(inp, rows_n=256, seed=4):
         t0 = time.perf_counter()
         I = O.indexer_score(qI, wI, ki_all, m, pos)
         idx = O.topk_select(I, m, pos, k)
-        O.sparse_mqa(q, kv_all, idx, wk, P - nw, nw, pos, inp["sink"].astype(np.float64), 1 / math.sqrt(c))
-        O.hca_dense(qh, hc_all, mp, wh, P - nw, nw, pos, inp["sink_hca"].astype(np.float64), 1 / math.sqrt(c))
+        O.out_rope(O.sparse_mqa(q, kv_all, idx, wk, P - nw, nw, pos, inp["sink"].astype(np.float64),
+                                1 / math.sqrt(c)), pos)
+        O.out_rope(O.hca_dense(qh, hc_all, mp, wh, P - nw, nw, pos, inp["sink_hca"].astype(np.float64),
+                               1 / math.sqrt(c)), pos)
         t_rows = time.perf_counter() - t0
     per_token = t_comp / n + t_rows / rows_n
     return {"value": 1.0 / per_token, "unit": "query tokens/s", "cores": int(blas_threads), "kind": "oracle",

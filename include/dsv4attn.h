@@ -437,6 +437,31 @@ typedef struct {
 } dsv4_norm_rope_t;
 
 /*
+ * dsv4_compress_chunk with the KV RMSNorm and partial RoPE of the pages
+ * (digest 模块 D: the compressed KV head is RMS-normalised before core
+ * attention and its last rope_dims dims carry RoPE) applied in the same call
+ * to what the CSA KV compressor (kv_nr) and the HCA compressor (hca_nr; each
+ * layer has its own gamma) emit, entries and window rows; a NULL descriptor
+ * leaves that compressor as dsv4_compress_chunk has it.  The results are
+ * those of dsv4_compress_chunk with F32 rows followed by
+ * dsv4_kv_norm_rope(F32 rows -> the caller's layout), bit for bit, for
+ *   CSA entries at positions m (s + 1) - 1 (s absolute, from block0),
+ *   HCA entry i of the chunk at m block0 + m' (i + 1) - 1,
+ *   window rows of chunk token i at m block0 + i
+ * (the chunk starts at token m block0).  norm 0: rotation only.  The indexer
+ * keys are not normalised.  The compressors' 64-channel tiles split a row
+ * across blocks, so the fp32 rows pass through the workspace
+ * (dsv4_compress_chunk_nr_workspace_size(n, m, c of the normalised CSA KV or
+ * 0, m', c of the normalised HCA or 0) bytes) to a second kernel of the call.
+ * Normalised outputs in F32, BF16 or FP8_ROPE_BF16.
+ */
+size_t dsv4_compress_chunk_nr_workspace_size(int64_t n, int m, int c_kv, int m_prime, int c_hca);
+int dsv4_compress_chunk_nr(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                           int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                           int m_prime, const dsv4_compressor_t* hca, const dsv4_norm_rope_t* kv_nr,
+                           const dsv4_norm_rope_t* hca_nr, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Feed n_new tokens of each of B sequences: H [B, n_new, d] (act_dtype) holds
  * the hidden states of positions pos0[b] + i (host array, >= 0).  W and bias
  * as the batch compressors (CSA, overlap = 1: W [4c, d] = W^{aKV} | W^{bKV} |

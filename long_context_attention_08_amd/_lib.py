@@ -15,7 +15,8 @@ F32, BF16 = 0, 1
 ROW_F32, ROW_BF16, ROW_FP8_ROPE_BF16, ROW_MXFP4 = 0, 1, 2, 3
 
 EXPORTS = [
-    "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_compress_chunk", "dsv4_indexer_score",
+    "dsv4_row_bytes", "dsv4_csa_compress", "dsv4_hca_compress", "dsv4_compress_chunk", "dsv4_compress_chunk_nr",
+    "dsv4_compress_chunk_nr_workspace_size", "dsv4_indexer_score",
     "dsv4_indexer_score_fp4q", "dsv4_indexer_score_fp8q", "dsv4_indexer_topk_workspace_size", "dsv4_indexer_topk", "dsv4_q_norm_rope", "dsv4_kv_norm_rope", "dsv4_out_rope",
     "dsv4_gemm_bf16_nt", "dsv4_query_proj_workspace_size", "dsv4_query_proj",
     "dsv4_output_proj_workspace_size", "dsv4_output_proj",
@@ -105,6 +106,12 @@ class NormRope(ctypes.Structure):
     _fields_ = [("norm", _int), ("gamma", _vp), ("eps", _f32), ("rope_dims", _int), ("theta", _f32)]
 
 
+_sig("dsv4_compress_chunk_nr_workspace_size", _sz, [_i64, _int, _int, _int, _int])
+_sig("dsv4_compress_chunk_nr", _int, [_vp, _i64, _i64, _i64, _int, _int, _i64, ctypes.POINTER(Compressor),
+                                      ctypes.POINTER(Compressor), _int, ctypes.POINTER(Compressor),
+                                      ctypes.POINTER(NormRope), ctypes.POINTER(NormRope), _vp, _sz, _vp])
+
+
 _sig("dsv4_stream_state_bytes", _sz, [_int, _int, _int])
 _sig("dsv4_stream_state_reset", _int, [_vp, _i64, _int, _int, _int, _vp])
 _sig("dsv4_stream_workspace_size", _sz, [_i64, _i64, _i64, _int, _int])
@@ -191,14 +198,32 @@ def compressor(W, bias, c, comp_out, comp_layout, *, comp_scales=None, raw_out=N
                       raw_layout)
 
 
-def compress_chunk(H, m, *, n_left=0, block0=0, csa_kv=None, csa_keys=None, m_prime=128, hca=None, stream=None):
+def norm_rope(gamma=None, *, eps=1e-6, theta=10000.0, rope_dims=64, norm=True):
+    """A dsv4_norm_rope_t: RMSNorm (times gamma [c] float32, or 1) and RoPE of the last rope_dims dims."""
+    return NormRope(1 if norm else 0, _ptr(gamma), eps, rope_dims, theta)
+
+
+def compress_chunk(H, m, *, n_left=0, block0=0, csa_kv=None, csa_keys=None, m_prime=128, hca=None,
+                   kv_nr=None, hca_nr=None, ws=None, stream=None):
     """The CSA KV, CSA indexer-key and HCA compressors of one chunk in one call
     (each a `compressor(...)` or None).  H [n_left + n, d]; the HCA compressor
-    takes rows n_left.. of H."""
+    takes rows n_left.. of H.  kv_nr / hca_nr (`norm_rope(...)`): the KV RMSNorm
+    and RoPE of the CSA KV / HCA rows in the same call (dsv4_compress_chunk_nr,
+    ws of compress_chunk_nr_workspace_size)."""
     n = H.shape[0] - n_left
     ref = lambda j: ctypes.byref(j) if j is not None else None
-    _check(lib.dsv4_compress_chunk(_ptr(H), n_left, n, H.shape[1], _act(H), m, block0, ref(csa_kv), ref(csa_keys),
-                                   m_prime, ref(hca), _stream(stream)))
+    if kv_nr is None and hca_nr is None:
+        _check(lib.dsv4_compress_chunk(_ptr(H), n_left, n, H.shape[1], _act(H), m, block0, ref(csa_kv),
+                                       ref(csa_keys), m_prime, ref(hca), _stream(stream)))
+        return
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsv4_compress_chunk_nr(_ptr(H), n_left, n, H.shape[1], _act(H), m, block0, ref(csa_kv),
+                                      ref(csa_keys), m_prime, ref(hca), ref(kv_nr), ref(hca_nr), _ptr(ws), wsb,
+                                      _stream(stream)))
+
+
+def compress_chunk_nr_workspace_size(n, m, c_kv, m_prime, c_hca):
+    return int(lib.dsv4_compress_chunk_nr_workspace_size(n, m, c_kv, m_prime, c_hca))
 
 
 def indexer_score(qI, wI, keys, k_layout, m, q_pos0, scores, *, k_scales=None, S=None, stream=None):

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <utility>
 
 #include "dsv4_common.h"
 #include "dsv4_internal.h"
@@ -149,6 +150,123 @@ static int check_csa_extra(const char* fn, int64_t n_left, int64_t n, int m, int
   return 0;
 }
 
+static int chunk_launch(const char* fn, const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                        int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                        int m_prime, const dsv4_compressor_t* hca, void* stream);
+
+static int chunk_check(const char* fn, const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                       int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                       int m_prime, const dsv4_compressor_t* hca) {
+  for (const dsv4_compressor_t* j : {csa_kv, csa_keys}) {
+    if (!j) continue;
+    int r = check_compress(fn, H, n_left, n, d, act_dtype, j->W, j->bias, m, j->c, j->comp_out, j->comp_scales,
+                           j->comp_layout, j->raw_out, j->raw_layout);
+    if (!r) r = check_csa_extra(fn, n_left, n, m, block0);
+    if (r) return r;
+  }
+  if (hca) {
+    int r = check_compress(fn, H, 0, n, d, act_dtype, hca->W, hca->bias, m_prime, hca->c, hca->comp_out,
+                           hca->comp_scales, hca->comp_layout, hca->raw_out, hca->raw_layout);
+    if (r) return r;
+  }
+  return DSV4_OK;
+}
+
+static int rope_args_ok(const char* fn, int c, float eps, float theta, int rope_dims);
+
+// fp32 rows of the normalised compressors in the workspace: CSA KV entries,
+// CSA KV window rows, HCA entries, HCA window rows (256-byte aligned each)
+struct ChunkNrLayout {
+  size_t o_kv, o_kvraw, o_hc, o_hcraw, bytes;
+};
+static ChunkNrLayout chunk_nr_layout(int64_t n, int m, int c_kv, int m_prime, int c_hca) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  ChunkNrLayout L{};
+  size_t o = 0;
+  L.o_kv = o; o = al(o + (c_kv > 0 && m > 0 ? (size_t)(n / m) * c_kv * 4 : 0));
+  L.o_kvraw = o; o = al(o + (c_kv > 0 ? (size_t)n * c_kv * 4 : 0));
+  L.o_hc = o; o = al(o + (c_hca > 0 && m_prime > 0 ? (size_t)(n / m_prime) * c_hca * 4 : 0));
+  L.o_hcraw = o; o = al(o + (c_hca > 0 ? (size_t)n * c_hca * 4 : 0));
+  L.bytes = o;
+  return L;
+}
+
+size_t dsv4_compress_chunk_nr_workspace_size(int64_t n, int m, int c_kv, int m_prime, int c_hca) {
+  if (n <= 0 || c_kv < 0 || c_hca < 0) return 0;
+  return chunk_nr_layout(n, m, c_kv, m_prime, c_hca).bytes;
+}
+
+int dsv4_compress_chunk_nr(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                           int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                           int m_prime, const dsv4_compressor_t* hca, const dsv4_norm_rope_t* kv_nr,
+                           const dsv4_norm_rope_t* hca_nr, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsv4_compress_chunk_nr";
+  int r = chunk_check(fn, H, n_left, n, d, act_dtype, m, block0, csa_kv, csa_keys, m_prime, hca);
+  if (r) return r;
+  // only a given compressor with its norm-rope descriptor is normalised
+  const dsv4_norm_rope_t* kvn = csa_kv ? kv_nr : nullptr;
+  const dsv4_norm_rope_t* hcn = hca ? hca_nr : nullptr;
+  for (auto jn : {std::make_pair(csa_kv, kvn), std::make_pair(hca, hcn)}) {
+    const dsv4_compressor_t* j = jn.first;
+    const dsv4_norm_rope_t* nr = jn.second;
+    if (!nr) continue;
+    if (nr->norm != 0 && nr->norm != 1) return fail(DSV4_ERR_INVALID_ARG, "%s: norm must be 0 or 1", fn);
+    if ((r = rope_args_ok(fn, j->c, nr->eps, nr->theta, nr->rope_dims))) return r;
+    for (int lay : {j->comp_layout, j->raw_out ? j->raw_layout : DSV4_ROW_F32})
+      if (lay != DSV4_ROW_F32 && lay != DSV4_ROW_BF16 && lay != DSV4_ROW_FP8_ROPE_BF16)
+        return fail(DSV4_ERR_UNSUPPORTED, "%s: normalised rows in layout %d (F32, BF16 or FP8_ROPE_BF16)", fn, lay);
+  }
+  const ChunkNrLayout lay = chunk_nr_layout(n, m, kvn ? csa_kv->c : 0, m_prime, hcn ? hca->c : 0);
+  if (ws_bytes < lay.bytes || (lay.bytes && !ws))
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, lay.bytes);
+  if (lay.bytes && !aligned16(ws)) return fail(DSV4_ERR_INVALID_ARG, "%s: ws is not 16-byte aligned", fn);
+  if (n == 0 || (!csa_kv && !csa_keys && !hca)) return ok();
+  // the KV compressors write fp32 rows into the workspace; the indexer keys
+  // are not normalised and go straight to their outputs
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  dsv4_compressor_t kv32{}, hc32{};
+  if (csa_kv) kv32 = *csa_kv;
+  if (hca) hc32 = *hca;
+  if (kvn) {
+    kv32.comp_out = w + lay.o_kv; kv32.comp_scales = nullptr; kv32.comp_layout = DSV4_ROW_F32;
+    kv32.raw_out = csa_kv->raw_out ? w + lay.o_kvraw : nullptr; kv32.raw_layout = DSV4_ROW_F32;
+  }
+  if (hcn) {
+    hc32.comp_out = w + lay.o_hc; hc32.comp_scales = nullptr; hc32.comp_layout = DSV4_ROW_F32;
+    hc32.raw_out = hca->raw_out ? w + lay.o_hcraw : nullptr; hc32.raw_layout = DSV4_ROW_F32;
+  }
+  r = chunk_launch(fn, H, n_left, n, d, act_dtype, m, block0, csa_kv ? &kv32 : nullptr, csa_keys, m_prime,
+                   hca ? &hc32 : nullptr, stream);
+  if (r) return r;
+  // RMSNorm + RoPE + packing at the rows' positions: chunk token i sits at
+  // position m block0 + i; CSA entry s (absolute) at m (s + 1) - 1; HCA entry
+  // i of the chunk at m block0 + m' (i + 1) - 1
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t p_tok = (int64_t)m * block0;
+  auto prep = [&](const dsv4_norm_rope_t* nr, const void* in, void* out, int out_layout, int64_t rows, int c,
+                  int64_t pos0, int64_t stride) {
+    if (rows <= 0) return DSV4_OK;
+    dsv4::KvPrepArgs a{in, DSV4_ROW_F32, out, out_layout, 1, rows, c, nr->norm ? nr->gamma : nullptr,
+                       nr->norm ? nr->eps : 0.f, nr->theta, nr->rope_dims, stride, nr->norm};
+    return hip_status(dsv4::launch_kv_prep(a, &pos0, s), fn);
+  };
+  if (kvn) {
+    if ((r = prep(kvn, kv32.comp_out, csa_kv->comp_out, csa_kv->comp_layout, n / m, csa_kv->c,
+                  (int64_t)m * (block0 + 1) - 1, m)))
+      return r;
+    if (csa_kv->raw_out &&
+        (r = prep(kvn, kv32.raw_out, csa_kv->raw_out, csa_kv->raw_layout, n, csa_kv->c, p_tok, 1)))
+      return r;
+  }
+  if (hcn) {
+    if ((r = prep(hcn, hc32.comp_out, hca->comp_out, hca->comp_layout, n / m_prime, hca->c, p_tok + m_prime - 1,
+                  m_prime)))
+      return r;
+    if (hca->raw_out && (r = prep(hcn, hc32.raw_out, hca->raw_out, hca->raw_layout, n, hca->c, p_tok, 1))) return r;
+  }
+  return ok();
+}
+
 int dsv4_compress_chunk(const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
                         int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
                         int m_prime, const dsv4_compressor_t* hca, void* stream) {
@@ -166,6 +284,14 @@ int dsv4_compress_chunk(const void* H, int64_t n_left, int64_t n, int64_t d, int
     if (r) return r;
   }
   if (n == 0 || (!csa_kv && !csa_keys && !hca)) return ok();
+  return chunk_launch(fn, H, n_left, n, d, act_dtype, m, block0, csa_kv, csa_keys, m_prime, hca, stream);
+}
+
+// the compressors of a validated chunk: one fused launch when every one can
+// take it, else one launch each
+static int chunk_launch(const char* fn, const void* H, int64_t n_left, int64_t n, int64_t d, int act_dtype, int m,
+                        int64_t block0, const dsv4_compressor_t* csa_kv, const dsv4_compressor_t* csa_keys,
+                        int m_prime, const dsv4_compressor_t* hca, void* stream) {
   const size_t esz = act_dtype == DSV4_F32 ? 4 : 2;
   const void* Hh = reinterpret_cast<const uint8_t*>(H) + (size_t)n_left * (size_t)d * esz;
   auto csa = [&](const dsv4_compressor_t* j) {
@@ -533,7 +659,7 @@ int dsv4_kv_norm_rope(const void* rows, int in_layout, int64_t B, int64_t n, int
   if (r) return r;
   if (rows == rows_out && dsv4_row_bytes(in_layout, c) != dsv4_row_bytes(out_layout, c))
     return fail(DSV4_ERR_INVALID_ARG, "%s: in place needs equal row sizes", fn);
-  dsv4::KvPrepArgs a{rows, in_layout, rows_out, out_layout, B, n, c, gamma, eps, theta, rope_dims, pos_stride};
+  dsv4::KvPrepArgs a{rows, in_layout, rows_out, out_layout, B, n, c, gamma, eps, theta, rope_dims, pos_stride, 1};
   return hip_status(dsv4::launch_kv_prep(a, pos0, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

@@ -215,6 +215,7 @@ struct KvPrepArgs {
   float eps, theta;
   int R;
   int64_t pos_stride;   // row i of batch entry b sits at pos0[b] + pos_stride * i
+  int norm;             // 1: RMSNorm (times gamma) before the rotation; 0: rotation only
 };
 hipError_t launch_q_prep(const QPrepArgs& a, const int64_t* q_pos0, hipStream_t s);
 hipError_t launch_kv_prep(const KvPrepArgs& a, const int64_t* pos0, hipStream_t s);

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NR_THREADS) void kv_norm_rope_k(KvPrepArgs a, PosTa
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) x[p][i2] = 0.f;
   }
-  const float inv = row_inv_rms<NP>(x, a.c, l, a.eps);
+  const float inv = a.norm ? row_inv_rms<NP>(x, a.c, l, a.eps) : 1.0f;
   uint8_t* dst = reinterpret_cast<uint8_t*>(a.out) + row * (int64_t)row_bytes(a.out_layout, a.c);
   const int nf8 = a.c - ROPE_DIMS;              // E4M3 dims of an FP8 row
 #pragma unroll
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(NR_THREADS) void kv_norm_rope_k(KvPrepArgs a, PosTa
 #pragma unroll
     for (int i2 = 0; i2 < 8; ++i2) {
       const int e = e0 + i2 < a.c ? e0 + i2 : a.c - 1;
-      y[i2] = x[p][i2] * inv * (a.gamma ? a.gamma[e] : 1.0f);
+      y[i2] = x[p][i2] * inv * (a.norm && a.gamma ? a.gamma[e] : 1.0f);
     }
 #pragma unroll
     for (int i2 = 0; i2 < 8; i2 += 2) {

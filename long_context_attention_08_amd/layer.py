@@ -9,7 +9,9 @@ One `step()` enqueues, on one stream, the calls of the pair:
   the three compressors of the chunk in one launch over the same tiles of H
        (CSA KV appended to the KV cache with its window rows to the CSA window
        buffer, CSA indexer keys appended, HCA entries appended with their
-       window rows to the HCA window buffer);
+       window rows to the HCA window buffer), the KV rows RMS-normalised and
+       rotated at their positions in the same call (kv_nr=dict(gamma=, eps=,
+       theta=, rope_dims=); None: stored as compressed);
   CSA: index scores and top-k in one call (the score rows are not stored),
        sparse MQA;
   HCA: dense MQA;
@@ -28,7 +30,8 @@ class PairLayer:
     def __init__(self, *, H, n_left, m, mp, c, cI, hI, nh, k, n_win,
                  W_kv, B_kv, W_ki, B_ki, W_hca, B_hca,
                  kv_cache, S0, ki_codes, ki_scales, hca_cache, Sh0, kv_win, hca_win, win_pos0,
-                 q, qI, wI, q_hca, sink, sink_hca, q_pos0, kv_layout, key_layout, out_rope=(10000.0, 64)):
+                 q, qI, wI, q_hca, sink, sink_hca, q_pos0, kv_layout, key_layout, out_rope=(10000.0, 64),
+                 kv_nr=dict(gamma=None, eps=1e-6, theta=10000.0, rope_dims=64)):
         import torch
         self.__dict__.update(locals())
         del self.__dict__["self"]
@@ -50,6 +53,15 @@ class PairLayer:
         nb = max(L.attn_workspace_size(False, 1, n, nh, c, k + n_win),
                  L.attn_workspace_size(True, 1, n, nh, c, self.Sh + n_win))
         self.ws_attn = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        if kv_nr is not None:
+            self.nr_kv = L.norm_rope(kv_nr["gamma"], eps=kv_nr["eps"], theta=kv_nr["theta"],
+                                     rope_dims=kv_nr["rope_dims"])
+            self.nr_hca = L.norm_rope(kv_nr["gamma"], eps=kv_nr["eps"], theta=kv_nr["theta"],
+                                      rope_dims=kv_nr["rope_dims"])
+            nb = L.compress_chunk_nr_workspace_size(n, m, c, mp, c)
+            self.ws_nr = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        else:
+            self.nr_kv = self.nr_hca = self.ws_nr = None
         rb = L.row_bytes(kv_layout, c)
         self.kv_new = kv_cache[S0:self.S]
         self.kv_win_new = kv_win[n_win:n_win + n]
@@ -68,14 +80,15 @@ class PairLayer:
                        n_left=self.n_left, block0=self.S0, comp_scales=self.ki_sc_new, stream=stream)
 
     def compress(self, stream=None):
-        """All three compressors of the chunk in one call (dsv4_compress_chunk)."""
+        """All three compressors of the chunk in one call (dsv4_compress_chunk, or
+        dsv4_compress_chunk_nr with the KV norm + RoPE)."""
         kv = L.compressor(self.W_kv, self.B_kv, self.c, self.kv_new, self.kv_layout, raw_out=self.kv_win_new,
                           raw_layout=self.kv_layout)
         ki = L.compressor(self.W_ki, self.B_ki, self.cI, self.ki_new, self.key_layout, comp_scales=self.ki_sc_new)
         hc = L.compressor(self.W_hca, self.B_hca, self.c, self.hca_new, self.kv_layout, raw_out=self.hca_win_new,
                           raw_layout=self.kv_layout)
         L.compress_chunk(self.H, self.m, n_left=self.n_left, block0=self.S0, csa_kv=kv, csa_keys=ki,
-                         m_prime=self.mp, hca=hc, stream=stream)
+                         m_prime=self.mp, hca=hc, kv_nr=self.nr_kv, hca_nr=self.nr_hca, ws=self.ws_nr, stream=stream)
 
     def indexer(self, stream=None):
         L.indexer_score(self.qI.view(1, self.n, self.hI, self.cI), self.wI.view(1, self.n, self.hI),

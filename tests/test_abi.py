@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(L):
     syms = declared_symbols()
-    assert len(syms) == 33
+    assert len(syms) == 35
     for s in syms:
         assert hasattr(L.lib, s), s
     assert sorted(L.EXPORTS) == syms
@@ -229,6 +229,28 @@ def test_attention_rope_validation(L):
         assert f(10000.0, 136) == 2                                  # wider than c
         assert f(0.0, 64) == 1                                       # theta <= 0
         assert f(-1.0, 64) == 1
+
+
+def test_compress_chunk_nr_validation(L):
+    """The chunk compressors with KV norm + RoPE check the descriptors, the
+    normalised layouts and the workspace before any HIP call."""
+    f = L.lib.dsv4_compress_chunk_nr
+    C = L._lib.Compressor
+    r = ctypes.byref
+    kv = C(FAKE, FAKE, 256, FAKE, None, 2, FAKE, 2)                       # FP8 entries and window rows
+    kv_mx = C(FAKE, FAKE, 64, FAKE, FAKE, 3, None, 0)                     # MXFP4 entries
+    nr = L.norm_rope(None, rope_dims=64)
+    need = L.lib.dsv4_compress_chunk_nr_workspace_size(512, 4, 256, 128, 0)
+    assert need >= (512 // 4 + 512) * 256 * 4
+    call = lambda j, knr, ws, wsb: f(FAKE, 4, 512, 256, 1, 4, 1, r(j), None, 128, None, knr, None, ws, wsb, None)
+    assert call(kv_mx, r(nr), FAKE, need) == 2 and "layout" in err(L)      # MXFP4 rows cannot be normalised
+    assert call(kv, r(L.norm_rope(None, rope_dims=60)), FAKE, need) == 2   # rope_dims not a multiple of 8
+    assert call(kv, r(L.norm_rope(None, theta=0.0)), FAKE, need) == 1      # theta <= 0
+    bad = L.norm_rope(None)
+    bad.norm = 2
+    assert call(kv, r(bad), FAKE, need) == 1
+    assert call(kv, r(nr), FAKE, need - 256) == 4 and "workspace" in err(L)
+    assert call(kv, r(nr), None, 0) == 4
 
 
 def test_topk_noalloc_validation(L):

@@ -229,6 +229,14 @@ def test_cfg5_layer_pair(L):
     comp, raw = O.csa_compress(H, decode_act(inp["W_kv"]), inp["B_kv"], m, block0=S0, n_left=nl)
     ki, _ = O.csa_compress(H, decode_act(inp["W_ki"]), inp["B_ki"], m, block0=S0, n_left=nl)
     hca, hraw = O.hca_compress(H[nl:], decode_act(inp["W_hca"]), inp["B_hca"], mp)
+    # the step normalises and rotates the KV rows at their positions (gamma 1): entries at their newest
+    # pooled token, window rows at their own
+    kvn = layer.kv_nr
+    prep = lambda x, p: O.kv_norm_rope(x, np.ones(c), p, kvn["eps"], kvn["theta"], kvn["rope_dims"])
+    comp = prep(comp, O.entry_positions(m, S0, comp.shape[0]))
+    raw = prep(raw, P + np.arange(n))
+    hca = prep(hca, P + mp * (np.arange(hca.shape[0]) + 1) - 1)
+    hraw = prep(hraw, P + np.arange(n))
     g_comp = K.decode_rows(host(layer.kv_new), ROW_FP8, c)
     g_raw = K.decode_rows(host(layer.kv_win_new), ROW_FP8, c)
     g_ki = K.mxfp4_decode(host(layer.ki_new), host(layer.ki_sc_new))
