@@ -1088,10 +1088,22 @@ static_assert(IT_SELCAP == SK_CAP, "a select block holds the candidates of one r
 // overflowed; when there are at least min(k, visible) of them, the k best
 // of the row are among them.  A row where either fails, or whose lists
 // exceed one block's buffer, is flagged and left to the full-score path.
+//
+// The lists' composites are ranked in one pass: a histogram of the 11 bits
+// below their highest differing bit (so every bin is a contiguous range of
+// composites), descending bin offsets, a scatter that groups each bin, and
+// for each composite its offset plus the number of larger ones in its bin is
+// its place in the output.  A row where a bin that reaches the first `need`
+// places holds more than IT_BIN_MAX composites (dense ties) takes the radix
+// select and the bitonic sort instead; both give the same sorted list.
+constexpr int IT_BIN_MAX = 64;
+constexpr int IT_EPT = (SK_CAP + SK_NT - 1) / SK_NT;   // composites per thread
 __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
   extern __shared__ __align__(16) uint8_t smem[];
   SkShared& sh = *reinterpret_cast<SkShared*>(smem);
   __shared__ uint32_t s_cnt[SK_NT], s_off[SK_NT];
+  __shared__ uint32_t s_boff[SK_BIN];       // first output place of each digit bin
+  __shared__ uint32_t s_maxc;
   const int64_t row = blockIdx.x;
   const int64_t bl = row / a.nq, t = row % a.nq;
   const int64_t nv = visible_count(pt.q_pos0[bl] + t, a.m, a.S);
@@ -1152,6 +1164,81 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
     base += sum;
   }
   const int n = (int)total;
+  // ---- one-pass rank by digit bins
+  uint64_t v[IT_EPT];
+  uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+  for (int j = 0; j < IT_EPT; ++j) {
+    const int i = (int)threadIdx.x + j * SK_NT;
+    v[j] = i < n ? sh.cand[i] : 0ull;
+    if (i < n) {
+      mn = v[j] < mn ? v[j] : mn;
+      mx = v[j] > mx ? v[j] : mx;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t p = shfl_xor_u64(mn, o), q = shfl_xor_u64(mx, o);
+    mn = p < mn ? p : mn;
+    mx = q > mx ? q : mx;
+  }
+  if ((threadIdx.x & 63) == 0) { sh.rmin[threadIdx.x >> 6] = mn; sh.rmax[threadIdx.x >> 6] = mx; }
+  for (int b = threadIdx.x; b < SK_BIN; b += SK_NT) sh.hist[b] = 0;
+  if (threadIdx.x == 0) s_maxc = 0;
+  __syncthreads();
+  mn = sh.rmin[0];
+  mx = sh.rmax[0];
+#pragma unroll
+  for (int w = 1; w < SK_NT / 64; ++w) {
+    mn = sh.rmin[w] < mn ? sh.rmin[w] : mn;
+    mx = sh.rmax[w] > mx ? sh.rmax[w] : mx;
+  }
+  // bits above the highest differing one are common: an 11-bit digit just
+  // below it orders the composites by bins
+  const int hb = mn == mx ? 0 : 63 - __clzll(mn ^ mx);
+  const int shift = hb >= 10 ? hb - 10 : 0;
+  auto digit = [&](uint64_t x) { return (uint32_t)(x >> shift) & (uint32_t)(SK_BIN - 1); };
+#pragma unroll
+  for (int j = 0; j < IT_EPT; ++j)
+    if ((int)threadIdx.x + j * SK_NT < n) atomicAdd(&sh.hist[digit(v[j])], 1u);
+  __syncthreads();
+  // thread t owns bins [SK_BIN - 8(t+1), SK_BIN - 8t), from the top
+  constexpr int PER = SK_BIN / SK_NT;
+  uint32_t c[PER];
+  uint32_t loc = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) { c[q] = sh.hist[SK_BIN - 1 - (PER * threadIdx.x + q)]; loc += c[q]; }
+  uint32_t all;
+  uint32_t above = sk_scan_excl(loc, sh.wsum, &all);
+  uint32_t maxc = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = SK_BIN - 1 - (PER * (int)threadIdx.x + q);
+    s_boff[b] = above;
+    sh.hist[b] = above;                     // the scatter cursor, which ends at the bin's end
+    if (above < need && c[q] > maxc) maxc = c[q];
+    above += c[q];
+  }
+  if (maxc > (uint32_t)IT_BIN_MAX) atomicMax(&s_maxc, maxc);
+  __syncthreads();
+  if (s_maxc == 0) {
+#pragma unroll
+    for (int j = 0; j < IT_EPT; ++j)
+      if ((int)threadIdx.x + j * SK_NT < n) sh.cand[atomicAdd(&sh.hist[digit(v[j])], 1u)] = v[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IT_EPT; ++j) {
+      if ((int)threadIdx.x + j * SK_NT >= n) continue;
+      const uint32_t b = digit(v[j]);
+      const uint32_t s = s_boff[b], e = sh.hist[b];
+      if (s >= need) continue;
+      uint32_t r = 0;
+      for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > v[j] ? 1u : 0u;
+      if (s + r < need) out[s + r] = (int32_t)(~(uint32_t)v[j]);
+    }
+    for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) out[i] = -1;
+    return;
+  }
+  // ---- dense ties: radix select, gather, bitonic sort (sh.cand is untouched)
   const uint64_t T = sk_select(sh, n, need);
   sk_gather(sh, n, T);
   const int n2 = pow2_ceil(a.k) > 256 ? SK_KMAX : pow2_ceil(a.k);

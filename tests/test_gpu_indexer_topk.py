@@ -44,6 +44,9 @@ IT_CASES = [
     ("f32", ROW_F32, 2, 10, 4, 32, 5000, 4, 64, [20000, 100], "normal"),         # no sampled path (fp32 queries)
     ("bf16", ROW_BF16, 1, 9, 16, 64, 6000, 1, 128, [5990], "normal"),            # no sampled path (hI = 16), m = 1
     ("bf16", ROW_MXFP4, 2, 1, 32, 64, 600000, 4, 1024, [2400000, 1800000], "normal"),   # sample rows > 16384
+    # small-integer scores: many equal scores among a row's candidates (the select's dense-tie path)
+    ("bf16", ROW_BF16, 1, 32, 32, 64, 3000, 4, 256, [6000], "int"),
+    ("bf16", ROW_MXFP4, 2, 20, 32, 64, 9000, 4, 512, [30000, 8000], "int"),
     # the layer-pair chunk's rows: 512 queries at 2^20 + 7000 + t over 2^18 + 2048 MXFP4 keys
     ("bf16", ROW_MXFP4, 1, 512, 32, 64, 264192, 4, 1024, [(1 << 20) + 7000], "normal"),
 ]
@@ -56,9 +59,16 @@ def _inputs(case, seed):
         qx[:] = 0.0
     elif kind == "mixed":
         qx[:, ::2] = 0.0
-    qI = G.to_bf16(qx) if qd == "bf16" else qx
     wI = G.normal(seed, "wI", (B, nq, hI))
     kx = G.normal(seed, "cache_ki", (B, S, cI))
+    if kind == "int":
+        # E2M1 values (exact in bf16 and MXFP4) and weights +-1: integer-valued scores, many of them equal
+        rng = np.random.default_rng(seed)
+        vals = np.array([0, 0.5, 1, -0.5, -1], dtype=np.float32)
+        qx = vals[rng.integers(0, len(vals), (B, nq, hI, cI))]
+        kx = vals[rng.integers(0, len(vals), (B, S, cI))]
+        wI = rng.choice(np.array([-1, 1], dtype=np.float32), (B, nq, hI))
+    qI = G.to_bf16(qx) if qd == "bf16" else qx
     keys, ksc = G.store(kx, kl) if kl != ROW_F32 else (kx, None)
     return qI, wI, keys, ksc
 
