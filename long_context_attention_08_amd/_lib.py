@@ -2,13 +2,14 @@
 
 Argument marshalling only: every step runs in the HIP library.  torch supplies
 device memory and the current stream.  Importing this module raises if the
-built library is missing -- there is no fallback.
+built library is missing -- there is no fallback.  DSV4ATTN_LIB names another
+build of the same C ABI to load instead (the host-sanitizer tests use it).
 """
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdsv4attn.so")
+LIB_PATH = os.environ.get("DSV4ATTN_LIB") or os.path.join(HERE, "libdsv4attn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1

@@ -9,7 +9,6 @@
 #include <cstdio>
 #include <utility>
 
-#include "dsv4_common.h"
 #include "dsv4_internal.h"
 
 namespace {

@@ -244,6 +244,10 @@ struct StreamArgs {
   float eps, theta;
   int rope_dims;
 };
+// sizes and the split of d for the projection partials (plan.cpp; host only)
+constexpr int STREAM_SP_COLS = 64;      // projection: output columns per block
+constexpr int STREAM_META_BYTES = 256;  // header of a sequence's state
+void stream_split(int64_t NC, int64_t d, int* ks, int64_t* kslice);
 size_t stream_state_bytes(int overlap, int m, int c);
 size_t stream_ws_bytes(int64_t rows, int overlap, int c, int64_t d);
 hipError_t launch_stream_reset(void* state, int64_t B, int overlap, int m, int c, hipStream_t s);

@@ -172,6 +172,38 @@ size_t idxtopk_workspace(const IndexerArgs& a, int k) {
   return best;
 }
 
+// ------------------------------------------------------------------ streaming compressors
+
+// slices of d for the projection partials: about 256 blocks for one row group,
+// slices of at least 256 (a multiple of 32)
+void stream_split(int64_t NC, int64_t d, int* ks, int64_t* kslice) {
+  const int64_t col_blocks = (NC + STREAM_SP_COLS - 1) / STREAM_SP_COLS;
+  int64_t want = (256 + col_blocks - 1) / col_blocks;
+  const int64_t most = d / 256 > 1 ? d / 256 : 1;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  int64_t sl = (d + want - 1) / want;
+  sl = (sl + 31) / 32 * 32;
+  *kslice = sl;
+  *ks = (int)((d + sl - 1) / sl);
+}
+
+// state: [header][max | sum | weighted sum] x c of the current entry, and for
+// CSA the same for the next entry's b-part
+size_t stream_state_bytes(int overlap, int m, int c) {
+  (void)m;
+  const size_t acc = (size_t)(overlap ? 6 : 3) * (size_t)c * 4;
+  return (STREAM_META_BYTES + acc + 255) / 256 * 256;
+}
+
+size_t stream_ws_bytes(int64_t rows, int overlap, int c, int64_t d) {
+  const int64_t nc = (overlap ? 4 : 2) * (int64_t)c;
+  int ks;
+  int64_t sl;
+  stream_split(nc, d, &ks, &sl);
+  return (size_t)ks * (size_t)rows * (size_t)nc * sizeof(float);
+}
+
 // ------------------------------------------------------------------ attention
 
 static int attn_path(const AttnArgs& a, bool dense) {

@@ -27,22 +27,9 @@
 
 namespace dsv4 {
 
-constexpr int SP_COLS = 64;            // projection: output columns per block (16 per wave)
+constexpr int SP_COLS = STREAM_SP_COLS;     // projection: output columns per block (16 per wave)
 constexpr int SP_ROWS = 64;            // projection: rows per block (four 16-row MFMA tiles)
 constexpr int SU_THREADS = 256;        // update: threads per block, two channels each
-
-// ---- slices of d for the projection partials (shapes only)
-static void stream_split(int64_t NC, int64_t d, int* ks, int64_t* kslice) {
-  const int64_t col_blocks = (NC + SP_COLS - 1) / SP_COLS;
-  int64_t want = (256 + col_blocks - 1) / col_blocks;      // about 256 blocks for one row group
-  const int64_t most = d / 256 > 1 ? d / 256 : 1;           // slices of at least 256
-  if (want > most) want = most;
-  if (want < 1) want = 1;
-  int64_t sl = (d + want - 1) / want;
-  sl = (sl + 31) / 32 * 32;
-  *kslice = sl;
-  *ks = (int)((d + sl - 1) / sl);
-}
 
 // state: [meta 256 B][mx | sum | wsum] x c of the current entry, and for CSA
 // the same for the next entry's b-part
@@ -51,21 +38,8 @@ struct StreamMeta {
   int32_t a_na, a_nb, b_cnt;    // a-rows and b-rows in it; b-rows in the next
   int32_t pad;
 };
-constexpr int SMETA = 256;
-
-size_t stream_state_bytes(int overlap, int m, int c) {
-  (void)m;
-  const size_t acc = (size_t)(overlap ? 6 : 3) * (size_t)c * 4;
-  return (SMETA + acc + 255) / 256 * 256;
-}
-
-size_t stream_ws_bytes(int64_t rows, int overlap, int c, int64_t d) {
-  const int64_t nc = (overlap ? 4 : 2) * (int64_t)c;
-  int ks;
-  int64_t sl;
-  stream_split(nc, d, &ks, &sl);
-  return (size_t)ks * (size_t)rows * (size_t)nc * sizeof(float);
-}
+constexpr int SMETA = STREAM_META_BYTES;
+static_assert(sizeof(StreamMeta) <= SMETA, "state header");
 
 // ---- 1. projection partials, bf16 rows on v_mfma_f32_16x16x32_bf16: lane l
 // of a wave holds W row (16 columns) l % 16 and H row l % 16 of each 16-row
