@@ -567,6 +567,8 @@ def main():
                     help="time the layer-pair step only (no side reports, no CPU baseline): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode step of configuration 4 (16 sequences at 2^20), as the `decode` field")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -580,6 +582,11 @@ def main():
 
     from long_context_attention_08_amd.layer import pair_from_arrays
     from synth import gen as G
+
+    if args.decode_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"decode": decode_report(args.steps, stream)}), flush=True)
+        return
 
     inp = G.make(5)
     cfg = inp["cfg"]

@@ -72,7 +72,16 @@ struct IndexerArgs {
   // restricted mode (row_flags != null): a block computes (and stores scores)
   // only if one of its rows has a non-zero flag
   const int* row_flags;
+  // key s of batch entry b is row b kbatch + koff + s kstride of keys (and
+  // k_scales); kbatch 0 means S, kstride 0 means 1 (a strided sample of a key
+  // array is scored in place)
+  int64_t kbatch, koff;
+  int kstride;
 };
+__host__ __device__ inline int64_t key_row(const IndexerArgs& a, int64_t b, int64_t s) {
+  const int64_t kb = a.kbatch ? a.kbatch : a.S;
+  return b * kb + a.koff + s * (a.kstride ? a.kstride : 1);
+}
 
 // Per-batch absolute positions travel to the kernels by value: a launch covers
 // at most MAXB batch entries (launchers loop over larger batches).
@@ -84,10 +93,6 @@ struct PosTable {
 
 // q_pos0: host array [B]
 hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s);
-
-// keys 32 j + 31 (j < Ss) of every batch entry into a compact [B, Ss] key array
-hipError_t launch_indexer_sample_keys(const IndexerArgs& a, int64_t Ss, void* keys_out, uint8_t* scales_out,
-                                      hipStream_t s);
 
 // ---- indexer planning (plan.cpp; host only)
 constexpr int IDX_KT = 256;       // keys per LDS tile of the MFMA indexer
@@ -151,7 +156,7 @@ struct IdxTopkPlan {
   IndexerGrid grid;  // of the full pass
   int64_t Ss;        // sample keys per batch entry
   TopkPlan tk_sample, tk_full;
-  size_t o_skeys, o_sscl, o_sscore, o_sidx, o_stk, o_lkey, o_cand, o_cnt, o_flags, o_scores, o_ftk;
+  size_t o_sscore, o_sidx, o_stk, o_lkey, o_cand, o_cnt, o_flags, o_scores, o_ftk;
   size_t bytes;
 };
 // plan of one launch slice (a.B <= MAXB batch entries)

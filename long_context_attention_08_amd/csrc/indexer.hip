@@ -23,7 +23,7 @@ namespace dsv4 {
 
 // ------------------------------------------------------------------ generic
 __device__ __forceinline__ float key_elem(const IndexerArgs& a, int64_t b, int64_t s, int j) {
-  const int64_t row = b * a.S + s;
+  const int64_t row = key_row(a, b, s);
   if (a.k_layout == ROW_MXFP4) {
     const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys) + row * (a.cI / 2);
     const uint32_t byte = codes[j >> 1];
@@ -315,8 +315,9 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
     if constexpr (Q4) {
       const int64_t s = s0 + threadIdx.x;
       const bool in = s < S;
-      const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + (b * S + (in ? s : 0)) * CB;
-      const uint8_t* sr = a.k_scales + (b * S + (in ? s : 0)) * NBS;
+      const int64_t kr = key_row(a, b, in ? s : 0);
+      const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + kr * CB;
+      const uint8_t* sr = a.k_scales + kr * NBS;
 #pragma unroll
       for (int i = 0; i < CB / 16; ++i) {
         u32x4 v = *reinterpret_cast<const u32x4*>(cr + 16 * i);
@@ -331,8 +332,9 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
       const int64_t s = s0 + threadIdx.x;
       uint32_t out[CI / 2];
       if (s < S) {
-        const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + (b * S + s) * CB;
-        const uint8_t* sr = a.k_scales + (b * S + s) * NB;
+        const int64_t kr = key_row(a, b, s);
+        const uint8_t* cr = reinterpret_cast<const uint8_t*>(a.keys) + kr * CB;
+        const uint8_t* sr = a.k_scales + kr * NB;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
           const float sc = e8m0_to_f32(sr[blk]);
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma(IndexerArgs a, PosTable p
         const int kr = i / CH, cc = i % CH;
         const int64_t s = s0 + kr;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (s < S) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.keys) + (b * S + s) * CI + 8 * cc);
+        if (s < S) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.keys) + key_row(a, b, s) * CI + 8 * cc);
         *reinterpret_cast<u32x4*>(Ks + kr * LDK + 8 * cc) = v;
       }
     }
@@ -505,30 +507,6 @@ static void launch_mfma_variant(const IndexerArgs& a, const PosTable& pt, int b0
   // queries when a sequence has fewer than 16 (indexer_grid matches these)
   if (a.nq >= 16) launch_mfma_grid<CI, KL, QF, 4, QF == 0 && CI == 128 ? 2 : 4>(a, pt, b0, nb, s);
   else launch_mfma_grid<CI, KL, QF, 1, 1>(a, pt, b0, nb, s);
-}
-
-// keys 32 j + 31 of every batch entry, copied to a compact [nb, Ss] array
-__global__ void indexer_sample_keys(const uint8_t* keys, const uint8_t* scl, int64_t S, int64_t Ss, int krow,
-                                    int nbs, int64_t n, uint8_t* okeys, uint8_t* oscl) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int64_t b = i / Ss, j = i % Ss;
-  const int64_t src = b * S + (int64_t)IT_STRIDE * j + (IT_STRIDE - 1);
-  const u32x4* sp = reinterpret_cast<const u32x4*>(keys + src * krow);
-  u32x4* dp = reinterpret_cast<u32x4*>(okeys + i * krow);
-  for (int c = 0; c < krow / 16; ++c) dp[c] = sp[c];
-  for (int c = 0; c < nbs; ++c) oscl[i * nbs + c] = scl[src * nbs + c];
-}
-
-hipError_t launch_indexer_sample_keys(const IndexerArgs& a, int64_t Ss, void* okeys, uint8_t* oscl, hipStream_t s) {
-  const int64_t n = a.B * Ss;
-  if (n <= 0) return hipSuccess;
-  const bool mx = a.k_layout == ROW_MXFP4;
-  const int krow = mx ? a.cI / 2 : row_bytes(a.k_layout, a.cI);
-  hipLaunchKernelGGL(indexer_sample_keys, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const uint8_t*>(a.keys), a.k_scales, a.S, Ss, krow, mx ? a.cI / 32 : 0, n,
-                     reinterpret_cast<uint8_t*>(okeys), oscl);
-  return hipGetLastError();
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, const int64_t* q_pos0, hipStream_t s) {

@@ -140,10 +140,7 @@ IdxTopkPlan idxtopk_make_plan(const IndexerArgs& a, int k) {
     int64_t cap = (int64_t)4 * IT_SELCAP / p.grid.splits;
     cap = cap < 256 ? 256 : (cap > IT_SELCAP ? IT_SELCAP : cap);
     p.cap = (int)((cap + 63) / 64 * 64);
-    const size_t krow = a.k_layout == ROW_MXFP4 ? (size_t)a.cI / 2 : (size_t)a.cI * 2;
     p.tk_sample = topk_make_plan(rows, p.Ss, p.ks);
-    p.o_skeys = o; o = al(o + (size_t)a.B * p.Ss * krow);
-    p.o_sscl = o; o = al(o + (a.k_layout == ROW_MXFP4 ? (size_t)a.B * p.Ss * (a.cI / 32) : 0));
     p.o_sscore = o; o = al(o + (size_t)rows * p.Ss * 4);
     p.o_sidx = o; o = al(o + (size_t)rows * p.ks * 4);
     p.o_stk = o; o = al(o + p.tk_sample.bytes);
@@ -152,7 +149,18 @@ IdxTopkPlan idxtopk_make_plan(const IndexerArgs& a, int k) {
     p.o_cnt = o; o = al(o + (size_t)rows * p.grid.splits * 4);
     p.o_flags = o; o = al(o + (size_t)rows * 4);
   }
-  p.tk_full = topk_make_plan(rows, a.S, k);
+  if (p.fused) {
+    // the full-score top-k sees only flagged rows (almost never any): one
+    // streaming block per row, a single launch that leaves at once otherwise
+    p.tk_full = TopkPlan{};
+    p.tk_full.kind = TOPK_STREAM;
+    p.tk_full.part = (int)((a.S + 3) / 4 * 4);
+    p.tk_full.nparts = 1;
+    p.tk_full.supported = true;
+    p.tk_full.bytes = 0;
+  } else {
+    p.tk_full = topk_make_plan(rows, a.S, k);
+  }
   p.o_scores = o; o = al(o + (size_t)rows * a.S * 4);
   p.o_ftk = o; o = al(o + p.tk_full.bytes);
   p.bytes = o;
@@ -281,13 +289,14 @@ AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
   // split the keys only when a sequence has few query groups.  The split size
   // depends on the key bound alone (never on the batch), so a sequence's
   // results do not depend on the batch.  The split count comes first and is
-  // non-decreasing in the bound: up to 16 splits of at least 256 slots, each
-  // split's fp32 partial (rows x c) small next to the rows it reads
+  // non-decreasing in the bound: up to 16 splits of at least 128 slots (a
+  // decode query's 1152 sparse slots take 9 blocks), each split's fp32
+  // partial (rows x c) small next to the rows it reads
   if (pl.units_per_b >= 32 || slots <= 0) {
     pl.chunk = 1 << 30;
     pl.max_splits = 1;
   } else {
-    int64_t ms = (slots + 255) / 256;
+    int64_t ms = (slots + 127) / 128;
     ms = ms < 1 ? 1 : (ms > 16 ? 16 : ms);
     const int64_t per = (slots + ms - 1) / ms;
     pl.chunk = (int)((per + 31) / 32 * 32);

@@ -1286,13 +1286,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, const int64_t* q_pos0, int
       IT_CHECK(launch_topk(scores, nb, a.nq, a.S, a.m, qp, k, oidx, w + p.o_ftk, p.tk_full, s));
       continue;
     }
-    // sample scores and their ks-th best per row
-    uint8_t* sscl = mx ? w + p.o_sscl : nullptr;
-    IT_CHECK(launch_indexer_sample_keys(a, p.Ss, w + p.o_skeys, sscl, s));
+    // sample scores (keys 32 j + 31, read in place) and their ks-th best per row
     IndexerArgs as = a;
-    as.keys = w + p.o_skeys;
-    as.k_scales = sscl;
     as.S = p.Ss;
+    as.kbatch = a.S;
+    as.koff = IT_STRIDE - 1;
+    as.kstride = IT_STRIDE;
     as.m = a.m * IT_STRIDE;
     as.scores = reinterpret_cast<float*>(w + p.o_sscore);
     IT_CHECK(launch_indexer(as, qp, s));

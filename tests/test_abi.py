@@ -206,11 +206,11 @@ def test_indexer_topk_workspace_sizes(L):
 
 def test_indexer_topk_sampled_path_workspace(L):
     """The bf16 / 32-head shapes take the sampled-threshold path: its
-    workspace holds candidate lists on top of the score rows and the top-k
-    workspace that the plain sequence needs; fp32 queries do not."""
+    workspace holds the score rows (for flagged rows only) and at least 256
+    candidate slots per row; fp32 queries take the plain sequence, whose
+    workspace is the score rows and the top-k workspace."""
     for B, nq, S, k in ((1, 512, 264192, 1024), (16, 1, 262144, 1024), (2, 40, 20011, 512)):
-        plain = B * nq * S * 4 + L.topk_workspace_size(B, nq, S, k)
-        assert L.indexer_topk_workspace_size(L.BF16, L.ROW_MXFP4, B, nq, 32, 64, S, k) > plain + B * nq * 8 * 256
+        assert L.indexer_topk_workspace_size(L.BF16, L.ROW_MXFP4, B, nq, 32, 64, S, k) > B * nq * (S * 4 + 8 * 256)
     plain = 2 * 10 * 5000 * 4 + L.topk_workspace_size(2, 10, 5000, 64)
     assert L.indexer_topk_workspace_size(L.F32, L.ROW_F32, 2, 10, 4, 32, 5000, 64) < plain + 1024
 
