@@ -794,7 +794,10 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 // come straight from the raw stage (E4M3 bytes converted in registers, the 64
 // bf16 RoPE channels as they are), which halves the LDS bytes per MFMA and
 // leaves LDS for three stages of copies in flight.
-//   * wave (rg, ch) holds Q^T and O^T of 32 rows x 256 channels, as above;
+//   * wave (rg, ch) holds Q^T and O^T of 32 rows x 256 channels: E4M3
+//     channels 224 ch .. 224 ch + 223 and bf16 RoPE channels 448 + 32 ch ..
+//     448 + 32 ch + 31, so that both waves of a pair convert the same number
+//     of E4M3 operands (they meet at every barrier);
 //   * S^T over the wave's channel half: A = K rows (ds_read_b64 of 8 E4M3
 //     bytes per lane, or ds_read_b128 of 8 bf16), B = Q^T;
 //   * both waves of a pair write their whole partial S^T and read the other's,
@@ -813,6 +816,7 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
 //   * per tile: [copies of tile it landed] barrier, copies of tile it+2, S^T,
 //     partial out, barrier, softmax, PV.
 constexpr int F8_NSTG = 3;
+constexpr int F8_K8 = 14;   // E4M3 k-steps (and pieces) of each channel half
 __device__ __forceinline__ int kperm(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 
 template <int NRG>
@@ -869,16 +873,16 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   const bool qvalid = t <= ui.tl;
   const int64_t tq = qvalid ? t : ui.tl;
 
-  // Q^T in the contraction order of S^T: k-step 2 j + hh of lane half G takes
-  // channels 16 (2 j + G) + 8 hh .. + 8 of the wave's slice for the E4M3 part
-  // (12 or 16 k-steps), then 16 kk + 8 G .. + 8 for the bf16 part
+  // Q^T in the contraction order of S^T: k-step 2 j + hh (< 14) of lane half
+  // G takes E4M3 channels 224 ch + 16 (2 j + G) + 8 hh .. + 8, k-steps 14 and
+  // 15 the bf16 channels 448 + 32 ch + 16 (kk - 14) + 8 G .. + 8
   bf16x8 qf[KQ];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C + ch * 256;
-    const int nf8k = ch == 0 ? 16 : 12;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C;
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) {
-      const int c8 = kk < nf8k ? 16 * (2 * (kk >> 1) + G) + 8 * (kk & 1) : 16 * kk + 8 * G;
+      const int c8 = kk < F8_K8 ? 224 * ch + 16 * (2 * (kk >> 1) + G) + 8 * (kk & 1)
+                                : (C - ROPE_DIMS) + 32 * ch + 16 * (kk - F8_K8) + 8 * G;
       qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + c8));
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile copies are counted from here on
@@ -977,34 +981,26 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef int v2i __attribute__((ext_vector_type(2)));
   // S^T operand: key m = l % 32 at stage slot kperm(m); channel half ch: E4M3
-  // pieces 16 ch + kk (kk < 16 - 4 ch), then bf16 pieces 28 + 2 (kk - 12) + G
+  // pieces 14 ch + 2 j + G, then bf16 pieces 28 + 4 ch + 2 (kk - 14) + G
   // (every piece a lane half reads has parity G)
   const int kslot = (kperm(col) ^ (8 * G)) * 16;
   auto score_tile = [&](auto chc, const uint8_t* stg) -> f32x16 {
     constexpr int CHW = decltype(chc)::value;
+    constexpr int P8 = F8_K8 * CHW, PB = NF8 + 4 * CHW;   // first E4M3 and bf16 piece of the half
     f32x16 sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
     // one 16-byte unit (16 E4M3 channels of key m) per lane feeds two k-steps
-    if constexpr (CHW == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (2 * j + G) * (TS * 16) + kslot);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], sacc, 0, 0, 0);
-      }
-    } else {
+    for (int j = 0; j < F8_K8 / 2; ++j) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (P8 + 2 * j + G) * (TS * 16) + kslot);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], sacc, 0, 0, 0);
+    }
 #pragma unroll
-      for (int j = 0; j < 6; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (16 + 2 * j + G) * (TS * 16) + kslot);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[0], w[1]}), qf[2 * j], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8((u32x2){w[2], w[3]}), qf[2 * j + 1], sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int kk = 12; kk < KQ; ++kk) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (NF8 + 2 * (kk - 12) + G) * (TS * 16) + kslot);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), qf[kk], sacc, 0, 0, 0);
-      }
+    for (int kk = F8_K8; kk < KQ; ++kk) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (PB + 2 * (kk - F8_K8) + G) * (TS * 16) + kslot);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), qf[kk], sacc, 0, 0, 0);
     }
     return sacc;
   };
@@ -1015,51 +1011,37 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   const int lam = l & 15, grp = (l >> 4) & 1;
   auto pv_half = [&](auto chc, const uint8_t* stg, int s, const bf16x8& pf) {
     constexpr int CHW = decltype(chc)::value;
+    constexpr int P8 = F8_K8 * CHW, PB = NF8 + 4 * CHW;
+    constexpr int M8 = F8_K8 / 2;                  // E4M3 m-tiles (32 channels each)
     const int slot8 = 16 * s + 8 * G;              // first of the 8 stage slots of this lane half
     const int pos8 = slot8 ^ (8 * grp);            // their positions in a piece of parity grp
-    if constexpr (CHW == 0) {
-      auto rd = [&](int mo) {                      // E4M3 pieces 2 mo + grp
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
-            stg + ((2 * mo + grp) * TS + pos8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
-      };
-      v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
+    auto rd = [&](int mo) {                        // E4M3 pieces P8 + 2 mo + grp
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+          stg + ((P8 + 2 * mo + grp) * TS + pos8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
+    };
+    v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
 #pragma unroll
-      for (int mo = 0; mo < MO; ++mo) {
-        const v2i w = w1;
-        w1 = w2;
-        w2 = w3;
-        if (mo + 3 < MO) w3 = rd(mo + 3);
-        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      auto rd = [&](int mo) {                      // E4M3 pieces 16 + 2 mo + grp
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
-            stg + ((16 + 2 * mo + grp) * TS + pos8 + (lam >> 1)) * 16 + 8 * (lam & 1)));
-      };
-      v2i w1 = rd(0), w2 = rd(1), w3 = rd(2);
-#pragma unroll
-      for (int mo = 0; mo < 6; ++mo) {
-        const v2i w = w1;
-        w1 = w2;
-        w2 = w3;
-        if (mo + 3 < 6) w3 = rd(mo + 3);
-        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int mo = 6; mo < MO; ++mo) {            // bf16 channels 448 + 32 (mo - 6) + 16 grp + lam
-        const int par = (lam >> 1) & 1;            // parity of the piece
-        const int piece = NF8 + 4 * (mo - 6) + 2 * grp + par;
-        const uint8_t* p0 = stg + (piece * TS + (slot8 ^ (8 * par)) + (lam >> 2)) * 16 + 8 * (lam & 1);
-        const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0));
-        const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * 16));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
-        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf,
-                                                          acc[mo], 0, 0, 0);
-      }
+    for (int mo = 0; mo < M8; ++mo) {
+      const v2i w = w1;
+      w1 = w2;
+      w2 = w3;
+      if (mo + 3 < M8) w3 = rd(mo + 3);
+      acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8(__builtin_bit_cast(u32x2, w)), pf, acc[mo], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {                                              // bf16 channels 448 + 32 ch + 16 grp + lam
+      const int par = (lam >> 1) & 1;              // parity of the piece
+      const int piece = PB + 2 * grp + par;
+      const uint8_t* p0 = stg + (piece * TS + (slot8 ^ (8 * par)) + (lam >> 2)) * 16 + 8 * (lam & 1);
+      const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0));
+      const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * 16));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1b = __builtin_bit_cast(u32x2, t1);
+      acc[M8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1b[0], w1b[1]}), pf,
+                                                        acc[M8], 0, 0, 0);
     }
   };
+  // channel of register r of m-tile mo: f8_chan(mo) + 8 (r / 4) + 4 G + r % 4
+  auto f8_chan = [&](int mo) { return mo < F8_K8 / 2 ? 224 * ch + 32 * mo : (C - ROPE_DIMS) + 32 * ch; };
 
   // prologue: copies of tiles 0 and 1 in flight, their masks
   if (ntiles > 0) issue(0, s_stage);
@@ -1153,28 +1135,29 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
       den = l_run * f + exp2f(z - M);
     }
     const float inv = den > 0.f ? f / den : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + ch * 256;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C;
     const float* qcs = tcs + qloc * (R >> 1);
     const float* qsn = tsn + qloc * (R >> 1);
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        store4_bf16_rot(orow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv,
-                        acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, ch * 256 + 32 * mo + 8 * j + 4 * G, C, R,
-                        qcs, qsn);
+      for (int j = 0; j < 4; ++j) {
+        const int e0 = f8_chan(mo) + 8 * j + 4 * G;
+        store4_bf16_rot(orow + e0, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv, acc[mo][4 * j + 2] * inv,
+                        acc[mo][4 * j + 3] * inv, e0, C, R, qcs, qsn);
+      }
   } else {
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
     float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
     float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + row) * C + ch * 256;
+                ((unit * pl.max_splits + split) * rows + row) * C;
     if (G == 0 && ch == 0) { ml[0] = m_run; ml[1] = l_run; }
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
+        *reinterpret_cast<f32x4*>(ow + f8_chan(mo) + 8 * j + 4 * G) =
             (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
   }
 }

@@ -456,6 +456,13 @@ DENSE_CASES = [
     # HCA decode with 3965 visible entries, in the workspace the call needs exactly (the visible counts where
     # the split plan of the size query, the argument check and the launch once disagreed)
     ("bf16", ROW_FP8, 1, 1, 64, 512, 8192, 128, 128, [3965 * 128 + 5], True),
+    # c = 512 prefill over 64 or more queries (ragged last block, visible count stepping mid-chunk, 1 / 2 / 4
+    # queries per block, window only, no window, two sequences)
+    ("bf16", ROW_FP8, 1, 67, 64, 512, 300, 128, 128, [38000], True),
+    ("bf16", ROW_FP8, 1, 130, 32, 512, 500, 128, 64, [64000], False),
+    ("bf16", ROW_FP8, 2, 260, 16, 512, 100, 128, 128, [12700, 200], True),
+    ("bf16", ROW_FP8, 1, 70, 64, 512, 10, 128, 128, [0], True),
+    ("bf16", ROW_FP8, 1, 64, 64, 512, 257, 128, 0, [40000], False),
 ]
 
 
