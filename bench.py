@@ -429,8 +429,36 @@ def decode_report(steps, stream):
                       ("hca_dense", f_hca)], steps, stream)
     # the step takes whichever selection path is faster at this shape (the two give the same indices)
     one_call = ms["indexer_topk"] < ms["indexer"] + ms["topk"]
-    step = (lambda: (f_it(), f_sparse(), f_hca())) if one_call else (lambda: (f_idx(), f_topk(), f_sparse(), f_hca()))
-    ms["step"] = _time_calls([("step", step)], steps, stream)["step"]
+    select = (lambda: f_it()) if one_call else (lambda: (f_idx(), f_topk()))
+    step = lambda: (select(), f_sparse(), f_hca())
+    ms["step_serial"] = _time_calls([("step", step)], steps, stream)["step"]
+    # HCA attention needs nothing the selection or the sparse call produce: on a second stream (its own
+    # workspace) it runs beside them.  At one query per sequence only the index-score pass fills the GPU
+    # (2048 blocks); the top-k and the sparse call are a few blocks per sequence, so the HCA launch goes
+    # out when the index scores are done (with the one-call selection, at the start)
+    side = torch.cuda.Stream()
+    aws2 = torch.empty_like(aws)
+    ev_in, ev_out = torch.cuda.Event(), torch.cuda.Event()
+    f_hca_side = lambda: L.hca_dense_fwd(d["q_hca"], d["hca_cache"], L.ROW_FP8_ROPE_BF16, mp, d["hca_win"], wp, nw,
+                                         qp, d["sink_hca"], scale, out_h, aws2, stream=side)
+
+    def fork():
+        ev_in.record(stream)
+        side.wait_event(ev_in)
+        f_hca_side()
+
+    def step_two_streams():
+        if one_call:
+            fork()
+            f_it()
+        else:
+            f_idx()
+            fork()
+            f_topk()
+        f_sparse()
+        ev_out.record(side)
+        stream.wait_event(ev_out)
+    ms["step"] = _time_calls([("step", step_two_streams)], steps, stream)["step"]
     rep = {}
     for name in ("indexer", "topk", "indexer_topk", "sparse", "hca_dense"):
         gbps = work[name] / (ms[name] * 1e-3) / 1e9
@@ -442,7 +470,8 @@ def decode_report(steps, stream):
     tot = sum(work[x] for x in sel + ["sparse", "hca_dense"])
     rep["step"] = {"us": round(ms["step"] * 1e3, 2), "query_tokens_per_s": round(B / (ms["step"] * 1e-3), 1),
                    "frac_hbm": round(tot / (ms["step"] * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(tot),
-                   "calls": sel + ["sparse", "hca_dense"]}
+                   "calls": sel + ["sparse", "hca_dense"], "hca_dense_stream": "second",
+                   "one_stream_us": round(ms["step_serial"] * 1e3, 2)}
     rep["shape"] = {"sequences": B, "position": qp[0], "csa_entries": S, "hca_entries": Sh, "top_k": k,
                     "window": nw, "heads": nh, "c": c}
     return rep
