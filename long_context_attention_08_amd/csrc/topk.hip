@@ -1139,13 +1139,13 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
     __syncthreads();
     const int nsp = a.splits - c0 < SK_NT ? a.splits - c0 : SK_NT;
     // flat positions [base, base + sum): list j holds [s_off[j], s_off[j] + s_cnt[j]);
-    // four loads in flight per thread
+    // eight loads in flight per thread
     const uint64_t* lists = a.cand + ((uint64_t)row * a.splits + c0) * (uint64_t)a.cap;
-    for (uint32_t p0 = base; p0 < base + sum; p0 += 4 * SK_NT) {
-      uint64_t v[4];
-      uint32_t at[4];
+    for (uint32_t p0 = base; p0 < base + sum; p0 += 8 * SK_NT) {
+      uint64_t v[8];
+      uint32_t at[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const uint32_t p = p0 + u * SK_NT + threadIdx.x;
         at[u] = p;
         int lo = 0, hi = nsp - 1;                  // last list starting at or before p
@@ -1157,7 +1157,7 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
         v[u] = p < base + sum ? lists[(uint64_t)lo * a.cap + (p - s_off[lo])] : 0ull;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
         if (at[u] < base + sum) sh.cand[at[u]] = v[u];
     }
     __syncthreads();
@@ -1225,15 +1225,17 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
     for (int j = 0; j < IT_EPT; ++j)
       if ((int)threadIdx.x + j * SK_NT < n) sh.cand[atomicAdd(&sh.hist[digit(v[j])], 1u)] = v[j];
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < IT_EPT; ++j) {
-      if ((int)threadIdx.x + j * SK_NT >= n) continue;
-      const uint32_t b = digit(v[j]);
+    // ranks by position in the grouped list: neighbouring threads take
+    // neighbouring composites, mostly of one bin, so a bin's reads are
+    // broadcasts and a dense bin's work is spread over many threads
+    for (int p = threadIdx.x; p < n; p += SK_NT) {
+      const uint64_t x = sh.cand[p];
+      const uint32_t b = digit(x);
       const uint32_t s = s_boff[b], e = sh.hist[b];
       if (s >= need) continue;
       uint32_t r = 0;
-      for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > v[j] ? 1u : 0u;
-      if (s + r < need) out[s + r] = (int32_t)(~(uint32_t)v[j]);
+      for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > x ? 1u : 0u;
+      if (s + r < need) out[s + r] = (int32_t)(~(uint32_t)x);
     }
     for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) out[i] = -1;
     return;
