@@ -809,10 +809,100 @@ __device__ __forceinline__ void hs_copy(uint64_t* dst, const uint64_t* src, uint
   }
 }
 
+// Descending order of n unique composites by one pass over digit bins.
+// Thread t holds positions t + j SK_NT (j < EPT) of the set in v; positions
+// at or past n are ignored.  A histogram of the 11 bits below their highest
+// differing bit (so every bin is a contiguous range of composites),
+// descending bin offsets, and a scatter that groups each bin into sh.cand;
+// then each composite's place is its bin's offset plus the number of larger
+// composites in its bin.  Places below `need` are written to out as the
+// index (~ low word).  A set where a bin that reaches the first `need`
+// places holds more than RANK_BIN_MAX composites (dense ties) returns false
+// before the scatter, having written nothing and left sh.cand as it was: the
+// caller sorts instead.  sh.hist (and the sh.out it shares memory with) is
+// overwritten; boff holds SK_BIN offsets, maxc one word (LDS).
+constexpr int RANK_BIN_MAX = 64;
+template <int EPT, int CAP>
+__device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_sh, const uint64_t (&v)[EPT], int n,
+                             uint32_t need, int32_t* out) {
+  uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if ((int)threadIdx.x + j * SK_NT < n) {
+      mn = v[j] < mn ? v[j] : mn;
+      mx = v[j] > mx ? v[j] : mx;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t p = shfl_xor_u64(mn, o), q = shfl_xor_u64(mx, o);
+    mn = p < mn ? p : mn;
+    mx = q > mx ? q : mx;
+  }
+  if ((threadIdx.x & 63) == 0) { sh.rmin[threadIdx.x >> 6] = mn; sh.rmax[threadIdx.x >> 6] = mx; }
+  for (int b = threadIdx.x; b < SK_BIN; b += SK_NT) sh.hist[b] = 0;
+  if (threadIdx.x == 0) *maxc_sh = 0;
+  __syncthreads();
+  mn = sh.rmin[0];
+  mx = sh.rmax[0];
+#pragma unroll
+  for (int w = 1; w < SK_NT / 64; ++w) {
+    mn = sh.rmin[w] < mn ? sh.rmin[w] : mn;
+    mx = sh.rmax[w] > mx ? sh.rmax[w] : mx;
+  }
+  // bits above the highest differing one are common: an 11-bit digit just
+  // below it orders the composites by bins
+  const int hb = mn == mx ? 0 : 63 - __clzll(mn ^ mx);
+  const int shift = hb >= 10 ? hb - 10 : 0;
+  auto digit = [&](uint64_t x) { return (uint32_t)(x >> shift) & (uint32_t)(SK_BIN - 1); };
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if ((int)threadIdx.x + j * SK_NT < n) atomicAdd(&sh.hist[digit(v[j])], 1u);
+  __syncthreads();
+  // thread t owns bins [SK_BIN - 8(t+1), SK_BIN - 8t), from the top
+  constexpr int PER = SK_BIN / SK_NT;
+  uint32_t c[PER];
+  uint32_t loc = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) { c[q] = sh.hist[SK_BIN - 1 - (PER * threadIdx.x + q)]; loc += c[q]; }
+  uint32_t all;
+  uint32_t above = sk_scan_excl(loc, sh.wsum, &all);
+  uint32_t maxc = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = SK_BIN - 1 - (PER * (int)threadIdx.x + q);
+    boff[b] = above;
+    sh.hist[b] = above;                     // the scatter cursor, which ends at the bin's end
+    if (above < need && c[q] > maxc) maxc = c[q];
+    above += c[q];
+  }
+  if (maxc > (uint32_t)RANK_BIN_MAX) atomicMax(maxc_sh, maxc);
+  __syncthreads();
+  if (*maxc_sh != 0) return false;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if ((int)threadIdx.x + j * SK_NT < n) sh.cand[atomicAdd(&sh.hist[digit(v[j])], 1u)] = v[j];
+  __syncthreads();
+  // ranks by position in the grouped list: neighbouring threads take
+  // neighbouring composites, mostly of one bin, so a bin's reads are
+  // broadcasts and a dense bin's work is spread over many threads
+  for (int p = threadIdx.x; p < n; p += SK_NT) {
+    const uint64_t x = sh.cand[p];
+    const uint32_t b = digit(x);
+    const uint32_t s = boff[b], e = sh.hist[b];
+    if (s >= need) continue;
+    uint32_t r = 0;
+    for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > x ? 1u : 0u;
+    if (s + r < need) out[s + r] = (int32_t)(~(uint32_t)x);
+  }
+  return true;
+}
+
 // dynamic LDS: sizeof(HsShared)
 __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
   extern __shared__ __align__(16) uint8_t smem[];
   HsShared& sh = *reinterpret_cast<HsShared*>(smem);
+  __shared__ uint32_t s_boff[SK_BIN];
+  __shared__ uint32_t s_maxc;
   const int64_t row = blockIdx.x;
   if (row_skipped(a, row)) return;
   int64_t nv;
@@ -893,11 +983,26 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
     }
   }
   __syncthreads();
-  for (int i = (int)need + threadIdx.x; i < SK_KMAX; i += SK_NT) sh.out[i] = 0;
+  // the `need` winners in order: ranked by digit bins, or (dense ties) sorted
+  constexpr int EPT = SK_KMAX / SK_NT;
+  uint64_t v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = (int)threadIdx.x + j * SK_NT;
+    v[j] = i < (int)need ? sh.out[i] : 0ull;
+  }
+  __syncthreads();                           // sh.out shares memory with sh.hist
+  int32_t* dst = a.idx + grow * a.k;
+  if (rank_by_bins<EPT>(sh, s_boff, &s_maxc, v, (int)need, need, dst)) {
+    for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) dst[i] = -1;
+    return;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) sh.out[threadIdx.x + j * SK_NT] = v[j];   // zero past `need`
   __syncthreads();
   bitonic1024_desc(sh.out);
-  for (int i = threadIdx.x; i < a.k; i += SK_NT)
-    a.idx[grow * a.k + i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
+  for (int i = threadIdx.x; i < a.k; i += SK_NT) dst[i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
 }
 
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
@@ -1089,14 +1194,9 @@ static_assert(IT_SELCAP == SK_CAP, "a select block holds the candidates of one r
 // of the row are among them.  A row where either fails, or whose lists
 // exceed one block's buffer, is flagged and left to the full-score path.
 //
-// The lists' composites are ranked in one pass: a histogram of the 11 bits
-// below their highest differing bit (so every bin is a contiguous range of
-// composites), descending bin offsets, a scatter that groups each bin, and
-// for each composite its offset plus the number of larger ones in its bin is
-// its place in the output.  A row where a bin that reaches the first `need`
-// places holds more than IT_BIN_MAX composites (dense ties) takes the radix
-// select and the bitonic sort instead; both give the same sorted list.
-constexpr int IT_BIN_MAX = 64;
+// The lists' composites are ranked in one pass by digit bins (rank_by_bins);
+// a row with dense ties there takes the radix select and the bitonic sort
+// instead; both give the same sorted list.
 constexpr int IT_EPT = (SK_CAP + SK_NT - 1) / SK_NT;   // composites per thread
 __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -1166,77 +1266,12 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
   const int n = (int)total;
   // ---- one-pass rank by digit bins
   uint64_t v[IT_EPT];
-  uint64_t mn = ~0ull, mx = 0;
 #pragma unroll
   for (int j = 0; j < IT_EPT; ++j) {
     const int i = (int)threadIdx.x + j * SK_NT;
     v[j] = i < n ? sh.cand[i] : 0ull;
-    if (i < n) {
-      mn = v[j] < mn ? v[j] : mn;
-      mx = v[j] > mx ? v[j] : mx;
-    }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t p = shfl_xor_u64(mn, o), q = shfl_xor_u64(mx, o);
-    mn = p < mn ? p : mn;
-    mx = q > mx ? q : mx;
-  }
-  if ((threadIdx.x & 63) == 0) { sh.rmin[threadIdx.x >> 6] = mn; sh.rmax[threadIdx.x >> 6] = mx; }
-  for (int b = threadIdx.x; b < SK_BIN; b += SK_NT) sh.hist[b] = 0;
-  if (threadIdx.x == 0) s_maxc = 0;
-  __syncthreads();
-  mn = sh.rmin[0];
-  mx = sh.rmax[0];
-#pragma unroll
-  for (int w = 1; w < SK_NT / 64; ++w) {
-    mn = sh.rmin[w] < mn ? sh.rmin[w] : mn;
-    mx = sh.rmax[w] > mx ? sh.rmax[w] : mx;
-  }
-  // bits above the highest differing one are common: an 11-bit digit just
-  // below it orders the composites by bins
-  const int hb = mn == mx ? 0 : 63 - __clzll(mn ^ mx);
-  const int shift = hb >= 10 ? hb - 10 : 0;
-  auto digit = [&](uint64_t x) { return (uint32_t)(x >> shift) & (uint32_t)(SK_BIN - 1); };
-#pragma unroll
-  for (int j = 0; j < IT_EPT; ++j)
-    if ((int)threadIdx.x + j * SK_NT < n) atomicAdd(&sh.hist[digit(v[j])], 1u);
-  __syncthreads();
-  // thread t owns bins [SK_BIN - 8(t+1), SK_BIN - 8t), from the top
-  constexpr int PER = SK_BIN / SK_NT;
-  uint32_t c[PER];
-  uint32_t loc = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) { c[q] = sh.hist[SK_BIN - 1 - (PER * threadIdx.x + q)]; loc += c[q]; }
-  uint32_t all;
-  uint32_t above = sk_scan_excl(loc, sh.wsum, &all);
-  uint32_t maxc = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int b = SK_BIN - 1 - (PER * (int)threadIdx.x + q);
-    s_boff[b] = above;
-    sh.hist[b] = above;                     // the scatter cursor, which ends at the bin's end
-    if (above < need && c[q] > maxc) maxc = c[q];
-    above += c[q];
-  }
-  if (maxc > (uint32_t)IT_BIN_MAX) atomicMax(&s_maxc, maxc);
-  __syncthreads();
-  if (s_maxc == 0) {
-#pragma unroll
-    for (int j = 0; j < IT_EPT; ++j)
-      if ((int)threadIdx.x + j * SK_NT < n) sh.cand[atomicAdd(&sh.hist[digit(v[j])], 1u)] = v[j];
-    __syncthreads();
-    // ranks by position in the grouped list: neighbouring threads take
-    // neighbouring composites, mostly of one bin, so a bin's reads are
-    // broadcasts and a dense bin's work is spread over many threads
-    for (int p = threadIdx.x; p < n; p += SK_NT) {
-      const uint64_t x = sh.cand[p];
-      const uint32_t b = digit(x);
-      const uint32_t s = s_boff[b], e = sh.hist[b];
-      if (s >= need) continue;
-      uint32_t r = 0;
-      for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > x ? 1u : 0u;
-      if (s + r < need) out[s + r] = (int32_t)(~(uint32_t)x);
-    }
+  if (rank_by_bins<IT_EPT>(sh, s_boff, &s_maxc, v, n, need, out)) {
     for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) out[i] = -1;
     return;
   }
