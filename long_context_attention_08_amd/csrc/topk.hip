@@ -7,7 +7,9 @@
 // largest composite T.  T is found by an MSD radix select in LDS (12-bit
 // digits in the k > 1024 stages, 11-bit digits in the streaming and histogram
 // selects; each stops as soon as a whole bin is taken), the winners are
-// gathered and bitonic-sorted in LDS.
+// gathered and put in order in LDS: bitonic-sorted by the streaming and the
+// k > 1024 selects, ranked by digit bins (rank_by_bins) by the histogram
+// select and the one-call select, which sort only sets with dense ties.
 //
 // k <= 1024, streaming: one block per (row, part) reads its scores once from
 //          HBM.  A running threshold tau (a composite no larger than the k-th
