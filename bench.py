@@ -350,6 +350,20 @@ def decode_cache_report(steps, stream, B=16, d=4096, c=512, cI=64, m=4, mp=128, 
     return rep
 
 
+def neighbour_overlap(idx, k):
+    """How many selected entries consecutive queries of the chunk share (the
+    fraction of query t + 1's k entries also selected by query t, averaged):
+    what a sparse-attention block serving several neighbouring queries over
+    the union of their index lists could save in gathered rows."""
+    import torch
+    s = idx.sort(dim=-1).values
+    a, b = s[:-1].contiguous(), s[1:].contiguous()
+    pos = torch.searchsorted(a, b).clamp(max=a.shape[1] - 1)
+    shared = ((a.gather(1, pos) == b) & (b >= 0)).sum(dim=1).float() / k
+    return {"shared_fraction_mean": round(float(shared.mean()), 4), "shared_fraction_max": round(float(shared.max()), 4),
+            "union_of_two_over_k": round(float(2.0 - shared.mean()), 4)}
+
+
 def _time_calls(calls, steps, stream):
     """Average ms of each callable over `steps` back-to-back launches (HIP
     events on the library's stream), after one untimed call each."""
@@ -676,6 +690,7 @@ def main():
     if args.step_only:
         print(json.dumps(line), flush=True)
         return
+    line["sparse_neighbours"] = neighbour_overlap(layer.idx[0], cfg["k"])
     line["indexer_then_topk"] = two_call_report(layer, work, args.steps, stream)
     line["fp4_indexer"] = quantised_indexer_report(layer, 4, work["indexer"]["flop"], args.steps, stream)
     line["fp8_indexer"] = quantised_indexer_report(layer, 8, work["indexer"]["flop"], args.steps, stream)
