@@ -476,6 +476,16 @@ def decode_report(steps, stream):
     one_call = t2["one"] < t2["two"]
     ms["step"] = t2["one" if one_call else "two"]
     ms["step_serial"] = _time_calls([("step", one_stream[one_call])], steps, stream)["step"]
+    # the two-stream step's outputs are those of the one-stream step, bit for bit
+    one_stream[one_call]()
+    torch.cuda.synchronize()
+    ref_o, ref_h = out.clone(), out_h.clone()
+    out.zero_()
+    out_h.zero_()
+    two_streams(one_call)()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and
+                torch.equal(out_h.view(torch.int16), ref_h.view(torch.int16)))
     rep = {}
     for name in ("indexer", "topk", "indexer_topk", "sparse", "hca_dense"):
         gbps = work[name] / (ms[name] * 1e-3) / 1e9
@@ -488,7 +498,7 @@ def decode_report(steps, stream):
     rep["step"] = {"us": round(ms["step"] * 1e3, 2), "query_tokens_per_s": round(B / (ms["step"] * 1e-3), 1),
                    "frac_hbm": round(tot / (ms["step"] * 1e-3) / 1e9 / PEAK["hbm"], 4), "bytes": int(tot),
                    "calls": sel + ["sparse", "hca_dense"], "hca_dense_stream": "second",
-                   "one_stream_us": round(ms["step_serial"] * 1e3, 2)}
+                   "one_stream_us": round(ms["step_serial"] * 1e3, 2), "outputs_equal_one_stream": same}
     rep["shape"] = {"sequences": B, "position": qp[0], "csa_entries": S, "hca_entries": Sh, "top_k": k,
                     "window": nw, "heads": nh, "c": c}
     return rep
