@@ -207,6 +207,46 @@ def test_cfg4_deterministic_and_batch_invariant(L, cfg4):
             assert np.array_equal(host(one[key])[0], host(a[key])[s]), (key, s)
 
 
+def test_cfg4_two_streams(L, cfg4):
+    """The decode step with HCA attention on a second stream (its own
+    workspace), forked once the index scores are done, beside the top-k and
+    sparse attention on the first: every output equals the one-stream run bit
+    for bit, on three repetitions (nothing in the library is shared between
+    calls on different streams)."""
+    import torch
+    ref = run_decode(L, cfg4)
+    inp, cfg = cfg4, cfg4["cfg"]
+    c, nh, k, nw, m, mp = cfg["c"], cfg["nh"], cfg["k"], cfg["n_win"], cfg["m"], cfg["mp"]
+    B, S, Sh = cfg["B"], inp["kv_cache"].shape[1], inp["hca_cache"].shape[1]
+    d = {key: dev(inp[key]) for key in ("qI", "wI", "ki_codes", "ki_scales", "q", "kv_cache", "kv_win", "sink", "q_hca",
+                                       "hca_cache", "hca_win", "sink_hca")}
+    qp, wp = [int(x) for x in inp["q_pos0"]], [int(x) for x in inp["win_pos0"]]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    scores = torch.empty((B, 1, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    tws = torch.empty(max(1, L.topk_workspace_size(B, 1, S, k)), dtype=torch.uint8, device="cuda")
+    need = max(1, L.attn_workspace_size(True, B, 1, nh, c, Sh + nw))
+    aws, aws2 = (torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2))
+    out, out_h = torch.empty_like(d["q"]), torch.empty_like(d["q_hca"])
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    for rep in range(3):
+        out.zero_()
+        out_h.zero_()
+        L.indexer_score(d["qI"], d["wI"], d["ki_codes"], ROW_MXFP4, m, qp, scores, k_scales=d["ki_scales"])
+        fork.record(main)
+        side.wait_event(fork)
+        L.hca_dense_fwd(d["q_hca"], d["hca_cache"], ROW_FP8, mp, d["hca_win"], wp, nw, qp, d["sink_hca"],
+                        1 / math.sqrt(c), out_h, aws2, stream=side)
+        L.topk_select(scores, m, qp, k, idx, tws)
+        L.sparse_mqa_fwd(d["q"], d["kv_cache"], ROW_FP8, idx, d["kv_win"], wp, nw, qp, d["sink"], 1 / math.sqrt(c), out,
+                         aws)
+        join.record(side)
+        main.wait_event(join)
+        torch.cuda.synchronize()
+        for key, got in (("scores", scores), ("idx", idx), ("out", out), ("out_h", out_h)):
+            assert np.array_equal(host(got), host(ref[key])), (rep, key)
+
+
 # ---------------------------------------------------------------------- configuration 5
 
 def test_cfg5_layer_pair(L):
