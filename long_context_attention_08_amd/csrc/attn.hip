@@ -1174,6 +1174,298 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   }
 }
 
+// ------------------------------------------------------------------ bf16 rows at c = 128
+// The stage, copies and operand reads of attn_f8 for rows of 128 bf16
+// channels (sixteen 16-byte pieces), with one wave holding all 128 channels
+// of its 32 rows: Q^T (8 k-steps) and O^T (4 m-tiles) fit in registers, so
+// every wave computes the full S^T itself and nothing is exchanged between
+// waves.  S^T reads 8 bf16 channels of one key per lane and k-step straight
+// from the stage (ds_read_b128; key j of a tile at slot kperm(j), odd pieces
+// at position slot ^ 8), V^T comes from ds_read_b64_tr_b16 as in attn_f8's
+// RoPE channels.  Per tile: [copies of tile it landed] barrier, copies of
+// tile it+2, S^T, softmax, PV; block = 32 rows per wave, NRG waves.
+template <int NRG>
+__global__ __launch_bounds__(64 * NRG) void attn_b16(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
+  constexpr int C = 128;
+  using Cf = AttnCfg<C, ROW_BF16, 1, NRG>;
+  constexpr int KQ = Cf::KQ, MO = Cf::MO, RB = Cf::RB, NW = Cf::NW;   // 8, 4, 256, NRG
+  static_assert(KQ == 8 && MO == 4 && RB == 256 && Cf::NF8 == 0, "c = 128, bf16 rows");
+  __shared__ __align__(16) uint8_t s_stage[F8_NSTG * Cf::STAGE];
+  __shared__ uint32_t s_vmask[F8_NSTG][8];
+  __shared__ int s_nvisq[8];
+  __shared__ int s_sidx[SIDX_CAP];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, G = l >> 5, col = l & 31;
+  const int64_t bl = blockIdx.x / pl.units_per_b, u = blockIdx.x % pl.units_per_b;
+  const int64_t b = b0 + bl;
+  const int64_t p0 = pt.q_pos0[bl], wpos0 = pt.win_pos0[bl];
+  const UnitInfo ui = unit_info(a, pl, p0, u);
+  const int64_t nsplit = pl.max_splits == 1 ? 1 : (ui.total + pl.chunk - 1) / pl.chunk;
+  const int split = blockIdx.y;
+  if (split > 0 && split >= nsplit) return;
+  const int slot_lo = split * pl.chunk;
+  const int slot_hi = (int)(pl.max_splits == 1 ? ui.total : (slot_lo + pl.chunk < ui.total ? slot_lo + pl.chunk : ui.total));
+  const int ncomp = (int)ui.ncomp;
+  const uint8_t* comp_base = reinterpret_cast<const uint8_t*>(a.kv_comp) + b * a.S * (int64_t)RB;
+  const uint8_t* win_base = reinterpret_cast<const uint8_t*>(a.kv_win) + (b * a.W + (ui.wlo - wpos0)) * (int64_t)RB;
+  static_assert(RB <= (int)sizeof(g_zero_row), "zero row shorter than a stored row");
+  const uint8_t* dummy = g_zero_row;
+  const int nq_blk = (int)(ui.tl - ui.t0 + 1);
+  const int pfirst = (int)(p0 + ui.t0);
+  const int ntiles = slot_hi > slot_lo ? (slot_hi - slot_lo + TS - 1) / TS : 0;
+
+  if (threadIdx.x < 8) s_nvisq[threadIdx.x] = pl.dense ? (int)visible_count(pfirst + threadIdx.x, a.ratio, a.S) : (int)a.S;
+  int bad_idx = 0;
+  if (a.idx) {
+    const int32_t* irow = a.idx + (b * a.nq + ui.t0) * a.k;
+    const int n_i = (ncomp < slot_hi ? ncomp : slot_hi) - slot_lo;
+    for (int i = threadIdx.x; i < n_i; i += Cf::NT) {
+      const int e = irow[slot_lo + i];
+      s_sidx[i] = e;
+      bad_idx |= (e < 0 || e >= a.S) ? 1 : 0;
+    }
+  }
+  const bool idx_ok = !__syncthreads_or(bad_idx);
+  const int plast = (int)(p0 + ui.tl);
+  const int nvis_first = pl.dense ? (int)visible_count(pfirst, a.ratio, a.S) : (int)a.S;
+
+  const int row = 32 * wv + col;
+  const int qloc = row / a.nh;
+  const int h = row % a.nh;
+  const int64_t t = ui.t0 + qloc;
+  const bool qvalid = t <= ui.tl;
+  const int64_t tq = qvalid ? t : ui.tl;
+
+  // Q^T: k-step kk of lane half G takes channels 16 kk + 8 G .. + 8 (piece 2 kk + G)
+  bf16x8 qf[KQ];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((b * a.nq + tq) * a.nh + h) * C;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * G));
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile copies are counted from here on
+  }
+  f32x16 acc[MO];
+#pragma unroll
+  for (int i = 0; i < MO; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl = pl.scale_log2;
+
+  auto slot_src = [&](int s, int* pos, bool* win) -> const uint8_t* {
+    if (s < ncomp) {
+      *win = false;
+      const int e = a.idx ? s_sidx[s - slot_lo] : s;
+      *pos = e;
+      if (e < 0 || e >= a.S) return nullptr;
+      return comp_base + (int64_t)e * RB;
+    }
+    *win = true;
+    *pos = (int)ui.wlo + (s - ncomp);
+    return win_base + (int64_t)(s - ncomp) * RB;
+  };
+  // copies of tile `it`: lane l fills position l % 32 of a piece of parity G,
+  // which holds slot (l % 32) ^ 8 G, that is key kperm((l % 32) ^ 8 G)
+  const int kp = kperm((l & 31) ^ (8 * G));
+  auto issue = [&](int it, uint8_t* stg) {
+    const int s0 = slot_lo + it * TS;
+    const uint8_t* rowp;
+    if (s0 + TS <= ncomp && s0 + TS <= slot_hi && (!a.idx || idx_ok)) {
+      const int e = a.idx ? s_sidx[s0 + kp - slot_lo] : s0 + kp;
+      rowp = comp_base + (int64_t)e * RB;
+    } else {
+      const int slot = s0 + kp;
+      int pos;
+      bool win;
+      rowp = slot < slot_hi ? slot_src(slot, &pos, &win) : nullptr;
+      rowp = rowp ? rowp : dummy;
+    }
+    const uint8_t* base = rowp + 16 * G + 32 * wv;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(stg + wv * 1024));
+    DmaCopies<0, (Cf::NDMA + NW - 1) / NW, NW, Cf::NDMA>::run(base, lds0, wv);
+  };
+  // this wave's copies per tile: NDMA / NW (NDMA = 8 divides evenly for NW = 1, 2, 4)
+  static_assert(Cf::NDMA % NW == 0, "copies per wave");
+  constexpr int MYDMA = Cf::NDMA / NW;
+  auto wait_copies = [&](bool one_more) {
+    if (!one_more) __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    else if constexpr (MYDMA == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if constexpr (MYDMA == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else __builtin_amdgcn_s_waitcnt(0x0F72);
+  };
+  static_assert(MYDMA == 8 || MYDMA == 4 || MYDMA == 2, "vmcnt encodings below");
+  auto tile_full = [&](int it) -> bool {
+    const int s0 = slot_lo + it * TS, s1 = s0 + TS;
+    if (s1 > slot_hi) return false;
+    if (s0 < ncomp) {
+      if (a.idx ? !idx_ok : (s1 < ncomp ? s1 : ncomp) > nvis_first) return false;
+    }
+    if (s1 > ncomp) {
+      const int lo = (int)ui.wlo + ((s0 > ncomp ? s0 : ncomp) - ncomp), hi = (int)ui.wlo + (s1 - 1 - ncomp);
+      if (hi > pfirst || lo < plast - a.n_win + 1) return false;
+    }
+    return true;
+  };
+  // per-query visibility bits of a tile that is not full, in key order (wave 0)
+  auto masks = [&](int it, int buf) {
+    if (wv != 0 || tile_full(it)) return;
+    const int s0 = slot_lo + it * TS;
+    uint32_t vbits = 0;
+    const int slot = s0 + l;
+    if (l < TS && slot < slot_hi) {
+      int pos;
+      bool win;
+      if (slot_src(slot, &pos, &win)) {
+        for (int q = 0; q < nq_blk; ++q) {
+          const int pq = pfirst + q;
+          const bool ok = win ? (pos <= pq && pos >= pq - a.n_win + 1) : (pos < s_nvisq[q]);
+          vbits |= (ok ? 1u : 0u) << q;
+        }
+      }
+    }
+    for (int q = 0; q < nq_blk; ++q) {
+      const uint32_t bal = (uint32_t)__ballot((vbits >> q) & 1u);
+      if (l == 0) s_vmask[buf][q] = bal;
+    }
+  };
+
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  // S^T: key m = l % 32 at stage slot kperm(m); k-step kk reads piece 2 kk + G
+  // (parity G), the reads two k-steps ahead of their MFMAs
+  const int kslot = (kperm(col) ^ (8 * G)) * 16;
+  auto score_tile = [&](const uint8_t* stg) -> f32x16 {
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    auto rd = [&](int kk) { return *reinterpret_cast<const u32x4*>(stg + (2 * kk + G) * (TS * 16) + kslot); };
+    u32x4 buf[2] = {rd(0), rd(1)};
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) {
+      const u32x4 w = buf[kk & 1];
+      if (kk + 2 < KQ) buf[kk & 1] = rd(kk + 2);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), qf[kk], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return sacc;
+  };
+  // PV over key half s: m-tile mo holds channels 32 mo + 16 grp + lam; lane
+  // half G takes the 8 slots 16 s + 8 G .. + 7 (keys of its P^T fragment)
+  const int lam = l & 15, grp = (l >> 4) & 1;
+  auto pv_half = [&](const uint8_t* stg, int s, const bf16x8& pf) {
+    const int slot8 = 16 * s + 8 * G;
+    const int par = (lam >> 1) & 1;                // parity of the piece
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo) {
+      const int piece = 4 * mo + 2 * grp + par;
+      const uint8_t* pp = stg + (piece * TS + (slot8 ^ (8 * par)) + (lam >> 2)) * 16 + 8 * (lam & 1);
+      const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(pp));
+      const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(pp + 4 * 16));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+      acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((u32x4){w0[0], w0[1], w1[0], w1[1]}), pf, acc[mo],
+                                                        0, 0, 0);
+    }
+  };
+
+  // prologue: copies of tiles 0 and 1 in flight, their masks
+  if (ntiles > 0) issue(0, s_stage);
+  if (ntiles > 1) issue(1, s_stage + Cf::STAGE);
+  if (ntiles > 0) masks(0, 0);
+  if (ntiles > 1) masks(1, 1);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it % F8_NSTG;
+    const uint8_t* stg = s_stage + buf * Cf::STAGE;
+    wait_copies(it + 1 < ntiles);                    // this wave's copies of tile it have landed
+    lds_barrier();                                   // tile it visible, stage of it-1 free
+    if (it + 2 < ntiles) {
+      const int nb = (it + 2) % F8_NSTG;
+      issue(it + 2, s_stage + nb * Cf::STAGE);
+      masks(it + 2, nb);
+    }
+    f32x16 sc = score_tile(stg);
+    if (!tile_full(it)) {
+      const uint32_t mk = s_vmask[buf][qloc] >> (4 * G);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = ((mk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sc[r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = max_halves(mx) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      float alpha = 1.f;
+      if (mx > m_run + 8.0f) {
+        alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+        m_run = mx;
+      }
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < MO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    }
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      // v_exp_f32 directly: results below 2^-126 flush to zero, which leaves
+      // the normalised output unchanged at fp32 resolution
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[r], sl, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], sl, mneg));
+      l_run += e0 + e1;
+      pk[r >> 1] = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)e0, (__bf16)e1});
+    }
+    pv_half(stg, 0, as_bf16x8((u32x4){pk[0], pk[1], pk[2], pk[3]}));
+    pv_half(stg, 1, as_bf16x8((u32x4){pk[4], pk[5], pk[6], pk[7]}));
+  }
+
+  l_run = sum_halves(l_run);
+  // output rotation table in the stage (after a barrier: every wave is done with it)
+  const int R = pl.max_splits == 1 ? a.rot_dims : 0;
+  float* tcs = reinterpret_cast<float*>(s_stage);
+  float* tsn = tcs + nq_blk * (R >> 1);
+  if (R > 0) {
+    lds_barrier();
+    out_rot_table(tcs, tsn, nq_blk, pfirst, R, a.rot_theta);
+    lds_barrier();
+  }
+  if (!qvalid) return;
+  // register r of m-tile mo holds channel 32 mo + 8 (r/4) + 4 G + r%4 of this lane's row
+  if (pl.max_splits == 1) {
+    float f = m_run == -INFINITY ? 0.f : 1.f, den = l_run;
+    if (a.sink) {
+      const float z = a.sink[h] * LOG2E;
+      const float M = fmaxf(m_run, z);
+      f = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+      den = l_run * f + exp2f(z - M);
+    }
+    const float inv = den > 0.f ? f / den : 0.f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C;
+    const float* qcs = tcs + qloc * (R >> 1);
+    const float* qsn = tsn + qloc * (R >> 1);
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store4_bf16_rot(orow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv,
+                        acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, 32 * mo + 8 * j + 4 * G, C, R, qcs, qsn);
+  } else {
+    // partials: [unit][split][R rows] {m, l} and [unit][split][R rows][C]
+    const int64_t unit = blockIdx.x;
+    const int64_t rows = Cf::R;
+    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
+    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
+                ((unit * pl.max_splits + split) * rows + row) * C;
+    if (G == 0) { ml[0] = m_run; ml[1] = l_run; }
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
+            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
+  }
+}
+
 // Merge of the split partials, splits in increasing order (deterministic).
 // A block takes 4 rows of one unit; each row's 64 threads own CPT = c / 64
 // consecutive channels and read every split's partial for them with vector
@@ -1284,7 +1576,9 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
         else hipLaunchKernelGGL(attn_f8<2>, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
       } else {
         if (a.kv_layout == ROW_FP8) launch_mfma_c<128, ROW_FP8, 1, 4>(a, grid, lp.nrg, pt, (int)b0, pl, s);
-        else launch_mfma_c<128, ROW_BF16, 1, 4>(a, grid, lp.nrg, pt, (int)b0, pl, s);
+        else if (lp.nrg == 1) hipLaunchKernelGGL(attn_b16<1>, grid, dim3(64), 0, s, a, pt, (int)b0, pl);
+        else if (lp.nrg == 2) hipLaunchKernelGGL(attn_b16<2>, grid, dim3(128), 0, s, a, pt, (int)b0, pl);
+        else hipLaunchKernelGGL(attn_b16<4>, grid, dim3(256), 0, s, a, pt, (int)b0, pl);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

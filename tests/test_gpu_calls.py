@@ -404,6 +404,8 @@ SPARSE_CASES = [
     ("bf16", ROW_FP8, 1, 33, 64, 512, 500, 100, 0, 0, [4000], False),        # no window
     ("bf16", ROW_BF16, 1, 5, 64, 128, 50, 0, 16, 40, [20], True),            # k = 0: window only
     ("bf16", ROW_BF16, 1, 6, 16, 128, 50, 8, 16, 40, [20], True),            # generic (nh = 16 sparse)
+    ("bf16", ROW_BF16, 2, 3, 32, 128, 900, 300, 128, 300, [800, 450], True), # c = 128, one row group, split
+    ("bf16", ROW_BF16, 1, 35, 128, 128, 600, 200, 64, 300, [500], False),    # c = 128, four row groups
 ]
 
 
@@ -463,6 +465,9 @@ DENSE_CASES = [
     ("bf16", ROW_FP8, 2, 260, 16, 512, 100, 128, 128, [12700, 200], True),
     ("bf16", ROW_FP8, 1, 70, 64, 512, 10, 128, 128, [0], True),
     ("bf16", ROW_FP8, 1, 64, 64, 512, 257, 128, 0, [40000], False),
+    # c = 128 bf16 rows: a split key range merged by the combine kernel, one query per block
+    ("bf16", ROW_BF16, 1, 3, 64, 128, 2100, 128, 128, [2000 * 128 + 50], True),
+    ("bf16", ROW_BF16, 1, 20, 128, 128, 300, 128, 128, [30000], True),
 ]
 
 
