@@ -625,6 +625,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode step of configuration 4 (16 sequences at 2^20), as the `decode` field")
+    ap.add_argument("--prefill-configs-only", action="store_true",
+                    help="only configurations 2 and 3 (c = 128 bf16 layers), as the `prefill_configs` field")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -642,6 +644,10 @@ def main():
     if args.decode_only:
         stream = torch.cuda.current_stream()
         print(json.dumps({"decode": decode_report(args.steps, stream)}), flush=True)
+        return
+    if args.prefill_configs_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"prefill_configs": prefill_configs_report(args.steps, stream)}), flush=True)
         return
 
     inp = G.make(5)
