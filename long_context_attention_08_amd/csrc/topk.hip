@@ -822,11 +822,14 @@ __device__ __forceinline__ void hs_copy(uint64_t* dst, const uint64_t* src, uint
 // places holds more than RANK_BIN_MAX composites (dense ties) returns false
 // before the scatter, having written nothing and left sh.cand as it was: the
 // caller sorts instead.  sh.hist (and the sh.out it shares memory with) is
-// overwritten; boff holds SK_BIN offsets, maxc one word (LDS).
+// overwritten; maxc is one word (LDS).  One array serves as histogram, bin
+// offsets and scatter cursor: the bins are placed from the top, so once the
+// scatter has moved each cursor to its bin's end, the start of bin b is the
+// cursor of bin b + 1.
 constexpr int RANK_BIN_MAX = 64;
 template <int EPT, int CAP>
-__device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_sh, const uint64_t (&v)[EPT], int n,
-                             uint32_t need, int32_t* out) {
+__device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* maxc_sh, const uint64_t (&v)[EPT], int n, uint32_t need,
+                             int32_t* out) {
   uint64_t mn = ~0ull, mx = 0;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -860,7 +863,9 @@ __device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_
   for (int j = 0; j < EPT; ++j)
     if ((int)threadIdx.x + j * SK_NT < n) atomicAdd(&sh.hist[digit(v[j])], 1u);
   __syncthreads();
-  // thread t owns bins [SK_BIN - 8(t+1), SK_BIN - 8t), from the top
+  // thread t owns bins [SK_BIN - 8(t+1), SK_BIN - 8t), from the top; its
+  // counts become the bins' first places (each thread reads and writes only
+  // its own bins here)
   constexpr int PER = SK_BIN / SK_NT;
   uint32_t c[PER];
   uint32_t loc = 0;
@@ -872,7 +877,6 @@ __device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int b = SK_BIN - 1 - (PER * (int)threadIdx.x + q);
-    boff[b] = above;
     sh.hist[b] = above;                     // the scatter cursor, which ends at the bin's end
     if (above < need && c[q] > maxc) maxc = c[q];
     above += c[q];
@@ -890,7 +894,7 @@ __device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_
   for (int p = threadIdx.x; p < n; p += SK_NT) {
     const uint64_t x = sh.cand[p];
     const uint32_t b = digit(x);
-    const uint32_t s = boff[b], e = sh.hist[b];
+    const uint32_t s = b + 1 < (uint32_t)SK_BIN ? sh.hist[b + 1] : 0u, e = sh.hist[b];
     if (s >= need) continue;
     uint32_t r = 0;
     for (uint32_t q = s; q < e; ++q) r += sh.cand[q] > x ? 1u : 0u;
@@ -903,7 +907,6 @@ __device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* boff, uint32_t* maxc_
 __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
   extern __shared__ __align__(16) uint8_t smem[];
   HsShared& sh = *reinterpret_cast<HsShared*>(smem);
-  __shared__ uint32_t s_boff[SK_BIN];
   __shared__ uint32_t s_maxc;
   const int64_t row = blockIdx.x;
   if (row_skipped(a, row)) return;
@@ -995,7 +998,7 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
   }
   __syncthreads();                           // sh.out shares memory with sh.hist
   int32_t* dst = a.idx + grow * a.k;
-  if (rank_by_bins<EPT>(sh, s_boff, &s_maxc, v, (int)need, need, dst)) {
+  if (rank_by_bins<EPT>(sh, &s_maxc, v, (int)need, need, dst)) {
     for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) dst[i] = -1;
     return;
   }
@@ -1189,6 +1192,11 @@ struct ItSelArgs {
 };
 
 static_assert(IT_SELCAP == SK_CAP, "a select block holds the candidates of one row");
+// the smaller select block, taken where the expected candidates of a row
+// (IT_STRIDE ks) leave it the margin (8/5) the one-call path asks of the larger
+constexpr int IT_CAP_S = 2944;
+static_assert(IT_CAP_S <= SK_CAP && IT_CAP_S % 64 == 0, "the smaller select block");
+static bool it_small_select(int ks) { return (int64_t)IT_STRIDE * ks * 8 / 5 <= IT_CAP_S; }
 
 // One block per row: the k best of the row's lists, sorted.  Every visible
 // score at or above the row's threshold is in the lists unless one
@@ -1199,12 +1207,20 @@ static_assert(IT_SELCAP == SK_CAP, "a select block holds the candidates of one r
 // The lists' composites are ranked in one pass by digit bins (rank_by_bins);
 // a row with dense ties there takes the radix select and the bitonic sort
 // instead; both give the same sorted list.
-constexpr int IT_EPT = (SK_CAP + SK_NT - 1) / SK_NT;   // composites per thread
+//
+// CAP composites fit the block's LDS: 3584 (37 KB, 4 blocks per CU), or,
+// where the expected candidates are fewer, IT_CAP_S (32 KB, 5 blocks per CU:
+// the block is a latency chain, so the rate follows the blocks per CU).  The
+// list counts and offsets of the loading phase live in sh.hist, which the
+// ranking only uses afterwards.
+template <int CAP>
 __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
+  constexpr int EPT = (CAP + SK_NT - 1) / SK_NT;   // composites per thread
   extern __shared__ __align__(16) uint8_t smem[];
-  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
-  __shared__ uint32_t s_cnt[SK_NT], s_off[SK_NT];
-  __shared__ uint32_t s_boff[SK_BIN];       // first output place of each digit bin
+  SkSharedT<CAP>& sh = *reinterpret_cast<SkSharedT<CAP>*>(smem);
+  static_assert(2 * SK_NT <= SK_BIN, "list counts and offsets fit the histogram's space");
+  uint32_t* const s_cnt = sh.hist;
+  uint32_t* const s_off = sh.hist + SK_NT;
   __shared__ uint32_t s_maxc;
   const int64_t row = blockIdx.x;
   const int64_t bl = row / a.nq, t = row % a.nq;
@@ -1220,7 +1236,7 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
   }
   uint32_t total;
   sk_scan_excl(tot, sh.wsum, &total);
-  const bool flag = __syncthreads_or(over) || total < need || total > (uint32_t)SK_CAP;
+  const bool flag = __syncthreads_or(over) || total < need || total > (uint32_t)CAP;
   if (threadIdx.x == 0) a.flags[row] = flag ? 1 : 0;
   if (flag) return;
   int32_t* out = a.idx + row * a.k;
@@ -1267,13 +1283,13 @@ __global__ __launch_bounds__(SK_NT) void it_select(ItSelArgs a, PosTable pt) {
   }
   const int n = (int)total;
   // ---- one-pass rank by digit bins
-  uint64_t v[IT_EPT];
+  uint64_t v[EPT];
 #pragma unroll
-  for (int j = 0; j < IT_EPT; ++j) {
+  for (int j = 0; j < EPT; ++j) {
     const int i = (int)threadIdx.x + j * SK_NT;
     v[j] = i < n ? sh.cand[i] : 0ull;
   }
-  if (rank_by_bins<IT_EPT>(sh, s_boff, &s_maxc, v, n, need, out)) {
+  if (rank_by_bins<EPT>(sh, &s_maxc, v, n, need, out)) {
     for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) out[i] = -1;
     return;
   }
@@ -1295,8 +1311,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, const int64_t* q_pos0, int
   const bool mx = a0.k_layout == ROW_MXFP4;
   const size_t krow = mx ? (size_t)a0.cI / 2 : (size_t)row_bytes(a0.k_layout, a0.cI);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
-  hipError_t e = hipFuncSetAttribute((const void*)it_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute((const void*)it_select<SK_CAP>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)sizeof(SkShared));
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)it_select<IT_CAP_S>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)sizeof(SkSharedT<IT_CAP_S>));
   if (e != hipSuccess) return e;
 #define IT_CHECK(x)            \
   do {                         \
@@ -1359,7 +1378,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a0, const int64_t* q_pos0, int
     // per-row select; flagged rows take the full-score path
     int* flags = reinterpret_cast<int*>(w + p.o_flags);
     ItSelArgs sa{ae.cand, ae.ccount, p.grid.splits, p.cap, a.nq, a.S, a.m, k, oidx, flags};
-    hipLaunchKernelGGL(it_select, dim3((unsigned)rows), dim3(SK_NT), sizeof(SkShared), s, sa, pt);
+    if (it_small_select(p.ks))
+      hipLaunchKernelGGL((it_select<IT_CAP_S>), dim3((unsigned)rows), dim3(SK_NT), sizeof(SkSharedT<IT_CAP_S>), s,
+                         sa, pt);
+    else
+      hipLaunchKernelGGL((it_select<SK_CAP>), dim3((unsigned)rows), dim3(SK_NT), sizeof(SkShared), s, sa, pt);
     IT_CHECK(hipGetLastError());
     IndexerArgs af = a;
     af.scores = scores;
