@@ -7,9 +7,10 @@
 // largest composite T.  T is found by an MSD radix select in LDS (12-bit
 // digits in the k > 1024 stages, 11-bit digits in the streaming and histogram
 // selects; each stops as soon as a whole bin is taken), the winners are
-// gathered and put in order in LDS: bitonic-sorted by the streaming and the
-// k > 1024 selects, ranked by digit bins (rank_by_bins) by the histogram
-// select and the one-call select, which sort only sets with dense ties.
+// gathered and put in order in LDS: bitonic-sorted by the k > 1024 selects
+// and the parts of a split streaming row, ranked by digit bins (rank_by_bins)
+// by the streaming select of a whole row, the histogram select and the
+// one-call select, which sort only sets with dense ties.
 //
 // k <= 1024, streaming: one block per (row, part) reads its scores once from
 //          HBM.  A running threshold tau (a composite no larger than the k-th
@@ -312,6 +313,9 @@ struct SkSharedT {
 using SkShared = SkSharedT<SK_CAP>;     // streaming select
 using HsShared = SkSharedT<HS_CAP>;     // last step of the histogram select
 static_assert(SK_CAP >= SK_STEP + SK_KMAX, "a step must fit next to the k kept candidates");
+constexpr int SK_KSMALL = 512;              // k up to which the streaming select uses the smaller buffer
+constexpr int SK_CAP_S = 2560;
+static_assert(SK_CAP_S >= SK_STEP + SK_KSMALL && SK_CAP_S % 64 == 0, "the smaller buffer holds a step and k");
 
 // Barrier for LDS traffic only (waits for this wave's LDS operations): unlike
 // __syncthreads() it carries no memory fence, so score loads in flight stay
@@ -491,13 +495,23 @@ __device__ void sk_gather(Sh& sh, int n, uint64_t T) {
   __syncthreads();
 }
 
-// dynamic LDS: sizeof(SkShared).  VEC: every part starts 16-byte aligned, so
-// whole steps are read with float4 loads (the last, partial step with
-// clamped scalar loads).
-template <bool VEC>
+// the k best of a set of unique composites in order by digit bins (below)
+template <int EPT, int CAP>
+__device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* maxc_sh, const uint64_t (&v)[EPT], int n, uint32_t need,
+                             int32_t* out);
+
+// dynamic LDS: sizeof(SkSharedT<CAP>).  VEC: every part starts 16-byte
+// aligned, so whole steps are read with float4 loads (the last, partial step
+// with clamped scalar loads).  CAP candidate slots hold a step next to the k
+// kept ones: 3584 for k <= 1024 (37 KB, 4 blocks per CU), 2560 for k <= 512
+// (29 KB, 5 blocks per CU; the loop is latency-bound, so more blocks raise the
+// rate).  A whole row's k best are put in order by rank_by_bins over the
+// buffer (the radix select and bitonic sort only for dense ties).
+template <bool VEC, int CAP>
 __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, int b0) {
   extern __shared__ __align__(16) uint8_t smem[];
-  SkShared& sh = *reinterpret_cast<SkShared*>(smem);
+  SkSharedT<CAP>& sh = *reinterpret_cast<SkSharedT<CAP>*>(smem);
+  __shared__ uint32_t s_maxc;
   const int64_t row = (int64_t)blockIdx.x;         // row within this launch's batch slice
   if (row_skipped(a, row)) return;
   const int pidx = blockIdx.y;
@@ -546,7 +560,7 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
   };
   auto process = [&](int i0, const f4 (&d)[SK_U]) {
     lds_barrier();                                     // every append of the last step is in
-    if (sh.cnt > (uint32_t)(SK_CAP - SK_STEP)) compact();
+    if (sh.cnt > (uint32_t)(CAP - SK_STEP)) compact();
     // survivors: scores not below tauf, then the exact composite test
     uint64_t keep[SK_U * 4];
     bool anyk = false;
@@ -618,7 +632,21 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
   __syncthreads();
   // final selection of the `need` largest, sorted descending
   const int n = (int)sh.cnt;
-  if (need > 0) {
+  if (a.nparts == 1) {
+    constexpr int EPT = (CAP + SK_NT - 1) / SK_NT;
+    uint64_t v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int i = (int)threadIdx.x + j * SK_NT;
+      v[j] = i < n ? sh.cand[i] : 0ull;
+    }
+    int32_t* dst = a.idx + grow * a.k;
+    if (rank_by_bins<EPT>(sh, &s_maxc, v, n, need, dst)) {
+      for (int i = (int)need + threadIdx.x; i < a.k; i += SK_NT) dst[i] = -1;
+      return;
+    }
+  }
+  if (need > 0) {                     // sh.cand is as it was when rank_by_bins declines
     const uint64_t T = sk_select(sh, n, need);
     sk_gather(sh, n, T);
   }
@@ -1052,11 +1080,14 @@ hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t 
   a.cand = reinterpret_cast<uint64_t*>(ws);
   const int n2 = [&] { int p = 1; while (p < k) p <<= 1; return p; }();
   const bool stream = plan.kind == TOPK_STREAM;
-  const size_t lds1 = stream ? sizeof(SkShared) : (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
+  const bool small = k <= SK_KSMALL;     // the smaller candidate buffer
+  const size_t lds1 = stream ? (small ? sizeof(SkSharedT<SK_CAP_S>) : sizeof(SkShared))
+                             : (size_t)a.part * 4 + NBIN * 4 + (size_t)n2 * 8;
   const size_t lds2 = (size_t)a.nparts * k * 8 + NBIN * 4 + (size_t)n2 * 8;
   const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && S % 4 == 0 && a.part % 4 == 0;
   const void* k1 = !stream ? (const void*)topk_stage1
-                           : vec ? (const void*)topk_stream<true> : (const void*)topk_stream<false>;
+                   : vec   ? (small ? (const void*)topk_stream<true, SK_CAP_S> : (const void*)topk_stream<true, SK_CAP>)
+                           : (small ? (const void*)topk_stream<false, SK_CAP_S> : (const void*)topk_stream<false, SK_CAP>);
   hipError_t e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
   if (a.nparts > 1) {
@@ -1067,12 +1098,15 @@ hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t 
     const int nb = (int)(B - b0 < MAXB ? B - b0 : MAXB);
     PosTable pt;
     for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
-    if (stream && vec)
-      hipLaunchKernelGGL(topk_stream<true>, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
-                         a, pt, (int)b0);
+    const dim3 g1((unsigned)(nb * nq), (unsigned)a.nparts);
+    if (stream && vec && small)
+      hipLaunchKernelGGL((topk_stream<true, SK_CAP_S>), g1, dim3(SK_NT), lds1, s, a, pt, (int)b0);
+    else if (stream && vec)
+      hipLaunchKernelGGL((topk_stream<true, SK_CAP>), g1, dim3(SK_NT), lds1, s, a, pt, (int)b0);
+    else if (stream && small)
+      hipLaunchKernelGGL((topk_stream<false, SK_CAP_S>), g1, dim3(SK_NT), lds1, s, a, pt, (int)b0);
     else if (stream)
-      hipLaunchKernelGGL(topk_stream<false>, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(SK_NT), lds1, s,
-                         a, pt, (int)b0);
+      hipLaunchKernelGGL((topk_stream<false, SK_CAP>), g1, dim3(SK_NT), lds1, s, a, pt, (int)b0);
     else
       hipLaunchKernelGGL(topk_stage1, dim3((unsigned)(nb * nq), (unsigned)a.nparts), dim3(TK_THREADS), lds1, s,
                          a, pt, (int)b0);
