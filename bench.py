@@ -632,7 +632,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (multi-GPU sharding is a "
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported (multi-GPU sharding is a "
               "design note only)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
