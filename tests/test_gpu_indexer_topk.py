@@ -44,6 +44,7 @@ IT_CASES = [
     ("f32", ROW_F32, 2, 10, 4, 32, 5000, 4, 64, [20000, 100], "normal"),         # no sampled path (fp32 queries)
     ("bf16", ROW_BF16, 1, 9, 16, 64, 6000, 1, 128, [5990], "normal"),            # no sampled path (hI = 16), m = 1
     ("bf16", ROW_MXFP4, 2, 1, 32, 64, 600000, 4, 1024, [2400000, 1800000], "normal"),   # sample rows > 16384
+    ("bf16", ROW_MXFP4, 1, 3, 32, 64, 400000, 4, 1024, [1600000], "normal"),   # 12500-score sample rows (LDS-staged)
     # small-integer scores: many equal scores among a row's candidates (the select's dense-tie path)
     ("bf16", ROW_BF16, 1, 32, 32, 64, 3000, 4, 256, [6000], "int"),
     ("bf16", ROW_MXFP4, 2, 20, 32, 64, 9000, 4, 512, [30000, 8000], "int"),
