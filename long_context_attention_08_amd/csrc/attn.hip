@@ -1485,7 +1485,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   const int64_t bl = unit / pl.units_per_b, u = unit % pl.units_per_b;
   const int64_t b = b0 + bl;
   const UnitInfo ui = unit_info(a, pl, pt.q_pos0[bl], u);
-  const int64_t nsplit = (ui.total + pl.chunk - 1) / pl.chunk;
+  const int64_t nsplit = (ui.total + pl.chunk - 1) / pl.chunk;   // <= ATTN_MAX_SPLITS by the plan
   const int64_t rows = (int64_t)pl.qpw * a.nh;
   const int64_t r = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1497,41 +1497,55 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   const float* mlb = reinterpret_cast<const float*>(a.ws);
   const float* owb = mlb + (int64_t)gridDim.x * pl.max_splits * rows * 2;
   const float* ml = mlb + (unit * pl.max_splits * rows + r) * 2;          // split s at + 2 s rows
+  const float* ow = owb + (unit * pl.max_splits * rows + r) * (int64_t)c + lane * CPT;   // split s at + s rows c
+  // every split's (m, l) and partial loads issued together, then the merge
+  // in increasing split order; a split that saw no visible key (m = -inf,
+  // zero partial) gets weight 0
+  constexpr int MS = ATTN_MAX_SPLITS;
+  float mv[MS], lv[MS], ov[MS][CPT];
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) {
+    mv[sp] = -INFINITY;
+    lv[sp] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) ov[sp][j] = 0.f;
+    if (sp < nsplit) {
+      mv[sp] = ml[sp * rows * 2];
+      lv[sp] = ml[sp * rows * 2 + 1];
+      const float* src = ow + sp * rows * (int64_t)c;
+      if constexpr (CPT % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; j += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
+          ov[sp][j] = v[0]; ov[sp][j + 1] = v[1]; ov[sp][j + 2] = v[2]; ov[sp][j + 3] = v[3];
+        }
+      } else {
+        static_assert(CPT % 2 == 0, "channels per thread");
+#pragma unroll
+        for (int j = 0; j < CPT; j += 2) {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          const f32x2 v = *reinterpret_cast<const f32x2*>(src + j);
+          ov[sp][j] = v[0]; ov[sp][j + 1] = v[1];
+        }
+      }
+    }
+  }
   float M = -INFINITY;
-#pragma unroll 4
-  for (int64_t sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[sp * rows * 2]);
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) M = fmaxf(M, mv[sp]);
   const float z = a.sink ? a.sink[h] * LOG2E : -INFINITY;
   const float Mt = fmaxf(M, z);
   float den = a.sink ? exp2f(z - Mt) : 0.f;
   float o[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) o[j] = 0.f;
-  const float* ow = owb + (unit * pl.max_splits * rows + r) * (int64_t)c + lane * CPT;   // split s at + s rows c
-  // splits in increasing order; a split that saw no visible key (m = -inf,
-  // zero partial) gets weight 0.  No branch in the loop, so that the partial
-  // loads of several splits are in flight together
-#pragma unroll 4
-  for (int64_t sp = 0; sp < nsplit; ++sp) {
-    const float ms = ml[sp * rows * 2];
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - Mt);
-    den = fmaf(ml[sp * rows * 2 + 1], w, den);
-    const float* src = ow + sp * rows * (int64_t)c;
-    if constexpr (CPT % 4 == 0) {
 #pragma unroll
-      for (int j = 0; j < CPT; j += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
-        o[j] = fmaf(v[0], w, o[j]); o[j + 1] = fmaf(v[1], w, o[j + 1]);
-        o[j + 2] = fmaf(v[2], w, o[j + 2]); o[j + 3] = fmaf(v[3], w, o[j + 3]);
-      }
-    } else {
-      static_assert(CPT % 2 == 0, "channels per thread");
+  for (int sp = 0; sp < MS; ++sp) {
+    if (sp >= nsplit) break;
+    const float w = mv[sp] == -INFINITY ? 0.f : exp2f(mv[sp] - Mt);
+    den = fmaf(lv[sp], w, den);
 #pragma unroll
-      for (int j = 0; j < CPT; j += 2) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 v = *reinterpret_cast<const f32x2*>(src + j);
-        o[j] = fmaf(v[0], w, o[j]); o[j + 1] = fmaf(v[1], w, o[j + 1]);
-      }
-    }
+    for (int j = 0; j < CPT; ++j) o[j] = fmaf(ov[sp][j], w, o[j]);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t obase = ((b * a.nq + t) * a.nh + h) * c + lane * CPT;

@@ -283,6 +283,7 @@ struct AttnPlan {
 };
 enum { ATTN_GENERIC = 0, ATTN_MFMA = 1, ATTN_F8 = 2 };
 constexpr int ATTN_SIDX_CAP = 2048;   // index-list slots a sparse MFMA block caches in LDS
+constexpr int ATTN_MAX_SPLITS = 16;   // key splits of one attention unit (the merge holds them all in registers)
 constexpr int ATTN_QPW_MAX = 8;       // most queries one MFMA block serves
 struct AttnLaunchPlan {
   int path;              // ATTN_*

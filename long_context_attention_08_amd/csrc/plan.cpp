@@ -297,7 +297,7 @@ AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
     pl.max_splits = 1;
   } else {
     int64_t ms = (slots + 127) / 128;
-    ms = ms < 1 ? 1 : (ms > 16 ? 16 : ms);
+    ms = ms < 1 ? 1 : (ms > ATTN_MAX_SPLITS ? ATTN_MAX_SPLITS : ms);
     const int64_t per = (slots + ms - 1) / ms;
     pl.chunk = (int)((per + 31) / 32 * 32);
     pl.max_splits = (int)ms;
