@@ -420,7 +420,9 @@ static bool gemm_path_ok(const CompressArgs& a, int want_m) {
 // rows, MT = 1 (64-token blocks, more of them) for narrow ones.  H rows
 // T0 - 32 .. T0 + 64 MT - 1 and the block's W rows travel
 // global -> LDS by global_load_lds_dwordx4 into an XOR-swizzled layout (chunk
-// j of row r at j ^ (r & 7)), two stages, one barrier per 64-wide k tile.
+// j of row r at j ^ ((r >> 1) & 7): 16 consecutive 128-byte rows then fill
+// the 64 LDS banks twice over in distinct 16-byte groups, so a 16-lane
+// fragment read is conflict-free), two stages, one barrier per 64-wide k tile.
 // Staged H rows outside the input are clamped copies that no entry uses.
 constexpr int CG_K = 64;
 template <bool HCA, int MT>
@@ -450,8 +452,9 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int64_t bx,
   const uint16_t* H = reinterpret_cast<const uint16_t*>(a.H);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
   // copy k of a tile covers staged rows [8k, 8k + 8): lane L takes row 8k + L/8
-  // and writes LDS chunk L % 8, which holds source chunk (L % 8) ^ (row & 7)
-  const int crow = l >> 3, gch = (l & 7) ^ (crow & 7);
+  // and writes LDS chunk L % 8, which holds source chunk (L % 8) ^ ((row >> 1) & 7);
+  // this wave's copies are k = wv + 4 i, so (row >> 1) & 7 = (4 wv + L/16) & 7
+  const int crow = l >> 3, gch = (l & 7) ^ ((4 * wv + (crow >> 1)) & 7);
   const int64_t hrows = a.n_left + a.n;
   const uint16_t* pa[CA];
   const uint16_t* pb[CB];
@@ -486,8 +489,8 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int64_t bx,
 
   // fragment rows: a-tokens at staged row (tile row + 32), b-tokens at (tile row + 28)
   const int ra = 32 * MT * wm + 32 + col, rbr = 32 * MT * wm + 28 + col;   // + 32 i
-  const int swa = ra & 7, swb = rbr & 7;
-  const int rw = 32 * NT * wn + col, sww = rw & 7;                  // + 32 t
+  const int swa = (ra >> 1) & 7, swb = (rbr >> 1) & 7;
+  const int rw = 32 * NT * wn + col, sww = (rw >> 1) & 7;           // + 32 t
   const int nk = (int)(a.d / CG_K);
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {

@@ -8,7 +8,8 @@
 // Block tile BM x BN x 64, four waves in 2 x 2, each wave (BM/2) x (BN/2) in
 // 32x32 tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs at 256 x 256).
 // Tiles travel global -> LDS by global_load_lds_dwordx4 into an XOR-swizzled
-// layout (16-byte chunk j of row r at chunk j ^ (r & 7)), two stages, one
+// layout (16-byte chunk j of row r at chunk j ^ ((r >> 1) & 7): 16 consecutive
+// 128-byte rows in distinct 16-byte groups of the 64 LDS banks), two stages, one
 // block barrier per K tile: the copies of tile k+1 run under the MFMAs of tile
 // k.  Rows past M or N read the last valid row; their results are not stored.
 #include "dsv4_common.h"
@@ -45,8 +46,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int x
   const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + (int64_t)blockIdx.z * a.sB;
 
   // copy q of a tile covers rows [8q, 8q + 8): lane L takes row 8q + L/8 and
-  // writes LDS chunk L % 8, which holds global chunk (L % 8) ^ (row & 7)
-  const int crow = l >> 3, gch = (l & 7) ^ (crow & 7);
+  // writes LDS chunk L % 8, which holds global chunk (L % 8) ^ ((row >> 1) & 7);
+  // this wave's copies are q = wv + 4 i, so (row >> 1) & 7 = (4 wv + L/16) & 7
+  const int crow = l >> 3, gch = (l & 7) ^ ((4 * wv + (crow >> 1)) & 7);
   auto src_row = [](const uint16_t* X, int64_t r0, int64_t r, int64_t rows, int64_t ld) {
     const int64_t rr = r0 + r < rows ? r0 + r : rows - 1;
     return X + rr * ld;
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt(GemmArgs a, int tiles_n, int x
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // fragment rows of this lane and their swizzle
-  const int ra0 = wm * WM + col, rb0 = wn * WN + col;       // + 32 i / 32 j; (r & 7) is col & 7
-  const int sw = col & 7;
+  const int ra0 = wm * WM + col, rb0 = wn * WN + col;       // + 32 i / 32 j; (r >> 1) & 7 is (col >> 1) & 7
+  const int sw = (col >> 1) & 7;
   const int nk = (int)(a.K / GK);
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
