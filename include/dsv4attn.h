@@ -264,8 +264,8 @@ size_t dsv4_attn_workspace_size(int dense, int64_t B, int64_t nq, int nh, int c,
 /*
  * Launch plan of an attention call (host only, no HIP call): the kernel that
  * runs, how many queries share a block, and how a block's key slots are split
- * across blocks (splits > 1: fp32 partials in the workspace, merged in split
- * order).  workspace_bytes is exactly what the call with these arguments
+ * across blocks (splits > 1: per-split {m, l} in fp32 and output rows in bf16
+ * in the workspace, merged in split order).  workspace_bytes is exactly what the call with these arguments
  * needs; dsv4_attn_workspace_size() bounds it from above.  Arguments as for
  * the calls themselves: dense 0 is dsv4_sparse_mqa_fwd (k used), dense 1 is
  * dsv4_hca_dense_fwd (m_prime used); q_pos0 is a host array [B].  Returns

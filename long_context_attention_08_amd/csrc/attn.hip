@@ -45,6 +45,27 @@ __device__ __forceinline__ UnitInfo unit_info(const AttnArgs& a, const AttnPlan&
   return ui;
 }
 
+// Split partials in the workspace: {m, l} in fp32 for every (unit, split,
+// row), then the unnormalised O rows in bf16, [unit][split][row][c] (half
+// the bytes of fp32 rows; the merge reads every split's row, so at decode
+// these bytes are of the order of the key rows themselves).
+struct PartialRow {
+  float* ml;
+  uint16_t* o;
+};
+__device__ __forceinline__ PartialRow partial_row(const AttnArgs& a, const AttnPlan& pl, int64_t units, int64_t unit,
+                                                  int64_t split, int64_t rows, int64_t row, int c) {
+  float* mlb = reinterpret_cast<float*>(a.ws);
+  uint16_t* ob = reinterpret_cast<uint16_t*>(mlb + units * pl.max_splits * rows * 2);
+  const int64_t i = (unit * pl.max_splits + split) * rows + row;
+  return {mlb + i * 2, ob + i * c};
+}
+
+// bf16 of 4 partial channels at dst (8-byte aligned)
+__device__ __forceinline__ void store_partial4(uint16_t* dst, float v0, float v1, float v2, float v3) {
+  *reinterpret_cast<u32x2*>(dst) = (u32x2){pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+}
+
 // row of key slot `slot` (null if padding); *pos = entry index or position,
 // *win = window row
 __device__ __forceinline__ const uint8_t* slot_row(const AttnArgs& a, int64_t b, int64_t t, const UnitInfo& ui,
@@ -773,19 +794,17 @@ void attn_mfma(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
                         acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, ch * CH + 32 * mo + 8 * j + 4 * G, C, R,
                         qcs, qsn);
   } else {
-    // partials: [unit][split][R rows] {m, l} and [unit][split][R rows][C]
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
-    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
-    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + row) * C + ch * CH;
-    if (G == 0 && ch == 0) { ml[0] = m_run; ml[1] = l_run; }
+    const PartialRow pr = partial_row(a, pl, gridDim.x, unit, split, rows, row, C);
+    uint16_t* ow = pr.o + ch * CH;
+    if (G == 0 && ch == 0) { pr.ml[0] = m_run; pr.ml[1] = l_run; }
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
-            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
+        store_partial4(ow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2],
+                       acc[mo][4 * j + 3]);
   }
 }
 
@@ -1161,16 +1180,14 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   } else {
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
-    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
-    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + row) * C;
-    if (G == 0 && ch == 0) { ml[0] = m_run; ml[1] = l_run; }
+    const PartialRow pr = partial_row(a, pl, gridDim.x, unit, split, rows, row, C);
+    if (G == 0 && ch == 0) { pr.ml[0] = m_run; pr.ml[1] = l_run; }
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(ow + f8_chan(mo) + 8 * j + 4 * G) =
-            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
+        store_partial4(pr.o + f8_chan(mo) + 8 * j + 4 * G, acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2],
+                       acc[mo][4 * j + 3]);
   }
 }
 
@@ -1459,26 +1476,23 @@ void attn_b16(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
         store4_bf16_rot(orow + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j] * inv, acc[mo][4 * j + 1] * inv,
                         acc[mo][4 * j + 2] * inv, acc[mo][4 * j + 3] * inv, 32 * mo + 8 * j + 4 * G, C, R, qcs, qsn);
   } else {
-    // partials: [unit][split][R rows] {m, l} and [unit][split][R rows][C]
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
-    float* ml = reinterpret_cast<float*>(a.ws) + ((unit * pl.max_splits + split) * rows + row) * 2;
-    float* ow = reinterpret_cast<float*>(a.ws) + (int64_t)gridDim.x * pl.max_splits * rows * 2 +
-                ((unit * pl.max_splits + split) * rows + row) * C;
-    if (G == 0) { ml[0] = m_run; ml[1] = l_run; }
+    const PartialRow pr = partial_row(a, pl, gridDim.x, unit, split, rows, row, C);
+    if (G == 0) { pr.ml[0] = m_run; pr.ml[1] = l_run; }
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(ow + 32 * mo + 8 * j + 4 * G) =
-            (f32x4){acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2], acc[mo][4 * j + 3]};
+        store_partial4(pr.o + 32 * mo + 8 * j + 4 * G, acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2],
+                       acc[mo][4 * j + 3]);
   }
 }
 
 // Merge of the split partials, splits in increasing order (deterministic).
 // A block takes 4 rows of one unit; each row's 64 threads own CPT = c / 64
-// consecutive channels and read every split's partial for them with vector
-// loads.
+// consecutive channels and read every split's bf16 partial for them with one
+// vector load per split, all issued before the merge.
 template <int CPT>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
   const int64_t unit = blockIdx.x;
@@ -1494,39 +1508,30 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   const int qw = (int)(r / a.nh), h = (int)(r % a.nh);
   const int64_t t = ui.t0 + qw;
   if (t > ui.tl) return;
-  const float* mlb = reinterpret_cast<const float*>(a.ws);
-  const float* owb = mlb + (int64_t)gridDim.x * pl.max_splits * rows * 2;
-  const float* ml = mlb + (unit * pl.max_splits * rows + r) * 2;          // split s at + 2 s rows
-  const float* ow = owb + (unit * pl.max_splits * rows + r) * (int64_t)c + lane * CPT;   // split s at + s rows c
-  // every split's (m, l) and partial loads issued together, then the merge
-  // in increasing split order; a split that saw no visible key (m = -inf,
-  // zero partial) gets weight 0
+  const PartialRow pr = partial_row(a, pl, gridDim.x, unit, 0, rows, r, c);
+  const float* ml = pr.ml;                                   // split s at + 2 s rows
+  const uint16_t* ow = pr.o + lane * CPT;                    // split s at + s rows c
+  // a split that saw no visible key (m = -inf, zero partial) gets weight 0
   constexpr int MS = ATTN_MAX_SPLITS;
-  float mv[MS], lv[MS], ov[MS][CPT];
+  constexpr int NW = CPT / 2;                                // bf16 pairs per thread and split
+  static_assert(NW == 4 || NW == 1, "channels per thread");
+  float mv[MS], lv[MS];
+  uint32_t ov[MS][NW];
 #pragma unroll
   for (int sp = 0; sp < MS; ++sp) {
     mv[sp] = -INFINITY;
     lv[sp] = 0.f;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) ov[sp][j] = 0.f;
+    for (int j = 0; j < NW; ++j) ov[sp][j] = 0u;
     if (sp < nsplit) {
       mv[sp] = ml[sp * rows * 2];
       lv[sp] = ml[sp * rows * 2 + 1];
-      const float* src = ow + sp * rows * (int64_t)c;
-      if constexpr (CPT % 4 == 0) {
-#pragma unroll
-        for (int j = 0; j < CPT; j += 4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
-          ov[sp][j] = v[0]; ov[sp][j + 1] = v[1]; ov[sp][j + 2] = v[2]; ov[sp][j + 3] = v[3];
-        }
+      const uint16_t* src = ow + sp * rows * (int64_t)c;
+      if constexpr (NW == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        ov[sp][0] = v[0]; ov[sp][1] = v[1]; ov[sp][2] = v[2]; ov[sp][3] = v[3];
       } else {
-        static_assert(CPT % 2 == 0, "channels per thread");
-#pragma unroll
-        for (int j = 0; j < CPT; j += 2) {
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
-          const f32x2 v = *reinterpret_cast<const f32x2*>(src + j);
-          ov[sp][j] = v[0]; ov[sp][j + 1] = v[1];
-        }
+        ov[sp][0] = *reinterpret_cast<const uint32_t*>(src);
       }
     }
   }
@@ -1545,7 +1550,10 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
     const float w = mv[sp] == -INFINITY ? 0.f : exp2f(mv[sp] - Mt);
     den = fmaf(lv[sp], w, den);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) o[j] = fmaf(ov[sp][j], w, o[j]);
+    for (int q = 0; q < NW; ++q) {
+      o[2 * q] = fmaf(bf16_to_f32(ov[sp][q] & 0xFFFFu), w, o[2 * q]);
+      o[2 * q + 1] = fmaf(bf16_to_f32(ov[sp][q] >> 16), w, o[2 * q + 1]);
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t obase = ((b * a.nq + t) * a.nh + h) * c + lane * CPT;

@@ -290,7 +290,7 @@ AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
   // depends on the key bound alone (never on the batch), so a sequence's
   // results do not depend on the batch.  The split count comes first and is
   // non-decreasing in the bound: up to 16 splits of at least 128 slots (a
-  // decode query's 1152 sparse slots take 9 blocks), each split's fp32
+  // decode query's 1152 sparse slots take 9 blocks), each split's bf16
   // partial (rows x c) small next to the rows it reads
   if (pl.units_per_b >= 32 || slots <= 0) {
     pl.chunk = 1 << 30;
@@ -304,7 +304,8 @@ AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
   }
   if (pl.max_splits > 1) {
     const int64_t units = (a.B < MAXB ? a.B : MAXB) * pl.units_per_b;
-    lp.ws_bytes = (size_t)units * pl.max_splits * pl.qpw * a.nh * (size_t)(a.c + 2) * sizeof(float);
+    // per (unit, split, row): {m, l} in fp32 and the row's partial in bf16
+    lp.ws_bytes = (size_t)units * pl.max_splits * pl.qpw * a.nh * (2 * sizeof(float) + (size_t)a.c * 2);
   }
   return lp;
 }

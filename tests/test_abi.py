@@ -307,7 +307,7 @@ def _group_slots(dense, k, m_prime, n_win, S, p0, t0, tl):
 def test_attention_workspace_plan_sweep(L, dense):
     """The size query bounds the exact need of every call, and the plan covers
     every key slot: for each query group, ceil(slots / split_slots) <= splits,
-    and the partials the kernels write (units x splits x rows x (c + 2) fp32,
+    and the partials the kernels write (units x splits x rows x ({m, l} fp32 + c bf16),
     units = groups of at most 64 sequences) fit the workspace the call needs.
     Visible counts sweep 0 .. 300k with the neighbourhoods of the split-count
     steps (multiples of 256 and 4096) in full."""
@@ -339,7 +339,7 @@ def test_attention_workspace_plan_sweep(L, dense):
                             assert max(-(-x // pl.split_slots) for x in slots) <= pl.splits
                             units = min(B, 64) * -(-nq // pl.queries_per_block)
                             rows = pl.queries_per_block * nh
-                            assert units * pl.splits * rows * (c + 2) * 4 <= pl.workspace_bytes
+                            assert units * pl.splits * rows * (8 + 2 * c) <= pl.workspace_bytes
                         else:
                             assert pl.workspace_bytes == 0
                         checked += 1
