@@ -454,6 +454,7 @@ DENSE_CASES = [
     ("bf16", ROW_FP8, 1, 13, 16, 512, 150, 128, 64, [19000], True),          # c = 512, 4 queries per block, ragged
     ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 128, [1 << 16, 30000], True), # decode: split + combine
     ("bf16", ROW_FP8, 1, 8, 64, 512, 10, 128, 128, [50], True),              # no entry visible yet: window only
+    ("bf16", ROW_FP8, 2, 1, 64, 512, 700, 128, 0, [1 << 16, 50], True),     # split launch, second sequence keyless
     ("bf16", ROW_BF16, 1, 37, 32, 128, 10, 16, 0, [100], False),             # 2 queries per block, no window
     # HCA decode with 3965 visible entries, in the workspace the call needs exactly (the visible counts where
     # the split plan of the size query, the argument check and the launch once disagreed)
