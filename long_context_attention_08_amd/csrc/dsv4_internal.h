@@ -110,15 +110,10 @@ IndexerGrid indexer_grid(const IndexerArgs& a, int nb);
 // ---- top-k planning (plan.cpp; host only)
 constexpr int SK_KMAX = 1024;     // largest k of the streaming and histogram selects
 constexpr int HS_BIN = 2048;      // histogram bins of the histogram select (11-bit digits)
+constexpr int HS_COARSE = 64;     // every 32nd bin's suffix count, stored again after a part's bins
+constexpr int HS_SUF = HS_BIN + HS_COARSE;   // words per part of the suffix counts
 constexpr int HS_CAP = 8192;      // threshold-bin candidates of the histogram select
 constexpr int TK_MAX_CAND = 16384;   // part winners a stage-2 merge holds in LDS
-
-struct HsMeta {
-  int bstar;         // threshold bin (-1: every visible score is taken)
-  uint32_t above;    // visible keys in bins above bstar (all winners)
-  uint32_t inbin;    // visible keys in bin bstar
-  uint32_t need;     // min(k, visible)
-};
 
 enum { TOPK_STREAM = 0, TOPK_STAGE = 1, TOPK_HIST = 2 };
 struct TopkPlan {
@@ -127,7 +122,7 @@ struct TopkPlan {
   bool supported;
   size_t bytes;      // workspace the launch uses
   // histogram select: byte offsets of its workspace arrays
-  size_t o_suf, o_off, o_meta, o_win, o_cand;
+  size_t o_suf, o_meta, o_win, o_cand;
 };
 // plan for `rows` rows (of one launch: at most MAXB batch entries) of S scores
 TopkPlan topk_make_plan(int64_t rows, int64_t S, int k);

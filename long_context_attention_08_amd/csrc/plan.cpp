@@ -64,9 +64,8 @@ TopkPlan topk_make_plan(int64_t rows, int64_t S, int k) {
     t.supported = true;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t o = 0;
-    t.o_suf = o; o = al(o + (size_t)rows * t.nparts * HS_BIN * 4);
-    t.o_off = o; o = al(o + (size_t)rows * t.nparts * 2 * 4);
-    t.o_meta = o; o = al(o + (size_t)rows * sizeof(HsMeta));
+    t.o_suf = o; o = al(o + (size_t)rows * t.nparts * HS_SUF * 4);
+    t.o_meta = o; o = al(o + (size_t)rows * 16);   // per-row threshold bin and counts
     t.o_win = o; o = al(o + (size_t)rows * k * 8);
     t.o_cand = o; o = al(o + (size_t)rows * HS_CAP * 8);
     t.bytes = o;

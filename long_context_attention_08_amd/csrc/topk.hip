@@ -174,9 +174,8 @@ struct TopkArgs {
   int32_t* idx;      // [rows, k]
   uint64_t* cand;    // [rows, nparts, k] (nparts > 1)
   // histogram select (few long rows)
-  uint32_t* hsuf;    // [rows, nparts, HS_BIN] suffix counts per part
-  uint32_t* hoff;    // [rows, nparts, 2] write offsets (winners, bin candidates)
-  HsMeta* hmeta;     // [rows]
+  uint32_t* hsuf;    // [rows, nparts, HS_SUF] suffix counts per part: HS_BIN bins, then every 32nd again
+  void* hmeta;       // [rows] HsMeta of the row (threshold bin and counts), 16 bytes each
   uint64_t* hwin;    // [rows, k] winners above the threshold bin
   uint64_t* hcand;   // [rows, HS_CAP] keys of the threshold bin
   const int* flags;  // [rows] or null: rows with a zero flag are skipped
@@ -666,20 +665,33 @@ __global__ __launch_bounds__(SK_NT) void topk_stream(TopkArgs a, PosTable pt, in
 
 // ------------------------------------------------------------------ histogram select (few long rows, k <= 1024)
 // Decode has a handful of rows of 2^18 scores.  Each row is cut into parts and
-// processed in four launches, each a plain pass:
+// processed in two launches:
 //   1. per part: a 2048-bin histogram of the top 11 key bits, stored as suffix
-//      counts (keys at or above each bin);
-//   2. per row: the threshold bin b* (the highest bin whose suffix count
-//      reaches min(k, visible)), how many keys lie above it and in it, and
-//      every part's write offsets into the winner and candidate lists;
-//   3. per part: keys above b* go to the winner list, keys in b* to the
-//      candidate list, as composites;
-//   4. per row: the candidates are cut to the missing count by the exact
-//      radix select, and the k winners are bitonic-sorted.  When b* holds more
-//      keys than the candidate list (heavy ties), the select runs over the row
-//      in global memory instead.
-// The selected set is the same exact set as on every other path.
+//      counts (keys at or above each bin), every 32nd of them once more in a
+//      short coarse array;
+//   2. per part: the threshold bin b* (the highest bin whose suffix count over
+//      all parts reaches min(k, visible)), found from the coarse counts and
+//      then the 32 bins of the coarse step that holds it; the part's write
+//      offsets from every part's counts above and in b*; keys above b* go to
+//      the winner list, keys in b* to the candidate list, as composites;
+//   3. per row: the candidates are cut to the missing count by the exact
+//      radix select, and the k winners are put in order.  When b* holds more
+//      keys than the candidate list (heavy ties), the select runs over the
+//      row in global memory instead.
+// The selected set is the same exact set as on every other path.  (Finishing
+// a row in the part that completes a count instead of a third launch needs a
+// device-scope release per part, whose L2 write-back doubled the decode time.)
 constexpr int HS_PER = HS_BIN / SK_NT;     // bins per thread
+static_assert(HS_PER == 8 && HS_COARSE * 32 == HS_BIN, "a coarse count every 32 bins, 4 per 32 threads");
+constexpr int HS_MAXPARTS = 64;            // parts per row (the plan's bound)
+
+struct HsMeta {
+  int bstar;         // threshold bin (-1: every visible score is taken)
+  uint32_t above;    // visible keys in bins above bstar (all winners)
+  uint32_t inbin;    // visible keys in bin bstar
+  uint32_t need;     // min(k, visible)
+};
+static_assert(sizeof(HsMeta) == 16, "the plan keeps 16 bytes per row");
 
 __device__ __forceinline__ int64_t hs_row(const TopkArgs& a, const PosTable& pt, int b0, int64_t row,
                                           int64_t* nv) {
@@ -720,109 +732,16 @@ __global__ __launch_bounds__(SK_NT) void topk_h_hist(TopkArgs a, PosTable pt, in
   uint32_t total;
   const uint32_t before = sk_scan_excl(loc, wsum, &total);
   uint32_t acc = total - before - loc;       // keys in the bins above this thread's range
-  uint32_t* dst = a.hsuf + (row * a.nparts + p) * HS_BIN + HS_PER * threadIdx.x;
+  uint32_t* dst = a.hsuf + (row * a.nparts + p) * HS_SUF;
 #pragma unroll
   for (int q = HS_PER - 1; q >= 0; --q) {
     acc += c[q];
-    dst[q] = acc;
+    dst[HS_PER * threadIdx.x + q] = acc;
   }
+  if ((threadIdx.x & 3) == 0) dst[HS_BIN + (threadIdx.x >> 2)] = acc;   // bin 32 j = HS_PER * 4 j
 }
 
-__global__ __launch_bounds__(SK_NT) void topk_h_thresh(TopkArgs a, PosTable pt, int b0) {
-  __shared__ uint32_t wsum[SK_NT / 64];
-  __shared__ int s_b;
-  __shared__ uint32_t s_t0[SK_NT + 1];
-  static_assert(HS_PER == 8, "two 16-byte loads per part and thread");
-  const int64_t row = blockIdx.x;
-  if (row_skipped(a, row)) return;
-  int64_t nv;
-  hs_row(a, pt, b0, row, &nv);
-  const uint32_t need = (uint32_t)(nv < a.k ? nv : a.k);
-  const uint32_t* suf = a.hsuf + row * a.nparts * HS_BIN;
-  const bool cut = need < (uint64_t)nv;
-  // total suffix counts of this thread's 8 bins over all parts (loads in flight together)
-  uint32_t tot[HS_PER];
-#pragma unroll
-  for (int q = 0; q < HS_PER; ++q) tot[q] = 0;
-  if (cut) {
-    const u32x4* sp = reinterpret_cast<const u32x4*>(suf) + 2 * threadIdx.x;
-#pragma unroll 8
-    for (int pp = 0; pp < a.nparts; ++pp) {
-      const u32x4 x0 = sp[pp * (HS_BIN / 4)], x1 = sp[pp * (HS_BIN / 4) + 1];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { tot[q] += x0[q]; tot[4 + q] += x1[q]; }
-    }
-  }
-  s_t0[threadIdx.x] = tot[0];
-  if (threadIdx.x == 0) { s_t0[SK_NT] = 0; s_b = -1; }
-  __syncthreads();
-  if (cut) {
-    // exactly one bin has suffix >= need while the next one up has less
-    const uint32_t nxt = s_t0[threadIdx.x + 1];
-#pragma unroll
-    for (int q = 0; q < HS_PER; ++q) {
-      const uint32_t up = q + 1 < HS_PER ? tot[q + 1] : nxt;
-      if (tot[q] >= need && up < need) s_b = HS_PER * threadIdx.x + q;
-    }
-  }
-  __syncthreads();
-  const int bstar = s_b;
-  uint32_t ca = 0, cb = 0;
-  if ((int)threadIdx.x < a.nparts) {
-    const uint32_t* sp = suf + threadIdx.x * HS_BIN;
-    ca = bstar + 1 < HS_BIN ? sp[bstar + 1] : 0u;
-    cb = bstar >= 0 ? sp[bstar] - ca : 0u;
-  }
-  uint32_t ta, tb;
-  const uint32_t ea = sk_scan_excl(ca, wsum, &ta);
-  const uint32_t eb = sk_scan_excl(cb, wsum, &tb);
-  if ((int)threadIdx.x < a.nparts) {
-    a.hoff[(row * a.nparts + threadIdx.x) * 2] = ea;
-    a.hoff[(row * a.nparts + threadIdx.x) * 2 + 1] = eb;
-  }
-  if (threadIdx.x == 0) a.hmeta[row] = HsMeta{bstar, ta, tb, need};
-}
-
-__global__ __launch_bounds__(SK_NT) void topk_h_compact(TopkArgs a, PosTable pt, int b0) {
-  __shared__ uint32_t na, nb;
-  const int64_t row = blockIdx.y;
-  if (row_skipped(a, row)) return;
-  const int p = blockIdx.x;
-  int64_t nv;
-  const int64_t grow = hs_row(a, pt, b0, row, &nv);
-  const HsMeta mt = a.hmeta[row];
-  if (mt.need == 0) return;
-  const uint32_t offa = a.hoff[(row * a.nparts + p) * 2], offb = a.hoff[(row * a.nparts + p) * 2 + 1];
-  if (threadIdx.x == 0) { na = 0; nb = 0; }
-  __syncthreads();
-  const int64_t s0 = (int64_t)p * a.part, s1 = s0 + a.part < nv ? s0 + a.part : nv;
-  const float* src = a.scores + grow * a.S;
-  uint64_t* win = a.hwin + row * a.k;
-  uint64_t* cand = a.hcand + row * HS_CAP;
-  for (int64_t base = s0; base < s1; base += 8 * SK_NT) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t s = base + u * SK_NT + threadIdx.x;
-      x[u] = src[s < s1 ? s : s1 - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t s = base + u * SK_NT + threadIdx.x;
-      if (s >= s1) continue;
-      const uint32_t key = score_key(x[u]);
-      const int bin = (int)(key >> 21);
-      if (bin > mt.bstar) {
-        win[offa + atomicAdd(&na, 1u)] = composite(key, (uint32_t)s);
-      } else if (bin == mt.bstar) {
-        const uint32_t at = offb + atomicAdd(&nb, 1u);
-        if (at < (uint32_t)HS_CAP) cand[at] = composite(key, (uint32_t)s);
-      }
-    }
-  }
-}
-
-// global -> LDS copy of n composites, eight loads in flight per thread
+// global -> LDS copy of n composites, eight loads in flight per thread// global -> LDS copy of n composites, eight loads in flight per thread
 __device__ __forceinline__ void hs_copy(uint64_t* dst, const uint64_t* src, uint32_t n) {
   for (uint32_t base = 0; base < n; base += 8 * SK_NT) {
     uint64_t x[8];
@@ -931,16 +850,11 @@ __device__ bool rank_by_bins(SkSharedT<CAP>& sh, uint32_t* maxc_sh, const uint64
   return true;
 }
 
-// dynamic LDS: sizeof(HsShared)
-__global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  HsShared& sh = *reinterpret_cast<HsShared*>(smem);
-  __shared__ uint32_t s_maxc;
-  const int64_t row = blockIdx.x;
-  if (row_skipped(a, row)) return;
-  int64_t nv;
-  const int64_t grow = hs_row(a, pt, b0, row, &nv);
-  const HsMeta mt = a.hmeta[row];
+// The last step of a row: the `above` winners listed above the threshold bin
+// plus the needed keys of the bin, in order, into the row's indices (block-wide)
+__device__ void hs_finish(const TopkArgs& a, int64_t row, int64_t grow, int64_t nv, const HsMeta& mt, HsShared& sh,
+                          uint32_t* maxc_sh) {
+  uint32_t& s_maxc = *maxc_sh;
   const uint32_t need = mt.need, nab = mt.above;
   const uint32_t needb = need - nab;                 // to take from bin b*
   const bool spill = mt.inbin > (uint32_t)HS_CAP;
@@ -1038,6 +952,134 @@ __global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, 
   for (int i = threadIdx.x; i < a.k; i += SK_NT) dst[i] = i < (int)need ? (int32_t)(~(uint32_t)sh.out[i]) : -1;
 }
 
+__global__ __launch_bounds__(SK_NT) void topk_h_cut(TopkArgs a, PosTable pt, int b0) {
+  __shared__ uint32_t s_part[SK_NT];
+  __shared__ uint32_t s_tot[HS_COARSE];
+  __shared__ uint32_t wsum[SK_NT / 64];
+  __shared__ int s_j, s_b;
+  __shared__ uint32_t s_offa, s_offb, na, nb;
+  const int64_t row = blockIdx.y;
+  if (row_skipped(a, row)) return;
+  const int p = blockIdx.x;
+  const int t = threadIdx.x;
+  int64_t nv;
+  const int64_t grow = hs_row(a, pt, b0, row, &nv);
+  const uint32_t need = (uint32_t)(nv < a.k ? nv : a.k);
+  const bool cut = need < (uint64_t)nv;
+  const uint32_t* suf = a.hsuf + row * a.nparts * HS_SUF;
+  const int64_t s0 = (int64_t)p * a.part, s1 = s0 + a.part < nv ? s0 + a.part : nv;
+  const float* src = a.scores + grow * a.S;
+  // threshold bin: the highest bin whose suffix count over the parts reaches
+  // `need` (suffix counts do not increase with the bin); none when every
+  // visible key is taken
+  if (t == 0) { s_j = 0; s_b = -1; }
+  if (cut) {
+    {   // coarse counts: thread g * 64 + j adds count j of parts g, g + 4, ... (all loads in flight)
+      const int j = t & (HS_COARSE - 1), g = t / HS_COARSE;
+      constexpr int NPC = HS_MAXPARTS / (SK_NT / HS_COARSE);
+      uint32_t v[NPC];
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) {
+        const int pp = g + i * (SK_NT / HS_COARSE);
+        v[i] = pp < a.nparts ? suf[pp * HS_SUF + HS_BIN + j] : 0u;
+      }
+      uint32_t sum = 0;
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) sum += v[i];
+      s_part[t] = sum;
+    }
+    __syncthreads();
+    if (t < HS_COARSE) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int g = 0; g < SK_NT / HS_COARSE; ++g) tot += s_part[g * HS_COARSE + t];
+      s_tot[t] = tot;
+    }
+    __syncthreads();
+    if (t < HS_COARSE && s_tot[t] >= need && (t + 1 == HS_COARSE || s_tot[t + 1] < need)) s_j = t;
+    __syncthreads();
+    const int jc = s_j;
+    {   // the 32 bins of coarse step jc: thread g * 32 + i adds bin 32 jc + i of parts g, g + 8, ...
+      const int i = t & 31, g = t >> 5;
+      constexpr int NPF = HS_MAXPARTS / (SK_NT / 32);
+      uint32_t v[NPF];
+#pragma unroll
+      for (int q = 0; q < NPF; ++q) {
+        const int pp = g + q * (SK_NT / 32);
+        v[q] = pp < a.nparts ? suf[pp * HS_SUF + 32 * jc + i] : 0u;
+      }
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < NPF; ++q) sum += v[q];
+      s_part[t] = sum;
+    }
+    __syncthreads();
+    if (t < 32) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int g = 0; g < SK_NT / 32; ++g) tot += s_part[g * 32 + t];
+      s_tot[t] = tot;                      // bins 32 jc .. 32 jc + 31 (coarse counts no longer needed)
+    }
+    __syncthreads();
+    // the bin after 32 jc + 31 is the next coarse step, below need by the choice of jc
+    if (t < 32 && s_tot[t] >= need && (t == 31 || s_tot[t + 1] < need)) s_b = 32 * jc + t;
+  }
+  __syncthreads();
+  const int bstar = s_b;
+  // every part's keys above and in b*; this part's write offsets
+  uint32_t ca = 0, cb = 0;
+  if (t < a.nparts) {
+    const uint32_t* sp = suf + t * HS_SUF;
+    ca = bstar + 1 < HS_BIN ? sp[bstar + 1] : 0u;
+    cb = bstar >= 0 ? sp[bstar] - ca : 0u;
+  }
+  uint32_t ta, tb;
+  const uint32_t ea = sk_scan_excl(ca, wsum, &ta);
+  const uint32_t eb = sk_scan_excl(cb, wsum, &tb);
+  if (t == p) { s_offa = ea; s_offb = eb; }
+  if (p == 0 && t == 0) reinterpret_cast<HsMeta*>(a.hmeta)[row] = HsMeta{bstar, ta, tb, need};
+  if (t == 0) { na = 0; nb = 0; }
+  __syncthreads();
+  if (need > 0) {
+    const uint32_t offa = s_offa, offb = s_offb;
+    uint64_t* win = a.hwin + row * a.k;
+    uint64_t* cand = a.hcand + row * HS_CAP;
+    auto place = [&](float x, int64_t s) {
+      if (s >= s1) return;
+      const uint32_t key = score_key(x);
+      const int bin = (int)(key >> 21);
+      if (bin > bstar) {
+        win[offa + atomicAdd(&na, 1u)] = composite(key, (uint32_t)s);
+      } else if (bin == bstar) {
+        const uint32_t at = offb + atomicAdd(&nb, 1u);
+        if (at < (uint32_t)HS_CAP) cand[at] = composite(key, (uint32_t)s);
+      }
+    };
+    for (int64_t base = s0; base < s1; base += 8 * SK_NT) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t s = base + u * SK_NT + t;
+        x[u] = src[s < s1 ? s : s1 - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) place(x[u], base + u * SK_NT + t);
+    }
+  }
+}
+
+// dynamic LDS: sizeof(HsShared)
+__global__ __launch_bounds__(SK_NT) void topk_h_finish(TopkArgs a, PosTable pt, int b0) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  HsShared& sh = *reinterpret_cast<HsShared*>(smem);
+  __shared__ uint32_t s_maxc;
+  const int64_t row = blockIdx.x;
+  if (row_skipped(a, row)) return;
+  int64_t nv;
+  const int64_t grow = hs_row(a, pt, b0, row, &nv);
+  hs_finish(a, row, grow, nv, reinterpret_cast<const HsMeta*>(a.hmeta)[row], sh, &s_maxc);
+}
+
 hipError_t launch_topk(const float* scores, int64_t B, int64_t nq, int64_t S, int m,
                        const int64_t* q_pos0, int k, int32_t* idx, void* ws, const TopkPlan& plan, hipStream_t s) {
   return launch_topk_rows(scores, B, nq, S, m, q_pos0, k, idx, ws, plan, nullptr, s);
@@ -1054,10 +1096,10 @@ hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t 
   a.part = plan.part;
   a.nparts = plan.nparts;
   if (plan.kind == TOPK_HIST) {
+    if (plan.nparts > HS_MAXPARTS || plan.nparts > SK_NT) return hipErrorInvalidValue;   // the cut pass's bound
     uint8_t* w = reinterpret_cast<uint8_t*>(ws);
     a.hsuf = reinterpret_cast<uint32_t*>(w + plan.o_suf);
-    a.hoff = reinterpret_cast<uint32_t*>(w + plan.o_off);
-    a.hmeta = reinterpret_cast<HsMeta*>(w + plan.o_meta);
+    a.hmeta = w + plan.o_meta;
     a.hwin = reinterpret_cast<uint64_t*>(w + plan.o_win);
     a.hcand = reinterpret_cast<uint64_t*>(w + plan.o_cand);
     hipError_t e = hipFuncSetAttribute((const void*)topk_h_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1069,8 +1111,7 @@ hipError_t launch_topk_rows(const float* scores, int64_t B, int64_t nq, int64_t 
       for (int i = 0; i < nb; ++i) { pt.q_pos0[i] = q_pos0[b0 + i]; pt.win_pos0[i] = 0; }
       const unsigned rows = (unsigned)(nb * nq);
       hipLaunchKernelGGL(topk_h_hist, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
-      hipLaunchKernelGGL(topk_h_thresh, dim3(rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
-      hipLaunchKernelGGL(topk_h_compact, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
+      hipLaunchKernelGGL(topk_h_cut, dim3((unsigned)a.nparts, rows), dim3(SK_NT), 0, s, a, pt, (int)b0);
       hipLaunchKernelGGL(topk_h_finish, dim3(rows), dim3(SK_NT), sizeof(HsShared), s, a, pt, (int)b0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
