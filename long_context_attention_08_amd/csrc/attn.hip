@@ -1180,14 +1180,17 @@ __global__ __launch_bounds__(128 * NRG, 2) void attn_f8(AttnArgs a, PosTable pt,
   } else {
     const int64_t unit = blockIdx.x;
     const int64_t rows = Cf::R;
+    // the unit's partial rows in fragment order (f8_frag_elem): each store is
+    // 64 lanes x 8 contiguous bytes
     const PartialRow pr = partial_row(a, pl, gridDim.x, unit, split, rows, row, C);
+    uint16_t* ob = pr.o - (int64_t)row * C;
     if (G == 0 && ch == 0) { pr.ml[0] = m_run; pr.ml[1] = l_run; }
 #pragma unroll
     for (int mo = 0; mo < MO; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        store_partial4(pr.o + f8_chan(mo) + 8 * j + 4 * G, acc[mo][4 * j], acc[mo][4 * j + 1], acc[mo][4 * j + 2],
-                       acc[mo][4 * j + 3]);
+        store_partial4(ob + 4 * (((wv * MO + mo) * 4 + j) * 64 + l), acc[mo][4 * j], acc[mo][4 * j + 1],
+                       acc[mo][4 * j + 2], acc[mo][4 * j + 3]);
   }
 }
 
@@ -1574,6 +1577,93 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, PosTable pt, int
   }
 }
 
+// attn_f8's split partials are stored in fragment order: 8-byte element
+// e = ((w * 8 + mo) * 4 + j) * 64 + l of a (unit, split) holds the 4 channels
+// that lane l of wave w kept in register group j of m-tile mo, that is
+// channels f8_chan(mo) + 8 j + 4 (l / 32) .. + 3 of row 32 (w / 2) + l % 32,
+// f8_chan(mo) = 224 ch + 32 mo (mo < 7) or 448 + 32 ch, ch = w % 2.
+struct F8Elem {
+  int row, chan;
+};
+__device__ __forceinline__ F8Elem f8_frag_elem(int e) {
+  const int w = e >> 11, mo = (e >> 8) & 7, j = (e >> 6) & 3, l = e & 63;
+  const int ch = w & 1;
+  return {32 * (w >> 1) + (l & 31), (mo < 7 ? 224 * ch + 32 * mo : 448 + 32 * ch) + 8 * j + 4 * (l >> 5)};
+}
+
+// Merge of attn_f8's split partials (c = 512), splits in increasing order
+// (deterministic): a thread takes one fragment element (4 channels of one
+// row) of every split, all loads issued before the merge.
+__global__ __launch_bounds__(256) void attn_combine_f8(AttnArgs a, PosTable pt, int b0, AttnPlan pl) {
+  constexpr int C = 512;
+  const int64_t unit = blockIdx.x;
+  const int64_t bl = unit / pl.units_per_b, u = unit % pl.units_per_b;
+  const int64_t b = b0 + bl;
+  const UnitInfo ui = unit_info(a, pl, pt.q_pos0[bl], u);
+  const int64_t nsplit = (ui.total + pl.chunk - 1) / pl.chunk;   // <= ATTN_MAX_SPLITS by the plan
+  const int64_t rows = (int64_t)pl.qpw * a.nh;
+  const int e = (int)blockIdx.y * 256 + (int)threadIdx.x;
+  if (e >= rows * (C / 4)) return;
+  const F8Elem fe = f8_frag_elem(e);
+  const int qw = fe.row / a.nh, h = fe.row % a.nh;
+  const int64_t t = ui.t0 + qw;
+  if (t > ui.tl) return;
+  const PartialRow pr = partial_row(a, pl, gridDim.x, unit, 0, rows, fe.row, C);
+  const float* ml = pr.ml;                                        // split s at + 2 s rows
+  const uint16_t* ob = pr.o - (int64_t)fe.row * C + 4 * e;        // split s at + s rows C
+  constexpr int MS = ATTN_MAX_SPLITS;
+  float mv[MS], lv[MS];
+  u32x2 ov[MS];
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) {
+    mv[sp] = -INFINITY;
+    lv[sp] = 0.f;
+    ov[sp] = (u32x2){0u, 0u};
+    if (sp < nsplit) {
+      mv[sp] = ml[sp * rows * 2];
+      lv[sp] = ml[sp * rows * 2 + 1];
+      ov[sp] = *reinterpret_cast<const u32x2*>(ob + sp * rows * (int64_t)C);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) M = fmaxf(M, mv[sp]);
+  const float z = a.sink ? a.sink[h] * LOG2E : -INFINITY;
+  const float Mt = fmaxf(M, z);
+  float den = a.sink ? exp2f(z - Mt) : 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) {
+    if (sp >= nsplit) break;
+    // a split that saw no visible key (m = -inf, zero partial) gets weight 0
+    const float w = mv[sp] == -INFINITY ? 0.f : exp2f(mv[sp] - Mt);
+    den = fmaf(lv[sp], w, den);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      o[2 * q] = fmaf(bf16_to_f32(ov[sp][q] & 0xFFFFu), w, o[2 * q]);
+      o[2 * q + 1] = fmaf(bf16_to_f32(ov[sp][q] >> 16), w, o[2 * q + 1]);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((b * a.nq + t) * a.nh + h) * C + fe.chan;
+  const int R = a.rot_dims;
+  if (R > 0 && fe.chan >= C - R) {
+    float x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = bf16_round(o[q] * inv);
+#pragma unroll
+    for (int q = 0; q < 4; q += 2) {
+      float cs, sn;
+      rope_cs(-(pt.q_pos0[bl] + t), (fe.chan + q - (C - R)) >> 1, R, a.rot_theta, &cs, &sn);
+      rope_pair(x[q], x[q + 1], cs, sn);
+    }
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  } else {
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){__builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(o[0] * inv), (__bf16)(o[1] * inv)}),
+                                            __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)(o[2] * inv), (__bf16)(o[3] * inv)})};
+  }
+}
+
 // ------------------------------------------------------------------ launch
 // The plan (path, rows per block, split) comes from attn_make_plan, the same
 // function the argument checks sized the workspace with.
@@ -1615,9 +1705,13 @@ hipError_t launch_attn(const AttnArgs& a, const int64_t* q_pos0, const int64_t* 
       if (e != hipSuccess) return e;
       if (pl.max_splits > 1) {
         const int rows = pl.qpw * a.nh;
-        const dim3 cg((unsigned)(nb * pl.units_per_b), (unsigned)((rows + 3) / 4));
-        if (a.c == 512) hipLaunchKernelGGL(attn_combine<8>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
-        else hipLaunchKernelGGL(attn_combine<2>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
+        if (lp.path == ATTN_F8) {        // fragment-order partials: one thread per 4 channels of a row
+          const dim3 cg((unsigned)(nb * pl.units_per_b), (unsigned)((rows * 128 + 255) / 256));
+          hipLaunchKernelGGL(attn_combine_f8, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
+        } else {
+          const dim3 cg((unsigned)(nb * pl.units_per_b), (unsigned)((rows + 3) / 4));
+          hipLaunchKernelGGL(attn_combine<2>, cg, dim3(256), 0, s, a, pt, (int)b0, pl);
+        }
       }
     } else {
       hipLaunchKernelGGL(attn_generic, dim3((unsigned)(nb * a.nq * a.nh)), dim3(256), 0, s, a, pt, (int)b0, pl);
