@@ -860,6 +860,14 @@ __device__ void hs_finish(const TopkArgs& a, int64_t row, int64_t grow, int64_t 
   const bool spill = mt.inbin > (uint32_t)HS_CAP;
   const float* src = a.scores + grow * a.S;
   const uint64_t pre = (uint64_t)(uint32_t)mt.bstar << 53;   // composites of bin b* start with it
+  // the winners above b* (nab < k <= SK_KMAX) are loaded now, in flight during the select
+  constexpr int WPT = SK_KMAX / SK_NT;
+  uint64_t wv[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t i = threadIdx.x + j * SK_NT;
+    wv[j] = i < nab ? a.hwin[row * a.k + i] : 0ull;
+  }
   uint64_t T = ~0ull;
   if (needb > 0 && !spill) {
     hs_copy(sh.cand, a.hcand + row * HS_CAP, mt.inbin);
@@ -910,7 +918,11 @@ __device__ void hs_finish(const TopkArgs& a, int64_t row, int64_t grow, int64_t 
   __syncthreads();
   // winners: the list above b*, then the bin's keys >= T
   if (threadIdx.x == 0) sh.cnt2 = 0;
-  hs_copy(sh.out, a.hwin + row * a.k, nab);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t i = threadIdx.x + j * SK_NT;
+    if (i < nab) sh.out[i] = wv[j];
+  }
   __syncthreads();
   if (needb > 0 && !spill) {
     for (uint32_t i = threadIdx.x; i < mt.inbin; i += SK_NT) {
