@@ -288,14 +288,14 @@ AttnLaunchPlan attn_make_plan(const AttnArgs& a, bool dense, int64_t slots) {
   // split the keys only when a sequence has few query groups.  The split size
   // depends on the key bound alone (never on the batch), so a sequence's
   // results do not depend on the batch.  The split count comes first and is
-  // non-decreasing in the bound: up to 16 splits of at least 128 slots (a
-  // decode query's 1152 sparse slots take 9 blocks), each split's bf16
+  // non-decreasing in the bound: up to 16 splits of at least 96 slots (a
+  // decode query's 1152 sparse slots take 12 blocks of 3 key tiles), each split's bf16
   // partial (rows x c) small next to the rows it reads
   if (pl.units_per_b >= 32 || slots <= 0) {
     pl.chunk = 1 << 30;
     pl.max_splits = 1;
   } else {
-    int64_t ms = (slots + 127) / 128;
+    int64_t ms = (slots + 95) / 96;
     ms = ms < 1 ? 1 : (ms > ATTN_MAX_SPLITS ? ATTN_MAX_SPLITS : ms);
     const int64_t per = (slots + ms - 1) / ms;
     pl.chunk = (int)((per + 31) / 32 * 32);
